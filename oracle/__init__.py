@@ -1,0 +1,11 @@
+"""CPU oracle (float64 NumPy) for paged decode attention and the cache write.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, the smoke check and the
+benchmark's CPU-baseline leg, never by the library or its Python binding.
+It shares no code with the HIP path.  Every function is pinned by CPU tests
+(brute force, closed forms, invariants, a library routine, the pages'
+page-table figure); no function is "parity unpinned".
+"""
+from .paged_attention import decode, gather_pages, reshape_and_cache, widen
+
+__all__ = ["decode", "gather_pages", "reshape_and_cache", "widen"]

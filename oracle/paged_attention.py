@@ -1,0 +1,157 @@
+"""CPU oracle for paged decode attention and the KV-cache write.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this module;
+only the tests, the smoke check and the benchmark's CPU-baseline leg call it.
+It shares no code with the HIP library: no kernels, headers, helpers or
+constants.  It is plain, slow and written to be checked by eye.
+
+What it computes (vLLM / PagedAttention pages):
+
+* The showapi.com article, section 2.1, and the tutorial page, chapter 4.2,
+  say that paging changes only *where* the KV cache lives: the cache is cut
+  into fixed-size pages, a per-request page table maps logical pages to
+  physical pages, and the attention kernel reads the pages through that table
+  with no data movement and no padding.  So decode attention over a paged
+  cache is ordinary single-query softmax attention over the sequence's tokens
+  in logical order; the only paged part is the gather.  ``decode`` walks each
+  sequence's logical pages in order, looks each up in the block table, reads
+  that page's tokens, and then applies softmax(q . K^T * scale) . V per head.
+* The tutorial page, chapter 4.3 (step 3 of the iteration), says each forward
+  step yields the next token together with the updated KV cache.
+  ``reshape_and_cache`` is that update: every new token's K and V rows go to
+  the pool slot named by its slot number, ``slot = physical_page * block_size
+  + offset``.
+
+Readings where the pages are silent (the attention formula, the scale, the
+GQA head map, the pool layout, ctx == 0, duplicate slots) are stated at each
+function.  Arithmetic is float64; bf16 inputs are widened exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["widen", "gather_pages", "decode", "reshape_and_cache"]
+
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of stored values to float64.
+
+    ``dtype == "bf16"``: ``x`` holds raw 16-bit patterns; a bfloat16 is the
+    top half of an IEEE binary32, so placing the 16 bits in the high half of a
+    32-bit word gives the same value as a float32, which widens exactly.
+    ``dtype == "f32"``: float32 widens exactly.
+    """
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+def gather_pages(pool: np.ndarray, table_row: np.ndarray, ctx: int,
+                 block_size: int) -> np.ndarray:
+    """Tokens 0..ctx-1 of one sequence, in logical order, as [Hkv, ctx, D].
+
+    Logical page j of the sequence is physical page ``table_row[j]``; token t
+    lives in logical page t // block_size at offset t % block_size (pages fill
+    in token order: the page table keeps the logical view contiguous while the
+    physical pages are scattered, tutorial page 4.2).  Only the first
+    ceil(ctx / block_size) table entries are read.
+    """
+    num_blocks, hkv, bs, d = pool.shape
+    assert bs == block_size
+    pieces = []
+    npages = (ctx + block_size - 1) // block_size
+    for j in range(npages):
+        phys = int(table_row[j])
+        if not 0 <= phys < num_blocks:
+            raise IndexError(f"logical page {j} maps to physical page {phys}, "
+                             f"outside the pool of {num_blocks}")
+        n = min(block_size, ctx - j * block_size)
+        pieces.append(pool[phys, :, :n, :])
+    if not pieces:
+        return np.zeros((hkv, 0, d), dtype=pool.dtype)
+    return np.concatenate(pieces, axis=1)
+
+
+def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+           block_tables: np.ndarray, context_lens: np.ndarray,
+           num_kv_heads: int, scale, block_size: int, dtype: str,
+           return_lse: bool = False):
+    """Single-token decode attention over a paged KV cache, in float64.
+
+    q            [S, H, D]          stored values (float32, or bf16 bits)
+    k_pool       [NB, Hkv, bs, D]   same
+    v_pool       [NB, Hkv, bs, D]   same
+    block_tables [S, max_blocks]    int, logical page -> physical page
+    context_lens [S]                tokens attended per sequence
+
+    Readings: out[s, h] = softmax(scale * K q[s, h]) V over the sequence's
+    ctx tokens, with the safe-softmax max subtracted (mathematically the same
+    result).  ``scale`` is used at the exact float32 value the GPU receives.
+    Query head h reads kv-head h // (H / Hkv): consecutive q heads form a
+    group (grouped-query attention).  ctx == 0 gives a zero row (and
+    lse = -inf).  Returns out [S, H, D] float64, and with ``return_lse`` also
+    the log-sum-exp of the scaled logits [S, H].
+    """
+    S, H, D = q.shape
+    if H % num_kv_heads:
+        raise ValueError("H must be a multiple of num_kv_heads")
+    group = H // num_kv_heads
+    sc = float(np.float32(scale))
+    out = np.zeros((S, H, D), dtype=np.float64)
+    lse = np.full((S, H), -np.inf, dtype=np.float64)
+    qf = widen(q, dtype)
+    for s in range(S):
+        L = int(context_lens[s])
+        if L < 0:
+            raise ValueError("negative context length")
+        if L == 0:
+            continue
+        if (L + block_size - 1) // block_size > block_tables.shape[1]:
+            raise ValueError("context longer than the block table")
+        K = widen(gather_pages(k_pool, block_tables[s], L, block_size), dtype)
+        V = widen(gather_pages(v_pool, block_tables[s], L, block_size), dtype)
+        for h in range(H):
+            g = h // group
+            logits = sc * (K[g] @ qf[s, h])              # [L]
+            m = logits.max()
+            p = np.exp(logits - m)
+            z = p.sum()
+            out[s, h] = (p @ V[g]) / z
+            lse[s, h] = m + np.log(z)
+    if return_lse:
+        return out, lse
+    return out
+
+
+def reshape_and_cache(k: np.ndarray, v: np.ndarray, k_pool: np.ndarray,
+                      v_pool: np.ndarray, slot_mapping: np.ndarray,
+                      block_size: int):
+    """Write each new token's K/V rows into its pool slot; returns new pools.
+
+    k, v [T, Hkv, D]; pools [NB, Hkv, bs, D]; slot_mapping [T] int.
+    Token i goes to physical page slot // block_size, offset
+    slot % block_size, for every kv-head.  Readings: a negative slot means
+    "no token" and is skipped; two tokens naming one slot would leave the
+    result order-dependent, so that is rejected, as is a slot outside the
+    pool.  Copies are bit-for-bit (the arrays are never converted).
+    """
+    kp = k_pool.copy()
+    vp = v_pool.copy()
+    nb = kp.shape[0]
+    sl = np.asarray(slot_mapping, dtype=np.int64)
+    used = sl[sl >= 0]
+    if len(np.unique(used)) != len(used):
+        raise ValueError("duplicate slots in one cache write")
+    for i in range(len(sl)):
+        slot = int(sl[i])
+        if slot < 0:
+            continue
+        page, off = divmod(slot, block_size)
+        if page >= nb:
+            raise IndexError(f"slot {slot} outside the pool")
+        kp[page, :, off, :] = k[i]
+        vp[page, :, off, :] = v[i]
+    return kp, vp
