@@ -1,0 +1,165 @@
+/*
+ * libpagedattn -- paged decode attention and the KV-cache write for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed (vLLM / PagedAttention pages):
+ *   - The KV cache is cut into fixed-size pages of 16 or 32 tokens that sit
+ *     anywhere in a physical page pool; a per-sequence page table maps
+ *     logical page j to a physical page, and the attention kernel reads the
+ *     pages through that table with no data movement and no padding
+ *     (showapi.com article, section 2.1; tutorial page, section 4.2 and its
+ *     page-table figure; pinggu.org thread, PagedAttention paragraph).
+ *   - Each decode step produces the next token and the updated KV cache
+ *     (tutorial page, section 4.3, step 3 of the iteration).
+ * The pages give neither the attention formula nor a memory layout; this
+ * library computes, per query head, softmax(q . K^T * scale) . V over the
+ * sequence's context tokens, and fixes the layouts below.
+ *
+ * Layouts (all row-major and contiguous):
+ *   q, out          [num_seqs, num_heads, head_dim]
+ *   k_pool, v_pool  [num_blocks, num_kv_heads, block_size, head_dim]
+ *                   token t of a sequence is at logical page t / block_size,
+ *                   offset t % block_size; one (page, kv-head) is a
+ *                   contiguous block_size * head_dim run of elements
+ *   block_tables    int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens    int32 [num_seqs]
+ *   k, v (new)      [num_tokens, num_kv_heads, head_dim]
+ *   slot_mapping    int64 [num_tokens], slot = physical_page * block_size + offset
+ * Query head h reads kv-head h / (num_heads / num_kv_heads).
+ *
+ * Ownership: every pointer is a device pointer owned by the caller
+ * (including the workspace).  The library allocates nothing, keeps no
+ * handle to caller memory, never synchronises, and launches all work on the
+ * given stream (NULL = the null stream), so calls are stream-ordered and
+ * re-entrant across streams.
+ *
+ * Errors: arguments are validated on the host before any HIP call; a
+ * rejected call returns a nonzero PA_ERR_* code and touches nothing.  A
+ * failed launch returns PA_ERR_HIP.  Faults inside a kernel surface, as with
+ * any HIP call, at the caller's next synchronisation.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  PA_ERR_UNSUPPORTED = 3, /* valid but not built: dtype, head_dim, block_size, group */
+  PA_ERR_ALIGN = 4,       /* a pointer is not 16-byte (tables: 4/8-byte) aligned */
+  PA_ERR_WORKSPACE = 5,   /* split-K workspace missing, too small or misaligned */
+  PA_ERR_HIP = 6          /* the HIP runtime reported a launch error */
+};
+
+enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
+
+/* Shapes and launch context of paged_attention_decode. */
+typedef struct pa_decode_dims {
+  int32_t num_seqs;            /* >= 0; 0 is a no-op */
+  int32_t num_heads;           /* query heads, a multiple of num_kv_heads */
+  int32_t head_dim;            /* 64 or 128 */
+  int32_t max_blocks_per_seq;  /* columns of block_tables, >= 1 */
+  int32_t num_blocks;          /* pages in each pool, >= 1 */
+  int32_t dtype;               /* PA_DTYPE_*: one type for q, out, k_pool, v_pool */
+  int32_t partition_size;      /* tokens per split-K partition; 0 = default (256);
+                                  a multiple of block_size, at most 64 pages */
+  int32_t reserved;            /* must be 0 */
+  void *workspace;             /* fp32 scratch for split-K partials, caller-owned;
+                                  may be NULL when max_blocks_per_seq * block_size
+                                  <= partition_size (no sequence can split) */
+  size_t workspace_bytes;
+  void *stream;                /* hipStream_t */
+  void *timing_events[2];      /* optional hipEvent_t pair (or NULLs): recorded on
+                                  the stream immediately before and after the
+                                  partition kernel, for measuring it alone */
+} pa_decode_dims;
+
+/*
+ * Single-token decode attention over a paged KV cache.
+ *
+ * For sequence s with L = context_lens[s] (clamped to
+ * [0, max_blocks_per_seq * block_size]) and every query head h:
+ *   out[s,h,:] = sum_t w_t V_t,  w = softmax_t(scale * q[s,h,:] . K_t),
+ * over tokens t = 0 .. L-1 read through block_tables[s, t / block_size].
+ * L = 0 writes a zero row.  Block-table columns at or past ceil(L /
+ * block_size) are never read.  Slots past L in the last page are never used
+ * in arithmetic (they may hold anything, NaN included).
+ *
+ * num_kv_heads: kv-heads in the pools; num_heads / num_kv_heads must be
+ *   1, 2, 4 or 8.
+ * scale: the logit scale, typically 1/sqrt(head_dim).
+ * block_size: tokens per page, 16 or 32.
+ *
+ * Sequences longer than partition_size tokens are split into partitions
+ * whose partial (max, sum, weighted V) go to the workspace and are merged by
+ * a log-sum-exp reduce kernel; the result is the same softmax up to fp32
+ * rounding.  Accumulation is fp32; bf16 results are rounded to nearest even.
+ *
+ * Device-side preconditions (not checked on the host, which cannot read
+ * device memory): the first ceil(L / block_size) entries of each used table
+ * row lie in [0, num_blocks).  A page id outside that range is skipped by
+ * the kernel (its tokens drop out of the softmax) instead of being read.
+ */
+int paged_attention_decode(void *out, const void *q, const void *k_pool,
+                           const void *v_pool, const int32_t *block_tables,
+                           const int32_t *context_lens, int32_t num_kv_heads,
+                           float scale, int32_t block_size,
+                           const pa_decode_dims *dims);
+
+/*
+ * Workspace bytes paged_attention_decode needs for these shapes:
+ * num_seqs * num_heads * P * (head_dim + 2) * 4 with
+ * P = ceil(max_blocks_per_seq * block_size / partition_size), or 0 when no
+ * sequence can span more than one partition.  Returns SIZE_MAX when the
+ * shapes are invalid.
+ */
+size_t paged_attention_decode_workspace_bytes(int32_t block_size,
+                                              const pa_decode_dims *dims);
+
+/* Shapes and launch context of reshape_and_cache. */
+typedef struct pa_cache_dims {
+  int32_t num_tokens;   /* >= 0; 0 is a no-op */
+  int32_t num_kv_heads; /* >= 1 */
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t block_size;   /* 16 or 32 */
+  int32_t num_blocks;   /* pages in each pool */
+  int32_t dtype;        /* PA_DTYPE_* of k, v and the pools */
+  void *stream;         /* hipStream_t */
+} pa_cache_dims;
+
+/*
+ * KV-cache write: for each token i with slot = slot_mapping[i] >= 0,
+ *   k_pool[slot / block_size, :, slot % block_size, :] = k[i, :, :]
+ *   v_pool[slot / block_size, :, slot % block_size, :] = v[i, :, :]
+ * bit for bit (no conversion).  A negative slot means "no token" and is
+ * skipped.  A slot at or past num_blocks * block_size is also skipped
+ * rather than written.  Two tokens naming the same slot is a precondition
+ * violation (the surviving value is unspecified).
+ */
+int reshape_and_cache(const void *k, const void *v, void *k_pool, void *v_pool,
+                      const int64_t *slot_mapping, const pa_cache_dims *dims);
+
+/* Static, human-readable text for a status code. */
+const char *pa_status_string(int status);
+
+/*
+ * Measurement kernel: streams `bytes` (a multiple of 16, >= 16) of `buf`
+ * with 16-byte loads and writes one 32-bit checksum per workgroup to
+ * `sink` (at least pa_hbm_read_probe_sink_bytes() bytes).  Gives the
+ * achievable HBM read bandwidth of the device the pools live on.
+ */
+int pa_hbm_read_probe(const void *buf, size_t bytes, void *sink, void *stream);
+size_t pa_hbm_read_probe_sink_bytes(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

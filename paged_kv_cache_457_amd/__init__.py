@@ -1,0 +1,18 @@
+"""libpagedattn: paged decode attention and the KV-cache write on MI355X.
+
+The compute path is the HIP library ``libpagedattn.so`` (C ABI in
+``include/pagedattn.h``); ``binding`` marshals torch tensors to it.  Import
+of the tensor functions is lazy so that ``workloads`` (input generation,
+NumPy only) can be used without torch or a built library.
+"""
+__all__ = [
+    "paged_attention_decode", "reshape_and_cache",
+    "paged_attention_decode_workspace_bytes", "hbm_read_probe", "PagedAttnError",
+]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

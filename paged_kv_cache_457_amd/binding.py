@@ -1,0 +1,164 @@
+"""Torch-tensor front end of libpagedattn (argument marshalling only).
+
+Every function here checks devices, dtypes and contiguity, reads shapes off
+the tensors, passes raw device pointers and torch's current HIP stream to
+the C ABI, and raises on a nonzero status.  All arithmetic runs in the HIP
+kernels; nothing here computes attention or touches tensor contents.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.PA_DTYPE_F32, torch.bfloat16: _lib.PA_DTYPE_BF16}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, rc: int, where: str):
+        self.rc = rc
+        super().__init__(f"{where}: {_lib.status_string(rc)}")
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != _lib.PA_OK:
+        raise PagedAttnError(rc, where)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_ptr(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _event_ptr(ev) -> Optional[int]:
+    """A raw hipEvent_t from a torch.cuda.Event (already recorded once, so
+    that it exists) or an int handle; None for no event."""
+    if ev is None:
+        return None
+    if isinstance(ev, int):
+        return ev
+    handle = getattr(ev, "cuda_event", 0)
+    if not handle:
+        raise ValueError("record a torch.cuda.Event once before passing it as a timing event")
+    return handle
+
+
+def decode_dims(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tensor,
+                partition_size: int = 0) -> _lib.DecodeDims:
+    S, H, D = q.shape
+    d = _lib.DecodeDims()
+    d.num_seqs, d.num_heads, d.head_dim = S, H, D
+    d.max_blocks_per_seq = block_tables.shape[1]
+    d.num_blocks = k_pool.shape[0]
+    d.dtype = _DTYPES[q.dtype]
+    d.partition_size = partition_size
+    return d
+
+
+def paged_attention_decode_workspace_bytes(q: torch.Tensor, k_pool: torch.Tensor,
+                                           block_tables: torch.Tensor,
+                                           partition_size: int = 0) -> int:
+    d = decode_dims(q, k_pool, block_tables, partition_size)
+    n = _lib.load().paged_attention_decode_workspace_bytes(k_pool.shape[2], ctypes.byref(d))
+    if n == _lib.SIZE_MAX:
+        raise ValueError("invalid shapes for paged_attention_decode")
+    return n
+
+
+def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                           v_pool: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, scale: Optional[float] = None,
+                           partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
+                           stream=None, timing_events: Sequence = (None, None)) -> torch.Tensor:
+    """out[S,H,D] <- paged decode attention (see paged_attention_decode in
+    include/pagedattn.h).  Pools are [num_blocks, num_kv_heads, block_size,
+    head_dim]; the kv-head count and block size are read off k_pool.
+    ``scale`` defaults to 1/sqrt(head_dim).  A workspace is allocated here
+    when none is given and the shapes need one."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("out", out), ("k_pool", k_pool), ("v_pool", v_pool)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if k_pool.shape != v_pool.shape or k_pool.dim() != 4:
+        raise ValueError("k_pool and v_pool must both be [num_blocks, num_kv_heads, block_size, head_dim]")
+    S, H, D = q.shape
+    if out.shape != q.shape or k_pool.shape[3] != D:
+        raise ValueError("out must match q, and the pools' head_dim must match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    hkv, bs = k_pool.shape[1], k_pool.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    d = decode_dims(q, k_pool, block_tables, partition_size)
+    lib = _lib.load()
+    need = lib.paged_attention_decode_workspace_bytes(bs, ctypes.byref(d))
+    if need == _lib.SIZE_MAX:
+        _check(_lib.PA_ERR_SHAPE, "paged_attention_decode")
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        d.workspace = _dev(workspace, "workspace")
+        d.workspace_bytes = workspace.numel() * workspace.element_size()
+    d.stream = _stream_ptr(stream)
+    d.timing_events[0] = _event_ptr(timing_events[0])
+    d.timing_events[1] = _event_ptr(timing_events[1])
+    rc = lib.paged_attention_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        hkv, ctypes.c_float(scale), bs, ctypes.byref(d))
+    _check(rc, "paged_attention_decode")
+    return out
+
+
+def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, k_pool: torch.Tensor,
+                      v_pool: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """Write k[i], v[i] ([T, num_kv_heads, head_dim]) to pool slot
+    slot_mapping[i] (see reshape_and_cache in include/pagedattn.h)."""
+    if k.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k.dtype}")
+    for name, t in (("v", v), ("k_pool", k_pool), ("v_pool", v_pool)):
+        if t.dtype != k.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from k dtype {k.dtype}")
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    if k.shape != v.shape or k.dim() != 3 or k_pool.shape != v_pool.shape or k_pool.dim() != 4:
+        raise ValueError("k, v must be [T, Hkv, D] and pools [NB, Hkv, bs, D]")
+    T, hkv, D = k.shape
+    if k_pool.shape[1] != hkv or k_pool.shape[3] != D or slot_mapping.shape != (T,):
+        raise ValueError("shape mismatch between k/v, pools and slot_mapping")
+    d = _lib.CacheDims()
+    d.num_tokens, d.num_kv_heads, d.head_dim = T, hkv, D
+    d.block_size, d.num_blocks = k_pool.shape[2], k_pool.shape[0]
+    d.dtype = _DTYPES[k.dtype]
+    d.stream = _stream_ptr(stream)
+    rc = _lib.load().reshape_and_cache(_dev(k, "k"), _dev(v, "v"), _dev(k_pool, "k_pool"),
+                                       _dev(v_pool, "v_pool"), _dev(slot_mapping, "slot_mapping"),
+                                       ctypes.byref(d))
+    _check(rc, "reshape_and_cache")
+
+
+def hbm_read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Stream all of ``buf`` through the read-bandwidth probe kernel."""
+    lib = _lib.load()
+    if sink is None:
+        sink = torch.empty(lib.pa_hbm_read_probe_sink_bytes(), dtype=torch.uint8, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    rc = lib.pa_hbm_read_probe(_dev(buf, "buf"), nbytes - nbytes % 16, _dev(sink, "sink"),
+                               _stream_ptr(stream))
+    _check(rc, "pa_hbm_read_probe")
+    return sink

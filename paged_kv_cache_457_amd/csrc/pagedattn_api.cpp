@@ -1,0 +1,170 @@
+// Host side of the C ABI declared in include/pagedattn.h: argument checks
+// (all before any HIP call, so every rejection is testable without a GPU),
+// workspace sizing, and hand-off to the launch code.
+#include "pagedattn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "pagedattn_internal.h"
+
+namespace {
+
+constexpr int kDefaultPartitionTokens = 256;
+constexpr int kMaxPartitionPages = 64;  // one page id per lane of a wavefront
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_dim(int d) { return d == 64 || d == 128; }
+bool supported_bs(int bs) { return bs == 16 || bs == 32; }
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+int elem_bytes(int dtype) { return dtype == PA_DTYPE_F32 ? 4 : 2; }
+
+int partition_tokens(const pa_decode_dims *d) {
+  return d->partition_size == 0 ? kDefaultPartitionTokens : d->partition_size;
+}
+
+// Shape checks shared by the decode call and the workspace query.
+int check_decode_dims(int32_t num_kv_heads, int32_t block_size, const pa_decode_dims *d) {
+  if (!d) return PA_ERR_NULL;
+  if (d->num_seqs < 0 || d->num_heads < 1 || num_kv_heads < 1 || d->max_blocks_per_seq < 1 ||
+      d->num_blocks < 1 || d->reserved != 0 || d->partition_size < 0)
+    return PA_ERR_SHAPE;
+  if (d->num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (!supported_dim(d->head_dim) || !supported_bs(block_size) ||
+      !supported_group(d->num_heads / num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  const int pt = partition_tokens(d);
+  if (pt % block_size != 0 || pt / block_size > kMaxPartitionPages) return PA_ERR_SHAPE;
+  // context capacity must fit in int32 token counts
+  if ((int64_t)d->max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+int max_partitions(int32_t block_size, const pa_decode_dims *d) {
+  const int pp = partition_tokens(d) / block_size;
+  return (d->max_blocks_per_seq + pp - 1) / pp;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attention_decode_workspace_bytes(int32_t block_size, const pa_decode_dims *dims) {
+  // The size does not depend on the kv-head count; checking with
+  // num_kv_heads = num_heads (group 1, always built) validates the rest.
+  if (!dims || dims->num_heads < 1) return SIZE_MAX;
+  if (check_decode_dims(dims->num_heads, block_size, dims) != PA_OK) return SIZE_MAX;
+  const int mp = max_partitions(block_size, dims);
+  if (mp <= 1) return 0;
+  return (size_t)dims->num_seqs * dims->num_heads * mp * (size_t)(dims->head_dim + 2) *
+         sizeof(float);
+}
+
+int paged_attention_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           int32_t num_kv_heads, float scale, int32_t block_size,
+                           const pa_decode_dims *dims) {
+  if (!dims) return PA_ERR_NULL;
+  int rc = check_decode_dims(num_kv_heads, block_size, dims);
+  if (rc != PA_OK) return rc;
+  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (dims->num_seqs == 0) return PA_OK;  // nothing is read or written; pointers may be NULL
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_ALIGN;
+  const int mp = max_partitions(block_size, dims);
+  float *ws_ml = nullptr;
+  float *ws_acc = nullptr;
+  if (mp > 1) {
+    const size_t need = (size_t)dims->num_seqs * dims->num_heads * mp *
+                        (size_t)(dims->head_dim + 2) * sizeof(float);
+    if (need > 0) {
+      if (!dims->workspace || dims->workspace_bytes < need || !aligned(dims->workspace, 16))
+        return PA_ERR_WORKSPACE;
+      ws_acc = static_cast<float *>(dims->workspace);
+      ws_ml = ws_acc + (size_t)dims->num_seqs * dims->num_heads * mp * dims->head_dim;
+    }
+  }
+
+  pa_internal::DecodeLaunch a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_ml = ws_ml;
+  a.ws_acc = ws_acc;
+  a.num_seqs = dims->num_seqs;
+  a.num_heads = dims->num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.block_size = block_size;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.num_blocks = dims->num_blocks;
+  a.dtype = dims->dtype;
+  a.part_pages = partition_tokens(dims) / block_size;
+  a.max_parts = mp;
+  a.scale = scale;
+  a.stream = dims->stream;
+  a.ev_begin = dims->timing_events[0];
+  a.ev_end = dims->timing_events[1];
+  return pa_internal::launch_decode(a);
+}
+
+int reshape_and_cache(const void *k, const void *v, void *k_pool, void *v_pool,
+                      const int64_t *slot_mapping, const pa_cache_dims *dims) {
+  if (!dims) return PA_ERR_NULL;
+  if (dims->num_tokens < 0 || dims->num_kv_heads < 1 || dims->num_blocks < 1)
+    return PA_ERR_SHAPE;
+  if (dims->dtype != PA_DTYPE_F32 && dims->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (!supported_dim(dims->head_dim) || !supported_bs(dims->block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (dims->num_tokens == 0) return PA_OK;  // nothing to write; pointers may be NULL
+  if (!k || !v || !k_pool || !v_pool || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(slot_mapping, 8))
+    return PA_ERR_ALIGN;
+  pa_internal::CacheLaunch a{};
+  a.k = k;
+  a.v = v;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = dims->num_tokens;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.block_size = dims->block_size;
+  a.num_blocks = dims->num_blocks;
+  a.elem_bytes = elem_bytes(dims->dtype);
+  a.stream = dims->stream;
+  return pa_internal::launch_reshape_and_cache(a);
+}
+
+const char *pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK: success";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: a size is out of range or inconsistent";
+    case PA_ERR_UNSUPPORTED:
+      return "PA_ERR_UNSUPPORTED: dtype, head_dim, block_size or head group not supported";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a pointer is misaligned";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: split-K workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported a launch error";
+  }
+  return "unknown status";
+}
+
+size_t pa_hbm_read_probe_sink_bytes(void) { return pa_internal::hbm_probe_sink_bytes(); }
+
+int pa_hbm_read_probe(const void *buf, size_t bytes, void *sink, void *stream) {
+  if (!buf || !sink) return PA_ERR_NULL;
+  if (bytes < 16 || bytes % 16 != 0) return PA_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return PA_ERR_ALIGN;
+  return pa_internal::launch_hbm_probe(buf, bytes, sink, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal interface between the host-side C ABI (argument checks) and the
+// HIP launch code.  Not installed; the public interface is include/pagedattn.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa_internal {
+
+struct DecodeLaunch {
+  void *out;
+  const void *q;
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  float *ws_ml;   // [S, H, max_parts, 2] (running max in log2 units, sum)
+  float *ws_acc;  // [S, H, max_parts, D] unnormalised weighted V
+  int num_seqs, num_heads, num_kv_heads, head_dim, block_size;
+  int max_blocks, num_blocks, dtype;
+  int part_pages;  // pages per partition (<= 64)
+  int max_parts;   // ceil(max_blocks / part_pages)
+  float scale;
+  void *stream;
+  void *ev_begin;
+  void *ev_end;
+};
+
+struct CacheLaunch {
+  const void *k;
+  const void *v;
+  void *k_pool;
+  void *v_pool;
+  const int64_t *slot_mapping;
+  int num_tokens, num_kv_heads, head_dim, block_size, num_blocks, elem_bytes;
+  void *stream;
+};
+
+// Each returns 0 on success or the PA_ERR_HIP code on a launch error.
+int launch_decode(const DecodeLaunch &a);
+int launch_reshape_and_cache(const CacheLaunch &a);
+int launch_hbm_probe(const void *buf, size_t bytes, void *sink, void *stream);
+size_t hbm_probe_sink_bytes();
+
+}  // namespace pa_internal

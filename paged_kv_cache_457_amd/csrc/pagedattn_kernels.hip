@@ -1,0 +1,491 @@
+// HIP kernels for paged decode attention and the KV-cache write, gfx950.
+//
+// Method (vLLM / PagedAttention pages): the KV cache is a pool of fixed-size
+// pages; a per-sequence page table maps logical to physical pages and the
+// attention kernel reads the pages through that table directly, with no
+// gather copy and no padding (showapi.com article, section 2.1; tutorial
+// page, section 4.2).  Each decode step also appends the new token's K/V to
+// the cache (tutorial page, section 4.3, step 3).
+//
+// Work decomposition: one 64-lane wavefront per (sequence, kv-head,
+// partition of up to 64 pages).  A wavefront reads each (page, kv-head) run
+// of block_size * head_dim elements as whole 16-byte chunks: lane l, load i
+// takes chunk i*64 + l, so every load instruction covers 1 KiB of
+// consecutive bytes.  With R = chunks per token row, a load instruction
+// holds 64/R tokens and lane l always sees the same R-chunk column
+// (l % R) of token rows (l / R) + i*64/R.  The partial q.K dot products of a
+// row are summed across its R lanes with DPP row operations, so every lane
+// of the row ends up holding the full logit.  Softmax is the online form
+// (running max, rescaled running sum and accumulator) in log2 units, with
+// log2(e) folded into the scale.  Sequences longer than one partition leave
+// (max, sum, unnormalised V accumulation) per partition in the workspace,
+// and a second kernel merges them by log-sum-exp.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pagedattn_internal.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Reinterpret a 32-bit word as two bf16.  Takes the word by value: a
+// bit-cast applied directly to an element of an ext_vector lvalue reads
+// element 0 whatever the index (seen with this compiler), so always copy
+// the element out first.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// ------------------------------------------------------------ element types
+struct F32 {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerChunk = 4;
+  __device__ static void unpack(const u32x4 c, float *f) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) f[w] = __uint_as_float(c[w]);
+  }
+  __device__ static u32x4 pack(const float *f) {
+    u32x4 c;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) c[w] = __float_as_uint(f[w]);
+    return c;
+  }
+  // q . k over one 16-byte chunk
+  __device__ static float dot(const u32x4 qc, const u32x4 kc) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc = fmaf(__uint_as_float(qc[w]), __uint_as_float(kc[w]), acc);
+    return acc;
+  }
+};
+
+struct BF16 {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerChunk = 8;
+  // a 32-bit word holds element 2w in its low half and 2w+1 in its high half
+  __device__ static void unpack(const u32x4 c, float *f) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      f[2 * w] = __uint_as_float(c[w] << 16);
+      f[2 * w + 1] = __uint_as_float(c[w] & 0xffff0000u);
+    }
+  }
+  // fp32 -> bf16, round to nearest even; NaN stays a quiet NaN
+  __device__ static uint32_t round_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  }
+  __device__ static u32x4 pack(const float *f) {
+    u32x4 c;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      c[w] = round_bits(f[2 * w]) | (round_bits(f[2 * w + 1]) << 16);
+    return c;
+  }
+  // q . k over one chunk with v_dot2_f32_bf16: products of bf16 pairs are
+  // exact in fp32, accumulated in fp32
+  __device__ static float dot(const u32x4 qc, const u32x4 kc) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qc[w]), as_bf16x2(kc[w]), acc, false);
+    return acc;
+  }
+};
+
+// ------------------------------------------------------- wavefront reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the R consecutive lanes that share a token row (R = 8, 16, 32).
+// quad_perm [1,0,3,2] and [2,3,0,1] sum each quad; row_half_mirror pairs
+// the two quads of each 8-lane half; row_mirror pairs the two halves of the
+// 16-lane row.  Every lane of the group gets the same bits (fp add commutes).
+template <int R>
+__device__ __forceinline__ float row_sum(float v) {
+  static_assert(R == 8 || R == 16 || R == 32, "row width");
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  if constexpr (R >= 16) v += dpp<0x140>(v);
+  if constexpr (R == 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+// Reduce over the 64/R row groups (lanes with equal l % R).
+template <int R>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (R <= 8) v += __shfl_xor(v, 8);
+  if constexpr (R <= 16) v += __shfl_xor(v, 16);
+  if constexpr (R <= 32) v += __shfl_xor(v, 32);
+  return v;
+}
+template <int R>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (R <= 8) v = fmaxf(v, __shfl_xor(v, 8));
+  if constexpr (R <= 16) v = fmaxf(v, __shfl_xor(v, 16));
+  if constexpr (R <= 32) v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u32x4 load16(const char *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// ------------------------------------------------------ decode, partition pass
+// Grid (max_parts, num_kv_heads, num_seqs), 64 threads.  Block (p, g, s)
+// handles the G query heads of kv-head g over pages [p*PP, (p+1)*PP) of
+// sequence s.
+template <class T, int D, int BS, int G>
+__global__ __launch_bounds__(64) void pa_decode_partition(
+    void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
+    const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
+    float *__restrict__ ws_acc, int num_heads, int num_kv_heads, int max_blocks,
+    int num_blocks, int part_pages, int max_parts, float scale_log2) {
+  constexpr int E = T::kPerChunk;      // elements per 16-byte chunk
+  constexpr int R = D / E;             // lanes (chunks) per token row
+  constexpr int TPI = 64 / R;          // token rows per load instruction
+  constexpr int NLD = BS / TPI;        // load instructions per page
+  constexpr int PAGE_BYTES = BS * D * T::kBytes;
+  static_assert(NLD * 1024 == PAGE_BYTES, "page = whole 1 KiB wave loads");
+
+  const int lane = threadIdx.x;
+  const int part = blockIdx.x;
+  const int g = blockIdx.y;
+  const int s = blockIdx.z;
+  const int dc = lane % R;
+  const int rg = lane / R;
+  const int h0 = g * G;
+
+  int ctx = context_lens[s];
+  ctx = min(max(ctx, 0), max_blocks * BS);
+  const int npages = (ctx + BS - 1) / BS;
+  const int p_begin = part * part_pages;
+
+  char *out_b = reinterpret_cast<char *>(out);
+  const size_t head_row_bytes = (size_t)D * T::kBytes;
+
+  if (ctx == 0) {
+    if (part == 0 && rg == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float z[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) z[e] = 0.f;
+        *reinterpret_cast<u32x4 *>(out_b + ((size_t)s * num_heads + h0 + h) * head_row_bytes +
+                                   dc * 16) = T::pack(z);
+      }
+    }
+    return;
+  }
+  if (p_begin >= npages) return;
+  const int np = min(npages - p_begin, part_pages);
+
+  // physical page ids of this partition, one per lane
+  int my_bid = 0;
+  if (lane < np) my_bid = block_tables[(size_t)s * max_blocks + p_begin + lane];
+
+  u32x4 qc[G];
+  const char *q_b = reinterpret_cast<const char *>(q);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qc[h] = load16(q_b + ((size_t)s * num_heads + h0 + h) * head_row_bytes + dc * 16);
+
+  float m[G], l[G], acc[G][E];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+  }
+
+  const size_t page_stride = (size_t)num_kv_heads * PAGE_BYTES;
+  const char *k_b = reinterpret_cast<const char *>(k_pool) + (size_t)g * PAGE_BYTES + lane * 16;
+  const char *v_b = reinterpret_cast<const char *>(v_pool) + (size_t)g * PAGE_BYTES + lane * 16;
+
+  for (int j = 0; j < np; ++j) {
+    const int bid = __builtin_amdgcn_readlane(my_bid, j);
+    if ((unsigned)bid >= (unsigned)num_blocks) continue;  // precondition violated: skip page
+    const char *kp = k_b + (size_t)bid * page_stride;
+    const char *vp = v_b + (size_t)bid * page_stride;
+    u32x4 kc[NLD], vc[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) kc[i] = load16(kp + i * 1024);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) vc[i] = load16(vp + i * 1024);
+
+    float lg[NLD][G];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) lg[i][h] = row_sum<R>(T::dot(qc[h], kc[i])) * scale_log2;
+
+    const int tok0 = (p_begin + j) * BS;
+    const bool tail = tok0 + BS > ctx;
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        if (tok0 + i * TPI + rg >= ctx)
+#pragma unroll
+          for (int h = 0; h < G; ++h) lg[i][h] = -INFINITY;
+    }
+
+    float p[NLD][G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float pm = lg[0][h];
+#pragma unroll
+      for (int i = 1; i < NLD; ++i) pm = fmaxf(pm, lg[i][h]);
+      pm = group_max<R>(pm);
+      const float mn = fmaxf(m[h], pm);
+      const float alpha = fast_exp2(m[h] - mn);
+      m[h] = mn;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        p[i][h] = fast_exp2(lg[i][h] - mn);
+        l[h] += p[i][h];
+      }
+    }
+
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      float vf[E];
+      T::unpack(vc[i], vf);
+      if (tail && tok0 + i * TPI + rg >= ctx) {
+        // a masked slot may hold anything (NaN): it must not reach an FMA
+#pragma unroll
+        for (int e = 0; e < E; ++e) vf[e] = 0.f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p[i][h], vf[e], acc[h][e]);
+    }
+  }
+
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    l[h] = group_sum<R>(l[h]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = group_sum<R>(acc[h][e]);
+  }
+
+  if (npages <= part_pages) {
+    // the whole sequence is in this partition: normalise and write out
+    if (rg == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float inv = 1.0f / l[h];
+        float o[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = acc[h][e] * inv;
+        *reinterpret_cast<u32x4 *>(out_b + ((size_t)s * num_heads + h0 + h) * head_row_bytes +
+                                   dc * 16) = T::pack(o);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const size_t row = ((size_t)s * num_heads + h0 + h) * max_parts + part;
+      if (rg == 0) {
+        float *dst = ws_acc + row * D + dc * E;
+#pragma unroll
+        for (int e = 0; e < E; e += 4)
+          *reinterpret_cast<float4 *>(dst + e) =
+              make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+      }
+      if (lane == 0) {
+        ws_ml[row * 2] = m[h];
+        ws_ml[row * 2 + 1] = l[h];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------- decode, log-sum-exp merge
+// Grid (num_heads, num_seqs), 64 threads.  Merges the partitions of
+// sequences that span more than one: M = max_p m_p, w_p = 2^(m_p - M),
+// out = sum_p w_p acc_p / sum_p w_p l_p.
+template <class T, int D>
+__global__ __launch_bounds__(64) void pa_decode_reduce(
+    void *__restrict__ out, const float *__restrict__ ws_ml, const float *__restrict__ ws_acc,
+    const int32_t *__restrict__ context_lens, int num_heads, int ctx_cap, int part_tokens,
+    int max_parts) {
+  constexpr int DPL = D / 64;  // output elements per lane
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  int ctx = context_lens[s];
+  ctx = min(max(ctx, 0), ctx_cap);
+  const int nparts = (ctx + part_tokens - 1) / part_tokens;
+  if (nparts <= 1) return;
+  const size_t row0 = ((size_t)s * num_heads + h) * max_parts;
+
+  float M = -INFINITY;
+  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ws_ml[(row0 + p) * 2]);
+  M = wave_max(M);
+  float L = 0.f;
+  for (int p = lane; p < nparts; p += 64)
+    L += ws_ml[(row0 + p) * 2 + 1] * fast_exp2(ws_ml[(row0 + p) * 2] - M);
+  L = wave_sum(L);
+
+  float o[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) o[j] = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float w = fast_exp2(ws_ml[(row0 + p) * 2] - M);
+    const float *a = ws_acc + (row0 + p) * D + lane * DPL;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[j] = fmaf(w, a[j], o[j]);
+  }
+  const float inv = 1.0f / L;
+  if constexpr (T::kBytes == 4) {
+    float *dst = reinterpret_cast<float *>(out) + ((size_t)s * num_heads + h) * D + lane * DPL;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) dst[j] = o[j] * inv;
+  } else {
+    uint16_t *dst = reinterpret_cast<uint16_t *>(out) + ((size_t)s * num_heads + h) * D + lane * DPL;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) dst[j] = (uint16_t)BF16::round_bits(o[j] * inv);
+  }
+}
+
+// ------------------------------------------------------------ cache write
+// Grid (num_tokens), 256 threads.  Copies token t's K and V rows, all
+// kv-heads, 16 bytes per lane, to page slot / bs at offset slot % bs.
+__global__ __launch_bounds__(256) void pa_reshape_and_cache(
+    const u32x4 *__restrict__ k, const u32x4 *__restrict__ v, u32x4 *__restrict__ k_pool,
+    u32x4 *__restrict__ v_pool, const int64_t *__restrict__ slot_mapping, int num_kv_heads,
+    int row_chunks, int block_size, int64_t num_slots) {
+  const int t = blockIdx.x;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t page = slot / block_size;
+  const int64_t off = slot - page * block_size;
+  const int total = num_kv_heads * row_chunks;
+  for (int c = threadIdx.x; c < total; c += blockDim.x) {
+    const int g = c / row_chunks;
+    const int dc = c - g * row_chunks;
+    const size_t src = ((size_t)t * num_kv_heads + g) * row_chunks + dc;
+    const size_t dst = (((size_t)page * num_kv_heads + g) * block_size + off) * row_chunks + dc;
+    k_pool[dst] = k[src];
+    v_pool[dst] = v[src];
+  }
+}
+
+// -------------------------------------------------------- HBM read probe
+constexpr int kProbeBlocks = 4096;
+constexpr int kProbeThreads = 256;
+
+__global__ __launch_bounds__(kProbeThreads) void pa_hbm_probe(const u32x4 *__restrict__ buf,
+                                                              size_t n16,
+                                                              uint32_t *__restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * kProbeThreads;
+  size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(buf + i);
+    const u32x4 b = __builtin_nontemporal_load(buf + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(buf + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(buf + i + 3 * stride);
+    x ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^
+         (d.x ^ d.y ^ d.z ^ d.w);
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = __builtin_nontemporal_load(buf + i);
+    x ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  sink[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = x;
+}
+
+// ------------------------------------------------------------- dispatch
+template <class T, int D, int BS, int G>
+int run_decode(const pa_internal::DecodeLaunch &a) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const float scale_log2 = a.scale * kLog2e;
+  if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
+  dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((pa_decode_partition<T, D, BS, G>), grid, dim3(64), 0, st, a.out, a.q,
+                     a.k_pool, a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc,
+                     a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks, a.part_pages,
+                     a.max_parts, scale_log2);
+  if (hipGetLastError() != hipSuccess) return 6;
+  if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
+  if (a.max_parts > 1) {
+    hipLaunchKernelGGL((pa_decode_reduce<T, D>), dim3(a.num_heads, a.num_seqs), dim3(64), 0, st,
+                       a.out, a.ws_ml, a.ws_acc, a.context_lens, a.num_heads,
+                       a.max_blocks * BS, a.part_pages * BS, a.max_parts);
+    if (hipGetLastError() != hipSuccess) return 6;
+  }
+  return 0;
+}
+
+template <class T, int D, int BS>
+int dispatch_group(const pa_internal::DecodeLaunch &a) {
+  switch (a.num_heads / a.num_kv_heads) {
+    case 1: return run_decode<T, D, BS, 1>(a);
+    case 2: return run_decode<T, D, BS, 2>(a);
+    case 4: return run_decode<T, D, BS, 4>(a);
+    case 8: return run_decode<T, D, BS, 8>(a);
+  }
+  return 3;
+}
+
+template <class T, int D>
+int dispatch_block(const pa_internal::DecodeLaunch &a) {
+  return a.block_size == 16 ? dispatch_group<T, D, 16>(a) : dispatch_group<T, D, 32>(a);
+}
+
+template <class T>
+int dispatch_dim(const pa_internal::DecodeLaunch &a) {
+  return a.head_dim == 64 ? dispatch_block<T, 64>(a) : dispatch_block<T, 128>(a);
+}
+
+}  // namespace
+
+namespace pa_internal {
+
+int launch_decode(const DecodeLaunch &a) {
+  return a.dtype == 0 ? dispatch_dim<F32>(a) : dispatch_dim<BF16>(a);
+}
+
+int launch_reshape_and_cache(const CacheLaunch &a) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const int row_chunks = a.head_dim * a.elem_bytes / 16;
+  hipLaunchKernelGGL(pa_reshape_and_cache, dim3(a.num_tokens), dim3(256), 0, st,
+                     reinterpret_cast<const u32x4 *>(a.k), reinterpret_cast<const u32x4 *>(a.v),
+                     reinterpret_cast<u32x4 *>(a.k_pool), reinterpret_cast<u32x4 *>(a.v_pool),
+                     a.slot_mapping, a.num_kv_heads, row_chunks, a.block_size,
+                     (int64_t)a.num_blocks * a.block_size);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+size_t hbm_probe_sink_bytes() { return (size_t)kProbeBlocks * kProbeThreads * 4; }
+
+int launch_hbm_probe(const void *buf, size_t bytes, void *sink, void *stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(pa_hbm_probe, dim3(kProbeBlocks), dim3(kProbeThreads), 0, st,
+                     reinterpret_cast<const u32x4 *>(buf), bytes / 16,
+                     reinterpret_cast<uint32_t *>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+}  // namespace pa_internal

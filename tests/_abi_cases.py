@@ -1,0 +1,144 @@
+"""Host-side argument checks of libpagedattn, run as a child process.
+
+tests/test_abi.py runs this file with every GPU hidden from the HIP runtime,
+so even a check that wrongly passed could not reach a device.  Each case
+passes stand-in (non-NULL, never dereferenced) pointers and expects a given
+status code.  Prints one line per case and exits nonzero on any mismatch.
+"""
+import ctypes
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+from paged_kv_cache_457_amd import _lib  # noqa: E402
+
+lib = _lib.load()
+P = 0x10000          # a 64 KiB-aligned stand-in address; never dereferenced
+MIS = P + 4          # misaligned for 16-byte data
+
+failures = 0
+
+
+def expect(name, got, want):
+    global failures
+    ok = got == want
+    failures += not ok
+    print(f"{'ok ' if ok else 'BAD'} {name}: got {got} want {want}", flush=True)
+
+
+def dims(**kw):
+    d = _lib.DecodeDims()
+    d.num_seqs, d.num_heads, d.head_dim = 0, 32, 128
+    d.max_blocks_per_seq, d.num_blocks, d.dtype = 128, 1000, _lib.PA_DTYPE_BF16
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def decode(d, hkv=32, bs=16, scale=0.088, ptrs=None):
+    p = ptrs or [P] * 6
+    return lib.paged_attention_decode(*p, hkv, ctypes.c_float(scale), bs, ctypes.byref(d))
+
+
+def cache(**kw):
+    d = _lib.CacheDims()
+    d.num_tokens, d.num_kv_heads, d.head_dim, d.block_size = 0, 8, 128, 16
+    d.num_blocks, d.dtype = 100, _lib.PA_DTYPE_BF16
+    ptrs = kw.pop("ptrs", [P] * 5)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return lib.reshape_and_cache(*ptrs, ctypes.byref(d))
+
+
+# ---- decode: shape cases use num_seqs == 0, so a check that wrongly passed
+# would end in a no-op; pointer cases need num_seqs >= 1 (an empty batch
+# accepts NULL pointers) and rely on the hidden GPUs.
+ONE = dict(num_seqs=1, max_blocks_per_seq=16)
+expect("dims NULL", lib.paged_attention_decode(P, P, P, P, P, P, 32, ctypes.c_float(1), 16, None),
+       _lib.PA_ERR_NULL)
+for i in range(6):
+    ptrs = [P] * 6
+    ptrs[i] = None
+    expect(f"decode pointer {i} NULL", decode(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_NULL)
+expect("valid empty batch is a no-op", decode(dims()), _lib.PA_OK)
+expect("empty batch accepts NULL pointers", decode(dims(), ptrs=[None] * 6), _lib.PA_OK)
+expect("negative num_seqs", decode(dims(num_seqs=-1)), _lib.PA_ERR_SHAPE)
+expect("zero heads", decode(dims(num_heads=0)), _lib.PA_ERR_SHAPE)
+expect("zero kv heads", decode(dims(), hkv=0), _lib.PA_ERR_SHAPE)
+expect("H not a multiple of Hkv", decode(dims(num_heads=30), hkv=8), _lib.PA_ERR_SHAPE)
+expect("group 3 unsupported", decode(dims(num_heads=24), hkv=8), _lib.PA_ERR_UNSUPPORTED)
+expect("group 16 unsupported", decode(dims(num_heads=32), hkv=2), _lib.PA_ERR_UNSUPPORTED)
+expect("head_dim 96 unsupported", decode(dims(head_dim=96)), _lib.PA_ERR_UNSUPPORTED)
+expect("block_size 8 unsupported", decode(dims(), bs=8), _lib.PA_ERR_UNSUPPORTED)
+expect("dtype 7 unsupported", decode(dims(dtype=7)), _lib.PA_ERR_UNSUPPORTED)
+expect("zero max_blocks", decode(dims(max_blocks_per_seq=0)), _lib.PA_ERR_SHAPE)
+expect("zero num_blocks", decode(dims(num_blocks=0)), _lib.PA_ERR_SHAPE)
+expect("reserved nonzero", decode(dims(reserved=1)), _lib.PA_ERR_SHAPE)
+expect("partition not a page multiple", decode(dims(partition_size=100)), _lib.PA_ERR_SHAPE)
+expect("partition over 64 pages", decode(dims(partition_size=16 * 65)), _lib.PA_ERR_SHAPE)
+expect("negative partition", decode(dims(partition_size=-16)), _lib.PA_ERR_SHAPE)
+expect("scale NaN", decode(dims(), scale=float("nan")), _lib.PA_ERR_SHAPE)
+expect("scale inf", decode(dims(), scale=float("inf")), _lib.PA_ERR_SHAPE)
+for i in range(4):
+    ptrs = [P] * 6
+    ptrs[i] = MIS
+    expect(f"decode pointer {i} misaligned", decode(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_ALIGN)
+ptrs = [P] * 6
+ptrs[4] = P + 2
+expect("block_tables misaligned", decode(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_ALIGN)
+
+# workspace cases: num_seqs > 0 is needed for a nonzero requirement; each
+# still fails validation (missing / small / misaligned workspace)
+need_d = dims(num_seqs=4)
+need = lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(need_d))
+expect("workspace bytes formula", need, 4 * 32 * ((128 * 16 + 255) // 256) * (128 + 2) * 4)
+expect("workspace missing", decode(dims(num_seqs=4)), _lib.PA_ERR_WORKSPACE)
+expect("workspace too small",
+       decode(dims(num_seqs=4, workspace=P, workspace_bytes=need - 4)), _lib.PA_ERR_WORKSPACE)
+expect("workspace misaligned",
+       decode(dims(num_seqs=4, workspace=P + 8, workspace_bytes=need + 64)), _lib.PA_ERR_WORKSPACE)
+expect("no workspace needed when one partition covers the table",
+       lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(dims(num_seqs=4, max_blocks_per_seq=16))), 0)
+expect("workspace bytes, partition 512 at bs 32",
+       lib.paged_attention_decode_workspace_bytes(32, ctypes.byref(
+           dims(num_seqs=8, max_blocks_per_seq=1024, partition_size=512))),
+       8 * 32 * 64 * 130 * 4)
+expect("workspace query rejects bad dims",
+       lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(dims(head_dim=80))), _lib.SIZE_MAX)
+expect("workspace query rejects NULL", lib.paged_attention_decode_workspace_bytes(16, None), _lib.SIZE_MAX)
+
+# ---- reshape_and_cache (num_tokens == 0: a wrong pass is a no-op)
+expect("cache dims NULL", lib.reshape_and_cache(P, P, P, P, P, None), _lib.PA_ERR_NULL)
+for i in range(5):
+    ptrs = [P] * 5
+    ptrs[i] = None
+    expect(f"cache pointer {i} NULL", cache(num_tokens=1, ptrs=ptrs), _lib.PA_ERR_NULL)
+expect("valid empty cache write is a no-op", cache(), _lib.PA_OK)
+expect("empty cache write accepts NULL pointers", cache(ptrs=[None] * 5), _lib.PA_OK)
+expect("negative tokens", cache(num_tokens=-2), _lib.PA_ERR_SHAPE)
+expect("zero kv heads", cache(num_kv_heads=0), _lib.PA_ERR_SHAPE)
+expect("zero blocks", cache(num_blocks=0), _lib.PA_ERR_SHAPE)
+expect("cache head_dim 32", cache(head_dim=32), _lib.PA_ERR_UNSUPPORTED)
+expect("cache block_size 64", cache(block_size=64), _lib.PA_ERR_UNSUPPORTED)
+expect("cache dtype 5", cache(dtype=5), _lib.PA_ERR_UNSUPPORTED)
+for i in range(4):
+    ptrs = [P] * 5
+    ptrs[i] = MIS
+    expect(f"cache pointer {i} misaligned", cache(num_tokens=1, ptrs=ptrs), _lib.PA_ERR_ALIGN)
+expect("slot_mapping misaligned", cache(num_tokens=1, ptrs=[P, P, P, P, P + 4]), _lib.PA_ERR_ALIGN)
+
+# ---- probe
+expect("probe NULL buffer", lib.pa_hbm_read_probe(None, 1024, P, None), _lib.PA_ERR_NULL)
+expect("probe size not a multiple of 16", lib.pa_hbm_read_probe(P, 1000, P, None), _lib.PA_ERR_SHAPE)
+expect("probe misaligned", lib.pa_hbm_read_probe(MIS, 1024, P, None), _lib.PA_ERR_ALIGN)
+
+# ---- status strings
+for rc in range(7):
+    s = lib.pa_status_string(rc).decode()
+    expect(f"status string {rc}", s.split(":")[0].startswith("PA_"), True)
+expect("unknown status", lib.pa_status_string(99).decode(), "unknown status")
+
+print(f"{failures} failures", flush=True)
+sys.exit(1 if failures else 0)
