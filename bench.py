@@ -40,8 +40,40 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", action="store_true", help="also measure achievable read GB/s")
     ap.add_argument("--traffic-json", default=None,
-                    help="measured HBM bytes per partition-kernel launch (from rocprofv3 counters)")
+                    help="HBM bytes per partition-kernel launch measured with rocprofv3 counters "
+                         "(default: profiles/traffic_pa_decode_partition_c<config>.json); used "
+                         "only while the kernel source still has the hash recorded there")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, run a plain device copy of this many MiB "
+                         "5 times, so a counter run can scale FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_457_amd",
+                        "csrc", "pagedattn_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(args):
+    """HBM bytes per partition-kernel launch from a committed counter run,
+    or None when there is none for this workload or the kernel source has
+    changed since the counters were taken."""
+    path = args.traffic_json or os.path.join(
+        os.path.dirname(os.path.abspath(__file__)), "profiles",
+        f"traffic_pa_decode_partition_c{args.config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    if rec.get("config_index") != args.config or rec.get("partition_size") != (
+            args.partition_size or 256) or rec.get("seed") != args.seed:
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(w, budget_s):
@@ -134,10 +166,17 @@ def main():
 
     kv_bytes = w.kv_bytes()
     achieved = kv_bytes / (k1_avg_ms * 1e-3) / 1e9
-    traffic = None
-    if args.traffic_json and os.path.exists(args.traffic_json):
-        with open(args.traffic_json) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    traffic = measured_traffic(args)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     probe_gbs = None
     if args.probe:
