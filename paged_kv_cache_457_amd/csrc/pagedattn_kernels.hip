@@ -146,7 +146,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ u32x4 load16(const char *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 // ------------------------------------------------------ decode, partition pass
-// Grid (max_parts, num_kv_heads, num_seqs), 64 threads.  Block (p, g, s)
+// 1-D grid of max_parts * num_seqs * num_kv_heads blocks, 64 threads.  Block (p, g, s)
 // handles the G query heads of kv-head g over pages [p*PP, (p+1)*PP) of
 // sequence s.
 template <class T, int D, int BS, int G>
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(64) void pa_decode_partition(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
-    float *__restrict__ ws_acc, int num_heads, int num_kv_heads, int max_blocks,
+    float *__restrict__ ws_acc, int num_seqs, int num_heads, int num_kv_heads, int max_blocks,
     int num_blocks, int part_pages, int max_parts, float scale_log2) {
   constexpr int E = T::kPerChunk;      // elements per 16-byte chunk
   constexpr int R = D / E;             // lanes (chunks) per token row
@@ -164,9 +164,15 @@ __global__ __launch_bounds__(64) void pa_decode_partition(
   static_assert(NLD * 1024 == PAGE_BYTES, "page = whole 1 KiB wave loads");
 
   const int lane = threadIdx.x;
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int s = blockIdx.z;
+  // Block order: kv-head fastest, then sequence, then partition.  The
+  // hardware hands consecutive workgroups to the 8 XCDs in turn, so this
+  // order gives every XCD the same share of each sequence's heads, whatever
+  // the spread of context lengths; partition-fastest order would send
+  // partition p of every sequence to the same XCD.
+  const int g = blockIdx.x % num_kv_heads;
+  const int sp = blockIdx.x / num_kv_heads;
+  const int s = sp % num_seqs;
+  const int part = sp / num_seqs;
   const int dc = lane % R;
   const int rg = lane / R;
   const int h0 = g * G;
@@ -422,10 +428,10 @@ int run_decode(const pa_internal::DecodeLaunch &a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   const float scale_log2 = a.scale * kLog2e;
   if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
-  dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  dim3 grid((unsigned)a.max_parts * a.num_kv_heads * a.num_seqs);
   hipLaunchKernelGGL((pa_decode_partition<T, D, BS, G>), grid, dim3(64), 0, st, a.out, a.q,
                      a.k_pool, a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc,
-                     a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks, a.part_pages,
+                     a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks, a.part_pages,
                      a.max_parts, scale_log2);
   if (hipGetLastError() != hipSuccess) return 6;
   if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
