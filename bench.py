@@ -34,7 +34,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="split-K partition in tokens (default: the workload's own, else the "
+                         "library default of 1024 tokens)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-baseline budget: oracle steps are repeated until this is spent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -70,8 +72,8 @@ def measured_traffic(args):
         rec = json.load(f)
     if rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
-    if rec.get("config_index") != args.config or rec.get("partition_size") != (
-            args.partition_size or 256) or rec.get("seed") != args.seed:
+    if rec.get("config_index") != args.config or rec.get("partition_size") != \
+            args.effective_partition or rec.get("seed") != args.seed:
         return None
     return rec.get("bytes_per_launch")
 
@@ -125,6 +127,10 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     w = make_config(args.config, args.seed)
+    if args.partition_size is None:
+        args.partition_size = w.partition_size
+    # 0 selects the library default, 1024 tokens (include/pagedattn.h)
+    args.effective_partition = args.partition_size or 1024
     dw = upload(w)
     stream = torch.cuda.current_stream()
     ws_bytes = binding.paged_attention_decode_workspace_bytes(dw.q, dw.k_pool, dw.block_tables,
@@ -217,7 +223,7 @@ def main():
             "block_size": w.block_size,
             "sum_context_tokens": int(w.context_lens.sum()),
             "num_blocks": w.num_blocks,
-            "partition_size": args.partition_size or 256,
+            "partition_size": args.effective_partition,
             "parallelism": "single GPU",
         },
         "kv_bytes_per_step": kv_bytes,

@@ -68,8 +68,8 @@ typedef struct pa_decode_dims {
   int32_t max_blocks_per_seq;  /* columns of block_tables, >= 1 */
   int32_t num_blocks;          /* pages in each pool, >= 1 */
   int32_t dtype;               /* PA_DTYPE_*: one type for q, out, k_pool, v_pool */
-  int32_t partition_size;      /* tokens per split-K partition; 0 = default (256);
-                                  a multiple of block_size, at most 64 pages */
+  int32_t partition_size;      /* tokens per split-K partition; 0 = default (1024);
+                                  a multiple of block_size, at most 256 pages */
   int32_t reserved;            /* must be 0 */
   void *workspace;             /* fp32 scratch for split-K partials, caller-owned;
                                   may be NULL when max_blocks_per_seq * block_size
@@ -89,8 +89,10 @@ typedef struct pa_decode_dims {
  *   out[s,h,:] = sum_t w_t V_t,  w = softmax_t(scale * q[s,h,:] . K_t),
  * over tokens t = 0 .. L-1 read through block_tables[s, t / block_size].
  * L = 0 writes a zero row.  Block-table columns at or past ceil(L /
- * block_size) are never read.  Slots past L in the last page are never used
- * in arithmetic (they may hold anything, NaN included).
+ * block_size) are never used (they may hold anything; the kernel may load
+ * them, so the whole [num_seqs, max_blocks_per_seq] table must be readable).
+ * Slots past L in the last page are never used in arithmetic (they may hold
+ * anything, NaN included).
  *
  * num_kv_heads: kv-heads in the pools; num_heads / num_kv_heads must be
  *   1, 2, 4 or 8.

@@ -10,8 +10,10 @@
 
 namespace {
 
-constexpr int kDefaultPartitionTokens = 256;
-constexpr int kMaxPartitionPages = 64;  // one page id per lane of a wavefront
+constexpr int kDefaultPartitionTokens = 1024;
+// The partition kernel runs 4 wavefronts per partition and deals its pages
+// to them in turn; each wavefront holds one page id per lane.
+constexpr int kMaxPartitionPages = 4 * 64;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -59,6 +59,10 @@ struct F32 {
     for (int w = 0; w < 4; ++w) acc = fmaf(__uint_as_float(qc[w]), __uint_as_float(kc[w]), acc);
     return acc;
   }
+  // four consecutive outputs (16 bytes)
+  __device__ static void store4(char *dst, const float *o) {
+    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+  }
 };
 
 struct BF16 {
@@ -84,6 +88,11 @@ struct BF16 {
     for (int w = 0; w < 4; ++w)
       c[w] = round_bits(f[2 * w]) | (round_bits(f[2 * w + 1]) << 16);
     return c;
+  }
+  // four consecutive outputs (8 bytes), rounded to nearest even
+  __device__ static void store4(char *dst, const float *o) {
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(round_bits(o[0]) | (round_bits(o[1]) << 16),
+                                                 round_bits(o[2]) | (round_bits(o[3]) << 16));
   }
   // q . k over one chunk with v_dot2_f32_bf16: products of bf16 pairs are
   // exact in fp32, accumulated in fp32
@@ -145,30 +154,131 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ u32x4 load16(const char *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// KV page chunks are read once per call: non-temporal loads keep them from
+// displacing reusable lines in the caches (measured on MI355X at the
+// Llama-2-7B decode shape: 200 us -> 182 us for the partition pass)
+__device__ __forceinline__ u32x4 load_kv16(const char *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
 // ------------------------------------------------------ decode, partition pass
-// 1-D grid of max_parts * num_seqs * num_kv_heads blocks, 64 threads.  Block (p, g, s)
-// handles the G query heads of kv-head g over pages [p*PP, (p+1)*PP) of
-// sequence s.
+// One workgroup of NW wavefronts per unit (sequence s, kv-head g, partition
+// p of at most part_pages pages).  The unit's pages are dealt to its waves
+// in turn: wave w takes partition pages w, w + NW, w + 2 NW, ...  Each wave
+// keeps a running (max, sum, V accumulator) for the G query heads of g over
+// its own pages, with PF pages of K and V in flight; the NW partial states
+// are merged through LDS at the end, which is the same log-sum-exp merge the
+// reduce kernel applies across partitions.
+//
+// Grid: 1-D, max_parts * num_seqs * num_kv_heads workgroups, ordered
+// kv-head fastest, then sequence, then partition.  The hardware hands
+// consecutive workgroups to the 8 XCDs in turn, so this order gives every
+// XCD the same share of each sequence's heads whatever the spread of
+// context lengths (partition-fastest order would send partition p of every
+// sequence to one XCD).
 template <class T, int D, int BS, int G>
-__global__ __launch_bounds__(64) void pa_decode_partition(
+struct DecodeShape {
+  static constexpr int E = T::kPerChunk;       // elements per 16-byte chunk
+  static constexpr int R = D / E;              // lanes (chunks) per token row
+  static constexpr int TPI = 64 / R;           // token rows per load instruction
+  static constexpr int NLD = BS / TPI;         // load instructions per page
+  static constexpr int PAGE_BYTES = BS * D * T::kBytes;
+  static_assert(NLD * 1024 == PAGE_BYTES, "a page is whole 1 KiB wave loads");
+  // pages in flight per wave: two where the registers allow it
+  static constexpr int PF = (NLD <= 4 && G <= 2) ? 2 : 1;
+};
+
+template <class T, int D, int BS, int G>
+struct WaveSoftmax {
+  using S = DecodeShape<T, D, BS, G>;
+  float m[G];           // running max of the logits, log2 units (wave-uniform)
+  float l[G];           // this lane's share of the running sum
+  float acc[G][S::E];   // this lane's share of sum p * V over its d-chunk
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < S::E; ++e) acc[h][e] = 0.f;
+    }
+  }
+
+  // Fold one page into the state.  tok0: logical index of the page's first
+  // token; live: whether the page id was valid; rg: this lane's token-row
+  // group.  Tokens at or past ctx get weight exactly 0 and their V is never
+  // used in arithmetic (a masked slot may hold NaN).
+  __device__ __forceinline__ void page(const u32x4 (&qc)[G], const u32x4 (&kc)[S::NLD],
+                                       const u32x4 (&vc)[S::NLD], int tok0, int ctx, bool live,
+                                       int rg, float scale_log2) {
+    float lg[S::NLD][G];
+#pragma unroll
+    for (int i = 0; i < S::NLD; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) lg[i][h] = row_sum<S::R>(T::dot(qc[h], kc[i])) * scale_log2;
+    bool keep[S::NLD];
+#pragma unroll
+    for (int i = 0; i < S::NLD; ++i) {
+      keep[i] = live && (tok0 + i * S::TPI + rg < ctx);
+      if (!keep[i])
+#pragma unroll
+        for (int h = 0; h < G; ++h) lg[i][h] = -INFINITY;
+    }
+    float p[S::NLD][G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float pm = lg[0][h];
+#pragma unroll
+      for (int i = 1; i < S::NLD; ++i) pm = fmaxf(pm, lg[i][h]);
+      pm = group_max<S::R>(pm);
+      const float mn = fmaxf(m[h], pm);
+      if (mn == -INFINITY) {
+        // nothing live so far (only possible when page ids are invalid)
+#pragma unroll
+        for (int i = 0; i < S::NLD; ++i) p[i][h] = 0.f;
+        continue;
+      }
+      const float alpha = fast_exp2(m[h] - mn);
+      m[h] = mn;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < S::E; ++e) acc[h][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < S::NLD; ++i) {
+        p[i][h] = fast_exp2(lg[i][h] - mn);
+        l[h] += p[i][h];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < S::NLD; ++i) {
+      float vf[S::E];
+      T::unpack(vc[i], vf);
+      if (!keep[i])
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) vf[e] = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) acc[h][e] = fmaf(p[i][h], vf[e], acc[h][e]);
+    }
+  }
+};
+
+template <class T, int D, int BS, int G, int NW>
+__global__ __launch_bounds__(64 * NW) void pa_decode_partition(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, int num_seqs, int num_heads, int num_kv_heads, int max_blocks,
     int num_blocks, int part_pages, int max_parts, float scale_log2) {
-  constexpr int E = T::kPerChunk;      // elements per 16-byte chunk
-  constexpr int R = D / E;             // lanes (chunks) per token row
-  constexpr int TPI = 64 / R;          // token rows per load instruction
-  constexpr int NLD = BS / TPI;        // load instructions per page
-  constexpr int PAGE_BYTES = BS * D * T::kBytes;
-  static_assert(NLD * 1024 == PAGE_BYTES, "page = whole 1 KiB wave loads");
+  using S = DecodeShape<T, D, BS, G>;
+  constexpr int E = S::E, R = S::R, NLD = S::NLD, PAGE_BYTES = S::PAGE_BYTES;
+  __shared__ float s_ml[NW][G][2];
+  __shared__ __attribute__((aligned(16))) float s_acc[NW][G][D];
 
-  const int lane = threadIdx.x;
-  // Block order: kv-head fastest, then sequence, then partition.  The
-  // hardware hands consecutive workgroups to the 8 XCDs in turn, so this
-  // order gives every XCD the same share of each sequence's heads, whatever
-  // the spread of context lengths; partition-fastest order would send
-  // partition p of every sequence to the same XCD.
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.x % num_kv_heads;
   const int sp = blockIdx.x / num_kv_heads;
   const int s = sp % num_seqs;
@@ -176,151 +286,147 @@ __global__ __launch_bounds__(64) void pa_decode_partition(
   const int dc = lane % R;
   const int rg = lane / R;
   const int h0 = g * G;
-
-  int ctx = context_lens[s];
-  ctx = min(max(ctx, 0), max_blocks * BS);
-  const int npages = (ctx + BS - 1) / BS;
   const int p_begin = part * part_pages;
 
-  char *out_b = reinterpret_cast<char *>(out);
+  // Independent loads first: the context length, this wave's page ids (one
+  // per lane; columns past the context are loaded but never used) and q.
+  int ctx = context_lens[s];
+  const int col = p_begin + wave + NW * lane;
+  int my_bid = -1;
+  if (wave + NW * lane < part_pages && col < max_blocks)
+    my_bid = block_tables[(size_t)s * max_blocks + col];
   const size_t head_row_bytes = (size_t)D * T::kBytes;
-
-  if (ctx == 0) {
-    if (part == 0 && rg == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float z[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) z[e] = 0.f;
-        *reinterpret_cast<u32x4 *>(out_b + ((size_t)s * num_heads + h0 + h) * head_row_bytes +
-                                   dc * 16) = T::pack(z);
-      }
-    }
-    return;
-  }
-  if (p_begin >= npages) return;
-  const int np = min(npages - p_begin, part_pages);
-
-  // physical page ids of this partition, one per lane
-  int my_bid = 0;
-  if (lane < np) my_bid = block_tables[(size_t)s * max_blocks + p_begin + lane];
-
   u32x4 qc[G];
   const char *q_b = reinterpret_cast<const char *>(q);
 #pragma unroll
   for (int h = 0; h < G; ++h)
     qc[h] = load16(q_b + ((size_t)s * num_heads + h0 + h) * head_row_bytes + dc * 16);
 
-  float m[G], l[G], acc[G][E];
+  ctx = min(max(ctx, 0), max_blocks * BS);
+  const int npages = (ctx + BS - 1) / BS;
+  char *out_b = reinterpret_cast<char *>(out);
+  if (ctx == 0) {
+    if (part == 0 && wave == 0 && rg == 0) {
+      float z[E];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
+      for (int e = 0; e < E; ++e) z[e] = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+      for (int h = 0; h < G; ++h)
+        *reinterpret_cast<u32x4 *>(out_b + ((size_t)s * num_heads + h0 + h) * head_row_bytes +
+                                   dc * 16) = T::pack(z);
+    }
+    return;
   }
+  if (p_begin >= npages) return;
+  const int np = min(npages - p_begin, part_pages);
+  const int np_w = wave < np ? (np - wave + NW - 1) / NW : 0;  // this wave's pages
 
+  WaveSoftmax<T, D, BS, G> st;
+  st.init();
   const size_t page_stride = (size_t)num_kv_heads * PAGE_BYTES;
   const char *k_b = reinterpret_cast<const char *>(k_pool) + (size_t)g * PAGE_BYTES + lane * 16;
   const char *v_b = reinterpret_cast<const char *>(v_pool) + (size_t)g * PAGE_BYTES + lane * 16;
 
-  for (int j = 0; j < np; ++j) {
+  // page j of this wave: its id, whether it is valid, and its loads
+  auto fetch = [&](u32x4 (&kc)[NLD], u32x4 (&vc)[NLD], int j) -> bool {
     const int bid = __builtin_amdgcn_readlane(my_bid, j);
-    if ((unsigned)bid >= (unsigned)num_blocks) continue;  // precondition violated: skip page
-    const char *kp = k_b + (size_t)bid * page_stride;
-    const char *vp = v_b + (size_t)bid * page_stride;
-    u32x4 kc[NLD], vc[NLD];
+    const bool ok = (unsigned)bid < (unsigned)num_blocks;
+    const size_t off = (size_t)(ok ? bid : 0) * page_stride;  // an invalid id reads page 0, unused
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) kc[i] = load16(kp + i * 1024);
+    for (int i = 0; i < NLD; ++i) kc[i] = load_kv16(k_b + off + i * 1024);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) vc[i] = load16(vp + i * 1024);
+    for (int i = 0; i < NLD; ++i) vc[i] = load_kv16(v_b + off + i * 1024);
+    return ok;
+  };
+  auto tok0 = [&](int j) { return (p_begin + wave + NW * j) * BS; };
 
-    float lg[NLD][G];
-#pragma unroll
-    for (int i = 0; i < NLD; ++i)
-#pragma unroll
-      for (int h = 0; h < G; ++h) lg[i][h] = row_sum<R>(T::dot(qc[h], kc[i])) * scale_log2;
-
-    const int tok0 = (p_begin + j) * BS;
-    const bool tail = tok0 + BS > ctx;
-    if (tail) {
-#pragma unroll
-      for (int i = 0; i < NLD; ++i)
-        if (tok0 + i * TPI + rg >= ctx)
-#pragma unroll
-          for (int h = 0; h < G; ++h) lg[i][h] = -INFINITY;
-    }
-
-    float p[NLD][G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float pm = lg[0][h];
-#pragma unroll
-      for (int i = 1; i < NLD; ++i) pm = fmaxf(pm, lg[i][h]);
-      pm = group_max<R>(pm);
-      const float mn = fmaxf(m[h], pm);
-      const float alpha = fast_exp2(m[h] - mn);
-      m[h] = mn;
-      l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        p[i][h] = fast_exp2(lg[i][h] - mn);
-        l[h] += p[i][h];
+  if constexpr (S::PF == 2) {
+    // Two buffers, one page ahead.  Inside the loop every fetch is
+    // unconditional, so the number of loads in flight is the same on every
+    // path and the compiler's wait before a page's use lets the next page's
+    // loads stay outstanding; the last one or two pages are done after it.
+    if (np_w > 0) {
+      u32x4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
+      bool oka = fetch(ka, va, 0), okb;
+      int j = 0;
+      for (; j + 2 < np_w; j += 2) {
+        okb = fetch(kb, vb, j + 1);
+        st.page(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2);
+        oka = fetch(ka, va, j + 2);
+        st.page(qc, kb, vb, tok0(j + 1), ctx, okb, rg, scale_log2);
       }
-    }
-
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      float vf[E];
-      T::unpack(vc[i], vf);
-      if (tail && tok0 + i * TPI + rg >= ctx) {
-        // a masked slot may hold anything (NaN): it must not reach an FMA
-#pragma unroll
-        for (int e = 0; e < E; ++e) vf[e] = 0.f;
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p[i][h], vf[e], acc[h][e]);
-    }
-  }
-
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    l[h] = group_sum<R>(l[h]);
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[h][e] = group_sum<R>(acc[h][e]);
-  }
-
-  if (npages <= part_pages) {
-    // the whole sequence is in this partition: normalise and write out
-    if (rg == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float inv = 1.0f / l[h];
-        float o[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = acc[h][e] * inv;
-        *reinterpret_cast<u32x4 *>(out_b + ((size_t)s * num_heads + h0 + h) * head_row_bytes +
-                                   dc * 16) = T::pack(o);
+      if (j + 1 < np_w) {
+        okb = fetch(kb, vb, j + 1);
+        st.page(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2);
+        st.page(qc, kb, vb, tok0(j + 1), ctx, okb, rg, scale_log2);
+      } else {
+        st.page(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2);
       }
     }
   } else {
+    for (int j = 0; j < np_w; ++j) {
+      u32x4 kc[NLD], vc[NLD];
+      const bool ok = fetch(kc, vc, j);
+      st.page(qc, kc, vc, tok0(j), ctx, ok, rg, scale_log2);
+    }
+  }
+
+  // this wave's totals: sum the row groups' shares
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.l[h] = group_sum<R>(st.l[h]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) st.acc[h][e] = group_sum<R>(st.acc[h][e]);
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<float4 *>(&s_acc[wave][h][dc * E + e]) =
+            make_float4(st.acc[h][e], st.acc[h][e + 1], st.acc[h][e + 2], st.acc[h][e + 3]);
+  }
+  if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const size_t row = ((size_t)s * num_heads + h0 + h) * max_parts + part;
-      if (rg == 0) {
-        float *dst = ws_acc + row * D + dc * E;
+      s_ml[wave][h][0] = st.m[h];
+      s_ml[wave][h][1] = st.l[h];
+    }
+  }
+  __syncthreads();
+
+  // merge the waves: thread t owns 4 consecutive outputs of one head
+  const bool whole = npages <= part_pages;
+  for (int idx = threadIdx.x; idx < G * D / 4; idx += 64 * NW) {
+    const int h = idx / (D / 4);
+    const int d = (idx % (D / 4)) * 4;
+    float M = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < E; e += 4)
-          *reinterpret_cast<float4 *>(dst + e) =
-              make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][h][0]);
+    float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float sc = fast_exp2(s_ml[w][h][0] - M);
+        L = fmaf(s_ml[w][h][1], sc, L);
+        const float4 a = *reinterpret_cast<const float4 *>(&s_acc[w][h][d]);
+        o[0] = fmaf(a.x, sc, o[0]);
+        o[1] = fmaf(a.y, sc, o[1]);
+        o[2] = fmaf(a.z, sc, o[2]);
+        o[3] = fmaf(a.w, sc, o[3]);
       }
-      if (lane == 0) {
-        ws_ml[row * 2] = m[h];
-        ws_ml[row * 2 + 1] = l[h];
+    }
+    if (whole) {
+      const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] *= inv;
+      T::store4(out_b + ((size_t)s * num_heads + h0 + h) * head_row_bytes + d * T::kBytes, o);
+    } else {
+      const size_t row = ((size_t)s * num_heads + h0 + h) * max_parts + part;
+      *reinterpret_cast<float4 *>(ws_acc + row * D + d) = make_float4(o[0], o[1], o[2], o[3]);
+      if (d == 0) {
+        ws_ml[row * 2] = M;
+        ws_ml[row * 2 + 1] = L;
       }
     }
   }
@@ -423,13 +529,16 @@ __global__ __launch_bounds__(kProbeThreads) void pa_hbm_probe(const u32x4 *__res
 }
 
 // ------------------------------------------------------------- dispatch
+constexpr int kWavesPerUnit = 4;
+
 template <class T, int D, int BS, int G>
 int run_decode(const pa_internal::DecodeLaunch &a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   const float scale_log2 = a.scale * kLog2e;
   if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
   dim3 grid((unsigned)a.max_parts * a.num_kv_heads * a.num_seqs);
-  hipLaunchKernelGGL((pa_decode_partition<T, D, BS, G>), grid, dim3(64), 0, st, a.out, a.q,
+  hipLaunchKernelGGL((pa_decode_partition<T, D, BS, G, kWavesPerUnit>), grid,
+                     dim3(64 * kWavesPerUnit), 0, st, a.out, a.q,
                      a.k_pool, a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc,
                      a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks, a.part_pages,
                      a.max_parts, scale_log2);

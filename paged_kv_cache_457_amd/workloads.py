@@ -113,6 +113,9 @@ class Workload:
     refcount: np.ndarray
     seed: int
     extra: Dict[str, object] = field(default_factory=dict)
+    # split-K partition size the configuration names, in tokens (0: the
+    # library's default)
+    partition_size: int = 0
 
     @property
     def group(self) -> int:
@@ -314,8 +317,10 @@ def make_config(index: int, seed: Optional[int] = None) -> Workload:
                               max_blocks_per_seq=8192 // 16, rng=rng)
     if index == 4:
         ctx = np.full(8, 32768, dtype=np.int64)
-        return build_workload("c4", ctx, 32, 8, 128, 32, "bf16", seed,
-                              max_blocks_per_seq=32768 // 32, rng=rng)
+        w = build_workload("c4", ctx, 32, 8, 128, 32, "bf16", seed,
+                           max_blocks_per_seq=32768 // 32, rng=rng)
+        w.partition_size = 512
+        return w
     if index == 5:
         prompts, samples, prefix = 16, 8, 1024
         div = rng.integers(0, 256, size=(prompts, samples), endpoint=True)

@@ -77,7 +77,8 @@ expect("zero max_blocks", decode(dims(max_blocks_per_seq=0)), _lib.PA_ERR_SHAPE)
 expect("zero num_blocks", decode(dims(num_blocks=0)), _lib.PA_ERR_SHAPE)
 expect("reserved nonzero", decode(dims(reserved=1)), _lib.PA_ERR_SHAPE)
 expect("partition not a page multiple", decode(dims(partition_size=100)), _lib.PA_ERR_SHAPE)
-expect("partition over 64 pages", decode(dims(partition_size=16 * 65)), _lib.PA_ERR_SHAPE)
+expect("partition over 256 pages", decode(dims(partition_size=16 * 257)), _lib.PA_ERR_SHAPE)
+expect("partition of 256 pages", decode(dims(partition_size=16 * 256)), _lib.PA_OK)
 expect("negative partition", decode(dims(partition_size=-16)), _lib.PA_ERR_SHAPE)
 expect("scale NaN", decode(dims(), scale=float("nan")), _lib.PA_ERR_SHAPE)
 expect("scale inf", decode(dims(), scale=float("inf")), _lib.PA_ERR_SHAPE)
@@ -93,7 +94,7 @@ expect("block_tables misaligned", decode(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_AL
 # still fails validation (missing / small / misaligned workspace)
 need_d = dims(num_seqs=4)
 need = lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(need_d))
-expect("workspace bytes formula", need, 4 * 32 * ((128 * 16 + 255) // 256) * (128 + 2) * 4)
+expect("workspace bytes formula", need, 4 * 32 * ((128 * 16 + 1023) // 1024) * (128 + 2) * 4)
 expect("workspace missing", decode(dims(num_seqs=4)), _lib.PA_ERR_WORKSPACE)
 expect("workspace too small",
        decode(dims(num_seqs=4, workspace=P, workspace_bytes=need - 4)), _lib.PA_ERR_WORKSPACE)

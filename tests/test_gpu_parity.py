@@ -104,7 +104,7 @@ def test_decode_step_parity(idx):
     say(f"decode step c{idx}: S={w.num_seqs} H={w.num_heads}/{w.num_kv_heads} "
         f"D={w.head_dim} bs={w.block_size} {w.dtype}")
     dw = upload(w)
-    got = gpu_step(dw)
+    got = gpu_step(dw, partition_size=w.partition_size)
     ref, kp, vp = oracle_step(w)
     assert to_host(dw.k_pool, w.dtype).tobytes() == kp.tobytes()
     err = max_err(got, ref, w.dtype)
