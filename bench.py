@@ -51,26 +51,44 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_sha256() -> str:
+# Sources that define each partition kernel; a recorded traffic figure is
+# valid only while their combined hash is unchanged.
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_457_amd", "csrc")
+KERNEL_SOURCES = {
+    "pa_decode_partition": ["pagedattn_decode.hip", "pagedattn_device.h", "pagedattn_internal.h"],
+    "pa_decode_partition_gqa": ["pagedattn_decode_gqa.hip", "pagedattn_device.h",
+                                "pagedattn_internal.h"],
+}
+
+
+def dominant_kernel(w) -> str:
+    """The partition kernel the library runs for this workload: bf16 with a
+    group of query heads per kv-head goes to the matrix-core kernel."""
+    return "pa_decode_partition_gqa" if (w.dtype == "bf16" and w.group >= 2) \
+        else "pa_decode_partition"
+
+
+def kernel_source_sha256(kernel: str) -> str:
     import hashlib
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_457_amd",
-                        "csrc", "pagedattn_kernels.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def measured_traffic(args):
+def measured_traffic(args, kernel):
     """HBM bytes per partition-kernel launch from a committed counter run,
     or None when there is none for this workload or the kernel source has
     changed since the counters were taken."""
     path = args.traffic_json or os.path.join(
         os.path.dirname(os.path.abspath(__file__)), "profiles",
-        f"traffic_pa_decode_partition_c{args.config}.json")
+        f"traffic_{kernel}_c{args.config}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+    if rec.get("kernel") != kernel or rec.get("kernel_source_sha256") != kernel_source_sha256(kernel):
         return None
     if rec.get("config_index") != args.config or rec.get("partition_size") != \
             args.effective_partition or rec.get("seed") != args.seed:
@@ -172,7 +190,8 @@ def main():
 
     kv_bytes = w.kv_bytes()
     achieved = kv_bytes / (k1_avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args)
+    kernel = dominant_kernel(w)
+    traffic = measured_traffic(args, kernel)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -233,7 +252,7 @@ def main():
         "wall_s_timed_region": round(t_wall, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode_partition",
+            "kernel": kernel,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -54,7 +54,7 @@ enum {
   PA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
   PA_ERR_UNSUPPORTED = 3, /* valid but not built: dtype, head_dim, block_size, group */
   PA_ERR_ALIGN = 4,       /* a pointer is not 16-byte (tables: 4/8-byte) aligned */
-  PA_ERR_WORKSPACE = 5,   /* split-K workspace missing, too small or misaligned */
+  PA_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
   PA_ERR_HIP = 6          /* the HIP runtime reported a launch error */
 };
 
@@ -71,9 +71,10 @@ typedef struct pa_decode_dims {
   int32_t partition_size;      /* tokens per split-K partition; 0 = default (1024);
                                   a multiple of block_size, at most 256 pages */
   int32_t reserved;            /* must be 0 */
-  void *workspace;             /* fp32 scratch for split-K partials, caller-owned;
-                                  may be NULL when max_blocks_per_seq * block_size
-                                  <= partition_size (no sequence can split) */
+  void *workspace;             /* device scratch, caller-owned, 16-byte aligned, at
+                                  least paged_attention_decode_workspace_bytes();
+                                  required whenever num_seqs > 0 (it holds the
+                                  work plan and the split-K partials) */
   size_t workspace_bytes;
   void *stream;                /* hipStream_t */
   void *timing_events[2];      /* optional hipEvent_t pair (or NULLs): recorded on
@@ -103,6 +104,16 @@ typedef struct pa_decode_dims {
  * whose partial (max, sum, weighted V) go to the workspace and are merged by
  * a log-sum-exp reduce kernel; the result is the same softmax up to fp32
  * rounding.  Accumulation is fp32; bf16 results are rounded to nearest even.
+ * With bf16 and 2-8 query heads per kv-head the contractions run on the
+ * matrix cores, with the softmax weights entering as a pair of bf16 terms
+ * (about 16 significant bits).
+ *
+ * Launches, all on dims->stream: a one-workgroup plan kernel (orders the
+ * (sequence, partition) work units by size into the workspace), the
+ * partition kernel (timing_events bracket this one), and the reduce kernel
+ * when some sequence can span more than one partition.  The result does not
+ * depend on the order units run in: each output element is computed by one
+ * fixed sequence of operations on its sequence's tokens.
  *
  * Device-side preconditions (not checked on the host, which cannot read
  * device memory): the first ceil(L / block_size) entries of each used table
@@ -116,11 +127,11 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool,
                            const pa_decode_dims *dims);
 
 /*
- * Workspace bytes paged_attention_decode needs for these shapes:
- * num_seqs * num_heads * P * (head_dim + 2) * 4 with
- * P = ceil(max_blocks_per_seq * block_size / partition_size), or 0 when no
- * sequence can span more than one partition.  Returns SIZE_MAX when the
- * shapes are invalid.
+ * Workspace bytes paged_attention_decode needs for these shapes, with
+ * P = ceil(max_blocks_per_seq * block_size / partition_size):
+ *   the work plan, 4 * (4 + num_seqs * P) rounded up to 256, plus, when
+ *   P > 1, the split-K partials num_seqs * num_heads * P * (head_dim + 2) * 4.
+ * 0 when num_seqs is 0.  Returns SIZE_MAX when the shapes are invalid.
  */
 size_t paged_attention_decode_workspace_bytes(int32_t block_size,
                                               const pa_decode_dims *dims);

@@ -85,8 +85,8 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     """out[S,H,D] <- paged decode attention (see paged_attention_decode in
     include/pagedattn.h).  Pools are [num_blocks, num_kv_heads, block_size,
     head_dim]; the kv-head count and block size are read off k_pool.
-    ``scale`` defaults to 1/sqrt(head_dim).  A workspace is allocated here
-    when none is given and the shapes need one."""
+    ``scale`` defaults to 1/sqrt(head_dim).  A workspace (unit plan and
+    split-K partials) is allocated here when none is given."""
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     for name, t in (("out", out), ("k_pool", k_pool), ("v_pool", v_pool)):

@@ -11,9 +11,8 @@
 namespace {
 
 constexpr int kDefaultPartitionTokens = 1024;
-// The partition kernel runs 4 wavefronts per partition and deals its pages
-// to them in turn; each wavefront holds one page id per lane.
-constexpr int kMaxPartitionPages = 4 * 64;
+using pa_internal::kMaxPartitionPages;
+using pa_internal::kPlanHeader;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -41,12 +40,27 @@ int check_decode_dims(int32_t num_kv_heads, int32_t block_size, const pa_decode_
   if (pt % block_size != 0 || pt / block_size > kMaxPartitionPages) return PA_ERR_SHAPE;
   // context capacity must fit in int32 token counts
   if ((int64_t)d->max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  // units (sequence, partition) and work items (unit, kv-head) are int32
+  const int64_t parts = ((int64_t)d->max_blocks_per_seq * block_size + pt - 1) / pt;
+  if ((int64_t)d->num_seqs * parts * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
   return PA_OK;
 }
 
 int max_partitions(int32_t block_size, const pa_decode_dims *d) {
   const int pp = partition_tokens(d) / block_size;
   return (d->max_blocks_per_seq + pp - 1) / pp;
+}
+
+// Workspace layout: the unit plan (int32, rounded up to 256 bytes), then,
+// when a sequence can span more than one partition, the partials:
+// fp32 accumulators [S, H, P, D] followed by (max, sum) pairs [S, H, P, 2].
+size_t plan_bytes(int num_seqs, int parts) {
+  const size_t b = ((size_t)kPlanHeader + (size_t)num_seqs * parts) * sizeof(int32_t);
+  return (b + 255) / 256 * 256;
+}
+size_t partial_bytes(const pa_decode_dims *d, int parts) {
+  if (parts <= 1) return 0;
+  return (size_t)d->num_seqs * d->num_heads * parts * (size_t)(d->head_dim + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -58,10 +72,9 @@ size_t paged_attention_decode_workspace_bytes(int32_t block_size, const pa_decod
   // num_kv_heads = num_heads (group 1, always built) validates the rest.
   if (!dims || dims->num_heads < 1) return SIZE_MAX;
   if (check_decode_dims(dims->num_heads, block_size, dims) != PA_OK) return SIZE_MAX;
+  if (dims->num_seqs == 0) return 0;
   const int mp = max_partitions(block_size, dims);
-  if (mp <= 1) return 0;
-  return (size_t)dims->num_seqs * dims->num_heads * mp * (size_t)(dims->head_dim + 2) *
-         sizeof(float);
+  return plan_bytes(dims->num_seqs, mp) + partial_bytes(dims, mp);
 }
 
 int paged_attention_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
@@ -78,17 +91,16 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool, const v
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PA_ERR_ALIGN;
   const int mp = max_partitions(block_size, dims);
-  float *ws_ml = nullptr;
+  const size_t pb = plan_bytes(dims->num_seqs, mp);
+  if (!dims->workspace || dims->workspace_bytes < pb + partial_bytes(dims, mp) ||
+      !aligned(dims->workspace, 16))
+    return PA_ERR_WORKSPACE;
+  char *ws = static_cast<char *>(dims->workspace);
   float *ws_acc = nullptr;
+  float *ws_ml = nullptr;
   if (mp > 1) {
-    const size_t need = (size_t)dims->num_seqs * dims->num_heads * mp *
-                        (size_t)(dims->head_dim + 2) * sizeof(float);
-    if (need > 0) {
-      if (!dims->workspace || dims->workspace_bytes < need || !aligned(dims->workspace, 16))
-        return PA_ERR_WORKSPACE;
-      ws_acc = static_cast<float *>(dims->workspace);
-      ws_ml = ws_acc + (size_t)dims->num_seqs * dims->num_heads * mp * dims->head_dim;
-    }
+    ws_acc = reinterpret_cast<float *>(ws + pb);
+    ws_ml = ws_acc + (size_t)dims->num_seqs * dims->num_heads * mp * dims->head_dim;
   }
 
   pa_internal::DecodeLaunch a{};
@@ -98,6 +110,7 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool, const v
   a.v_pool = v_pool;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.plan = reinterpret_cast<int32_t *>(ws);
   a.ws_ml = ws_ml;
   a.ws_acc = ws_acc;
   a.num_seqs = dims->num_seqs;

@@ -1,0 +1,485 @@
+// Paged decode attention, partition pass (VALU path) and log-sum-exp reduce.
+//
+// Method (vLLM / PagedAttention pages): the KV cache is a pool of fixed-size
+// pages; a per-sequence page table maps logical to physical pages and the
+// attention kernel reads the pages through that table directly, with no
+// gather copy and no padding (showapi.com article, section 2.1; tutorial
+// page, section 4.2).
+//
+// This file holds the VALU partition kernel (every dtype and head group;
+// used for fp32 and for bf16 with one query head per kv-head), the reduce
+// kernel that merges split-K partitions, and the dispatch that picks the
+// partition kernel.  The grouped-query bf16 kernel on the matrix cores is
+// in pagedattn_decode_gqa.hip.
+//
+// Lane layout of the VALU kernel: each (page, kv-head) run of
+// block_size * head_dim elements is read as whole 16-byte chunks; lane l,
+// load i takes chunk i*64 + l, so every load instruction covers 1 KiB of
+// consecutive bytes.  With R = chunks per token row, a load instruction holds
+// 64/R tokens and lane l always sees the same R-chunk column (l % R) of
+// token rows (l / R) + i*64/R.  The partial q.K dot products of a row are
+// summed across its R lanes with DPP row operations, so every lane of the
+// row ends up holding the full logit.  Softmax is the online form (running
+// max, rescaled running sum and accumulator) in log2 units, with log2(e)
+// folded into the scale.
+#include <atomic>
+
+#include "pagedattn_device.h"
+#include "pagedattn_internal.h"
+
+namespace {
+
+using namespace pa_dev;
+using pa_internal::kMaxPartitionPages;
+using pa_internal::kPlanHeader;
+
+// ------------------------------------------------------ decode, partition pass
+// One workgroup of NW wavefronts per unit (sequence s, kv-head g, partition
+// p of at most part_pages pages).  The unit's pages are dealt to its waves
+// in turn: wave w takes partition pages w, w + NW, w + 2 NW, ...  Each wave
+// keeps a running (max, sum, V accumulator) for the G query heads of g over
+// its own pages, with PF pages of K and V in flight; the NW partial states
+// are merged through LDS at the end, which is the same log-sum-exp merge the
+// reduce kernel applies across partitions.
+//
+// Scheduling: a plan kernel sorts the (sequence, partition) units by size,
+// largest first, and a persistent grid (as many workgroups as the GPU holds
+// at once) walks that list with the kv-head fastest; see pa_decode_plan and
+// pa_decode_partition below.
+template <class T, int D, int BS, int G>
+struct DecodeShape {
+  static constexpr int E = T::kPerChunk;       // elements per 16-byte chunk
+  static constexpr int R = D / E;              // lanes (chunks) per token row
+  static constexpr int TPI = 64 / R;           // token rows per load instruction
+  static constexpr int NLD = BS / TPI;         // load instructions per page
+  static constexpr int PAGE_BYTES = BS * D * T::kBytes;
+  static_assert(NLD * 1024 == PAGE_BYTES, "a page is whole 1 KiB wave loads");
+  // pages in flight per wave: two where the registers allow it
+  static constexpr int PF = (NLD <= 4 && G <= 2) ? 2 : 1;
+};
+
+template <class T, int D, int BS, int G>
+struct WaveSoftmax {
+  using S = DecodeShape<T, D, BS, G>;
+  float m[G];           // running max of the logits, log2 units (wave-uniform)
+  float l[G];           // this lane's share of the running sum
+  float acc[G][S::E];   // this lane's share of sum p * V over its d-chunk
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < S::E; ++e) acc[h][e] = 0.f;
+    }
+  }
+
+  // Fold one page into the state.  tok0: logical index of the page's first
+  // token; live: whether the page id was valid; rg: this lane's token-row
+  // group.  Tokens at or past ctx get weight exactly 0 and their V is never
+  // used in arithmetic (a masked slot may hold NaN).
+  __device__ __forceinline__ void page(const u32x4 (&qc)[G], const u32x4 (&kc)[S::NLD],
+                                       const u32x4 (&vc)[S::NLD], int tok0, int ctx, bool live,
+                                       int rg, float scale_log2) {
+    float lg[S::NLD][G];
+#pragma unroll
+    for (int i = 0; i < S::NLD; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) lg[i][h] = row_sum<S::R>(T::dot(qc[h], kc[i])) * scale_log2;
+    bool keep[S::NLD];
+#pragma unroll
+    for (int i = 0; i < S::NLD; ++i) {
+      keep[i] = live && (tok0 + i * S::TPI + rg < ctx);
+      if (!keep[i])
+#pragma unroll
+        for (int h = 0; h < G; ++h) lg[i][h] = -INFINITY;
+    }
+    float p[S::NLD][G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float pm = lg[0][h];
+#pragma unroll
+      for (int i = 1; i < S::NLD; ++i) pm = fmaxf(pm, lg[i][h]);
+      pm = group_max<S::R>(pm);
+      const float mn = fmaxf(m[h], pm);
+      if (mn == -INFINITY) {
+        // nothing live so far (only possible when page ids are invalid)
+#pragma unroll
+        for (int i = 0; i < S::NLD; ++i) p[i][h] = 0.f;
+        continue;
+      }
+      const float alpha = fast_exp2(m[h] - mn);
+      m[h] = mn;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < S::E; ++e) acc[h][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < S::NLD; ++i) {
+        p[i][h] = fast_exp2(lg[i][h] - mn);
+        l[h] += p[i][h];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < S::NLD; ++i) {
+      float vf[S::E];
+      T::unpack(vc[i], vf);
+      if (!keep[i])
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) vf[e] = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < S::E; ++e) acc[h][e] = fmaf(p[i][h], vf[e], acc[h][e]);
+    }
+  }
+};
+
+// One work unit: the G query heads of kv-head g over partition `part` of
+// sequence s.  All threads of the workgroup call it with the same unit.
+template <class T, int D, int BS, int G, int NW>
+__device__ __forceinline__ void decode_unit(
+    void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
+    const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
+    float *__restrict__ ws_acc, int num_heads, int num_kv_heads, int max_blocks,
+    int num_blocks, int part_pages, int max_parts, float scale_log2, int s, int g, int part) {
+  using S = DecodeShape<T, D, BS, G>;
+  constexpr int E = S::E, R = S::R, NLD = S::NLD, PAGE_BYTES = S::PAGE_BYTES;
+  __shared__ float s_ml[NW][G][2];
+  __shared__ __attribute__((aligned(16))) float s_acc[NW][G][D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int dc = lane % R;
+  const int rg = lane / R;
+  const int h0 = g * G;
+  const int p_begin = part * part_pages;
+
+  // Independent loads first: the context length, this wave's page ids (one
+  // per lane; columns past the context are loaded but never used) and q.
+  int ctx = context_lens[s];
+  const int col = p_begin + wave + NW * lane;
+  int my_bid = -1;
+  if (wave + NW * lane < part_pages && col < max_blocks)
+    my_bid = block_tables[(size_t)s * max_blocks + col];
+  const size_t head_row_bytes = (size_t)D * T::kBytes;
+  u32x4 qc[G];
+  const char *q_b = reinterpret_cast<const char *>(q);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qc[h] = load16(q_b + ((size_t)s * num_heads + h0 + h) * head_row_bytes + dc * 16);
+
+  ctx = min(max(ctx, 0), max_blocks * BS);
+  const int npages = (ctx + BS - 1) / BS;
+  char *out_b = reinterpret_cast<char *>(out);
+  if (ctx == 0) {
+    if (part == 0 && wave == 0 && rg == 0) {
+      float z[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) z[e] = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        *reinterpret_cast<u32x4 *>(out_b + ((size_t)s * num_heads + h0 + h) * head_row_bytes +
+                                   dc * 16) = T::pack(z);
+    }
+    return;
+  }
+  if (p_begin >= npages) return;
+  const int np = min(npages - p_begin, part_pages);
+  const int np_w = wave < np ? (np - wave + NW - 1) / NW : 0;  // this wave's pages
+
+  WaveSoftmax<T, D, BS, G> st;
+  st.init();
+  const size_t page_stride = (size_t)num_kv_heads * PAGE_BYTES;
+  const char *k_b = reinterpret_cast<const char *>(k_pool) + (size_t)g * PAGE_BYTES + lane * 16;
+  const char *v_b = reinterpret_cast<const char *>(v_pool) + (size_t)g * PAGE_BYTES + lane * 16;
+
+  // page j of this wave: its id, whether it is valid, and its loads
+  auto fetch = [&](u32x4 (&kc)[NLD], u32x4 (&vc)[NLD], int j) -> bool {
+    const int bid = __builtin_amdgcn_readlane(my_bid, j);
+    const bool ok = (unsigned)bid < (unsigned)num_blocks;
+    const size_t off = (size_t)(ok ? bid : 0) * page_stride;  // an invalid id reads page 0, unused
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) kc[i] = load_kv16(k_b + off + i * 1024);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) vc[i] = load_kv16(v_b + off + i * 1024);
+    return ok;
+  };
+  auto tok0 = [&](int j) { return (p_begin + wave + NW * j) * BS; };
+
+  if constexpr (S::PF == 2) {
+    // Two buffers, one page ahead.  Inside the loop every fetch is
+    // unconditional, so the number of loads in flight is the same on every
+    // path and the compiler's wait before a page's use lets the next page's
+    // loads stay outstanding; the last one or two pages are done after it.
+    if (np_w > 0) {
+      u32x4 ka[NLD], va[NLD], kb[NLD], vb[NLD];
+      bool oka = fetch(ka, va, 0), okb;
+      int j = 0;
+      for (; j + 2 < np_w; j += 2) {
+        okb = fetch(kb, vb, j + 1);
+        st.page(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2);
+        oka = fetch(ka, va, j + 2);
+        st.page(qc, kb, vb, tok0(j + 1), ctx, okb, rg, scale_log2);
+      }
+      if (j + 1 < np_w) {
+        okb = fetch(kb, vb, j + 1);
+        st.page(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2);
+        st.page(qc, kb, vb, tok0(j + 1), ctx, okb, rg, scale_log2);
+      } else {
+        st.page(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2);
+      }
+    }
+  } else {
+    for (int j = 0; j < np_w; ++j) {
+      u32x4 kc[NLD], vc[NLD];
+      const bool ok = fetch(kc, vc, j);
+      st.page(qc, kc, vc, tok0(j), ctx, ok, rg, scale_log2);
+    }
+  }
+
+  // this wave's totals: sum the row groups' shares
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.l[h] = group_sum<R>(st.l[h]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) st.acc[h][e] = group_sum<R>(st.acc[h][e]);
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<float4 *>(&s_acc[wave][h][dc * E + e]) =
+            make_float4(st.acc[h][e], st.acc[h][e + 1], st.acc[h][e + 2], st.acc[h][e + 3]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_ml[wave][h][0] = st.m[h];
+      s_ml[wave][h][1] = st.l[h];
+    }
+  }
+  __syncthreads();
+
+  merge_waves<T, D, G, NW>(
+      [&](int w, int h, int d) -> float4 {
+        return *reinterpret_cast<const float4 *>(&s_acc[w][h][d]);
+      },
+      [&](int w, int h) { return s_ml[w][h][0]; }, [&](int w, int h) { return s_ml[w][h][1]; },
+      npages <= part_pages, out_b + ((size_t)s * num_heads + h0) * head_row_bytes,
+      ws_acc + (((size_t)s * num_heads + h0) * max_parts + part) * D,
+      ws_ml + (((size_t)s * num_heads + h0) * max_parts + part) * 2, (size_t)max_parts);
+}
+
+// Persistent partition kernel: a grid sized to what the GPU holds at once
+// walks the unit list the plan kernel wrote, longest units first, item i =
+// (list[i / num_kv_heads], kv-head i % num_kv_heads); workgroup b takes items
+// b, b + gridDim.x, ...  Kv-head fastest gives every XCD (the hardware hands
+// consecutive workgroups to the 8 XCDs in turn) an equal share of each
+// sequence's heads.
+template <class T, int D, int BS, int G, int NW>
+__global__ __launch_bounds__(64 * NW) void pa_decode_partition(
+    void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
+    const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
+    float *__restrict__ ws_acc, const int32_t *__restrict__ plan, int num_heads,
+    int num_kv_heads, int max_blocks, int num_blocks, int part_pages, int max_parts,
+    float scale_log2) {
+  const int items = plan[0] * num_kv_heads;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int unit = plan[kPlanHeader + it / num_kv_heads];
+    decode_unit<T, D, BS, G, NW>(out, q, k_pool, v_pool, block_tables, context_lens, ws_ml,
+                                 ws_acc, num_heads, num_kv_heads, max_blocks, num_blocks,
+                                 part_pages, max_parts, scale_log2, unit / max_parts,
+                                 it % num_kv_heads, unit % max_parts);
+    __syncthreads();  // the next unit reuses the LDS the merge just read
+  }
+}
+
+// ----------------------------------------------------------- decode, plan
+// One workgroup orders the (sequence, partition) units for the persistent
+// partition kernels: a counting sort by page count, largest first, so the
+// shortest units finish the pass and no workgroup starts a long unit at the
+// end.  A sequence with context 0 gets one unit of size 0 (its output rows
+// are written as zeros).  Layout: plan[0] = unit count, plan[kPlanHeader +
+// k] = sequence * max_parts + partition.  Units of equal size are placed in
+// arbitrary order; results do not depend on the order units run in.
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void pa_decode_plan(
+    const int32_t *__restrict__ context_lens, int32_t *__restrict__ plan, int num_seqs,
+    int ctx_cap, int block_size, int part_pages, int max_parts) {
+  __shared__ int s_count[kMaxPartitionPages + 1];  // units per size 0..part_pages
+  __shared__ int s_next[kMaxPartitionPages + 1];   // next free slot per size
+  for (int i = threadIdx.x; i <= part_pages; i += kPlanThreads) s_count[i] = 0;
+  __syncthreads();
+  for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
+    const int ctx = min(max(context_lens[s], 0), ctx_cap);
+    const int np = (ctx + block_size - 1) / block_size;
+    if (np == 0) atomicAdd(&s_count[0], 1);
+    for (int p0 = 0; p0 < np; p0 += part_pages) atomicAdd(&s_count[min(part_pages, np - p0)], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int at = 0;
+    for (int z = part_pages; z >= 0; --z) {
+      s_next[z] = at;
+      at += s_count[z];
+    }
+    plan[0] = at;
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
+    const int ctx = min(max(context_lens[s], 0), ctx_cap);
+    const int np = (ctx + block_size - 1) / block_size;
+    if (np == 0) plan[kPlanHeader + atomicAdd(&s_next[0], 1)] = s * max_parts;
+    for (int p0 = 0, p = 0; p0 < np; p0 += part_pages, ++p)
+      plan[kPlanHeader + atomicAdd(&s_next[min(part_pages, np - p0)], 1)] = s * max_parts + p;
+  }
+}
+
+// ------------------------------------------------- decode, log-sum-exp merge
+// Grid (num_heads, num_seqs), 64 threads.  Merges the partitions of
+// sequences that span more than one: M = max_p m_p, w_p = 2^(m_p - M),
+// out = sum_p w_p acc_p / sum_p w_p l_p.
+template <class T, int D>
+__global__ __launch_bounds__(64) void pa_decode_reduce(
+    void *__restrict__ out, const float *__restrict__ ws_ml, const float *__restrict__ ws_acc,
+    const int32_t *__restrict__ context_lens, int num_heads, int ctx_cap, int part_tokens,
+    int max_parts) {
+  constexpr int DPL = D / 64;  // output elements per lane
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  int ctx = context_lens[s];
+  ctx = min(max(ctx, 0), ctx_cap);
+  const int nparts = (ctx + part_tokens - 1) / part_tokens;
+  if (nparts <= 1) return;
+  const size_t row0 = ((size_t)s * num_heads + h) * max_parts;
+
+  float M = -INFINITY;
+  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ws_ml[(row0 + p) * 2]);
+  M = wave_max(M);
+  float L = 0.f;
+  for (int p = lane; p < nparts; p += 64)
+    L += ws_ml[(row0 + p) * 2 + 1] * fast_exp2(ws_ml[(row0 + p) * 2] - M);
+  L = wave_sum(L);
+
+  float o[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) o[j] = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float w = fast_exp2(ws_ml[(row0 + p) * 2] - M);
+    const float *a = ws_acc + (row0 + p) * D + lane * DPL;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[j] = fmaf(w, a[j], o[j]);
+  }
+  const float inv = 1.0f / L;
+  if constexpr (T::kBytes == 4) {
+    float *dst = reinterpret_cast<float *>(out) + ((size_t)s * num_heads + h) * D + lane * DPL;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) dst[j] = o[j] * inv;
+  } else {
+    uint16_t *dst = reinterpret_cast<uint16_t *>(out) + ((size_t)s * num_heads + h) * D + lane * DPL;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) dst[j] = (uint16_t)BF16::round_bits(o[j] * inv);
+  }
+}
+
+constexpr int kWavesPerUnit = 4;
+
+template <class T, int D, int BS, int G>
+int launch_valu(const pa_internal::DecodeLaunch &a, float scale_log2) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  auto kernel = pa_decode_partition<T, D, BS, G, kWavesPerUnit>;
+  static const int per_cu = pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel),
+                                                       64 * kWavesPerUnit);
+  const unsigned grid = pa_internal::persistent_grid(a, per_cu);
+  if (grid == 0) return 6;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.out, a.q,
+                     a.k_pool, a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc,
+                     a.plan, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
+                     a.part_pages, a.max_parts, scale_log2);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+template <class T, int D, int BS>
+int partition_pass(const pa_internal::DecodeLaunch &a, float scale_log2) {
+  const int g = a.num_heads / a.num_kv_heads;
+  if constexpr (T::kBytes == 2) {
+    // bf16: one query head per kv-head here; head groups on the matrix cores
+    if (g >= 2) return pa_internal::launch_partition_gqa(a, scale_log2);
+    return launch_valu<T, D, BS, 1>(a, scale_log2);
+  } else {
+    switch (g) {
+      case 1: return launch_valu<T, D, BS, 1>(a, scale_log2);
+      case 2: return launch_valu<T, D, BS, 2>(a, scale_log2);
+      case 4: return launch_valu<T, D, BS, 4>(a, scale_log2);
+      case 8: return launch_valu<T, D, BS, 8>(a, scale_log2);
+    }
+    return 3;
+  }
+}
+
+template <class T, int D>
+int run_decode(const pa_internal::DecodeLaunch &a) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const float scale_log2 = a.scale * kLog2e;
+  hipLaunchKernelGGL(pa_decode_plan, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens, a.plan,
+                     a.num_seqs, a.max_blocks * a.block_size, a.block_size, a.part_pages,
+                     a.max_parts);
+  if (hipGetLastError() != hipSuccess) return 6;
+  if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
+  const int rc = a.block_size == 16 ? partition_pass<T, D, 16>(a, scale_log2)
+                                    : partition_pass<T, D, 32>(a, scale_log2);
+  if (rc != 0) return rc;
+  if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
+  if (a.max_parts > 1) {
+    hipLaunchKernelGGL((pa_decode_reduce<T, D>), dim3(a.num_heads, a.num_seqs), dim3(64), 0, st,
+                       a.out, a.ws_ml, a.ws_acc, a.context_lens, a.num_heads,
+                       a.max_blocks * a.block_size, a.part_pages * a.block_size, a.max_parts);
+    if (hipGetLastError() != hipSuccess) return 6;
+  }
+  return 0;
+}
+
+template <class T>
+int dispatch_dim(const pa_internal::DecodeLaunch &a) {
+  return a.head_dim == 64 ? run_decode<T, 64>(a) : run_decode<T, 128>(a);
+}
+
+}  // namespace
+
+namespace pa_internal {
+
+int blocks_per_cu(const void *kernel, int block_threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block_threads, 0) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+unsigned persistent_grid(const DecodeLaunch &a, int per_cu) {
+  // compute units of the current device, queried once per device
+  static std::atomic<int> cus_of[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  int cus = dev < kMaxDevices ? cus_of[dev].load(std::memory_order_relaxed) : 0;
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return 0;
+    if (dev < kMaxDevices) cus_of[dev].store(cus, std::memory_order_relaxed);
+  }
+  const long long resident = (long long)cus * per_cu;
+  const long long items = (long long)a.num_seqs * a.max_parts * a.num_kv_heads;
+  return (unsigned)(resident < items ? resident : items);
+}
+
+int launch_decode(const DecodeLaunch &a) {
+  return a.dtype == 0 ? dispatch_dim<F32>(a) : dispatch_dim<BF16>(a);
+}
+
+}  // namespace pa_internal

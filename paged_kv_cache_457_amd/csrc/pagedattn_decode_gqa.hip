@@ -1,0 +1,349 @@
+// Paged decode attention, partition pass for grouped-query attention in bf16
+// on the matrix cores (gfx950 MFMA).
+//
+// When G query heads share one kv-head (grouped-query attention; not on the
+// vLLM / PagedAttention pages, which describe the paged cache itself: page
+// table, fixed-size pages, attention reading pages through the table with no
+// copy -- showapi.com article, section 2.1; tutorial page, section 4.2), one
+// read of a K or V page serves G heads, so each page step is a small dense
+// contraction: S = K q^T over head_dim, then O = V^T P^T over the page's
+// tokens.  Both run on v_mfma instructions with the head group padded to 16
+// columns; the pass stays bound by HBM, and the matrix cores take the
+// multiply-adds off the vector ALUs.
+//
+// Work decomposition, scheduling and the merge of the NW waves' partial
+// states are those of the VALU partition kernel (pagedattn_decode.hip):
+// one workgroup of NW wavefronts per (sequence, kv-head, partition), pages
+// dealt to the waves in turn, a persistent grid walking the plan kernel's
+// largest-first unit list with the kv-head fastest.
+//
+// Lane layouts (lane l = 16*q4 + j16; 16x16 MFMA tiles):
+//   q.K   v_mfma_f32_16x16x32_bf16, one per 32-wide slab c of head_dim and
+//         16-token sub-block sb of the page.  A = K rows: lane l holds
+//         K[16*sb + j16][32*c + 8*q4 .. +7], one 16-byte global load.
+//         B = q^T: lane l holds q[head j16][32*c + 8*q4 .. +7] (zero for
+//         j16 >= G).  Result: lane l holds S[token 16*sb + 4*q4 + r][head j16],
+//         r = 0..3.
+//   P.V   v_mfma_f32_16x16x16_bf16, one per 16-wide column block n of
+//         head_dim and sub-block sb, accumulating O^T[d][head].
+//         B = P^T: lane l holds P[head j16][token 16*sb + 4*q4 + e] -- the
+//         q.K result registers after exp, so P never moves between lanes.
+//         A = V^T: lane l holds V[16*sb + 4*q4 + e][16*n + j16], e = 0..3,
+//         which is one ds_read_b64_tr_b16 from the page staged row-major in
+//         LDS (within each 16-lane group, lane j of the read supplies 4
+//         consecutive 16-bit values M[j][0..3] and lane i receives
+//         M[4e + i/4][i%4], e = 0..3).  Result: lane l holds
+//         O^T[16*n + 4*q4 + r][head j16], so the running max, sum and the
+//         rescale of O are all per lane (per head).
+// P enters the matrix cores as a bf16 pair hi + lo (hi = bf16(p), lo =
+// bf16(p - hi)), two MFMAs per tile, so the weights carry about 16
+// significant bits; the running sum uses the fp32 weights.
+// Masked tokens (at or past the context length, or on an invalid page) get
+// weight 0 and their V rows are written to LDS as zeros, so a poisoned slot
+// (NaN) never reaches a multiply.
+#include "pagedattn_device.h"
+#include "pagedattn_internal.h"
+
+namespace {
+
+using namespace pa_dev;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <int D, int BS, int G>
+struct GqaShape {
+  static_assert(G >= 2 && G <= 16, "head group padded to 16 MFMA columns");
+  static constexpr int NSB = BS / 16;              // 16-token sub-blocks per page
+  static constexpr int NC = D / 32;                // 32-wide head_dim slabs (q.K)
+  static constexpr int NN = D / 16;                // 16-wide head_dim blocks (P.V)
+  static constexpr int ROW = D * 2;                // bytes per token row
+  static constexpr int NVLD = BS * ROW / 1024;     // 1 KiB V loads per page
+  // LDS row pitch of the staged V page: 32 bytes of padding put the 8 rows a
+  // transposing read touches per half-wave in distinct banks
+  static constexpr int PITCH = ROW + 32;
+  static constexpr int VBYTES = BS * PITCH;
+  static constexpr int ACC_BYTES = G * D * 4;
+  // per-wave LDS: the staged V page, later reused for the wave's partial O
+  static constexpr int WAVE_LDS = VBYTES > ACC_BYTES ? VBYTES : ACC_BYTES;
+  static constexpr int PF = NSB == 1 ? 2 : 1;      // pages in flight per wave
+};
+
+template <int D, int BS, int G>
+struct GqaPage {
+  using S = GqaShape<D, BS, G>;
+  bf16x8 k[S::NSB][S::NC];
+  u32x4 v[S::NVLD];
+  bool ok;
+};
+
+// One work unit: the G query heads of kv-head g over partition `part` of
+// sequence s.  All threads of the workgroup call it with the same unit.
+template <int D, int BS, int G, int NW>
+__device__ __forceinline__ void decode_unit_gqa(
+    void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
+    const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
+    float *__restrict__ ws_acc, int num_heads, int num_kv_heads, int max_blocks,
+    int num_blocks, int part_pages, int max_parts, float scale_log2, int s, int g, int part) {
+  using S = GqaShape<D, BS, G>;
+  constexpr int NSB = S::NSB, NC = S::NC, NN = S::NN, ROW = S::ROW, NVLD = S::NVLD;
+  constexpr int PITCH = S::PITCH;
+  __shared__ __attribute__((aligned(16))) char s_wave[NW][S::WAVE_LDS];
+  __shared__ float s_ml[NW][G][2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q4 = lane >> 4;
+  const int j16 = lane & 15;
+  const int h0 = g * G;
+  const int p_begin = part * part_pages;
+
+  // Independent loads first: context length, this wave's page ids (one per
+  // lane; columns past the context are loaded but never used) and q as the
+  // B operand of the q.K tiles.
+  int ctx = context_lens[s];
+  const int col = p_begin + wave + NW * lane;
+  int my_bid = -1;
+  if (wave + NW * lane < part_pages && col < max_blocks)
+    my_bid = block_tables[(size_t)s * max_blocks + col];
+  bf16x8 qb[NC];
+  {
+    const char *qrow = reinterpret_cast<const char *>(q) + ((size_t)s * num_heads + h0 + j16) * ROW;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (j16 < G) w = load16(qrow + 64 * c + 16 * q4);
+      qb[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  ctx = min(max(ctx, 0), max_blocks * BS);
+  const int npages = (ctx + BS - 1) / BS;
+  char *out_b = reinterpret_cast<char *>(out);
+  if (ctx == 0) {
+    // the G output rows (contiguous) become zeros, 16 bytes per lane and step
+    if (part == 0 && wave == 0) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int off = lane * 16; off < G * ROW; off += 64 * 16)
+        *reinterpret_cast<u32x4 *>(out_b + ((size_t)s * num_heads + h0) * ROW + off) = z;
+    }
+    return;
+  }
+  if (p_begin >= npages) return;
+  const int np = min(npages - p_begin, part_pages);
+  const int np_w = wave < np ? (np - wave + NW - 1) / NW : 0;
+
+  // running state for head j16 (lanes j16 >= G carry a padding column)
+  float m = -INFINITY;  // max of the logits so far, log2 units, same in all 4 lane groups
+  float l = 0.f;        // this lane's share of the sum of weights
+  f32x4 o[NN];          // O^T[16n + 4*q4 + r][head j16]
+#pragma unroll
+  for (int n = 0; n < NN; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const size_t page_stride = (size_t)num_kv_heads * BS * ROW;
+  const char *k_b = reinterpret_cast<const char *>(k_pool) + (size_t)g * BS * ROW;
+  const char *v_b = reinterpret_cast<const char *>(v_pool) + (size_t)g * BS * ROW;
+  char *vs = s_wave[wave];
+
+  auto fetch = [&](GqaPage<D, BS, G> &pg, int j) {
+    const int bid = __builtin_amdgcn_readlane(my_bid, j);
+    pg.ok = (unsigned)bid < (unsigned)num_blocks;
+    const size_t off = (size_t)(pg.ok ? bid : 0) * page_stride;  // invalid id: page 0, unused
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        pg.k[sb][c] = __builtin_bit_cast(
+            bf16x8, load_kv16(k_b + off + (16 * sb + j16) * ROW + 64 * c + 16 * q4));
+#pragma unroll
+    for (int i = 0; i < NVLD; ++i) pg.v[i] = load_kv16(v_b + off + i * 1024 + 16 * lane);
+  };
+
+  auto process = [&](const GqaPage<D, BS, G> &pg, int j) {
+    const int tok0 = (p_begin + wave + NW * j) * BS;
+    // stage V row-major in LDS; masked rows as zeros
+#pragma unroll
+    for (int i = 0; i < NVLD; ++i) {
+      const int byte = i * 1024 + 16 * lane;
+      const int row = byte / ROW;
+      u32x4 w = pg.v[i];
+      if (!pg.ok || tok0 + row >= ctx) w = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(vs + row * PITCH + byte % ROW) = w;
+    }
+    // logits S[token][head] for each 16-token sub-block
+    float sc[NSB][4];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pg.k[sb][c], qb[c], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool keep = pg.ok && tok0 + 16 * sb + 4 * q4 + r < ctx;
+        sc[sb][r] = keep ? acc[r] * scale_log2 : -INFINITY;
+      }
+    }
+    // online softmax for head j16: page max over the 4 lane groups
+    float pm = sc[0][0];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pm = fmaxf(pm, sc[sb][r]);
+    pm = fmaxf(pm, __shfl_xor(pm, 16));
+    pm = fmaxf(pm, __shfl_xor(pm, 32));
+    const float mn = fmaxf(m, pm);
+    if (mn == -INFINITY) return;  // nothing live yet (only with invalid page ids)
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    l *= alpha;
+#pragma unroll
+    for (int n = 0; n < NN; ++n) o[n] *= alpha;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      i16x4 phi, plo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(sc[sb][r] - mn);
+        l += p;
+        const __bf16 hi = (__bf16)p;
+        const __bf16 lo = (__bf16)(p - (float)hi);
+        phi[r] = __builtin_bit_cast(short, hi);
+        plo[r] = __builtin_bit_cast(short, lo);
+      }
+      // V^T operand rows: token 16*sb + 4*q4 + j16/4, columns 16n + 4*(j16%4)
+      const int base = (16 * sb + 4 * q4 + (j16 >> 2)) * PITCH + 8 * (j16 & 3);
+#pragma unroll
+      for (int n = 0; n < NN; ++n) {
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)((lds_char *)vs + base + 32 * n));
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, o[n], 0, 0, 0);
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, o[n], 0, 0, 0);
+      }
+    }
+  };
+
+  if constexpr (S::PF == 2) {
+    // one page ahead; unconditional fetches inside the loop keep the number
+    // of loads in flight the same on every path
+    if (np_w > 0) {
+      GqaPage<D, BS, G> pa, pb;
+      fetch(pa, 0);
+      int j = 0;
+      for (; j + 2 < np_w; j += 2) {
+        fetch(pb, j + 1);
+        process(pa, j);
+        fetch(pa, j + 2);
+        process(pb, j + 1);
+      }
+      if (j + 1 < np_w) {
+        fetch(pb, j + 1);
+        process(pa, j);
+        process(pb, j + 1);
+      } else {
+        process(pa, j);
+      }
+    }
+  } else {
+    for (int j = 0; j < np_w; ++j) {
+      GqaPage<D, BS, G> pg;
+      fetch(pg, j);
+      process(pg, j);
+    }
+  }
+
+  // this wave's totals: the sum of weights over the 4 lane groups; O is
+  // already summed over tokens by the MFMAs
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  // the V staging area becomes this wave's partial O (its own region)
+  float *s_acc = reinterpret_cast<float *>(vs);
+  if (j16 < G) {
+#pragma unroll
+    for (int n = 0; n < NN; ++n)
+      *reinterpret_cast<float4 *>(&s_acc[j16 * D + 16 * n + 4 * q4]) =
+          make_float4(o[n][0], o[n][1], o[n][2], o[n][3]);
+    if (q4 == 0) {
+      s_ml[wave][j16][0] = m;
+      s_ml[wave][j16][1] = l;
+    }
+  }
+  __syncthreads();
+  merge_waves<BF16, D, G, NW>(
+      [&](int w, int h, int d) -> float4 {
+        return *reinterpret_cast<const float4 *>(
+            reinterpret_cast<const float *>(s_wave[w]) + h * D + d);
+      },
+      [&](int w, int h) { return s_ml[w][h][0]; }, [&](int w, int h) { return s_ml[w][h][1]; },
+      npages <= part_pages, out_b + ((size_t)s * num_heads + h0) * ROW,
+      ws_acc + (((size_t)s * num_heads + h0) * max_parts + part) * D,
+      ws_ml + (((size_t)s * num_heads + h0) * max_parts + part) * 2, (size_t)max_parts);
+}
+
+// Persistent partition kernel over the plan's unit list (largest units
+// first), item i = (list[i / num_kv_heads], kv-head i % num_kv_heads);
+// workgroup b takes items b, b + gridDim.x, ...
+template <int D, int BS, int G, int NW>
+__global__ __launch_bounds__(64 * NW) void pa_decode_partition_gqa(
+    void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
+    const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
+    float *__restrict__ ws_acc, const int32_t *__restrict__ plan, int num_heads,
+    int num_kv_heads, int max_blocks, int num_blocks, int part_pages, int max_parts,
+    float scale_log2) {
+  const int items = plan[0] * num_kv_heads;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int unit = plan[pa_internal::kPlanHeader + it / num_kv_heads];
+    decode_unit_gqa<D, BS, G, NW>(out, q, k_pool, v_pool, block_tables, context_lens, ws_ml,
+                                  ws_acc, num_heads, num_kv_heads, max_blocks, num_blocks,
+                                  part_pages, max_parts, scale_log2, unit / max_parts,
+                                  it % num_kv_heads, unit % max_parts);
+    __syncthreads();  // the next unit reuses the LDS the merge just read
+  }
+}
+
+constexpr int kWavesPerUnit = 4;
+
+template <int D, int BS, int G>
+int launch(const pa_internal::DecodeLaunch &a, float scale_log2) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  auto kernel = pa_decode_partition_gqa<D, BS, G, kWavesPerUnit>;
+  static const int per_cu = pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel),
+                                                       64 * kWavesPerUnit);
+  const unsigned grid = pa_internal::persistent_grid(a, per_cu);
+  if (grid == 0) return 6;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.out, a.q, a.k_pool,
+                     a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc, a.plan,
+                     a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks, a.part_pages,
+                     a.max_parts, scale_log2);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+template <int D, int BS>
+int by_group(const pa_internal::DecodeLaunch &a, float scale_log2) {
+  switch (a.num_heads / a.num_kv_heads) {
+    case 2: return launch<D, BS, 2>(a, scale_log2);
+    case 4: return launch<D, BS, 4>(a, scale_log2);
+    case 8: return launch<D, BS, 8>(a, scale_log2);
+  }
+  return 3;
+}
+
+template <int D>
+int by_block(const pa_internal::DecodeLaunch &a, float scale_log2) {
+  return a.block_size == 16 ? by_group<D, 16>(a, scale_log2) : by_group<D, 32>(a, scale_log2);
+}
+
+}  // namespace
+
+namespace pa_internal {
+
+int launch_partition_gqa(const DecodeLaunch &a, float scale_log2) {
+  return a.head_dim == 64 ? by_block<64>(a, scale_log2) : by_block<128>(a, scale_log2);
+}
+
+}  // namespace pa_internal

@@ -7,6 +7,14 @@
 
 namespace pa_internal {
 
+// Partitions are dealt to 4 wavefronts per workgroup, each holding one page
+// id per lane.
+constexpr int kMaxPartitionPages = 4 * 64;
+// The plan: int32 [kPlanHeader + num_seqs * max_parts]; element 0 is the
+// number of units, then one (sequence * max_parts + partition) per unit.
+constexpr int kPlanHeader = 4;
+constexpr int kMaxDevices = 64;
+
 struct DecodeLaunch {
   void *out;
   const void *q;
@@ -14,6 +22,7 @@ struct DecodeLaunch {
   const void *v_pool;
   const int32_t *block_tables;
   const int32_t *context_lens;
+  int32_t *plan;  // unit list written by the plan kernel
   float *ws_ml;   // [S, H, max_parts, 2] (running max in log2 units, sum)
   float *ws_acc;  // [S, H, max_parts, D] unnormalised weighted V
   int num_seqs, num_heads, num_kv_heads, head_dim, block_size;
@@ -38,6 +47,14 @@ struct CacheLaunch {
 
 // Each returns 0 on success or the PA_ERR_HIP code on a launch error.
 int launch_decode(const DecodeLaunch &a);
+// The partition pass for bf16 with 2, 4 or 8 query heads per kv-head, on
+// the matrix cores; called by launch_decode.
+int launch_partition_gqa(const DecodeLaunch &a, float scale_log2);
+// Workgroups of `kernel` one compute unit holds at once (at least 1).
+int blocks_per_cu(const void *kernel, int block_threads);
+// Grid of a persistent partition kernel: what the current device holds at
+// once, capped by the number of work items; 0 on a runtime error.
+unsigned persistent_grid(const DecodeLaunch &a, int per_cu);
 int launch_reshape_and_cache(const CacheLaunch &a);
 int launch_hbm_probe(const void *buf, size_t bytes, void *sink, void *stream);
 size_t hbm_probe_sink_bytes();

@@ -90,22 +90,35 @@ ptrs = [P] * 6
 ptrs[4] = P + 2
 expect("block_tables misaligned", decode(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_ALIGN)
 
-# workspace cases: num_seqs > 0 is needed for a nonzero requirement; each
-# still fails validation (missing / small / misaligned workspace)
+# workspace cases: every call with num_seqs > 0 needs one (the unit plan,
+# plus split-K partials when a sequence can span more than one partition);
+# each case still fails validation (missing / small / misaligned workspace)
+def plan_bytes(S, parts):
+    return -(-(4 + S * parts) * 4 // 256) * 256
+
+
 need_d = dims(num_seqs=4)
 need = lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(need_d))
-expect("workspace bytes formula", need, 4 * 32 * ((128 * 16 + 1023) // 1024) * (128 + 2) * 4)
+expect("workspace bytes formula", need,
+       plan_bytes(4, 2) + 4 * 32 * ((128 * 16 + 1023) // 1024) * (128 + 2) * 4)
 expect("workspace missing", decode(dims(num_seqs=4)), _lib.PA_ERR_WORKSPACE)
+expect("workspace missing, one partition", decode(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
 expect("workspace too small",
        decode(dims(num_seqs=4, workspace=P, workspace_bytes=need - 4)), _lib.PA_ERR_WORKSPACE)
 expect("workspace misaligned",
        decode(dims(num_seqs=4, workspace=P + 8, workspace_bytes=need + 64)), _lib.PA_ERR_WORKSPACE)
-expect("no workspace needed when one partition covers the table",
-       lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(dims(num_seqs=4, max_blocks_per_seq=16))), 0)
+expect("one partition: the workspace holds only the plan",
+       lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(dims(num_seqs=4, max_blocks_per_seq=16))),
+       plan_bytes(4, 1))
+expect("empty batch needs no workspace",
+       lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(dims(num_seqs=0))), 0)
 expect("workspace bytes, partition 512 at bs 32",
        lib.paged_attention_decode_workspace_bytes(32, ctypes.byref(
            dims(num_seqs=8, max_blocks_per_seq=1024, partition_size=512))),
-       8 * 32 * 64 * 130 * 4)
+       plan_bytes(8, 64) + 8 * 32 * 64 * 130 * 4)
+expect("too many work items",
+       decode(dims(num_seqs=1 << 20, max_blocks_per_seq=1 << 14, partition_size=16), hkv=32),
+       _lib.PA_ERR_SHAPE)
 expect("workspace query rejects bad dims",
        lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(dims(head_dim=80))), _lib.SIZE_MAX)
 expect("workspace query rejects NULL", lib.paged_attention_decode_workspace_bytes(16, None), _lib.SIZE_MAX)
