@@ -147,9 +147,9 @@ def main():
     w = make_config(args.config, args.seed)
     if args.partition_size is None:
         args.partition_size = w.partition_size
-    # 0 selects the library default, 1024 tokens (include/pagedattn.h)
-    args.effective_partition = args.partition_size or 1024
     dw = upload(w)
+    args.effective_partition = binding.paged_attention_decode_partition_tokens(
+        dw.q, dw.k_pool, dw.block_tables, args.partition_size)
     stream = torch.cuda.current_stream()
     ws_bytes = binding.paged_attention_decode_workspace_bytes(dw.q, dw.k_pool, dw.block_tables,
                                                               args.partition_size)

@@ -68,8 +68,10 @@ typedef struct pa_decode_dims {
   int32_t max_blocks_per_seq;  /* columns of block_tables, >= 1 */
   int32_t num_blocks;          /* pages in each pool, >= 1 */
   int32_t dtype;               /* PA_DTYPE_*: one type for q, out, k_pool, v_pool */
-  int32_t partition_size;      /* tokens per split-K partition; 0 = default (1024);
-                                  a multiple of block_size, at most 256 pages */
+  int32_t partition_size;      /* tokens per split-K partition, a multiple of
+                                  block_size, at most 256 pages; 0 = default: no
+                                  split when max_blocks_per_seq * block_size
+                                  <= 2048, else 1024 */
   int32_t reserved;            /* must be 0 */
   void *workspace;             /* device scratch, caller-owned, 16-byte aligned, at
                                   least paged_attention_decode_workspace_bytes();
@@ -135,6 +137,14 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool,
  */
 size_t paged_attention_decode_workspace_bytes(int32_t block_size,
                                               const pa_decode_dims *dims);
+
+/*
+ * The partition size, in tokens, paged_attention_decode uses for these
+ * shapes (dims->partition_size, or the default when that is 0); -1 when the
+ * shapes are invalid.
+ */
+int32_t paged_attention_decode_partition_tokens(int32_t block_size,
+                                                const pa_decode_dims *dims);
 
 /* Shapes and launch context of reshape_and_cache. */
 typedef struct pa_cache_dims {

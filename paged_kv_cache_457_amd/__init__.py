@@ -7,7 +7,8 @@ NumPy only) can be used without torch or a built library.
 """
 __all__ = [
     "paged_attention_decode", "reshape_and_cache",
-    "paged_attention_decode_workspace_bytes", "hbm_read_probe", "PagedAttnError",
+    "paged_attention_decode_workspace_bytes", "paged_attention_decode_partition_tokens",
+    "hbm_read_probe", "PagedAttnError",
 ]
 
 

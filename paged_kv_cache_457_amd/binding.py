@@ -77,6 +77,17 @@ def paged_attention_decode_workspace_bytes(q: torch.Tensor, k_pool: torch.Tensor
     return n
 
 
+def paged_attention_decode_partition_tokens(q: torch.Tensor, k_pool: torch.Tensor,
+                                            block_tables: torch.Tensor,
+                                            partition_size: int = 0) -> int:
+    """Partition size in tokens the library uses for these shapes."""
+    d = decode_dims(q, k_pool, block_tables, partition_size)
+    n = _lib.load().paged_attention_decode_partition_tokens(k_pool.shape[2], ctypes.byref(d))
+    if n < 0:
+        raise ValueError("invalid shapes for paged_attention_decode")
+    return n
+
+
 def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
                            v_pool: torch.Tensor, block_tables: torch.Tensor,
                            context_lens: torch.Tensor, scale: Optional[float] = None,

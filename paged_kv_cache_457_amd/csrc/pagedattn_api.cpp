@@ -21,8 +21,16 @@ bool supported_bs(int bs) { return bs == 16 || bs == 32; }
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 int elem_bytes(int dtype) { return dtype == PA_DTYPE_F32 ? 4 : 2; }
 
-int partition_tokens(const pa_decode_dims *d) {
-  return d->partition_size == 0 ? kDefaultPartitionTokens : d->partition_size;
+// Default split: none when the whole block table holds at most
+// kSinglePartitionTokens tokens (one pass, no reduce launch), else
+// kDefaultPartitionTokens per partition.
+constexpr int kSinglePartitionTokens = 2048;
+
+int partition_tokens(const pa_decode_dims *d, int32_t block_size) {
+  if (d->partition_size != 0) return d->partition_size;
+  const int64_t table_tokens = (int64_t)d->max_blocks_per_seq * block_size;
+  if (table_tokens <= kSinglePartitionTokens) return (int)table_tokens;
+  return kDefaultPartitionTokens;
 }
 
 // Shape checks shared by the decode call and the workspace query.
@@ -36,7 +44,7 @@ int check_decode_dims(int32_t num_kv_heads, int32_t block_size, const pa_decode_
   if (!supported_dim(d->head_dim) || !supported_bs(block_size) ||
       !supported_group(d->num_heads / num_kv_heads))
     return PA_ERR_UNSUPPORTED;
-  const int pt = partition_tokens(d);
+  const int pt = partition_tokens(d, block_size);
   if (pt % block_size != 0 || pt / block_size > kMaxPartitionPages) return PA_ERR_SHAPE;
   // context capacity must fit in int32 token counts
   if ((int64_t)d->max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
@@ -47,7 +55,7 @@ int check_decode_dims(int32_t num_kv_heads, int32_t block_size, const pa_decode_
 }
 
 int max_partitions(int32_t block_size, const pa_decode_dims *d) {
-  const int pp = partition_tokens(d) / block_size;
+  const int pp = partition_tokens(d, block_size) / block_size;
   return (d->max_blocks_per_seq + pp - 1) / pp;
 }
 
@@ -75,6 +83,12 @@ size_t paged_attention_decode_workspace_bytes(int32_t block_size, const pa_decod
   if (dims->num_seqs == 0) return 0;
   const int mp = max_partitions(block_size, dims);
   return plan_bytes(dims->num_seqs, mp) + partial_bytes(dims, mp);
+}
+
+int32_t paged_attention_decode_partition_tokens(int32_t block_size, const pa_decode_dims *dims) {
+  if (!dims || dims->num_heads < 1) return -1;
+  if (check_decode_dims(dims->num_heads, block_size, dims) != PA_OK) return -1;
+  return partition_tokens(dims, block_size);
 }
 
 int paged_attention_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
@@ -121,7 +135,7 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool, const v
   a.max_blocks = dims->max_blocks_per_seq;
   a.num_blocks = dims->num_blocks;
   a.dtype = dims->dtype;
-  a.part_pages = partition_tokens(dims) / block_size;
+  a.part_pages = partition_tokens(dims, block_size) / block_size;
   a.max_parts = mp;
   a.scale = scale;
   a.stream = dims->stream;

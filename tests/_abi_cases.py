@@ -97,16 +97,18 @@ def plan_bytes(S, parts):
     return -(-(4 + S * parts) * 4 // 256) * 256
 
 
-need_d = dims(num_seqs=4)
+need_d = dims(num_seqs=4, max_blocks_per_seq=256)
 need = lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(need_d))
 expect("workspace bytes formula", need,
-       plan_bytes(4, 2) + 4 * 32 * ((128 * 16 + 1023) // 1024) * (128 + 2) * 4)
+       plan_bytes(4, 4) + 4 * 32 * ((256 * 16 + 1023) // 1024) * (128 + 2) * 4)
 expect("workspace missing", decode(dims(num_seqs=4)), _lib.PA_ERR_WORKSPACE)
 expect("workspace missing, one partition", decode(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
 expect("workspace too small",
-       decode(dims(num_seqs=4, workspace=P, workspace_bytes=need - 4)), _lib.PA_ERR_WORKSPACE)
+       decode(dims(num_seqs=4, max_blocks_per_seq=256, workspace=P, workspace_bytes=need - 4)),
+       _lib.PA_ERR_WORKSPACE)
 expect("workspace misaligned",
-       decode(dims(num_seqs=4, workspace=P + 8, workspace_bytes=need + 64)), _lib.PA_ERR_WORKSPACE)
+       decode(dims(num_seqs=4, max_blocks_per_seq=256, workspace=P + 8, workspace_bytes=need + 64)),
+       _lib.PA_ERR_WORKSPACE)
 expect("one partition: the workspace holds only the plan",
        lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(dims(num_seqs=4, max_blocks_per_seq=16))),
        plan_bytes(4, 1))
@@ -122,6 +124,18 @@ expect("too many work items",
 expect("workspace query rejects bad dims",
        lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(dims(head_dim=80))), _lib.SIZE_MAX)
 expect("workspace query rejects NULL", lib.paged_attention_decode_workspace_bytes(16, None), _lib.SIZE_MAX)
+
+# ---- effective partition size
+pt = lib.paged_attention_decode_partition_tokens
+expect("default partition: table of 2048 tokens is one partition",
+       pt(16, ctypes.byref(dims(max_blocks_per_seq=128))), 2048)
+expect("default partition: larger tables split by 1024", pt(16, ctypes.byref(dims(max_blocks_per_seq=129))), 1024)
+expect("default partition at bs 32", pt(32, ctypes.byref(dims(max_blocks_per_seq=1024))), 1024)
+expect("explicit partition", pt(32, ctypes.byref(dims(max_blocks_per_seq=1024, partition_size=512))), 512)
+expect("partition query rejects bad dims", pt(16, ctypes.byref(dims(head_dim=80))), -1)
+expect("workspace for a one-partition default table",
+       lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(dims(num_seqs=4, max_blocks_per_seq=128))),
+       plan_bytes(4, 1))
 
 # ---- reshape_and_cache (num_tokens == 0: a wrong pass is a no-op)
 expect("cache dims NULL", lib.reshape_and_cache(P, P, P, P, P, None), _lib.PA_ERR_NULL)
