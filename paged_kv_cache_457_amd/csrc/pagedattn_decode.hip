@@ -274,11 +274,11 @@ __device__ __forceinline__ void decode_unit(
 }
 
 // Persistent partition kernel: a grid sized to what the GPU holds at once
-// walks the unit list the plan kernel wrote, longest units first, item i =
-// (list[i / num_kv_heads], kv-head i % num_kv_heads); workgroup b takes items
-// b, b + gridDim.x, ...  Kv-head fastest gives every XCD (the hardware hands
-// consecutive workgroups to the 8 XCDs in turn) an equal share of each
-// sequence's heads.
+// walks the unit list the plan kernel wrote, largest units first, item i =
+// (list[i / num_kv_heads], kv-head i % num_kv_heads), in the snake order of
+// snake_item.  Kv-head fastest puts the heads of one unit on workgroups
+// that start together on different XCDs (the hardware hands consecutive
+// workgroups to the 8 XCDs in turn).
 template <class T, int D, int BS, int G, int NW>
 __global__ __launch_bounds__(64 * NW) void pa_decode_partition(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
@@ -288,7 +288,9 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_partition(
     int num_kv_heads, int max_blocks, int num_blocks, int part_pages, int max_parts,
     float scale_log2) {
   const int items = plan[0] * num_kv_heads;
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+  for (int k = 0;; ++k) {
+    const int it = snake_item(k);
+    if (it >= items) break;
     const int unit = plan[kPlanHeader + it / num_kv_heads];
     decode_unit<T, D, BS, G, NW>(out, q, k_pool, v_pool, block_tables, context_lens, ws_ml,
                                  ws_acc, num_heads, num_kv_heads, max_blocks, num_blocks,
@@ -304,7 +306,9 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_partition(
 // shortest units finish the pass and no workgroup starts a long unit at the
 // end.  A sequence with context 0 gets one unit of size 0 (its output rows
 // are written as zeros).  Layout: plan[0] = unit count, plan[kPlanHeader +
-// k] = sequence * max_parts + partition.  Units of equal size are placed in
+// k] = sequence * max_parts + partition.  Threads take candidate units
+// (sequence, partition) in turn, so short batches of long sequences spread
+// over the workgroup too.  Units of equal size are placed in
 // arbitrary order; results do not depend on the order units run in.
 constexpr int kPlanThreads = 1024;
 
@@ -313,13 +317,22 @@ __global__ __launch_bounds__(kPlanThreads) void pa_decode_plan(
     int ctx_cap, int block_size, int part_pages, int max_parts) {
   __shared__ int s_count[kMaxPartitionPages + 1];  // units per size 0..part_pages
   __shared__ int s_next[kMaxPartitionPages + 1];   // next free slot per size
-  for (int i = threadIdx.x; i <= part_pages; i += kPlanThreads) s_count[i] = 0;
-  __syncthreads();
-  for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
+  // size of candidate unit u = (sequence u / max_parts, partition u % max_parts):
+  // its page count, 0 for the single unit of an empty sequence, -1 if none
+  auto unit_size = [&](int u) {
+    const int s = u / max_parts;
+    const int p = u - s * max_parts;
     const int ctx = min(max(context_lens[s], 0), ctx_cap);
     const int np = (ctx + block_size - 1) / block_size;
-    if (np == 0) atomicAdd(&s_count[0], 1);
-    for (int p0 = 0; p0 < np; p0 += part_pages) atomicAdd(&s_count[min(part_pages, np - p0)], 1);
+    if (np == 0) return p == 0 ? 0 : -1;
+    return p * part_pages < np ? min(part_pages, np - p * part_pages) : -1;
+  };
+  const int candidates = num_seqs * max_parts;
+  for (int i = threadIdx.x; i <= part_pages; i += kPlanThreads) s_count[i] = 0;
+  __syncthreads();
+  for (int u = threadIdx.x; u < candidates; u += kPlanThreads) {
+    const int z = unit_size(u);
+    if (z >= 0) atomicAdd(&s_count[z], 1);
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -331,60 +344,94 @@ __global__ __launch_bounds__(kPlanThreads) void pa_decode_plan(
     plan[0] = at;
   }
   __syncthreads();
-  for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
-    const int ctx = min(max(context_lens[s], 0), ctx_cap);
-    const int np = (ctx + block_size - 1) / block_size;
-    if (np == 0) plan[kPlanHeader + atomicAdd(&s_next[0], 1)] = s * max_parts;
-    for (int p0 = 0, p = 0; p0 < np; p0 += part_pages, ++p)
-      plan[kPlanHeader + atomicAdd(&s_next[min(part_pages, np - p0)], 1)] = s * max_parts + p;
+  for (int u = threadIdx.x; u < candidates; u += kPlanThreads) {
+    const int z = unit_size(u);
+    if (z >= 0) plan[kPlanHeader + atomicAdd(&s_next[z], 1)] = u;
   }
 }
 
 // ------------------------------------------------- decode, log-sum-exp merge
-// Grid (num_heads, num_seqs), 64 threads.  Merges the partitions of
-// sequences that span more than one: M = max_p m_p, w_p = 2^(m_p - M),
-// out = sum_p w_p acc_p / sum_p w_p l_p.
+// Grid (num_heads, num_seqs), kReduceWaves wavefronts.  Merges the
+// partitions of sequences that span more than one:
+//   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p acc_p / sum_p w_p l_p.
+// Wave w folds partitions w, w + kReduceWaves, ... with eight partitions'
+// loads in flight; lane l owns D/64 consecutive outputs; the waves' sums meet
+// in LDS.
+constexpr int kReduceWaves = 4;
+constexpr int kReduceUnroll = 8;
+
 template <class T, int D>
-__global__ __launch_bounds__(64) void pa_decode_reduce(
+__global__ __launch_bounds__(64 * kReduceWaves) void pa_decode_reduce(
     void *__restrict__ out, const float *__restrict__ ws_ml, const float *__restrict__ ws_acc,
     const int32_t *__restrict__ context_lens, int num_heads, int ctx_cap, int part_tokens,
     int max_parts) {
   constexpr int DPL = D / 64;  // output elements per lane
-  const int lane = threadIdx.x;
+  __shared__ float s_o[kReduceWaves][D];
+  __shared__ float s_l[kReduceWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  int ctx = context_lens[s];
-  ctx = min(max(ctx, 0), ctx_cap);
+  const int ctx = min(max(context_lens[s], 0), ctx_cap);
   const int nparts = (ctx + part_tokens - 1) / part_tokens;
   if (nparts <= 1) return;
   const size_t row0 = ((size_t)s * num_heads + h) * max_parts;
+  const float *ml = ws_ml + row0 * 2;
+  const float *acc = ws_acc + row0 * D + lane * DPL;
 
   float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ws_ml[(row0 + p) * 2]);
+  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ml[2 * p]);
   M = wave_max(M);
-  float L = 0.f;
-  for (int p = lane; p < nparts; p += 64)
-    L += ws_ml[(row0 + p) * 2 + 1] * fast_exp2(ws_ml[(row0 + p) * 2] - M);
-  L = wave_sum(L);
 
-  float o[DPL];
+  float L = 0.f, o[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) o[j] = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = fast_exp2(ws_ml[(row0 + p) * 2] - M);
-    const float *a = ws_acc + (row0 + p) * D + lane * DPL;
+  if (M != -INFINITY) {
+    for (int p0 = wave; p0 < nparts; p0 += kReduceWaves * kReduceUnroll) {
+      float w[kReduceUnroll], lp[kReduceUnroll], a[kReduceUnroll][DPL];
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) o[j] = fmaf(w, a[j], o[j]);
+      for (int u = 0; u < kReduceUnroll; ++u) {
+        const int p = p0 + u * kReduceWaves;
+        const bool in = p < nparts;
+        w[u] = in ? ml[2 * p] : -INFINITY;
+        lp[u] = in ? ml[2 * p + 1] : 0.f;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) a[u][j] = in ? acc[(size_t)p * D + j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kReduceUnroll; ++u) {
+        const float sc = fast_exp2(w[u] - M);
+        L = fmaf(lp[u], sc, L);
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) o[j] = fmaf(a[u][j], sc, o[j]);
+      }
+    }
   }
-  const float inv = 1.0f / L;
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) s_o[wave][lane * DPL + j] = o[j];
+  if (lane == 0) s_l[wave] = L;
+  __syncthreads();
+  if (wave != 0) return;
+  float Lt = 0.f;
+#pragma unroll
+  for (int w = 0; w < kReduceWaves; ++w) Lt += s_l[w];
+  const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
+  float r[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kReduceWaves; ++w) t += s_o[w][lane * DPL + j];
+    r[j] = t * inv;
+  }
   if constexpr (T::kBytes == 4) {
     float *dst = reinterpret_cast<float *>(out) + ((size_t)s * num_heads + h) * D + lane * DPL;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) dst[j] = o[j] * inv;
+    for (int j = 0; j < DPL; ++j) dst[j] = r[j];
   } else {
     uint16_t *dst = reinterpret_cast<uint16_t *>(out) + ((size_t)s * num_heads + h) * D + lane * DPL;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) dst[j] = (uint16_t)BF16::round_bits(o[j] * inv);
+    for (int j = 0; j < DPL; ++j) dst[j] = (uint16_t)BF16::round_bits(r[j]);
   }
 }
 
@@ -437,7 +484,8 @@ int run_decode(const pa_internal::DecodeLaunch &a) {
   if (rc != 0) return rc;
   if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
   if (a.max_parts > 1) {
-    hipLaunchKernelGGL((pa_decode_reduce<T, D>), dim3(a.num_heads, a.num_seqs), dim3(64), 0, st,
+    hipLaunchKernelGGL((pa_decode_reduce<T, D>), dim3(a.num_heads, a.num_seqs),
+                       dim3(64 * kReduceWaves), 0, st,
                        a.out, a.ws_ml, a.ws_acc, a.context_lens, a.num_heads,
                        a.max_blocks * a.block_size, a.part_pages * a.block_size, a.max_parts);
     if (hipGetLastError() != hipSuccess) return 6;

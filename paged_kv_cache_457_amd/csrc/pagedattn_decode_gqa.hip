@@ -18,18 +18,18 @@
 // largest-first unit list with the kv-head fastest.
 //
 // Lane layouts (lane l = 16*q4 + j16; 16x16 MFMA tiles):
-//   q.K   v_mfma_f32_16x16x32_bf16, one per 32-wide slab c of head_dim and
-//         16-token sub-block sb of the page.  A = K rows: lane l holds
-//         K[16*sb + j16][32*c + 8*q4 .. +7], one 16-byte global load.
-//         B = q^T: lane l holds q[head j16][32*c + 8*q4 .. +7] (zero for
-//         j16 >= G).  Result: lane l holds S[token 16*sb + 4*q4 + r][head j16],
-//         r = 0..3.
+// Tokens go through in granules of 16 (a 32-token page is two granules).
+//   q.K   v_mfma_f32_16x16x32_bf16, one per 32-wide slab c of head_dim.
+//         A = K rows: lane l holds K[token j16][32*c + 8*q4 .. +7] of the
+//         granule, one 16-byte global load.  B = q^T: lane l holds
+//         q[head j16][32*c + 8*q4 .. +7] (zero for j16 >= G).  Result: lane l
+//         holds S[token 4*q4 + r][head j16], r = 0..3.
 //   P.V   v_mfma_f32_16x16x16_bf16, one per 16-wide column block n of
-//         head_dim and sub-block sb, accumulating O^T[d][head].
-//         B = P^T: lane l holds P[head j16][token 16*sb + 4*q4 + e] -- the
-//         q.K result registers after exp, so P never moves between lanes.
-//         A = V^T: lane l holds V[16*sb + 4*q4 + e][16*n + j16], e = 0..3,
-//         which is one ds_read_b64_tr_b16 from the page staged row-major in
+//         head_dim, accumulating O^T[d][head].
+//         B = P^T: lane l holds P[head j16][token 4*q4 + e] -- the q.K result
+//         registers after exp, so P never moves between lanes.
+//         A = V^T: lane l holds V[4*q4 + e][16*n + j16], e = 0..3, which is
+//         one ds_read_b64_tr_b16 from the granule staged row-major in
 //         LDS (within each 16-lane group, lane j of the read supplies 4
 //         consecutive 16-bit values M[j][0..3] and lane i receives
 //         M[4e + i/4][i%4], e = 0..3).  Result: lane l holds
@@ -57,31 +57,32 @@ typedef __attribute__((address_space(3))) char lds_char;
 template <int D, int BS, int G>
 struct GqaShape {
   static_assert(G >= 2 && G <= 16, "head group padded to 16 MFMA columns");
-  static constexpr int NSB = BS / 16;              // 16-token sub-blocks per page
+  // The wave works in granules of 16 tokens (one MFMA tile of tokens): a
+  // 32-token page is two granules with the same page id, so the prefetch
+  // depth and the registers it needs do not depend on the page size.
+  static constexpr int GPP = BS / 16;              // granules per page
   static constexpr int NC = D / 32;                // 32-wide head_dim slabs (q.K)
   static constexpr int NN = D / 16;                // 16-wide head_dim blocks (P.V)
   static constexpr int ROW = D * 2;                // bytes per token row
-  static constexpr int NVLD = BS * ROW / 1024;     // 1 KiB V loads per page
-  // LDS row pitch of the staged V page: 32 bytes of padding put the 8 rows a
-  // transposing read touches per half-wave in distinct banks
+  static constexpr int GBYTES = 16 * ROW;          // bytes of one granule of K or V
+  static constexpr int NVLD = GBYTES / 1024;       // 1 KiB V loads per granule
+  // LDS row pitch of the staged V granule: 32 bytes of padding put the 8
+  // rows a transposing read touches per half-wave in distinct banks
   static constexpr int PITCH = ROW + 32;
-  static constexpr int VBYTES = BS * PITCH;
+  static constexpr int VBYTES = 16 * PITCH;
   static constexpr int ACC_BYTES = G * D * 4;
-  // per-wave LDS: the staged V page, later reused for the wave's partial O
+  // per-wave LDS: the staged V granule, later reused for the wave's partial O
   static constexpr int WAVE_LDS = VBYTES > ACC_BYTES ? VBYTES : ACC_BYTES;
-  static constexpr int PF = NSB == 1 ? 2 : 1;      // pages in flight per wave
 };
 
 template <int D, int BS, int G>
-struct GqaPage {
+struct GqaGranule {
   using S = GqaShape<D, BS, G>;
-  bf16x8 k[S::NSB][S::NC];
+  bf16x8 k[S::NC];
   u32x4 v[S::NVLD];
   bool ok;
 };
 
-// One work unit: the G query heads of kv-head g over partition `part` of
-// sequence s.  All threads of the workgroup call it with the same unit.
 template <int D, int BS, int G, int NW>
 __device__ __forceinline__ void decode_unit_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
@@ -90,7 +91,7 @@ __device__ __forceinline__ void decode_unit_gqa(
     float *__restrict__ ws_acc, int num_heads, int num_kv_heads, int max_blocks,
     int num_blocks, int part_pages, int max_parts, float scale_log2, int s, int g, int part) {
   using S = GqaShape<D, BS, G>;
-  constexpr int NSB = S::NSB, NC = S::NC, NN = S::NN, ROW = S::ROW, NVLD = S::NVLD;
+  constexpr int GPP = S::GPP, NC = S::NC, NN = S::NN, ROW = S::ROW, NVLD = S::NVLD;
   constexpr int PITCH = S::PITCH;
   __shared__ __attribute__((aligned(16))) char s_wave[NW][S::WAVE_LDS];
   __shared__ float s_ml[NW][G][2];
@@ -149,51 +150,44 @@ __device__ __forceinline__ void decode_unit_gqa(
   const char *v_b = reinterpret_cast<const char *>(v_pool) + (size_t)g * BS * ROW;
   char *vs = s_wave[wave];
 
-  auto fetch = [&](GqaPage<D, BS, G> &pg, int j) {
-    const int bid = __builtin_amdgcn_readlane(my_bid, j);
-    pg.ok = (unsigned)bid < (unsigned)num_blocks;
-    const size_t off = (size_t)(pg.ok ? bid : 0) * page_stride;  // invalid id: page 0, unused
+  // granule jg of this wave: page jg / GPP of the wave's pages, tokens
+  // 16 * (jg % GPP) .. +15 of it
+  auto fetch = [&](GqaGranule<D, BS, G> &gr, int jg) {
+    const int bid = __builtin_amdgcn_readlane(my_bid, jg / GPP);
+    gr.ok = (unsigned)bid < (unsigned)num_blocks;
+    // an invalid id reads page 0, whose values are never used
+    const size_t off = (size_t)(gr.ok ? bid : 0) * page_stride + (jg % GPP) * S::GBYTES;
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
+    for (int c = 0; c < NC; ++c)
+      gr.k[c] = __builtin_bit_cast(bf16x8, load_kv16(k_b + off + j16 * ROW + 64 * c + 16 * q4));
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        pg.k[sb][c] = __builtin_bit_cast(
-            bf16x8, load_kv16(k_b + off + (16 * sb + j16) * ROW + 64 * c + 16 * q4));
-#pragma unroll
-    for (int i = 0; i < NVLD; ++i) pg.v[i] = load_kv16(v_b + off + i * 1024 + 16 * lane);
+    for (int i = 0; i < NVLD; ++i) gr.v[i] = load_kv16(v_b + off + i * 1024 + 16 * lane);
   };
 
-  auto process = [&](const GqaPage<D, BS, G> &pg, int j) {
-    const int tok0 = (p_begin + wave + NW * j) * BS;
+  auto process = [&](const GqaGranule<D, BS, G> &gr, int jg) {
+    const int tok0 = (p_begin + wave + NW * (jg / GPP)) * BS + 16 * (jg % GPP);
     // stage V row-major in LDS; masked rows as zeros
 #pragma unroll
     for (int i = 0; i < NVLD; ++i) {
       const int byte = i * 1024 + 16 * lane;
       const int row = byte / ROW;
-      u32x4 w = pg.v[i];
-      if (!pg.ok || tok0 + row >= ctx) w = u32x4{0u, 0u, 0u, 0u};
+      u32x4 w = gr.v[i];
+      if (!gr.ok || tok0 + row >= ctx) w = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4 *>(vs + row * PITCH + byte % ROW) = w;
     }
-    // logits S[token][head] for each 16-token sub-block
-    float sc[NSB][4];
+    // logits S[token][head] of the granule's 16 tokens
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gr.k[c], qb[c], acc, 0, 0, 0);
+    float sc[4];
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pg.k[sb][c], qb[c], acc, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool keep = pg.ok && tok0 + 16 * sb + 4 * q4 + r < ctx;
-        sc[sb][r] = keep ? acc[r] * scale_log2 : -INFINITY;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const bool keep = gr.ok && tok0 + 4 * q4 + r < ctx;
+      sc[r] = keep ? acc[r] * scale_log2 : -INFINITY;
     }
-    // online softmax for head j16: page max over the 4 lane groups
-    float pm = sc[0][0];
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pm = fmaxf(pm, sc[sb][r]);
+    // online softmax for head j16: granule max over the 4 lane groups
+    float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     pm = fmaxf(pm, __shfl_xor(pm, 16));
     pm = fmaxf(pm, __shfl_xor(pm, 32));
     const float mn = fmaxf(m, pm);
@@ -203,56 +197,47 @@ __device__ __forceinline__ void decode_unit_gqa(
     l *= alpha;
 #pragma unroll
     for (int n = 0; n < NN; ++n) o[n] *= alpha;
+    i16x4 phi, plo;
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-      i16x4 phi, plo;
+    for (int r = 0; r < 4; ++r) {
+      const float p = fast_exp2(sc[r] - mn);
+      l += p;
+      const __bf16 hi = (__bf16)p;
+      const __bf16 lo = (__bf16)(p - (float)hi);
+      phi[r] = __builtin_bit_cast(short, hi);
+      plo[r] = __builtin_bit_cast(short, lo);
+    }
+    // V^T operand rows: token 4*q4 + j16/4, columns 16n + 4*(j16%4)
+    const int base = (4 * q4 + (j16 >> 2)) * PITCH + 8 * (j16 & 3);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(sc[sb][r] - mn);
-        l += p;
-        const __bf16 hi = (__bf16)p;
-        const __bf16 lo = (__bf16)(p - (float)hi);
-        phi[r] = __builtin_bit_cast(short, hi);
-        plo[r] = __builtin_bit_cast(short, lo);
-      }
-      // V^T operand rows: token 16*sb + 4*q4 + j16/4, columns 16n + 4*(j16%4)
-      const int base = (16 * sb + 4 * q4 + (j16 >> 2)) * PITCH + 8 * (j16 & 3);
-#pragma unroll
-      for (int n = 0; n < NN; ++n) {
-        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)((lds_char *)vs + base + 32 * n));
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, o[n], 0, 0, 0);
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, o[n], 0, 0, 0);
-      }
+    for (int n = 0; n < NN; ++n) {
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4 *)((lds_char *)vs + base + 32 * n));
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, o[n], 0, 0, 0);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, o[n], 0, 0, 0);
     }
   };
 
-  if constexpr (S::PF == 2) {
-    // one page ahead; unconditional fetches inside the loop keep the number
-    // of loads in flight the same on every path
-    if (np_w > 0) {
-      GqaPage<D, BS, G> pa, pb;
-      fetch(pa, 0);
-      int j = 0;
-      for (; j + 2 < np_w; j += 2) {
-        fetch(pb, j + 1);
-        process(pa, j);
-        fetch(pa, j + 2);
-        process(pb, j + 1);
-      }
-      if (j + 1 < np_w) {
-        fetch(pb, j + 1);
-        process(pa, j);
-        process(pb, j + 1);
-      } else {
-        process(pa, j);
-      }
+  // One granule ahead; inside the loop every fetch is unconditional, so the
+  // number of loads in flight is the same on every path and the wait before
+  // a granule's use leaves the next one's loads outstanding.
+  const int ng = np_w * GPP;
+  if (ng > 0) {
+    GqaGranule<D, BS, G> ga, gb;
+    fetch(ga, 0);
+    int j = 0;
+    for (; j + 2 < ng; j += 2) {
+      fetch(gb, j + 1);
+      process(ga, j);
+      fetch(ga, j + 2);
+      process(gb, j + 1);
     }
-  } else {
-    for (int j = 0; j < np_w; ++j) {
-      GqaPage<D, BS, G> pg;
-      fetch(pg, j);
-      process(pg, j);
+    if (j + 1 < ng) {
+      fetch(gb, j + 1);
+      process(ga, j);
+      process(gb, j + 1);
+    } else {
+      process(ga, j);
     }
   }
 
@@ -285,8 +270,8 @@ __device__ __forceinline__ void decode_unit_gqa(
 }
 
 // Persistent partition kernel over the plan's unit list (largest units
-// first), item i = (list[i / num_kv_heads], kv-head i % num_kv_heads);
-// workgroup b takes items b, b + gridDim.x, ...
+// first), item i = (list[i / num_kv_heads], kv-head i % num_kv_heads), in
+// the snake order of snake_item.
 template <int D, int BS, int G, int NW>
 __global__ __launch_bounds__(64 * NW) void pa_decode_partition_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
@@ -296,7 +281,9 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_partition_gqa(
     int num_kv_heads, int max_blocks, int num_blocks, int part_pages, int max_parts,
     float scale_log2) {
   const int items = plan[0] * num_kv_heads;
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+  for (int k = 0;; ++k) {
+    const int it = snake_item(k);
+    if (it >= items) break;
     const int unit = plan[pa_internal::kPlanHeader + it / num_kv_heads];
     decode_unit_gqa<D, BS, G, NW>(out, q, k_pool, v_pool, block_tables, context_lens, ws_ml,
                                   ws_acc, num_heads, num_kv_heads, max_blocks, num_blocks,

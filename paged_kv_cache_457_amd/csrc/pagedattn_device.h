@@ -142,6 +142,18 @@ __device__ __forceinline__ u32x4 load_kv16(const char *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
+// Item of the k-th round of a persistent grid walking a list sorted largest
+// first: rounds alternate direction (workgroup b takes items b, 2P-1-b,
+// 2P+b, 4P-1-b, ... for a grid of P), so the workgroups that start with the
+// largest items of one round take the smallest of the next and the totals
+// even out.  Beyond the last item a workgroup has nothing left in later
+// rounds either.
+__device__ __forceinline__ int snake_item(int k) {
+  const int b = (k & 1) ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  const long long it = (long long)k * gridDim.x + b;
+  return it > 0x7fffffffLL ? 0x7fffffff : (int)it;
+}
+
 // Merge the NW waves' partial softmax states of one work unit (sequence,
 // kv-head, partition) and store the result: normalised output rows when the
 // unit covers the whole sequence, else the partition's unnormalised
