@@ -256,3 +256,81 @@ def test_full_table_and_unused_columns():
         err = max_err(gpu_step(upload(w), partition_size=ps), ref, "bf16")
         say(f"full table partition {ps}: {err:.3e}")
         assert err <= TOL["bf16"]
+
+
+# ------------------------------------------------ scheduling and edge cases
+def test_many_tiny_sequences():
+    """Thousands of short sequences: many plan units, many persistent rounds."""
+    rng = np.random.default_rng(17)
+    ctx = rng.integers(0, 40, size=3000)
+    w = build_workload("tiny", ctx, 8, 2, 64, 16, "bf16", seed=17, max_blocks_per_seq=3)
+    say(f"{len(ctx)} sequences, ctx 0..39, partition 16")
+    ref, _, _ = oracle_step(w)
+    for ps in (0, 16):
+        err = max_err(gpu_step(upload(w), partition_size=ps), ref, "bf16")
+        say(f"  partition {ps}: max abs err {err:.3e}")
+        assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dt,G", [("bf16", 1), ("bf16", 4), ("f32", 2)])
+def test_hundreds_of_partitions(dt, G):
+    """One-page partitions on long sequences: the reduce merges up to 320
+    partials per head, beyond one 64-lane pass."""
+    w = build_workload("parts", [5000, 4096, 17, 3333], 2 * G, 2, 128, 16, dt, seed=23,
+                       max_blocks_per_seq=320)
+    ref, _, _ = oracle_step(w)
+    for ps in (16, 48, 4096):
+        say(f"{dt} G{G} partition {ps}")
+        err = max_err(gpu_step(upload(w), partition_size=ps), ref, dt)
+        say(f"  max abs err {err:.3e}")
+        assert err <= TOL[dt]
+
+
+def test_repeated_calls_are_bitwise_identical():
+    w = make_config(3)
+    dw = upload(w)
+    first = gpu_step(dw)
+    for _ in range(3):
+        assert gpu_step(dw, write=False).tobytes() == first.tobytes()
+
+
+def test_context_clamped_to_table_capacity():
+    """Context lengths past max_blocks_per_seq * block_size count as the
+    capacity; negative ones as 0 (the header's stated clamp)."""
+    w = build_workload("clamp", [64, 40, 1], 4, 4, 64, 16, "bf16", seed=29, max_blocks_per_seq=4)
+    ref, _, _ = oracle_step(w)
+    dw = upload(w)
+    binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
+    dw.context_lens.copy_(torch.tensor([10_000, 40, -7], dtype=torch.int32))
+    binding.paged_attention_decode(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
+                                   dw.context_lens, scale=float(w.scale))
+    torch.cuda.synchronize()
+    got = to_host(dw.out, "bf16")
+    assert max_err(got[:2], ref[:2], "bf16") <= TOL["bf16"]
+    assert np.all(got[2] == 0)
+
+
+@pytest.mark.parametrize("dt,G", [("bf16", 1), ("bf16", 4), ("f32", 1)])
+def test_out_of_range_page_id_is_skipped(dt, G):
+    """A used table entry outside the pool is a precondition violation; the
+    kernel must not read it and its tokens drop out, which equals the
+    oracle over the sequence without that (full, interior) page."""
+    L, bs = 200, 16
+    w = build_workload("badid", [L, L], 2 * G, 2, 64, bs, dt, seed=31,
+                       max_blocks_per_seq=(L + bs - 1) // bs)
+    kp, vp = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping, bs)
+    bad_col = 5
+    bt = w.block_tables.copy()
+    bt[0, bad_col] = w.num_blocks + 1000
+    dw = upload(w)
+    dw.block_tables.copy_(torch.from_numpy(bt))
+    got = gpu_step(dw)
+    # expected: sequence 0 without page bad_col (a full page), sequence 1 as is
+    bt_ref = np.full_like(w.block_tables, -1)
+    bt_ref[0, :bt.shape[1] - 1] = np.delete(w.block_tables[0], bad_col)
+    bt_ref[1] = w.block_tables[1]
+    ref = oracle.decode(w.q, kp, vp, bt_ref, np.array([L - bs, L]), w.num_kv_heads, w.scale,
+                        bs, dt)
+    err = max_err(got, ref, dt)
+    say(f"{dt} G{G} skipped page: max abs err {err:.3e}")
+    assert err <= TOL[dt]
