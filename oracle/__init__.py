@@ -6,6 +6,6 @@ It shares no code with the HIP path.  Every function is pinned by CPU tests
 (brute force, closed forms, invariants, a library routine, the pages'
 page-table figure); no function is "parity unpinned".
 """
-from .paged_attention import decode, gather_pages, reshape_and_cache, widen
+from .paged_attention import copy_blocks, decode, gather_pages, reshape_and_cache, widen
 
-__all__ = ["decode", "gather_pages", "reshape_and_cache", "widen"]
+__all__ = ["copy_blocks", "decode", "gather_pages", "reshape_and_cache", "widen"]

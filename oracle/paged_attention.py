@@ -30,7 +30,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["widen", "gather_pages", "decode", "reshape_and_cache"]
+__all__ = ["widen", "gather_pages", "decode", "reshape_and_cache", "copy_blocks"]
 
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -155,3 +155,37 @@ def reshape_and_cache(k: np.ndarray, v: np.ndarray, k_pool: np.ndarray,
         kp[page, :, off, :] = k[i]
         vp[page, :, off, :] = v[i]
     return kp, vp
+
+
+def copy_blocks(k_src: np.ndarray, v_src: np.ndarray, k_dst: np.ndarray,
+                v_dst: np.ndarray, block_mapping: np.ndarray):
+    """Copy whole pages between pools; returns the new destination pools.
+
+    block_mapping [N, 2] int: pair i copies page block_mapping[i, 0] of the
+    source pools to page block_mapping[i, 1] of the destination pools, every
+    kv-head, K and V, bit for bit.  This is the page move behind two things
+    the tutorial page describes: giving a sequence its own copy of a page it
+    shares with others before writing into it (section 4.2, shared pages),
+    and moving a preempted sequence's pages to a CPU-side pool and back
+    (sections 4.4 and 4.5).  Readings: the source and destination may be the
+    same pool (pass the same arrays); two pairs naming one destination page,
+    or a destination page that is also some pair's source when the pools
+    are the same, would make the result order-dependent, so both are
+    rejected, as is a page index outside its pool.
+    """
+    m = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    same = k_src is k_dst
+    kd = k_dst.copy()
+    vd = v_dst.copy()
+    src, dst = m[:, 0], m[:, 1]
+    if len(np.unique(dst)) != len(dst):
+        raise ValueError("two pairs write the same destination page")
+    if same and np.intersect1d(src, dst).size:
+        raise ValueError("a destination page is also a source page")
+    for i in range(len(m)):
+        s_page, d_page = int(src[i]), int(dst[i])
+        if not (0 <= s_page < k_src.shape[0] and 0 <= d_page < kd.shape[0]):
+            raise IndexError(f"pair {i} ({s_page} -> {d_page}) outside the pools")
+        kd[d_page] = k_src[s_page]
+        vd[d_page] = v_src[s_page]
+    return kd, vd

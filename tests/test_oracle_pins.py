@@ -385,11 +385,67 @@ def pin_cache_write_then_decode(o):
     assert got_v.tobytes() == np.ascontiguousarray(v.transpose(1, 0, 2)).tobytes()
 
 
+def pin_copy_blocks(o):
+    """Exact page moves by an explicit element loop; untouched pages stay."""
+    rng = np.random.default_rng(14)
+    nb_s, nb_d, Hkv, bs, D = 6, 9, 2, 4, 3
+    ks = rng.integers(0, 1 << 16, size=(nb_s, Hkv, bs, D), dtype=np.uint16)
+    vs = rng.integers(0, 1 << 16, size=(nb_s, Hkv, bs, D), dtype=np.uint16)
+    kd = rng.integers(0, 1 << 16, size=(nb_d, Hkv, bs, D), dtype=np.uint16)
+    vd = rng.integers(0, 1 << 16, size=(nb_d, Hkv, bs, D), dtype=np.uint16)
+    pairs = np.array([[0, 8], [5, 0], [0, 3], [2, 4]])
+    k2, v2 = o.copy_blocks(ks, vs, kd, vd, pairs)
+    want_k, want_v = kd.copy(), vd.copy()
+    for s_page, d_page in pairs:
+        for g in range(Hkv):
+            for t in range(bs):
+                for d in range(D):
+                    want_k[d_page, g, t, d] = ks[s_page, g, t, d]
+                    want_v[d_page, g, t, d] = vs[s_page, g, t, d]
+    assert k2.tobytes() == want_k.tobytes() and v2.tobytes() == want_v.tobytes()
+    assert kd.tobytes() != k2.tobytes()          # inputs are not modified in place
+    with pytest.raises(ValueError):
+        o.copy_blocks(ks, vs, kd, vd, np.array([[0, 1], [2, 1]]))
+    with pytest.raises(ValueError):
+        o.copy_blocks(ks, vs, ks, vs, np.array([[0, 1], [1, 2]]))
+    with pytest.raises(IndexError):
+        o.copy_blocks(ks, vs, kd, vd, np.array([[nb_s, 0]]))
+
+
+def pin_copy_on_write_keeps_attention(o):
+    """Copy-on-write of a shared page: after copying page p to a free page
+    and pointing one sequence's table at the copy, attention is unchanged;
+    a swap out to a second pool and back restores the pool bit for bit."""
+    rng = np.random.default_rng(15)
+    nb, Hkv, bs, D, H = 10, 2, 4, 8, 4
+    kp = rng.standard_normal((nb, Hkv, bs, D)).astype(np.float32)
+    vp = rng.standard_normal((nb, Hkv, bs, D)).astype(np.float32)
+    q = rng.standard_normal((2, H, D)).astype(np.float32)
+    table = np.array([[3, 7, 1], [3, 7, 5]], dtype=np.int32)   # pages 3, 7 shared
+    ctx = np.array([11, 10])
+    base = o.decode(q, kp, vp, table, ctx, Hkv, 0.3, bs, "f32")
+    k2, v2 = o.copy_blocks(kp, vp, kp, vp, np.array([[7, 9]]))
+    t2 = table.copy()
+    t2[1, 1] = 9
+    moved = o.decode(q, k2, v2, t2, ctx, Hkv, 0.3, bs, "f32")
+    assert np.array_equal(base, moved)
+    host_k = np.zeros((4, Hkv, bs, D), np.float32)
+    host_v = np.zeros((4, Hkv, bs, D), np.float32)
+    out_pairs = np.array([[3, 0], [7, 1], [5, 2]])
+    hk, hv = o.copy_blocks(kp, vp, host_k, host_v, out_pairs)
+    wiped_k, wiped_v = kp.copy(), vp.copy()
+    wiped_k[[3, 7, 5]] = np.nan
+    wiped_v[[3, 7, 5]] = np.nan
+    back_k, back_v = o.copy_blocks(hk, hv, wiped_k, wiped_v, out_pairs[:, ::-1])
+    assert back_k.tobytes() == kp.tobytes() and back_v.tobytes() == vp.tobytes()
+
+
 PINS = [
     pin_widen_bf16_definition, pin_hand_worked_example, pin_page_table_figure,
     pin_brute_force, pin_sdpa_identity_table, pin_ctx1_is_v0, pin_uniform_logits_mean,
     pin_permutation_invariance, pin_gqa_equals_mha, pin_split_combine,
     pin_peaked_softmax, pin_ctx0_and_poison, pin_cache_write, pin_cache_write_then_decode,
+    pin_copy_blocks, pin_copy_on_write_keeps_attention,
 ]
 
 
@@ -401,6 +457,7 @@ def test_oracle_pin(pin):
 def test_package_exports_pinned_functions():
     assert oracle.decode is oracle_mod.decode
     assert oracle.reshape_and_cache is oracle_mod.reshape_and_cache
+    assert oracle.copy_blocks is oracle_mod.copy_blocks
 
 
 # ------------------------------------------------------- planted mistakes
@@ -423,6 +480,9 @@ MUTANTS = {
     "cache write V from K": ("vp[page, :, off, :] = v[i]", "vp[page, :, off, :] = k[i]"),
     "cache write ignores skip": ("if slot < 0:\n            continue", "if slot < -1:\n            continue"),
     "lse sign": ("lse[s, h] = m + np.log(z)", "lse[s, h] = m - np.log(z)"),
+    "page copy direction": ("kd[d_page] = k_src[s_page]", "kd[s_page] = k_src[d_page]"),
+    "page copy V from K": ("vd[d_page] = v_src[s_page]", "vd[d_page] = k_src[s_page]"),
+    "page copy pair order": ("src, dst = m[:, 0], m[:, 1]", "dst, src = m[:, 0], m[:, 1]"),
 }
 
 
