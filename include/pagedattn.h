@@ -169,6 +169,46 @@ typedef struct pa_cache_dims {
 int reshape_and_cache(const void *k, const void *v, void *k_pool, void *v_pool,
                       const int64_t *slot_mapping, const pa_cache_dims *dims);
 
+/* Shapes and launch context of copy_blocks. */
+typedef struct pa_copy_dims {
+  int32_t num_pairs;       /* rows of block_mapping, >= 0; 0 is a no-op */
+  int32_t num_kv_heads;    /* >= 1 */
+  int32_t head_dim;        /* 64 or 128 */
+  int32_t block_size;      /* 16 or 32 */
+  int32_t dtype;           /* PA_DTYPE_* of all four pools */
+  int32_t src_num_blocks;  /* pages in k_src / v_src */
+  int32_t dst_num_blocks;  /* pages in k_dst / v_dst */
+  int32_t reserved;        /* must be 0 */
+  void *stream;            /* hipStream_t */
+} pa_copy_dims;
+
+/*
+ * Whole-page copy between pools (vLLM / PagedAttention pages: several
+ * sequences may share prefix pages, so a sequence about to write into a
+ * shared page first gets its own copy -- tutorial page, section 4.2; under
+ * memory pressure a preempted sequence's KV pages move to a CPU-side pool
+ * and back -- tutorial page, sections 4.4 and 4.5).
+ *
+ * For each pair i of block_mapping ([num_pairs, 2] int64: source page,
+ * destination page), page block_mapping[i][0] of k_src / v_src (every
+ * kv-head, [num_kv_heads, block_size, head_dim] elements) is copied bit for
+ * bit to page block_mapping[i][1] of k_dst / v_dst.  Pools have the layout
+ * of paged_attention_decode.  A pair with a page outside its pool (negative
+ * included) is skipped.
+ *
+ * Memory: the four pools and block_mapping may be device memory or pinned
+ * host memory (hipHostMalloc), so one call swaps pages out to a host pool,
+ * back in, or copies within a device pool (source and destination pools the
+ * same).  Pageable host memory gives PA_ERR_UNSUPPORTED.  Pointers are
+ * classified with hipPointerGetAttributes after the argument checks.
+ *
+ * Preconditions: no two pairs name the same destination page; when source
+ * and destination are the same pools, no destination page is also a
+ * source page (the result would depend on the order of the copies).
+ */
+int copy_blocks(const void *k_src, const void *v_src, void *k_dst, void *v_dst,
+                const int64_t *block_mapping, const pa_copy_dims *dims);
+
 /* Static, human-readable text for a status code. */
 const char *pa_status_string(int status);
 

@@ -53,6 +53,20 @@ class CacheDims(ctypes.Structure):
     ]
 
 
+class CopyDims(ctypes.Structure):
+    _fields_ = [
+        ("num_pairs", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("src_num_blocks", ctypes.c_int32),
+        ("dst_num_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
 # name -> (restype, argtypes); every symbol include/pagedattn.h declares
 SIGNATURES = {
     "paged_attention_decode": (ctypes.c_int, [
@@ -66,6 +80,9 @@ SIGNATURES = {
     "reshape_and_cache": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.POINTER(CacheDims)]),
+    "copy_blocks": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.POINTER(CopyDims)]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_hbm_read_probe": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),

@@ -163,6 +163,45 @@ def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, k_pool: torch.Tensor,
     _check(rc, "reshape_and_cache")
 
 
+def _pool_ptr(t: torch.Tensor, name: str) -> int:
+    """Device tensor, or pinned host tensor (mapped into the device's
+    address space); pageable host memory is refused by the library."""
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    return t.data_ptr()
+
+
+def copy_blocks(k_src: torch.Tensor, v_src: torch.Tensor, k_dst: torch.Tensor,
+                v_dst: torch.Tensor, block_mapping: torch.Tensor, stream=None) -> None:
+    """Copy page block_mapping[i, 0] of the source pools to page
+    block_mapping[i, 1] of the destination pools (see copy_blocks in
+    include/pagedattn.h).  Pools are [num_blocks, num_kv_heads, block_size,
+    head_dim], on the device or in pinned host memory."""
+    for name, t in (("v_src", v_src), ("k_dst", k_dst), ("v_dst", v_dst)):
+        if t.dtype != k_src.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from k_src dtype {k_src.dtype}")
+    if k_src.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k_src.dtype}")
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be int64 [num_pairs, 2]")
+    if k_src.shape != v_src.shape or k_dst.shape != v_dst.shape or k_src.dim() != 4 \
+            or k_src.shape[1:] != k_dst.shape[1:]:
+        raise ValueError("pools must be [num_blocks, num_kv_heads, block_size, head_dim] "
+                         "with matching page shapes")
+    d = _lib.CopyDims()
+    d.num_pairs = block_mapping.shape[0]
+    d.num_kv_heads, d.block_size, d.head_dim = k_src.shape[1], k_src.shape[2], k_src.shape[3]
+    d.dtype = _DTYPES[k_src.dtype]
+    d.src_num_blocks, d.dst_num_blocks = k_src.shape[0], k_dst.shape[0]
+    d.stream = _stream_ptr(stream)
+    rc = _lib.load().copy_blocks(_pool_ptr(k_src, "k_src"), _pool_ptr(v_src, "v_src"),
+                                 _pool_ptr(k_dst, "k_dst"), _pool_ptr(v_dst, "v_dst"),
+                                 _pool_ptr(block_mapping, "block_mapping"), ctypes.byref(d))
+    _check(rc, "copy_blocks")
+
+
 def hbm_read_probe(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Stream all of ``buf`` through the read-bandwidth probe kernel."""
     lib = _lib.load()

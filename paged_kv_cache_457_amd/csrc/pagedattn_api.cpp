@@ -173,6 +173,34 @@ int reshape_and_cache(const void *k, const void *v, void *k_pool, void *v_pool,
   return pa_internal::launch_reshape_and_cache(a);
 }
 
+int copy_blocks(const void *k_src, const void *v_src, void *k_dst, void *v_dst,
+                const int64_t *block_mapping, const pa_copy_dims *dims) {
+  if (!dims) return PA_ERR_NULL;
+  if (dims->num_pairs < 0 || dims->num_kv_heads < 1 || dims->src_num_blocks < 1 ||
+      dims->dst_num_blocks < 1 || dims->reserved != 0)
+    return PA_ERR_SHAPE;
+  if (dims->dtype != PA_DTYPE_F32 && dims->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (!supported_dim(dims->head_dim) || !supported_bs(dims->block_size)) return PA_ERR_UNSUPPORTED;
+  if (dims->num_pairs == 0) return PA_OK;  // nothing to copy; pointers may be NULL
+  if (!k_src || !v_src || !k_dst || !v_dst || !block_mapping) return PA_ERR_NULL;
+  if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(k_dst, 16) || !aligned(v_dst, 16) ||
+      !aligned(block_mapping, 8))
+    return PA_ERR_ALIGN;
+  pa_internal::CopyLaunch a{};
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.k_dst = k_dst;
+  a.v_dst = v_dst;
+  a.mapping = block_mapping;
+  a.num_pairs = dims->num_pairs;
+  a.page_bytes = (int64_t)dims->num_kv_heads * dims->block_size * dims->head_dim *
+                 elem_bytes(dims->dtype);
+  a.src_blocks = dims->src_num_blocks;
+  a.dst_blocks = dims->dst_num_blocks;
+  a.stream = dims->stream;
+  return pa_internal::launch_copy_pages(a);
+}
+
 const char *pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "PA_OK: success";

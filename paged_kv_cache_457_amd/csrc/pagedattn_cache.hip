@@ -1,8 +1,12 @@
-// KV-cache write and the HBM read probe.
+// KV-cache write, whole-page copies, and the HBM read probe.
 //
 // Each decode step produces the next token together with the updated KV
 // cache (tutorial page, section 4.3, step 3 of the iteration): the new
 // token's K and V rows go to the page slot its sequence's page table gives.
+// Whole pages move when a sequence needs its own copy of a page it shares
+// with others before writing into it (tutorial page, section 4.2, shared
+// pages) and when a preempted sequence's pages go to a CPU-side pool and
+// come back (sections 4.4 and 4.5).
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
 
@@ -30,6 +34,45 @@ __global__ __launch_bounds__(256) void pa_reshape_and_cache(
     const size_t dst = (((size_t)page * num_kv_heads + g) * block_size + off) * row_chunks + dc;
     k_pool[dst] = k[src];
     v_pool[dst] = v[src];
+  }
+}
+
+// ------------------------------------------------------------ page copy
+// Grid (num_pairs, chunks per page), 256 threads.  Workgroup (i, c) copies
+// chunk c (16 KiB) of page mapping[i][0] of the source pools to page
+// mapping[i][1] of the destination pools, K and V, with 16-byte
+// non-temporal loads and stores; all eight loads of a thread are issued
+// before its stores.  A pair with a page index outside its pool (negative
+// included) is skipped.  Source and destination may be device memory or
+// pinned host memory mapped into the device's address space.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+constexpr int kCopyChunk16 = kCopyThreads * kCopyUnroll;  // 16-byte units per chunk
+
+__global__ __launch_bounds__(kCopyThreads) void pa_copy_pages(
+    const u32x4 *__restrict__ k_src, const u32x4 *__restrict__ v_src, u32x4 *__restrict__ k_dst,
+    u32x4 *__restrict__ v_dst, const int64_t *__restrict__ mapping, int64_t page16,
+    int64_t src_blocks, int64_t dst_blocks) {
+  const int64_t src = mapping[2 * (size_t)blockIdx.x];
+  const int64_t dst = mapping[2 * (size_t)blockIdx.x + 1];
+  if (src < 0 || dst < 0 || src >= src_blocks || dst >= dst_blocks) return;
+  const int64_t base = (int64_t)blockIdx.y * kCopyChunk16 + threadIdx.x;
+  u32x4 kv[kCopyUnroll], vv[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + u * kCopyThreads;
+    if (i < page16) {
+      kv[u] = __builtin_nontemporal_load(k_src + src * page16 + i);
+      vv[u] = __builtin_nontemporal_load(v_src + src * page16 + i);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + u * kCopyThreads;
+    if (i < page16) {
+      __builtin_nontemporal_store(kv[u], k_dst + dst * page16 + i);
+      __builtin_nontemporal_store(vv[u], v_dst + dst * page16 + i);
+    }
   }
 }
 
@@ -74,6 +117,48 @@ int launch_reshape_and_cache(const CacheLaunch &a) {
                      reinterpret_cast<u32x4 *>(a.k_pool), reinterpret_cast<u32x4 *>(a.v_pool),
                      a.slot_mapping, a.num_kv_heads, row_chunks, a.block_size,
                      (int64_t)a.num_blocks * a.block_size);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+// The address a kernel uses for p: device memory as it is; pinned host
+// memory through its mapping into the device's address space.  Anything
+// else (pageable host memory) gives nullptr, since a kernel access to it
+// would fault.
+const void *device_address(const void *p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // a failed query must not look like a launch error
+    return nullptr;
+  }
+  switch (at.type) {
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged:
+    case hipMemoryTypeUnified:
+      return p;
+    case hipMemoryTypeHost: {
+      if (!at.devicePointer || !at.hostPointer) return nullptr;
+      const ptrdiff_t off = static_cast<const char *>(p) - static_cast<const char *>(at.hostPointer);
+      return static_cast<const char *>(at.devicePointer) + off;
+    }
+    default:
+      return nullptr;
+  }
+}
+
+int launch_copy_pages(const CopyLaunch &a) {
+  const void *ks = device_address(a.k_src), *vs = device_address(a.v_src);
+  const void *kd = device_address(a.k_dst), *vd = device_address(a.v_dst);
+  const void *map = device_address(a.mapping);
+  if (!ks || !vs || !kd || !vd || !map) return 3;  // PA_ERR_UNSUPPORTED: not device-accessible
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const int64_t page16 = a.page_bytes / 16;
+  const unsigned chunks = (unsigned)((page16 + kCopyChunk16 - 1) / kCopyChunk16);
+  hipLaunchKernelGGL(pa_copy_pages, dim3(a.num_pairs, chunks), dim3(kCopyThreads), 0, st,
+                     static_cast<const u32x4 *>(ks), static_cast<const u32x4 *>(vs),
+                     static_cast<u32x4 *>(const_cast<void *>(kd)),
+                     static_cast<u32x4 *>(const_cast<void *>(vd)),
+                     static_cast<const int64_t *>(map), page16, (int64_t)a.src_blocks,
+                     (int64_t)a.dst_blocks);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

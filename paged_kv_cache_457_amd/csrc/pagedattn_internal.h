@@ -45,6 +45,18 @@ struct CacheLaunch {
   void *stream;
 };
 
+struct CopyLaunch {
+  const void *k_src;
+  const void *v_src;
+  void *k_dst;
+  void *v_dst;
+  const int64_t *mapping;  // [num_pairs, 2] (source page, destination page)
+  int num_pairs;
+  int64_t page_bytes;      // bytes of one page of one pool, all kv-heads
+  int src_blocks, dst_blocks;
+  void *stream;
+};
+
 // Each returns 0 on success or the PA_ERR_HIP code on a launch error.
 int launch_decode(const DecodeLaunch &a);
 // The partition pass for bf16 with 2, 4 or 8 query heads per kv-head, on
@@ -56,6 +68,8 @@ int blocks_per_cu(const void *kernel, int block_threads);
 // once, capped by the number of work items; 0 on a runtime error.
 unsigned persistent_grid(const DecodeLaunch &a, int per_cu);
 int launch_reshape_and_cache(const CacheLaunch &a);
+// Also PA_ERR_UNSUPPORTED (3) when a pointer is not device-accessible.
+int launch_copy_pages(const CopyLaunch &a);
 int launch_hbm_probe(const void *buf, size_t bytes, void *sink, void *stream);
 size_t hbm_probe_sink_bytes();
 

@@ -157,6 +157,37 @@ for i in range(4):
     expect(f"cache pointer {i} misaligned", cache(num_tokens=1, ptrs=ptrs), _lib.PA_ERR_ALIGN)
 expect("slot_mapping misaligned", cache(num_tokens=1, ptrs=[P, P, P, P, P + 4]), _lib.PA_ERR_ALIGN)
 
+# ---- copy_blocks (num_pairs == 0: a wrong pass is a no-op)
+def copy(ptrs=None, **kw):
+    d = _lib.CopyDims()
+    d.num_pairs, d.num_kv_heads, d.head_dim, d.block_size = 0, 8, 128, 16
+    d.dtype, d.src_num_blocks, d.dst_num_blocks = _lib.PA_DTYPE_BF16, 100, 50
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return lib.copy_blocks(*(ptrs or [P] * 5), ctypes.byref(d))
+
+
+expect("copy dims NULL", lib.copy_blocks(P, P, P, P, P, None), _lib.PA_ERR_NULL)
+expect("valid empty copy is a no-op", copy(), _lib.PA_OK)
+expect("empty copy accepts NULL pointers", copy(ptrs=[None] * 5), _lib.PA_OK)
+for i in range(5):
+    ptrs = [P] * 5
+    ptrs[i] = None
+    expect(f"copy pointer {i} NULL", copy(ptrs=ptrs, num_pairs=1), _lib.PA_ERR_NULL)
+for i in range(4):
+    ptrs = [P] * 5
+    ptrs[i] = MIS
+    expect(f"copy pointer {i} misaligned", copy(ptrs=ptrs, num_pairs=1), _lib.PA_ERR_ALIGN)
+expect("copy mapping misaligned", copy(ptrs=[P, P, P, P, P + 4], num_pairs=1), _lib.PA_ERR_ALIGN)
+expect("copy negative pairs", copy(num_pairs=-1), _lib.PA_ERR_SHAPE)
+expect("copy zero kv heads", copy(num_kv_heads=0), _lib.PA_ERR_SHAPE)
+expect("copy zero source blocks", copy(src_num_blocks=0), _lib.PA_ERR_SHAPE)
+expect("copy zero destination blocks", copy(dst_num_blocks=0), _lib.PA_ERR_SHAPE)
+expect("copy reserved nonzero", copy(reserved=2), _lib.PA_ERR_SHAPE)
+expect("copy head_dim 96", copy(head_dim=96), _lib.PA_ERR_UNSUPPORTED)
+expect("copy block_size 8", copy(block_size=8), _lib.PA_ERR_UNSUPPORTED)
+expect("copy dtype 3", copy(dtype=3), _lib.PA_ERR_UNSUPPORTED)
+
 # ---- probe
 expect("probe NULL buffer", lib.pa_hbm_read_probe(None, 1024, P, None), _lib.PA_ERR_NULL)
 expect("probe size not a multiple of 16", lib.pa_hbm_read_probe(P, 1000, P, None), _lib.PA_ERR_SHAPE)

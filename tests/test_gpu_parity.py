@@ -7,6 +7,7 @@ with bf16 KV (fp32 accumulation); special cases with a unique exact answer
 permutation and batch composition (the reduction order depends only on a
 token's logical position).
 """
+import ctypes
 import math
 
 import numpy as np
@@ -334,3 +335,117 @@ def test_out_of_range_page_id_is_skipped(dt, G):
     err = max_err(got, ref, dt)
     say(f"{dt} G{G} skipped page: max abs err {err:.3e}")
     assert err <= TOL[dt]
+
+
+# ------------------------------------------------------------- page copies
+def _random_pairs(rng, n, src_pages, dst_pages, disjoint):
+    src = rng.choice(src_pages, size=n, replace=False)
+    pool = np.setdiff1d(np.arange(dst_pages), src) if disjoint else np.arange(dst_pages)
+    dst = rng.choice(pool, size=n, replace=False)
+    return np.stack([src, dst], axis=1).astype(np.int64)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 4])
+def test_copy_blocks_within_pool_bit_exact(idx):
+    """Copy-on-write moves: pages copied inside one device pool."""
+    w = make_config(idx)
+    rng = np.random.default_rng(100 + idx)
+    n = min(200, w.num_blocks // 3)
+    pairs = _random_pairs(rng, n, w.num_blocks, w.num_blocks, disjoint=True)
+    say(f"c{idx}: {n} pages within a pool of {w.num_blocks}")
+    dw = upload(w)
+    binding.copy_blocks(dw.k_pool, dw.v_pool, dw.k_pool, dw.v_pool, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    kp, vp = oracle.copy_blocks(w.k_pool, w.v_pool, w.k_pool, w.v_pool, pairs)
+    assert to_host(dw.k_pool, w.dtype).tobytes() == kp.tobytes()
+    assert to_host(dw.v_pool, w.dtype).tobytes() == vp.tobytes()
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_swap_out_and_in_through_pinned_host_pool(dt):
+    """Preemption swap: device pages to a pinned host pool and back, bit
+    exact; skipped pairs (negative or outside a pool) leave pages alone."""
+    w = build_workload("swap", [300, 17, 1000, 64], 16, 4, 128, 32, dt, seed=41)
+    rng = np.random.default_rng(41)
+    host_pages = 24
+    pairs = _random_pairs(rng, 20, w.num_blocks, host_pages, disjoint=False)
+    pairs[3] = (-1, 5)
+    pairs[7] = (2, host_pages + 3)
+    dw = upload(w)
+    tdt = torch_dtype(dt)
+    hk = torch.zeros((host_pages,) + tuple(w.k_pool.shape[1:]), dtype=tdt, pin_memory=True)
+    hv = torch.zeros_like(hk).pin_memory()
+    mapping = torch.from_numpy(pairs).cuda()
+    binding.copy_blocks(dw.k_pool, dw.v_pool, hk, hv, mapping)
+    torch.cuda.synchronize()
+    z = np.zeros((host_pages,) + w.k_pool.shape[1:], dtype=w.k_pool.dtype)
+    keep = (pairs[:, 0] >= 0) & (pairs[:, 1] < host_pages)
+    want_k, want_v = oracle.copy_blocks(w.k_pool, w.v_pool, z, z.copy(), pairs[keep])
+    assert to_host(hk, dt).tobytes() == want_k.tobytes()
+    assert to_host(hv, dt).tobytes() == want_v.tobytes()
+    say(f"{dt}: swapped out {int(keep.sum())} pages")
+    # wipe the device copies of the swapped pages, then swap back in
+    back = pairs[keep][:, ::-1].copy()
+    dw.k_pool[torch.from_numpy(back[:, 1]).cuda()] = 0
+    dw.v_pool[torch.from_numpy(back[:, 1]).cuda()] = 0
+    binding.copy_blocks(hk, hv, dw.k_pool, dw.v_pool, torch.from_numpy(back).cuda())
+    torch.cuda.synchronize()
+    assert to_host(dw.k_pool, dt).tobytes() == w.k_pool.tobytes()
+    assert to_host(dw.v_pool, dt).tobytes() == w.v_pool.tobytes()
+
+
+def test_copy_on_write_then_decode():
+    """Shared prefix ending inside a page: before a sample appends into the
+    shared last page it gets its own copy (copy_blocks), its table entry is
+    pointed at the copy, the token is written there, and attention over all
+    samples matches the oracle run through the same three steps."""
+    bs, prefix, samples = 16, 1000, 4           # the prefix's last page holds 8 tokens
+    ctx = [prefix + 1] * samples                 # every sample appends one token
+    # built with ctx = prefix + 1: the pools hold the prefix's 1000 tokens and
+    # the new token goes to position 1000
+    base = build_workload("cow", ctx, 16, 4, 128, bs, "bf16", seed=43,
+                          max_blocks_per_seq=(prefix + 1 + bs - 1) // bs)
+    # make every sample share sample 0's pages (a 1000-token shared prefix)
+    bt = np.repeat(base.block_tables[:1], samples, axis=0)
+    npg = (prefix + bs - 1) // bs
+    last = int(bt[0, npg - 1])
+    free = np.setdiff1d(np.arange(base.num_blocks), bt[0, :npg])[:samples]
+    pairs = np.stack([np.full(samples, last), free], axis=1).astype(np.int64)
+    bt[:, npg - 1] = free                        # each sample now owns a copy of the last page
+    slot = (free * bs + prefix % bs).astype(np.int64)
+    kp, vp = oracle.copy_blocks(base.k_pool, base.v_pool, base.k_pool, base.v_pool, pairs)
+    kp, vp = oracle.reshape_and_cache(base.k_new, base.v_new, kp, vp, slot, bs)
+    ref = oracle.decode(base.q, kp, vp, bt, np.array(ctx), 4, base.scale, bs, "bf16")
+    dw = upload(base)
+    binding.copy_blocks(dw.k_pool, dw.v_pool, dw.k_pool, dw.v_pool, torch.from_numpy(pairs).cuda())
+    binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, torch.from_numpy(slot).cuda())
+    dw.block_tables.copy_(torch.from_numpy(bt))
+    dw.context_lens.copy_(torch.tensor(ctx, dtype=torch.int32))
+    binding.paged_attention_decode(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
+                                   dw.context_lens, scale=float(base.scale))
+    torch.cuda.synchronize()
+    assert to_host(dw.k_pool, "bf16").tobytes() == kp.tobytes()
+    err = max_err(to_host(dw.out, "bf16"), ref, "bf16")
+    say(f"copy-on-write decode: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_copy_blocks_refuses_pageable_host_memory():
+    w = build_workload("pageable", [20], 4, 4, 64, 16, "bf16", seed=5)
+    dw = upload(w)
+    host = torch.zeros((4,) + tuple(w.k_pool.shape[1:]), dtype=torch.bfloat16)
+    # the one pair is a skipped one (source -1): even if the library let the
+    # pointer through, the kernel would touch no page
+    mapping = torch.tensor([[-1, 1]], dtype=torch.int64, device="cuda")
+    with pytest.raises(ValueError):
+        binding.copy_blocks(dw.k_pool, dw.v_pool, host, host, mapping)
+    # through the C ABI directly: the library's own check answers UNSUPPORTED
+    from paged_kv_cache_457_amd import _lib
+    d = _lib.CopyDims()
+    d.num_pairs, d.num_kv_heads, d.head_dim, d.block_size = 1, 4, 64, 16
+    d.dtype, d.src_num_blocks, d.dst_num_blocks = _lib.PA_DTYPE_BF16, w.num_blocks, 4
+    d.stream = torch.cuda.current_stream().cuda_stream
+    rc = _lib.load().copy_blocks(dw.k_pool.data_ptr(), dw.v_pool.data_ptr(), host.data_ptr(),
+                                 host.data_ptr(), mapping.data_ptr(), ctypes.byref(d))
+    assert rc == _lib.PA_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
