@@ -45,6 +45,12 @@ def parse():
                     help="HBM bytes per partition-kernel launch measured with rocprofv3 counters "
                          "(default: profiles/traffic_pa_decode_partition_c<config>.json); used "
                          "only while the kernel source still has the hash recorded there")
+    ap.add_argument("--op", choices=["decode-step", "copy", "swap-out", "swap-in"],
+                    default="decode-step",
+                    help="decode-step (default): the hot path; copy / swap-out / swap-in: "
+                         "copy_blocks within the device pool, to a pinned host pool, back")
+    ap.add_argument("--pages", type=int, default=2048,
+                    help="pages moved per copy_blocks call (--op copy/swap-*)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run a plain device copy of this many MiB "
                          "5 times, so a counter run can scale FETCH_SIZE / WRITE_SIZE")
@@ -127,6 +133,82 @@ def cpu_baseline(w, budget_s):
     }
 
 
+def bench_copy(args):
+    """copy_blocks on the workload's pool: --pages random pages per call,
+    within the device pool (copy-on-write), to a pinned host pool (swap-out)
+    or back (swap-in).  Bytes per call = pages * page bytes * 2 pools read
+    and the same written; the call is timed with HIP events on its stream.
+    For the swaps, a contiguous pinned copy of the same byte count through
+    torch (one DMA transfer) is timed beside it."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_457_amd import binding
+    from paged_kv_cache_457_amd.device_inputs import upload
+    from paged_kv_cache_457_amd.workloads import CONFIG_NAMES, make_config
+
+    w = make_config(args.config, args.seed)
+    dw = upload(w)
+    rng = np.random.default_rng(7)
+    n = min(args.pages, w.num_blocks // 2)
+    page_shape = tuple(w.k_pool.shape[1:])
+    page_bytes = int(np.prod(page_shape)) * w.elem_bytes
+    src = rng.choice(w.num_blocks, size=n, replace=False)
+    if args.op == "copy":
+        dst = rng.choice(np.setdiff1d(np.arange(w.num_blocks), src), size=n, replace=False)
+        ks, vs, kd, vd = dw.k_pool, dw.v_pool, dw.k_pool, dw.v_pool
+    else:
+        hk = torch.empty((n,) + page_shape, dtype=dw.k_pool.dtype, pin_memory=True)
+        hv = torch.empty_like(hk).pin_memory()
+        if args.op == "swap-out":
+            dst = np.arange(n)
+            ks, vs, kd, vd = dw.k_pool, dw.v_pool, hk, hv
+        else:
+            src, dst = np.arange(n), src
+            ks, vs, kd, vd = hk, hv, dw.k_pool, dw.v_pool
+    mapping = torch.from_numpy(np.stack([src, dst], 1).astype(np.int64)).cuda()
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        binding.copy_blocks(ks, vs, kd, vd, mapping)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        binding.copy_blocks(ks, vs, kd, vd, mapping)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    moved = 2 * n * page_bytes                    # K and V pages
+    gbs = 2 * moved / (ms * 1e-3) / 1e9           # read + write
+    result = {
+        "metric": f"copy_blocks {args.op} GB/s (read + write)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": CONFIG_NAMES[args.config] + f"; {n} random pages per call",
+                   "page_bytes_per_pool": page_bytes, "op": args.op},
+    }
+    if args.op == "copy":
+        result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        dev = torch.empty(moved // 2, dtype=torch.uint8, device="cuda")
+        host = torch.empty(moved // 2, dtype=torch.uint8, pin_memory=True)
+        pair = (dev, host) if args.op == "swap-out" else (host, dev)
+        for _ in range(3):
+            pair[1].copy_(pair[0], non_blocking=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(args.steps):
+            pair[1].copy_(pair[0], non_blocking=True)
+            pair[1].copy_(pair[0], non_blocking=True)
+        b.record(stream)
+        torch.cuda.synchronize()
+        result["contiguous_dma_gbs_one_way"] = round(moved / (a.elapsed_time(b) / args.steps
+                                                               * 1e-3) / 1e9, 1)
+        result["paged_gbs_one_way"] = round(moved / (ms * 1e-3) / 1e9, 1)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -144,6 +226,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.op != "decode-step":
+        bench_copy(args)
+        return
     w = make_config(args.config, args.seed)
     if args.partition_size is None:
         args.partition_size = w.partition_size
