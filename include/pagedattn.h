@@ -146,6 +146,53 @@ size_t paged_attention_decode_workspace_bytes(int32_t block_size,
 int32_t paged_attention_decode_partition_tokens(int32_t block_size,
                                                 const pa_decode_dims *dims);
 
+/*
+ * Decode attention for batches in which groups of consecutive sequences
+ * share their first pages (vLLM / PagedAttention pages: in parallel
+ * sampling the outputs of one request share the prefix's KV pages --
+ * tutorial page, section 4.2).  The result is that of
+ * paged_attention_decode on the same arguments; the shared pages are read
+ * once per group (up to 32 query rows, members x query heads per kv-head,
+ * per read) instead of once per sequence.
+ *
+ * group_starts  int32 [num_groups + 1], device: group i is sequences
+ *               group_starts[i] .. group_starts[i + 1] - 1 (nondecreasing,
+ *               group_starts[0] = 0, group_starts[num_groups] = num_seqs;
+ *               sequences outside every group have no shared prefix)
+ * prefix_lens   int32 [num_groups], device: tokens at the start of every
+ *               member's context on the same physical pages; the first
+ *               prefix_lens[i] / block_size table columns of every member
+ *               hold the same page ids (tokens of a partial last page count
+ *               as the members' own)
+ * A member's own context may end inside the prefix (its tokens past its
+ * context length are masked).  bf16 only (PA_ERR_UNSUPPORTED otherwise);
+ * head groups of 1, 2, 4 or 8.  The workspace must hold
+ * paged_attention_decode_shared_prefix_workspace_bytes(); dims, stream and
+ * timing events as for paged_attention_decode (the events bracket the
+ * pass over the units).
+ *
+ * Launches: a plan kernel (prefix units per group chunk and partition,
+ * own-page units per sequence, largest first), the unit pass (partials for
+ * every unit) and the reduce kernel (merges each sequence's partials).
+ */
+int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k_pool,
+                                         const void *v_pool, const int32_t *block_tables,
+                                         const int32_t *context_lens, int32_t num_kv_heads,
+                                         float scale, int32_t block_size,
+                                         const int32_t *group_starts,
+                                         const int32_t *prefix_lens, int32_t num_groups,
+                                         const pa_decode_dims *dims);
+
+/*
+ * Workspace bytes of paged_attention_decode_shared_prefix, with
+ * P = ceil(max_blocks_per_seq * block_size / partition_size):
+ *   plan 4 * (4 + 10 * num_seqs * P + 2 * num_seqs) rounded up to 256, plus
+ *   partials num_seqs * num_heads * 2P * (head_dim + 2) * 4.
+ * 0 when num_seqs is 0; SIZE_MAX for invalid shapes.
+ */
+size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t block_size,
+                                                            const pa_decode_dims *dims);
+
 /* Shapes and launch context of reshape_and_cache. */
 typedef struct pa_cache_dims {
   int32_t num_tokens;   /* >= 0; 0 is a no-op */

@@ -77,6 +77,13 @@ SIGNATURES = {
         ctypes.c_int32, ctypes.POINTER(DecodeDims)]),
     "paged_attention_decode_partition_tokens": (ctypes.c_int32, [
         ctypes.c_int32, ctypes.POINTER(DecodeDims)]),
+    "paged_attention_decode_shared_prefix": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+        ctypes.POINTER(DecodeDims)]),
+    "paged_attention_decode_shared_prefix_workspace_bytes": (ctypes.c_size_t, [
+        ctypes.c_int32, ctypes.POINTER(DecodeDims)]),
     "reshape_and_cache": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.POINTER(CacheDims)]),

@@ -136,6 +136,65 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     return out
 
 
+def paged_attention_decode_shared_prefix(
+        out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+        block_tables: torch.Tensor, context_lens: torch.Tensor, group_starts: torch.Tensor,
+        prefix_lens: torch.Tensor, scale: Optional[float] = None, partition_size: int = 0,
+        workspace: Optional[torch.Tensor] = None, stream=None,
+        timing_events: Sequence = (None, None)) -> torch.Tensor:
+    """paged_attention_decode for batches whose groups of consecutive
+    sequences share prefix pages (see paged_attention_decode_shared_prefix
+    in include/pagedattn.h); group_starts int32 [G+1], prefix_lens int32 [G]."""
+    if q.dtype != torch.bfloat16:
+        raise ValueError("shared-prefix decode is built for bf16")
+    for name, t in (("out", out), ("k_pool", k_pool), ("v_pool", v_pool)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    for name, t in (("block_tables", block_tables), ("context_lens", context_lens),
+                    ("group_starts", group_starts), ("prefix_lens", prefix_lens)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if group_starts.dim() != 1 or prefix_lens.shape != (group_starts.shape[0] - 1,):
+        raise ValueError("group_starts must be [G + 1] and prefix_lens [G]")
+    S, H, D = q.shape
+    if out.shape != q.shape or k_pool.shape != v_pool.shape or k_pool.dim() != 4 \
+            or k_pool.shape[3] != D or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("shapes as for paged_attention_decode")
+    hkv, bs = k_pool.shape[1], k_pool.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    d = decode_dims(q, k_pool, block_tables, partition_size)
+    lib = _lib.load()
+    need = lib.paged_attention_decode_shared_prefix_workspace_bytes(bs, ctypes.byref(d))
+    if need == _lib.SIZE_MAX:
+        _check(_lib.PA_ERR_SHAPE, "paged_attention_decode_shared_prefix")
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        d.workspace = _dev(workspace, "workspace")
+        d.workspace_bytes = workspace.numel() * workspace.element_size()
+    d.stream = _stream_ptr(stream)
+    d.timing_events[0] = _event_ptr(timing_events[0])
+    d.timing_events[1] = _event_ptr(timing_events[1])
+    rc = lib.paged_attention_decode_shared_prefix(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), hkv,
+        ctypes.c_float(scale), bs, _dev(group_starts, "group_starts"),
+        _dev(prefix_lens, "prefix_lens"), prefix_lens.shape[0], ctypes.byref(d))
+    _check(rc, "paged_attention_decode_shared_prefix")
+    return out
+
+
+def paged_attention_decode_shared_prefix_workspace_bytes(q, k_pool, block_tables,
+                                                         partition_size: int = 0) -> int:
+    d = decode_dims(q, k_pool, block_tables, partition_size)
+    n = _lib.load().paged_attention_decode_shared_prefix_workspace_bytes(k_pool.shape[2],
+                                                                         ctypes.byref(d))
+    if n == _lib.SIZE_MAX:
+        raise ValueError("invalid shapes for paged_attention_decode_shared_prefix")
+    return n
+
+
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, k_pool: torch.Tensor,
                       v_pool: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
     """Write k[i], v[i] ([T, num_kv_heads, head_dim]) to pool slot

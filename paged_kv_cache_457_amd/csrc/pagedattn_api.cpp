@@ -71,6 +71,21 @@ size_t partial_bytes(const pa_decode_dims *d, int parts) {
   return (size_t)d->num_seqs * d->num_heads * parts * (size_t)(d->head_dim + 2) * sizeof(float);
 }
 
+// Shared-prefix decode: slots per sequence are prefix partitions then
+// suffix partitions, each at most ceil(max_blocks / partition pages).
+int prefix_slots(int32_t block_size, const pa_decode_dims *d) {
+  return 2 * max_partitions(block_size, d);
+}
+size_t prefix_plan_ints(int num_seqs, int slots) {
+  return (size_t)kPlanHeader + (size_t)pa_internal::kPrefixUnitInts * num_seqs * slots +
+         2 * (size_t)num_seqs;
+}
+size_t prefix_workspace_bytes(int32_t block_size, const pa_decode_dims *d) {
+  const int ms = prefix_slots(block_size, d);
+  const size_t plan = (prefix_plan_ints(d->num_seqs, ms) * sizeof(int32_t) + 255) / 256 * 256;
+  return plan + (size_t)d->num_seqs * d->num_heads * ms * (size_t)(d->head_dim + 2) * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -83,6 +98,81 @@ size_t paged_attention_decode_workspace_bytes(int32_t block_size, const pa_decod
   if (dims->num_seqs == 0) return 0;
   const int mp = max_partitions(block_size, dims);
   return plan_bytes(dims->num_seqs, mp) + partial_bytes(dims, mp);
+}
+
+size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t block_size,
+                                                            const pa_decode_dims *dims) {
+  if (!dims || dims->num_heads < 1) return SIZE_MAX;
+  if (check_decode_dims(dims->num_heads, block_size, dims) != PA_OK) return SIZE_MAX;
+  if ((int64_t)dims->num_seqs * prefix_slots(block_size, dims) * dims->num_heads > INT32_MAX)
+    return SIZE_MAX;
+  if (dims->num_seqs == 0) return 0;
+  return prefix_workspace_bytes(block_size, dims);
+}
+
+int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k_pool,
+                                         const void *v_pool, const int32_t *block_tables,
+                                         const int32_t *context_lens, int32_t num_kv_heads,
+                                         float scale, int32_t block_size,
+                                         const int32_t *group_starts,
+                                         const int32_t *prefix_lens, int32_t num_groups,
+                                         const pa_decode_dims *dims) {
+  if (!dims) return PA_ERR_NULL;
+  int rc = check_decode_dims(num_kv_heads, block_size, dims);
+  if (rc != PA_OK) return rc;
+  if (dims->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;  // matrix cores: bf16 only
+  if (!std::isfinite(scale) || num_groups < 0) return PA_ERR_SHAPE;
+  const int ms = prefix_slots(block_size, dims);
+  if ((int64_t)dims->num_seqs * ms * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (num_groups < 1) return PA_ERR_SHAPE;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !group_starts ||
+      !prefix_lens)
+    return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(group_starts, 4) ||
+      !aligned(prefix_lens, 4))
+    return PA_ERR_ALIGN;
+  if (!dims->workspace || dims->workspace_bytes < prefix_workspace_bytes(block_size, dims) ||
+      !aligned(dims->workspace, 16))
+    return PA_ERR_WORKSPACE;
+  int32_t *plan = static_cast<int32_t *>(dims->workspace);
+  const size_t plan_ints = prefix_plan_ints(dims->num_seqs, ms);
+  const size_t plan_bytes = (plan_ints * sizeof(int32_t) + 255) / 256 * 256;
+  float *ws_acc = reinterpret_cast<float *>(static_cast<char *>(dims->workspace) + plan_bytes);
+
+  pa_internal::PrefixLaunch p{};
+  pa_internal::DecodeLaunch &a = p.base;
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.plan = plan;
+  a.ws_acc = ws_acc;
+  a.ws_ml = ws_acc + (size_t)dims->num_seqs * dims->num_heads * ms * dims->head_dim;
+  a.num_seqs = dims->num_seqs;
+  a.num_heads = dims->num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.block_size = block_size;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.num_blocks = dims->num_blocks;
+  a.dtype = dims->dtype;
+  a.part_pages = partition_tokens(dims, block_size) / block_size;
+  a.max_parts = ms;
+  a.scale = scale;
+  a.stream = dims->stream;
+  a.ev_begin = dims->timing_events[0];
+  a.ev_end = dims->timing_events[1];
+  p.group_starts = group_starts;
+  p.prefix_lens = prefix_lens;
+  p.num_groups = num_groups;
+  p.nslots = plan + kPlanHeader + (size_t)pa_internal::kPrefixUnitInts * dims->num_seqs * ms;
+  p.seq_pre = p.nslots + dims->num_seqs;
+  p.max_units = (long long)dims->num_seqs * ms;
+  return pa_internal::launch_decode_shared_prefix(p);
 }
 
 int32_t paged_attention_decode_partition_tokens(int32_t block_size, const pa_decode_dims *dims) {

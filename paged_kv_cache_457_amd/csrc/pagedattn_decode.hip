@@ -360,11 +360,14 @@ __global__ __launch_bounds__(kPlanThreads) void pa_decode_plan(
 constexpr int kReduceWaves = 4;
 constexpr int kReduceUnroll = 8;
 
+// With nslots (shared-prefix decode) sequence s has nslots[s] partials,
+// written by the prefix and suffix units, and every sequence is finished
+// here, also with one partial or none (a zero row).
 template <class T, int D>
 __global__ __launch_bounds__(64 * kReduceWaves) void pa_decode_reduce(
     void *__restrict__ out, const float *__restrict__ ws_ml, const float *__restrict__ ws_acc,
-    const int32_t *__restrict__ context_lens, int num_heads, int ctx_cap, int part_tokens,
-    int max_parts) {
+    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ nslots,
+    int num_heads, int ctx_cap, int part_tokens, int max_parts) {
   constexpr int DPL = D / 64;  // output elements per lane
   __shared__ float s_o[kReduceWaves][D];
   __shared__ float s_l[kReduceWaves];
@@ -372,9 +375,14 @@ __global__ __launch_bounds__(64 * kReduceWaves) void pa_decode_reduce(
   const int wave = threadIdx.x >> 6;
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int ctx = min(max(context_lens[s], 0), ctx_cap);
-  const int nparts = (ctx + part_tokens - 1) / part_tokens;
-  if (nparts <= 1) return;
+  int nparts;
+  if (nslots) {
+    nparts = min(nslots[s], max_parts);
+  } else {
+    const int ctx = min(max(context_lens[s], 0), ctx_cap);
+    nparts = (ctx + part_tokens - 1) / part_tokens;
+    if (nparts <= 1) return;  // the partition pass wrote the output itself
+  }
   const size_t row0 = ((size_t)s * num_heads + h) * max_parts;
   const float *ml = ws_ml + row0 * 2;
   const float *acc = ws_acc + row0 * D + lane * DPL;
@@ -486,7 +494,7 @@ int run_decode(const pa_internal::DecodeLaunch &a) {
   if (a.max_parts > 1) {
     hipLaunchKernelGGL((pa_decode_reduce<T, D>), dim3(a.num_heads, a.num_seqs),
                        dim3(64 * kReduceWaves), 0, st,
-                       a.out, a.ws_ml, a.ws_acc, a.context_lens, a.num_heads,
+                       a.out, a.ws_ml, a.ws_acc, a.context_lens, nullptr, a.num_heads,
                        a.max_blocks * a.block_size, a.part_pages * a.block_size, a.max_parts);
     if (hipGetLastError() != hipSuccess) return 6;
   }
@@ -510,6 +518,10 @@ int blocks_per_cu(const void *kernel, int block_threads) {
 }
 
 unsigned persistent_grid(const DecodeLaunch &a, int per_cu) {
+  return persistent_grid_items((long long)a.num_seqs * a.max_parts * a.num_kv_heads, per_cu);
+}
+
+unsigned persistent_grid_items(long long items, int per_cu) {
   // compute units of the current device, queried once per device
   static std::atomic<int> cus_of[kMaxDevices];
   int dev = 0;
@@ -522,8 +534,23 @@ unsigned persistent_grid(const DecodeLaunch &a, int per_cu) {
     if (dev < kMaxDevices) cus_of[dev].store(cus, std::memory_order_relaxed);
   }
   const long long resident = (long long)cus * per_cu;
-  const long long items = (long long)a.num_seqs * a.max_parts * a.num_kv_heads;
   return (unsigned)(resident < items ? resident : items);
+}
+
+int launch_decode_shared_prefix(const PrefixLaunch &p) {
+  const DecodeLaunch &a = p.base;
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  int rc = launch_prefix_plan(p);
+  if (rc != 0) return rc;
+  if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
+  rc = launch_prefix_units(p, a.scale * kLog2e);
+  if (rc != 0) return rc;
+  if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
+  auto reduce = a.head_dim == 64 ? pa_decode_reduce<BF16, 64> : pa_decode_reduce<BF16, 128>;
+  hipLaunchKernelGGL(reduce, dim3(a.num_heads, a.num_seqs), dim3(64 * kReduceWaves), 0, st,
+                     a.out, a.ws_ml, a.ws_acc, a.context_lens, p.nslots, a.num_heads,
+                     a.max_blocks * a.block_size, a.part_pages * a.block_size, a.max_parts);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
 int launch_decode(const DecodeLaunch &a) {

@@ -1,0 +1,444 @@
+// Paged decode attention with shared prefixes (bf16, matrix cores).
+//
+// Parallel sampling keeps one prompt's KV cache on pages that all samples of
+// the prompt share (tutorial page, section 4.2: several outputs of one
+// request share the same prefix pages; showapi.com article, section 2.2).
+// Plain decode reads such a page once per sample.  Here the samples of a
+// group read each shared page once: the G query heads of every member form
+// one grouped contraction over the shared pages (up to 32 query rows, two
+// 16-row MFMA tiles), and each member's own pages past the prefix are a
+// separate unit.  Every unit leaves partial (max, sum, accumulator) rows in
+// the workspace and the reduce kernel merges a sequence's prefix and suffix
+// partials by log-sum-exp, so the result is the same softmax as plain decode.
+//
+// Units (plan kernel, largest first):
+//   prefix unit: members seq0 .. seq0 + nmem - 1 of one group (nmem * G <=
+//                32 rows), pages [pb, pe) of the shared prefix, read through
+//                seq0's table row (the members' rows agree there)
+//   suffix unit: one sequence (nmem = 1), pages [pb, pe) past the prefix
+// Each unit writes partial slot `slot` of its rows; a sequence's slots are
+// its group's prefix partitions first, then its own suffix partitions.
+//
+// Lane layouts are those of the grouped-query kernel (pagedattn_decode_gqa
+// .hip), with the head-group columns widened to member x head rows:
+// tile t, lane 16*q4 + j holds query row 16*t + j = member (16t+j) / G, head
+// g*G + (16t+j) % G.  Each query row masks the tokens at or past its own
+// sequence's context.  V rows at or past the longest member's context are
+// staged as zeros, so a poisoned slot (NaN) never reaches a multiply; a
+// row's other masked tokens only multiply finite, live values by 0.
+#include <type_traits>
+
+#include "pagedattn_device.h"
+#include "pagedattn_internal.h"
+
+namespace {
+
+using namespace pa_dev;
+using pa_internal::kMaxPartitionPages;
+using pa_internal::kPlanHeader;
+using pa_internal::kPrefixRows;
+using pa_internal::kPrefixUnitInts;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int kTiles = kPrefixRows / 16;
+
+// ------------------------------------------------------------------ plan
+// One workgroup.  Layout of the plan area:
+//   plan[0]                          unit count
+//   plan[kPlanHeader + 5k .. +4]     unit k: seq0, nmem, pb, pe, slot
+//   nslots[s]                        partial slots sequence s fills
+//   seq_pre[s]                       shared prefix pages of s's group
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void pa_prefix_plan(
+    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ group_starts,
+    const int32_t *__restrict__ prefix_lens, int num_groups, int num_seqs, int group_size,
+    int ctx_cap, int block_size, int part_pages, int32_t *__restrict__ plan,
+    int32_t *__restrict__ nslots, int32_t *__restrict__ seq_pre) {
+  __shared__ int s_count[kMaxPartitionPages + 1];
+  __shared__ int s_next[kMaxPartitionPages + 1];
+  const int members_per_chunk = kPrefixRows / group_size;
+  const int max_pages = ctx_cap / block_size;
+  for (int i = threadIdx.x; i <= part_pages; i += kPlanThreads) s_count[i] = 0;
+  for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) seq_pre[s] = 0;
+  __syncthreads();
+  for (int gi = threadIdx.x; gi < num_groups; gi += kPlanThreads) {
+    const int b = min(max(group_starts[gi], 0), num_seqs);
+    const int e = min(max(group_starts[gi + 1], b), num_seqs);
+    const int pre = min(max(prefix_lens[gi], 0), ctx_cap) / block_size;
+    for (int s = b; s < e; ++s) seq_pre[s] = pre;
+  }
+  __syncthreads();
+  // pages of sequence s past its prefix
+  auto own_pages = [&](int s) {
+    const int ctx = min(max(context_lens[s], 0), ctx_cap);
+    return max(0, min((ctx + block_size - 1) / block_size, max_pages) - seq_pre[s]);
+  };
+  // pass 1: count units per size; slots per sequence
+  for (int gi = threadIdx.x; gi < num_groups; gi += kPlanThreads) {
+    const int b = min(max(group_starts[gi], 0), num_seqs);
+    const int e = min(max(group_starts[gi + 1], b), num_seqs);
+    if (e == b) continue;
+    const int pre = seq_pre[b];
+    const int chunks = (e - b + members_per_chunk - 1) / members_per_chunk;
+    for (int p0 = 0; p0 < pre; p0 += part_pages)
+      atomicAdd(&s_count[min(part_pages, pre - p0)], chunks);
+  }
+  for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
+    const int own = own_pages(s);
+    for (int p0 = 0; p0 < own; p0 += part_pages) atomicAdd(&s_count[min(part_pages, own - p0)], 1);
+    nslots[s] = (seq_pre[s] + part_pages - 1) / part_pages + (own + part_pages - 1) / part_pages;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int at = 0;
+    for (int z = part_pages; z >= 1; --z) {
+      s_next[z] = at;
+      at += s_count[z];
+    }
+    plan[0] = at;
+  }
+  __syncthreads();
+  // pass 2: write the records, largest first
+  auto put = [&](int seq0, int nmem, int pb, int pe, int slot) {
+    int32_t *r = plan + kPlanHeader + kPrefixUnitInts * atomicAdd(&s_next[pe - pb], 1);
+    r[0] = seq0;
+    r[1] = nmem;
+    r[2] = pb;
+    r[3] = pe;
+    r[4] = slot;
+  };
+  for (int gi = threadIdx.x; gi < num_groups; gi += kPlanThreads) {
+    const int b = min(max(group_starts[gi], 0), num_seqs);
+    const int e = min(max(group_starts[gi + 1], b), num_seqs);
+    if (e == b) continue;
+    const int pre = seq_pre[b];
+    for (int s0 = b; s0 < e; s0 += members_per_chunk)
+      for (int p0 = 0, k = 0; p0 < pre; p0 += part_pages, ++k)
+        put(s0, min(members_per_chunk, e - s0), p0, min(pre, p0 + part_pages), k);
+  }
+  for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
+    const int pre = seq_pre[s];
+    const int own = own_pages(s);
+    const int slot0 = (pre + part_pages - 1) / part_pages;
+    for (int p0 = 0, k = 0; p0 < own; p0 += part_pages, ++k)
+      put(s, 1, pre + p0, pre + min(own, p0 + part_pages), slot0 + k);
+  }
+}
+
+// ------------------------------------------------------------ unit kernel
+template <int D, int BS>
+struct PrefixShape {
+  static constexpr int GPP = BS / 16;          // 16-token granules per page
+  static constexpr int NC = D / 32;            // 32-wide head_dim slabs (q.K)
+  static constexpr int NN = D / 16;            // 16-wide head_dim blocks (P.V)
+  static constexpr int ROW = D * 2;            // bytes per token row
+  static constexpr int GBYTES = 16 * ROW;      // bytes of one granule of K or V
+  static constexpr int NVLD = GBYTES / 1024;   // 1 KiB V loads per granule
+  static constexpr int PITCH = ROW + 32;       // LDS row pitch of a staged V granule
+  static constexpr int VBYTES = 16 * PITCH;
+  static constexpr int ACC_BYTES = 16 * D * 4; // one tile's partial O
+  static constexpr int WAVE_LDS = VBYTES > ACC_BYTES ? VBYTES : ACC_BYTES;
+};
+
+template <int D>
+struct PrefixGranule {
+  bf16x8 k[D / 32];
+  u32x4 v[16 * D * 2 / 1024];
+  bool ok;
+};
+
+template <int D, int BS, int G, int NW>
+__device__ __forceinline__ void prefix_unit(
+    const void *__restrict__ q, const void *__restrict__ k_pool, const void *__restrict__ v_pool,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+    float *__restrict__ ws_ml, float *__restrict__ ws_acc, int num_heads, int num_kv_heads,
+    int max_blocks, int num_blocks, int max_slots, float scale_log2, int seq0, int nmem, int pb,
+    int pe, int slot, int g) {
+  using S = PrefixShape<D, BS>;
+  constexpr int GPP = S::GPP, NC = S::NC, NN = S::NN, ROW = S::ROW, NVLD = S::NVLD;
+  constexpr int PITCH = S::PITCH;
+  __shared__ __attribute__((aligned(16))) char s_wave[NW][S::WAVE_LDS];
+  __shared__ float s_ml[NW][16][2];
+  // the unit's query rows as MFMA B operands: [tile][slab][lane] 16 bytes
+  __shared__ __attribute__((aligned(16))) u32x4 s_q[kTiles][NC][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q4 = lane >> 4;
+  const int j16 = lane & 15;
+  const int rows = nmem * G;                       // query rows of this unit (<= 32)
+  const int ntiles = (rows + 15) / 16;             // 1 or 2, same for the whole workgroup
+  const int ctx_cap = max_blocks * BS;
+
+  // this wave's page ids (one per lane), q rows as B operands, each row's
+  // context length
+  const int np = pe - pb;
+  const int col = pb + wave + NW * lane;
+  int my_bid = -1;
+  if (wave + NW * lane < np) my_bid = block_tables[(size_t)seq0 * max_blocks + col];
+  int ctx_row[kTiles];
+  int ctx_max = 0;
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    const int r = 16 * t + j16;
+    const bool live = r < rows;
+    const int s = seq0 + (live ? r / G : 0);
+    if (wave == 0) {
+      const char *qrow =
+          reinterpret_cast<const char *>(q) + ((size_t)s * num_heads + g * G + r % G) * ROW;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (live) w = load16(qrow + 64 * c + 16 * q4);
+        s_q[t][c][lane] = w;
+      }
+    }
+    ctx_row[t] = live ? min(max(context_lens[s], 0), ctx_cap) : 0;
+    ctx_max = max(ctx_max, ctx_row[t]);
+  }
+  __syncthreads();  // s_q is written by wave 0 and read by all
+#pragma unroll
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) ctx_max = max(ctx_max, __shfl_xor(ctx_max, o2));
+  const int np_w = wave < np ? (np - wave + NW - 1) / NW : 0;
+
+  float m[kTiles], l[kTiles];
+  f32x4 o[kTiles][NN];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NN; ++n) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const size_t page_stride = (size_t)num_kv_heads * BS * ROW;
+  const char *k_b = reinterpret_cast<const char *>(k_pool) + (size_t)g * BS * ROW;
+  const char *v_b = reinterpret_cast<const char *>(v_pool) + (size_t)g * BS * ROW;
+  char *vs = s_wave[wave];
+
+  auto fetch = [&](PrefixGranule<D> &gr, int jg) {
+    const int bid = __builtin_amdgcn_readlane(my_bid, jg / GPP);
+    gr.ok = (unsigned)bid < (unsigned)num_blocks;
+    const size_t off = (size_t)(gr.ok ? bid : 0) * page_stride + (jg % GPP) * S::GBYTES;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      gr.k[c] = __builtin_bit_cast(bf16x8, load_kv16(k_b + off + j16 * ROW + 64 * c + 16 * q4));
+#pragma unroll
+    for (int i = 0; i < NVLD; ++i) gr.v[i] = load_kv16(v_b + off + i * 1024 + 16 * lane);
+  };
+
+  auto process = [&](const PrefixGranule<D> &gr, int jg) {
+    const int tok0 = (pb + wave + NW * (jg / GPP)) * BS + 16 * (jg % GPP);
+#pragma unroll
+    for (int i = 0; i < NVLD; ++i) {
+      const int byte = i * 1024 + 16 * lane;
+      const int row = byte / ROW;
+      u32x4 w = gr.v[i];
+      if (!gr.ok || tok0 + row >= ctx_max) w = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(vs + row * PITCH + byte % ROW) = w;
+    }
+    i16x4 phi[kTiles], plo[kTiles];
+    // q.K and the softmax update of tile T (query rows 16T .. 16T+15)
+    auto tile_logits = [&](auto tc) {
+      constexpr int T = decltype(tc)::value;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            gr.k[c], __builtin_bit_cast(bf16x8, s_q[T][c][lane]), acc, 0, 0, 0);
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool keep = gr.ok && tok0 + 4 * q4 + r < ctx_row[T];
+        sc[r] = keep ? acc[r] * scale_log2 : -INFINITY;
+      }
+      float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      pm = fmaxf(pm, __shfl_xor(pm, 16));
+      pm = fmaxf(pm, __shfl_xor(pm, 32));
+      // rows differ in context length, so a row may have nothing live yet
+      const float mn = fmaxf(m[T], pm);
+      const bool none = mn == -INFINITY;
+      const float alpha = none ? 1.f : fast_exp2(m[T] - mn);
+      const float base = none ? 0.f : mn;
+      m[T] = mn;
+      l[T] *= alpha;
+#pragma unroll
+      for (int n = 0; n < NN; ++n) o[T][n] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(sc[r] - base);
+        l[T] += p;
+        const __bf16 hi = (__bf16)p;
+        const __bf16 lo = (__bf16)(p - (float)hi);
+        phi[T][r] = __builtin_bit_cast(short, hi);
+        plo[T][r] = __builtin_bit_cast(short, lo);
+      }
+    };
+    tile_logits(std::integral_constant<int, 0>());
+    if (ntiles > 1) tile_logits(std::integral_constant<int, 1>());
+    const int vbase = (4 * q4 + (j16 >> 2)) * PITCH + 8 * (j16 & 3);
+#pragma unroll
+    for (int n = 0; n < NN; ++n) {
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4 *)((lds_char *)vs + vbase + 32 * n));
+      o[0][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi[0], o[0][n], 0, 0, 0);
+      o[0][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo[0], o[0][n], 0, 0, 0);
+      if (ntiles > 1) {
+        o[1][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi[1], o[1][n], 0, 0, 0);
+        o[1][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo[1], o[1][n], 0, 0, 0);
+      }
+    }
+  };
+
+  const int ng = np_w * GPP;
+  if (ng > 0) {
+    PrefixGranule<D> ga, gb;
+    fetch(ga, 0);
+    int j = 0;
+    for (; j + 2 < ng; j += 2) {
+      fetch(gb, j + 1);
+      process(ga, j);
+      fetch(ga, j + 2);
+      process(gb, j + 1);
+    }
+    if (j + 1 < ng) {
+      fetch(gb, j + 1);
+      process(ga, j);
+      process(gb, j + 1);
+    } else {
+      process(ga, j);
+    }
+  }
+
+  // merge the NW waves tile by tile through LDS and store the partials
+  auto merge_tile = [&](auto tc) {
+    constexpr int T = decltype(tc)::value;
+    float lt = l[T];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    float *s_acc = reinterpret_cast<float *>(vs);
+    __syncthreads();  // every wave is done with its staging area / the previous tile
+#pragma unroll
+    for (int n = 0; n < NN; ++n)
+      *reinterpret_cast<float4 *>(&s_acc[j16 * D + 16 * n + 4 * q4]) =
+          make_float4(o[T][n][0], o[T][n][1], o[T][n][2], o[T][n][3]);
+    if (q4 == 0) {
+      s_ml[wave][j16][0] = m[T];
+      s_ml[wave][j16][1] = lt;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * D / 4; idx += 64 * NW) {
+      const int j = idx / (D / 4);
+      const int d = (idx % (D / 4)) * 4;
+      const int r = 16 * T + j;
+      if (r >= rows) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][j][0]);
+      float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float sc = fast_exp2(s_ml[w][j][0] - M);
+          L = fmaf(s_ml[w][j][1], sc, L);
+          const float4 a = *reinterpret_cast<const float4 *>(
+              reinterpret_cast<const float *>(s_wave[w]) + j * D + d);
+          acc[0] = fmaf(a.x, sc, acc[0]);
+          acc[1] = fmaf(a.y, sc, acc[1]);
+          acc[2] = fmaf(a.z, sc, acc[2]);
+          acc[3] = fmaf(a.w, sc, acc[3]);
+        }
+      }
+      const size_t wrow =
+          ((size_t)(seq0 + r / G) * num_heads + g * G + r % G) * max_slots + slot;
+      *reinterpret_cast<float4 *>(ws_acc + wrow * D + d) =
+          make_float4(acc[0], acc[1], acc[2], acc[3]);
+      if (d == 0) {
+        ws_ml[wrow * 2] = M;
+        ws_ml[wrow * 2 + 1] = L;
+      }
+    }
+  };
+  merge_tile(std::integral_constant<int, 0>());
+  if (ntiles > 1) merge_tile(std::integral_constant<int, 1>());
+}
+
+// Persistent kernel over the plan's units (largest first), item i = (unit
+// i / num_kv_heads, kv-head i % num_kv_heads), snake order.
+template <int D, int BS, int G, int NW>
+__global__ __launch_bounds__(64 * NW) void pa_decode_prefix_gqa(
+    const void *__restrict__ q, const void *__restrict__ k_pool, const void *__restrict__ v_pool,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+    float *__restrict__ ws_ml, float *__restrict__ ws_acc, const int32_t *__restrict__ plan,
+    int num_heads, int num_kv_heads, int max_blocks, int num_blocks, int max_slots,
+    float scale_log2) {
+  const int items = plan[0] * num_kv_heads;
+  for (int k = 0;; ++k) {
+    const int it = snake_item(k);
+    if (it >= items) break;
+    const int32_t *u = plan + kPlanHeader + (size_t)kPrefixUnitInts * (it / num_kv_heads);
+    prefix_unit<D, BS, G, NW>(q, k_pool, v_pool, block_tables, context_lens, ws_ml, ws_acc,
+                              num_heads, num_kv_heads, max_blocks, num_blocks, max_slots,
+                              scale_log2, u[0], u[1], u[2], u[3], u[4], it % num_kv_heads);
+    __syncthreads();  // the next unit reuses the LDS
+  }
+}
+
+constexpr int kWavesPerUnit = 4;
+
+template <int D, int BS, int G>
+int launch(const pa_internal::PrefixLaunch &p, float scale_log2) {
+  const pa_internal::DecodeLaunch &a = p.base;
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  auto kernel = pa_decode_prefix_gqa<D, BS, G, kWavesPerUnit>;
+  static const int per_cu = pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel),
+                                                       64 * kWavesPerUnit);
+  const unsigned grid = pa_internal::persistent_grid_items(p.max_units * (long long)a.num_kv_heads,
+                                                           per_cu);
+  if (grid == 0) return 6;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.q, a.k_pool,
+                     a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc, a.plan,
+                     a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks, a.max_parts,
+                     scale_log2);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+template <int D, int BS>
+int by_group(const pa_internal::PrefixLaunch &p, float scale_log2) {
+  switch (p.base.num_heads / p.base.num_kv_heads) {
+    case 1: return launch<D, BS, 1>(p, scale_log2);
+    case 2: return launch<D, BS, 2>(p, scale_log2);
+    case 4: return launch<D, BS, 4>(p, scale_log2);
+    case 8: return launch<D, BS, 8>(p, scale_log2);
+  }
+  return 3;
+}
+
+}  // namespace
+
+namespace pa_internal {
+
+int launch_prefix_plan(const PrefixLaunch &p) {
+  const DecodeLaunch &a = p.base;
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  hipLaunchKernelGGL(pa_prefix_plan, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens,
+                     p.group_starts, p.prefix_lens, p.num_groups, a.num_seqs,
+                     a.num_heads / a.num_kv_heads, a.max_blocks * a.block_size, a.block_size,
+                     a.part_pages, a.plan, p.nslots, p.seq_pre);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+int launch_prefix_units(const PrefixLaunch &p, float scale_log2) {
+  const DecodeLaunch &a = p.base;
+  if (a.head_dim == 64)
+    return a.block_size == 16 ? by_group<64, 16>(p, scale_log2) : by_group<64, 32>(p, scale_log2);
+  return a.block_size == 16 ? by_group<128, 16>(p, scale_log2) : by_group<128, 32>(p, scale_log2);
+}
+
+}  // namespace pa_internal

@@ -14,6 +14,10 @@ constexpr int kMaxPartitionPages = 4 * 64;
 // number of units, then one (sequence * max_parts + partition) per unit.
 constexpr int kPlanHeader = 4;
 constexpr int kMaxDevices = 64;
+// Shared-prefix decode: query rows (members x heads of a group) one prefix
+// unit serves, and the ints of one unit record in the plan.
+constexpr int kPrefixRows = 32;
+constexpr int kPrefixUnitInts = 5;
 
 struct DecodeLaunch {
   void *out;
@@ -33,6 +37,16 @@ struct DecodeLaunch {
   void *stream;
   void *ev_begin;
   void *ev_end;
+};
+
+struct PrefixLaunch {
+  DecodeLaunch base;            // max_parts holds the partial slots per sequence
+  const int32_t *group_starts;  // [num_groups + 1]
+  const int32_t *prefix_lens;   // [num_groups]
+  int num_groups;
+  int32_t *nslots;              // [num_seqs] slots each sequence fills
+  int32_t *seq_pre;             // [num_seqs] shared prefix pages of its group
+  long long max_units;          // bound on the plan's units
 };
 
 struct CacheLaunch {
@@ -67,6 +81,11 @@ int blocks_per_cu(const void *kernel, int block_threads);
 // Grid of a persistent partition kernel: what the current device holds at
 // once, capped by the number of work items; 0 on a runtime error.
 unsigned persistent_grid(const DecodeLaunch &a, int per_cu);
+unsigned persistent_grid_items(long long items, int per_cu);
+// Shared-prefix decode: plan, unit pass and the final merge.
+int launch_decode_shared_prefix(const PrefixLaunch &p);
+int launch_prefix_plan(const PrefixLaunch &p);
+int launch_prefix_units(const PrefixLaunch &p, float scale_log2);
 int launch_reshape_and_cache(const CacheLaunch &a);
 // Also PA_ERR_UNSUPPORTED (3) when a pointer is not device-accessible.
 int launch_copy_pages(const CopyLaunch &a);

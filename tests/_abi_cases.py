@@ -157,6 +157,37 @@ for i in range(4):
     expect(f"cache pointer {i} misaligned", cache(num_tokens=1, ptrs=ptrs), _lib.PA_ERR_ALIGN)
 expect("slot_mapping misaligned", cache(num_tokens=1, ptrs=[P, P, P, P, P + 4]), _lib.PA_ERR_ALIGN)
 
+# ---- shared-prefix decode (valid num_seqs == 0 calls are no-ops)
+def shared(d, hkv=32, ptrs=None, groups=1):
+    p = ptrs or [P] * 8
+    return lib.paged_attention_decode_shared_prefix(*p[:6], hkv, ctypes.c_float(0.088), 16,
+                                                    p[6], p[7], groups, ctypes.byref(d))
+
+
+expect("shared: valid empty batch", shared(dims()), _lib.PA_OK)
+expect("shared: empty batch accepts NULL pointers", shared(dims(), ptrs=[None] * 8), _lib.PA_OK)
+expect("shared: fp32 unsupported", shared(dims(dtype=_lib.PA_DTYPE_F32, **ONE)), _lib.PA_ERR_UNSUPPORTED)
+expect("shared: no groups", shared(dims(**ONE), groups=0), _lib.PA_ERR_SHAPE)
+expect("shared: negative groups", shared(dims(), groups=-1), _lib.PA_ERR_SHAPE)
+for i in range(8):
+    ptrs = [P] * 8
+    ptrs[i] = None
+    expect(f"shared: pointer {i} NULL", shared(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_NULL)
+for i in (6, 7):
+    ptrs = [P] * 8
+    ptrs[i] = P + 2
+    expect(f"shared: pointer {i} misaligned", shared(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_ALIGN)
+expect("shared: workspace missing", shared(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
+sp_need = lib.paged_attention_decode_shared_prefix_workspace_bytes(16, ctypes.byref(dims(num_seqs=4)))
+# P = 2048 tokens / 2048 = 1 partition -> 2 slots per sequence
+expect("shared: workspace bytes formula", sp_need,
+       -(-(4 + 5 * 4 * 2 + 2 * 4) * 4 // 256) * 256 + 4 * 32 * 2 * 130 * 4)
+expect("shared: workspace too small",
+       shared(dims(num_seqs=4, workspace=P, workspace_bytes=sp_need - 4)), _lib.PA_ERR_WORKSPACE)
+expect("shared: workspace query rejects bad dims",
+       lib.paged_attention_decode_shared_prefix_workspace_bytes(16, ctypes.byref(dims(head_dim=80))),
+       _lib.SIZE_MAX)
+
 # ---- copy_blocks (num_pairs == 0: a wrong pass is a no-op)
 def copy(ptrs=None, **kw):
     d = _lib.CopyDims()

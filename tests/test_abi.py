@@ -30,6 +30,8 @@ def built():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("paged_attention_decode", "reshape_and_cache", "copy_blocks",
+                 "paged_attention_decode_shared_prefix",
+                 "paged_attention_decode_shared_prefix_workspace_bytes",
                  "paged_attention_decode_workspace_bytes",
                  "paged_attention_decode_partition_tokens", "pa_status_string"):
         assert want in names

@@ -449,3 +449,104 @@ def test_copy_blocks_refuses_pageable_host_memory():
                                  host.data_ptr(), mapping.data_ptr(), ctypes.byref(d))
     assert rc == _lib.PA_ERR_UNSUPPORTED
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------ shared-prefix decode
+def shared_step(dw, group_starts, prefix_lens, partition_size=0, write=True):
+    """Cache write, then decode through the shared-prefix entry point."""
+    if write:
+        binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
+    binding.paged_attention_decode_shared_prefix(
+        dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables, dw.context_lens,
+        torch.tensor(group_starts, dtype=torch.int32, device="cuda"),
+        torch.tensor(prefix_lens, dtype=torch.int32, device="cuda"),
+        scale=float(dw.w.scale), partition_size=partition_size)
+    torch.cuda.synchronize()
+    return to_host(dw.out, dw.w.dtype)
+
+
+def test_shared_prefix_c5():
+    """The parallel-sampling configuration: 16 prompts x 8 samples sharing a
+    1024-token prefix; same result as plain decode (the oracle)."""
+    w = make_config(5)
+    starts = list(range(0, 129, 8))
+    ref, kp, _ = oracle_step(w)
+    for ps in (0, 512, 256):
+        dw = upload(w)
+        got = shared_step(dw, starts, [1024] * 16, partition_size=ps)
+        assert to_host(dw.k_pool, "bf16").tobytes() == kp.tobytes()
+        err = max_err(got, ref, "bf16")
+        say(f"c5 shared prefix, partition {ps}: max abs err {err:.3e}")
+        assert err <= TOL["bf16"]
+
+
+def _shared_workload(groups, prefix, own, H, Hkv, D, bs, seed, extra=()):
+    """Groups of sequences sharing `prefix` tokens (whole pages) plus
+    own[g][i] tokens each; `extra` sequences outside every group."""
+    ctx, members = [], []
+    for g, sizes in enumerate(groups):
+        members.append(list(range(len(ctx), len(ctx) + sizes)))
+        ctx += [prefix + own[g][i] + 1 for i in range(sizes)]
+    ctx += list(extra)
+    mb = max((c + bs - 1) // bs for c in ctx)
+    return build_workload("sp", ctx, H, Hkv, D, bs, "bf16", seed=seed, max_blocks_per_seq=mb,
+                          shared_prefix=members, shared_prefix_len=prefix)
+
+
+SHARED_VARIANTS = [(D, bs, G) for D in (64, 128) for bs in (16, 32) for G in (1, 2, 4, 8)]
+
+
+@pytest.mark.parametrize("D,bs,G", SHARED_VARIANTS,
+                         ids=[f"D{a}-bs{b}-G{c}" for a, b, c in SHARED_VARIANTS])
+def test_shared_prefix_variants(D, bs, G):
+    """Groups of 1, 3, 8 and 17 members (17 * G rows need several prefix
+    units per group), own parts from 0 tokens up, plus ungrouped sequences."""
+    rng = np.random.default_rng(D + bs + G)
+    groups = [1, 3, 8, 17]
+    prefix = 10 * bs
+    own = [rng.integers(0, 3 * bs, size=n) for n in groups]
+    extra = (5, 2 * bs + 3)
+    w = _shared_workload(groups, prefix, own, 2 * G, 2, D, bs, seed=D * bs + G, extra=extra)
+    n_grouped = sum(groups)
+    starts = np.concatenate([[0], np.cumsum(groups)]).tolist()
+    # ungrouped sequences as groups without a prefix
+    starts += [n_grouped + 1, n_grouped + 2]
+    prefixes = [prefix] * len(groups) + [0, 0]
+    ref, _, _ = oracle_step(w)
+    for ps in (0, 4 * bs):
+        got = shared_step(upload(w), starts, prefixes, partition_size=ps)
+        err = max_err(got, ref, "bf16")
+        say(f"D{D} bs{bs} G{G} partition {ps}: max abs err {err:.3e}")
+        assert err <= TOL["bf16"]
+
+
+def test_shared_prefix_short_members_and_partial_pages():
+    """Members whose context ends inside the shared prefix (or is 0), and a
+    prefix length that is not a whole number of pages (its partial page
+    counts as the members' own)."""
+    bs, prefix = 16, 64
+    w = _shared_workload([6], prefix, [[5, 0, 9, 20, 3, 1]], 16, 4, 128, bs, seed=61)
+    ctx = w.context_lens.copy()
+    ctx[1], ctx[3], ctx[5] = 40, 0, 64       # inside the prefix, empty, exactly the prefix
+    w.context_lens = ctx.astype(np.int32)
+    slot = w.slot_mapping.copy()
+    slot[[1, 3, 5]] = -1                      # the cut members append nothing
+    w.slot_mapping = slot
+    ref, _, _ = oracle_step(w)
+    for plen in (prefix, prefix + 7):
+        got = shared_step(upload(w), [0, 6], [plen])
+        err = max_err(got, ref, "bf16")
+        say(f"prefix_len {plen}: max abs err {err:.3e}")
+        assert err <= TOL["bf16"]
+        assert np.all(got[3] == 0)
+
+
+def test_shared_prefix_matches_plain_decode_on_unshared_batch():
+    """Every sequence its own group with no prefix: the own-page units only."""
+    w = make_config(3)
+    ref, _, _ = oracle_step(w)
+    starts = list(range(0, w.num_seqs + 1))
+    got = shared_step(upload(w), starts, [0] * w.num_seqs)
+    err = max_err(got, ref, "bf16")
+    say(f"c3 through the shared-prefix path: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
