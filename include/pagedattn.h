@@ -169,7 +169,8 @@ int32_t paged_attention_decode_partition_tokens(int32_t block_size,
  * head groups of 1, 2, 4 or 8.  The workspace must hold
  * paged_attention_decode_shared_prefix_workspace_bytes(); dims, stream and
  * timing events as for paged_attention_decode (the events bracket the
- * pass over the units).
+ * pass over the units), except that partition_size 0 here means 512 tokens
+ * (or the whole table when it is smaller).
  *
  * Launches: a plan kernel (prefix units per group chunk and partition,
  * own-page units per sequence, largest first), the unit pass (partials for
@@ -185,7 +186,8 @@ int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k
 
 /*
  * Workspace bytes of paged_attention_decode_shared_prefix, with
- * P = ceil(max_blocks_per_seq * block_size / partition_size):
+ * P = ceil(max_blocks_per_seq * block_size / partition_size) (partition
+ * size as that call resolves it):
  *   plan 4 * (4 + 10 * num_seqs * P + 2 * num_seqs) rounded up to 256, plus
  *   partials num_seqs * num_heads * 2P * (head_dim + 2) * 4.
  * 0 when num_seqs is 0; SIZE_MAX for invalid shapes.

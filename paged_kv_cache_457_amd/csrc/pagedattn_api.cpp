@@ -71,10 +71,20 @@ size_t partial_bytes(const pa_decode_dims *d, int parts) {
   return (size_t)d->num_seqs * d->num_heads * parts * (size_t)(d->head_dim + 2) * sizeof(float);
 }
 
-// Shared-prefix decode: slots per sequence are prefix partitions then
-// suffix partitions, each at most ceil(max_blocks / partition pages).
+// Shared-prefix decode: the default partition is kSharedPartitionTokens (a
+// group's prefix unit is one long read, so it is split finer than plain
+// decode splits a sequence).  Slots per sequence are prefix partitions
+// then own-page partitions, each at most ceil(max_blocks / partition pages).
+constexpr int kSharedPartitionTokens = 512;
+
+int shared_partition_tokens(const pa_decode_dims *d, int32_t block_size) {
+  if (d->partition_size != 0) return d->partition_size;
+  const int64_t table_tokens = (int64_t)d->max_blocks_per_seq * block_size;
+  return (int)(table_tokens < kSharedPartitionTokens ? table_tokens : kSharedPartitionTokens);
+}
 int prefix_slots(int32_t block_size, const pa_decode_dims *d) {
-  return 2 * max_partitions(block_size, d);
+  const int pp = shared_partition_tokens(d, block_size) / block_size;
+  return 2 * ((d->max_blocks_per_seq + pp - 1) / pp);
 }
 size_t prefix_plan_ints(int num_seqs, int slots) {
   return (size_t)kPlanHeader + (size_t)pa_internal::kPrefixUnitInts * num_seqs * slots +
@@ -160,7 +170,7 @@ int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k
   a.max_blocks = dims->max_blocks_per_seq;
   a.num_blocks = dims->num_blocks;
   a.dtype = dims->dtype;
-  a.part_pages = partition_tokens(dims, block_size) / block_size;
+  a.part_pages = shared_partition_tokens(dims, block_size) / block_size;
   a.max_parts = ms;
   a.scale = scale;
   a.stream = dims->stream;

@@ -26,8 +26,6 @@
 // sequence's context.  V rows at or past the longest member's context are
 // staged as zeros, so a poisoned slot (NaN) never reaches a multiply; a
 // row's other masked tokens only multiply finite, live values by 0.
-#include <type_traits>
-
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
 
@@ -141,9 +139,12 @@ struct PrefixShape {
   static constexpr int GBYTES = 16 * ROW;      // bytes of one granule of K or V
   static constexpr int NVLD = GBYTES / 1024;   // 1 KiB V loads per granule
   static constexpr int PITCH = ROW + 32;       // LDS row pitch of a staged V granule
-  static constexpr int VBYTES = 16 * PITCH;
-  static constexpr int ACC_BYTES = 16 * D * 4; // one tile's partial O
-  static constexpr int WAVE_LDS = VBYTES > ACC_BYTES ? VBYTES : ACC_BYTES;
+  static constexpr int VBYTES = 16 * PITCH;    // per-wave LDS: staging, then partial O
+  // the merge stores a wave's 16 x D partial O in head_dim slices that fit
+  // its staging area
+  static constexpr int PASSES = (16 * D * 4 + VBYTES - 1) / VBYTES;
+  static constexpr int DH = D / PASSES;        // head_dim columns per merge pass
+  static_assert(DH % 16 == 0 && 16 * DH * 4 <= VBYTES, "merge slice");
 };
 
 template <int D>
@@ -153,6 +154,12 @@ struct PrefixGranule {
   bool ok;
 };
 
+// One unit.  Wave roles: with two row tiles, waves [0, NW/2) carry tile 0
+// and the others tile 1; with one tile all NW waves carry it.  The waves of
+// a tile deal the unit's pages among themselves in turn, so every wave
+// holds the state of one 16-row tile and a granule of K/V is loaded once
+// per tile (the second load of a page by the other tile's waves, at about
+// the same time in the same workgroup, is served by the caches).
 template <int D, int BS, int G, int NW>
 __device__ __forceinline__ void prefix_unit(
     const void *__restrict__ q, const void *__restrict__ k_pool, const void *__restrict__ v_pool,
@@ -162,8 +169,8 @@ __device__ __forceinline__ void prefix_unit(
     int pe, int slot, int g) {
   using S = PrefixShape<D, BS>;
   constexpr int GPP = S::GPP, NC = S::NC, NN = S::NN, ROW = S::ROW, NVLD = S::NVLD;
-  constexpr int PITCH = S::PITCH;
-  __shared__ __attribute__((aligned(16))) char s_wave[NW][S::WAVE_LDS];
+  constexpr int PITCH = S::PITCH, DH = S::DH;
+  __shared__ __attribute__((aligned(16))) char s_wave[NW][S::VBYTES];
   __shared__ float s_ml[NW][16][2];
   // the unit's query rows as MFMA B operands: [tile][slab][lane] 16 bytes
   __shared__ __attribute__((aligned(16))) u32x4 s_q[kTiles][NC][64];
@@ -174,16 +181,13 @@ __device__ __forceinline__ void prefix_unit(
   const int j16 = lane & 15;
   const int rows = nmem * G;                       // query rows of this unit (<= 32)
   const int ntiles = (rows + 15) / 16;             // 1 or 2, same for the whole workgroup
+  const int wpt = ntiles == 2 ? NW / 2 : NW;       // waves per tile
+  const int tile = wave / wpt;                     // this wave's tile
+  const int wslot = wave % wpt;                    // its place among the tile's waves
   const int ctx_cap = max_blocks * BS;
 
-  // this wave's page ids (one per lane), q rows as B operands, each row's
-  // context length
-  const int np = pe - pb;
-  const int col = pb + wave + NW * lane;
-  int my_bid = -1;
-  if (wave + NW * lane < np) my_bid = block_tables[(size_t)seq0 * max_blocks + col];
-  int ctx_row[kTiles];
-  int ctx_max = 0;
+  // q of both tiles to LDS (wave 0), each row's context length, the longest
+  int ctx_max = 0, my_ctx = 0;
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
     const int r = 16 * t + j16;
@@ -199,28 +203,31 @@ __device__ __forceinline__ void prefix_unit(
         s_q[t][c][lane] = w;
       }
     }
-    ctx_row[t] = live ? min(max(context_lens[s], 0), ctx_cap) : 0;
-    ctx_max = max(ctx_max, ctx_row[t]);
+    const int c = live ? min(max(context_lens[s], 0), ctx_cap) : 0;
+    ctx_max = max(ctx_max, c);
+    if (t == tile) my_ctx = c;
   }
-  __syncthreads();  // s_q is written by wave 0 and read by all
 #pragma unroll
   for (int o2 = 32; o2 >= 1; o2 >>= 1) ctx_max = max(ctx_max, __shfl_xor(ctx_max, o2));
-  const int np_w = wave < np ? (np - wave + NW - 1) / NW : 0;
 
-  float m[kTiles], l[kTiles];
-  f32x4 o[kTiles][NN];
+  // this wave's page ids: unit pages wslot, wslot + wpt, ... (one per lane)
+  const int np = pe - pb;
+  int my_bid = -1;
+  if (wslot + wpt * lane < np)
+    my_bid = block_tables[(size_t)seq0 * max_blocks + pb + wslot + wpt * lane];
+  const int np_w = wslot < np ? (np - wslot + wpt - 1) / wpt : 0;
+  __syncthreads();  // s_q is written by wave 0 and read by all
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[NN];
 #pragma unroll
-  for (int t = 0; t < kTiles; ++t) {
-    m[t] = -INFINITY;
-    l[t] = 0.f;
-#pragma unroll
-    for (int n = 0; n < NN; ++n) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int n = 0; n < NN; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const size_t page_stride = (size_t)num_kv_heads * BS * ROW;
   const char *k_b = reinterpret_cast<const char *>(k_pool) + (size_t)g * BS * ROW;
   const char *v_b = reinterpret_cast<const char *>(v_pool) + (size_t)g * BS * ROW;
   char *vs = s_wave[wave];
+  const u32x4 *qt = &s_q[tile][0][lane];
 
   auto fetch = [&](PrefixGranule<D> &gr, int jg) {
     const int bid = __builtin_amdgcn_readlane(my_bid, jg / GPP);
@@ -234,7 +241,7 @@ __device__ __forceinline__ void prefix_unit(
   };
 
   auto process = [&](const PrefixGranule<D> &gr, int jg) {
-    const int tok0 = (pb + wave + NW * (jg / GPP)) * BS + 16 * (jg % GPP);
+    const int tok0 = (pb + wslot + wpt * (jg / GPP)) * BS + 16 * (jg % GPP);
 #pragma unroll
     for (int i = 0; i < NVLD; ++i) {
       const int byte = i * 1024 + 16 * lane;
@@ -243,56 +250,46 @@ __device__ __forceinline__ void prefix_unit(
       if (!gr.ok || tok0 + row >= ctx_max) w = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4 *>(vs + row * PITCH + byte % ROW) = w;
     }
-    i16x4 phi[kTiles], plo[kTiles];
-    // q.K and the softmax update of tile T (query rows 16T .. 16T+15)
-    auto tile_logits = [&](auto tc) {
-      constexpr int T = decltype(tc)::value;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            gr.k[c], __builtin_bit_cast(bf16x8, s_q[T][c][lane]), acc, 0, 0, 0);
-      float sc[4];
+    for (int c = 0; c < NC; ++c)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gr.k[c], __builtin_bit_cast(bf16x8, qt[64 * c]),
+                                                    acc, 0, 0, 0);
+    float sc[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool keep = gr.ok && tok0 + 4 * q4 + r < ctx_row[T];
-        sc[r] = keep ? acc[r] * scale_log2 : -INFINITY;
-      }
-      float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      pm = fmaxf(pm, __shfl_xor(pm, 16));
-      pm = fmaxf(pm, __shfl_xor(pm, 32));
-      // rows differ in context length, so a row may have nothing live yet
-      const float mn = fmaxf(m[T], pm);
-      const bool none = mn == -INFINITY;
-      const float alpha = none ? 1.f : fast_exp2(m[T] - mn);
-      const float base = none ? 0.f : mn;
-      m[T] = mn;
-      l[T] *= alpha;
+    for (int r = 0; r < 4; ++r) {
+      const bool keep = gr.ok && tok0 + 4 * q4 + r < my_ctx;
+      sc[r] = keep ? acc[r] * scale_log2 : -INFINITY;
+    }
+    float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    pm = fmaxf(pm, __shfl_xor(pm, 16));
+    pm = fmaxf(pm, __shfl_xor(pm, 32));
+    // rows differ in context length, so a row may have nothing live yet
+    const float mn = fmaxf(m, pm);
+    const bool none = mn == -INFINITY;
+    const float alpha = none ? 1.f : fast_exp2(m - mn);
+    const float base = none ? 0.f : mn;
+    m = mn;
+    l *= alpha;
 #pragma unroll
-      for (int n = 0; n < NN; ++n) o[T][n] *= alpha;
+    for (int n = 0; n < NN; ++n) o[n] *= alpha;
+    i16x4 phi, plo;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(sc[r] - base);
-        l[T] += p;
-        const __bf16 hi = (__bf16)p;
-        const __bf16 lo = (__bf16)(p - (float)hi);
-        phi[T][r] = __builtin_bit_cast(short, hi);
-        plo[T][r] = __builtin_bit_cast(short, lo);
-      }
-    };
-    tile_logits(std::integral_constant<int, 0>());
-    if (ntiles > 1) tile_logits(std::integral_constant<int, 1>());
+    for (int r = 0; r < 4; ++r) {
+      const float p = fast_exp2(sc[r] - base);
+      l += p;
+      const __bf16 hi = (__bf16)p;
+      const __bf16 lo = (__bf16)(p - (float)hi);
+      phi[r] = __builtin_bit_cast(short, hi);
+      plo[r] = __builtin_bit_cast(short, lo);
+    }
     const int vbase = (4 * q4 + (j16 >> 2)) * PITCH + 8 * (j16 & 3);
 #pragma unroll
     for (int n = 0; n < NN; ++n) {
       const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_i16x4 *)((lds_char *)vs + vbase + 32 * n));
-      o[0][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi[0], o[0][n], 0, 0, 0);
-      o[0][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo[0], o[0][n], 0, 0, 0);
-      if (ntiles > 1) {
-        o[1][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi[1], o[1][n], 0, 0, 0);
-        o[1][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo[1], o[1][n], 0, 0, 0);
-      }
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, o[n], 0, 0, 0);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, o[n], 0, 0, 0);
     }
   };
 
@@ -316,39 +313,41 @@ __device__ __forceinline__ void prefix_unit(
     }
   }
 
-  // merge the NW waves tile by tile through LDS and store the partials
-  auto merge_tile = [&](auto tc) {
-    constexpr int T = decltype(tc)::value;
-    float lt = l[T];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    float *s_acc = reinterpret_cast<float *>(vs);
-    __syncthreads();  // every wave is done with its staging area / the previous tile
+  // Merge: each tile's waves by log-sum-exp, through LDS, in head_dim slices
+  // of DH columns (a wave's slice of its partial O fits its staging area).
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (q4 == 0) {
+    s_ml[wave][j16][0] = m;
+    s_ml[wave][j16][1] = l;
+  }
+  float *s_acc = reinterpret_cast<float *>(vs);
 #pragma unroll
-    for (int n = 0; n < NN; ++n)
-      *reinterpret_cast<float4 *>(&s_acc[j16 * D + 16 * n + 4 * q4]) =
-          make_float4(o[T][n][0], o[T][n][1], o[T][n][2], o[T][n][3]);
-    if (q4 == 0) {
-      s_ml[wave][j16][0] = m[T];
-      s_ml[wave][j16][1] = lt;
+  for (int h = 0; h < S::PASSES; ++h) {
+    __syncthreads();  // staging areas (or the previous slice) no longer in use
+#pragma unroll
+    for (int n = 0; n < DH / 16; ++n) {
+      const int nn = h * (DH / 16) + n;
+      *reinterpret_cast<float4 *>(&s_acc[j16 * DH + 16 * n + 4 * q4]) =
+          make_float4(o[nn][0], o[nn][1], o[nn][2], o[nn][3]);
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * D / 4; idx += 64 * NW) {
-      const int j = idx / (D / 4);
-      const int d = (idx % (D / 4)) * 4;
-      const int r = 16 * T + j;
+    for (int idx = threadIdx.x; idx < ntiles * 16 * (DH / 4); idx += 64 * NW) {
+      const int t = idx / (16 * (DH / 4));
+      const int j = (idx / (DH / 4)) % 16;
+      const int d = (idx % (DH / 4)) * 4;
+      const int r = 16 * t + j;
       if (r >= rows) continue;
+      const int w0 = t * wpt;
       float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][j][0]);
+      for (int w = w0; w < w0 + wpt; ++w) M = fmaxf(M, s_ml[w][j][0]);
       float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
       if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
+        for (int w = w0; w < w0 + wpt; ++w) {
           const float sc = fast_exp2(s_ml[w][j][0] - M);
           L = fmaf(s_ml[w][j][1], sc, L);
           const float4 a = *reinterpret_cast<const float4 *>(
-              reinterpret_cast<const float *>(s_wave[w]) + j * D + d);
+              reinterpret_cast<const float *>(s_wave[w]) + j * DH + d);
           acc[0] = fmaf(a.x, sc, acc[0]);
           acc[1] = fmaf(a.y, sc, acc[1]);
           acc[2] = fmaf(a.z, sc, acc[2]);
@@ -357,16 +356,14 @@ __device__ __forceinline__ void prefix_unit(
       }
       const size_t wrow =
           ((size_t)(seq0 + r / G) * num_heads + g * G + r % G) * max_slots + slot;
-      *reinterpret_cast<float4 *>(ws_acc + wrow * D + d) =
+      *reinterpret_cast<float4 *>(ws_acc + wrow * D + h * DH + d) =
           make_float4(acc[0], acc[1], acc[2], acc[3]);
-      if (d == 0) {
+      if (h == 0 && d == 0) {
         ws_ml[wrow * 2] = M;
         ws_ml[wrow * 2 + 1] = L;
       }
     }
-  };
-  merge_tile(std::integral_constant<int, 0>());
-  if (ntiles > 1) merge_tile(std::integral_constant<int, 1>());
+  }
 }
 
 // Persistent kernel over the plan's units (largest first), item i = (unit

@@ -332,5 +332,8 @@ def make_config(index: int, seed: Optional[int] = None) -> Workload:
                            max_blocks_per_seq=(prefix + 256 + 1 + 15) // 16,
                            shared_prefix=groups, shared_prefix_len=prefix, rng=rng)
         w.extra["divergent"] = div.reshape(-1)
+        # the sharing structure, for the shared-prefix decode entry point
+        w.extra["group_starts"] = np.arange(0, prompts * samples + 1, samples, dtype=np.int32)
+        w.extra["prefix_lens"] = np.full(prompts, prefix, dtype=np.int32)
         return w
     raise ValueError(f"no configuration {index}")

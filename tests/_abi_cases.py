@@ -179,9 +179,9 @@ for i in (6, 7):
     expect(f"shared: pointer {i} misaligned", shared(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_ALIGN)
 expect("shared: workspace missing", shared(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
 sp_need = lib.paged_attention_decode_shared_prefix_workspace_bytes(16, ctypes.byref(dims(num_seqs=4)))
-# P = 2048 tokens / 2048 = 1 partition -> 2 slots per sequence
+# default shared partition 512 tokens: P = 2048 / 512 = 4 -> 8 slots per sequence
 expect("shared: workspace bytes formula", sp_need,
-       -(-(4 + 5 * 4 * 2 + 2 * 4) * 4 // 256) * 256 + 4 * 32 * 2 * 130 * 4)
+       -(-(4 + 5 * 4 * 8 + 2 * 4) * 4 // 256) * 256 + 4 * 32 * 8 * 130 * 4)
 expect("shared: workspace too small",
        shared(dims(num_seqs=4, workspace=P, workspace_bytes=sp_need - 4)), _lib.PA_ERR_WORKSPACE)
 expect("shared: workspace query rejects bad dims",
