@@ -361,6 +361,7 @@ def main():
             "parallelism": "single GPU",
         },
         "kv_bytes_per_step": kv_bytes,
+        "kernel_bytes_per_launch": kernel_bytes,
         "kv_read_gbs_step": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
         "kv_read_frac_of_peak_step": round(kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "partition_kernel_ms": round(k1_avg_ms, 5),

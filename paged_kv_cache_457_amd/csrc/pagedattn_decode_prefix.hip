@@ -142,9 +142,12 @@ struct PrefixShape {
   static constexpr int VBYTES = 16 * PITCH;    // per-wave LDS: staging, then partial O
   // the merge stores a wave's 16 x D partial O in head_dim slices that fit
   // its staging area
-  static constexpr int PASSES = (16 * D * 4 + VBYTES - 1) / VBYTES;
+  static constexpr int PASSES = (16 * (D + 8) * 4 + VBYTES - 1) / VBYTES;
   static constexpr int DH = D / PASSES;        // head_dim columns per merge pass
-  static_assert(DH % 16 == 0 && 16 * DH * 4 <= VBYTES, "merge slice");
+  // row pitch of a stored slice: 8 floats of padding spread the 16 rows a
+  // store instruction writes over all LDS banks
+  static constexpr int DHP = DH + 8;
+  static_assert(DH % 16 == 0 && 16 * DHP * 4 <= VBYTES, "merge slice");
 };
 
 template <int D>
@@ -169,7 +172,7 @@ __device__ __forceinline__ void prefix_unit(
     int pe, int slot, int g) {
   using S = PrefixShape<D, BS>;
   constexpr int GPP = S::GPP, NC = S::NC, NN = S::NN, ROW = S::ROW, NVLD = S::NVLD;
-  constexpr int PITCH = S::PITCH, DH = S::DH;
+  constexpr int PITCH = S::PITCH, DH = S::DH, DHP = S::DHP;
   __shared__ __attribute__((aligned(16))) char s_wave[NW][S::VBYTES];
   __shared__ float s_ml[NW][16][2];
   // the unit's query rows as MFMA B operands: [tile][slab][lane] 16 bytes
@@ -328,7 +331,7 @@ __device__ __forceinline__ void prefix_unit(
 #pragma unroll
     for (int n = 0; n < DH / 16; ++n) {
       const int nn = h * (DH / 16) + n;
-      *reinterpret_cast<float4 *>(&s_acc[j16 * DH + 16 * n + 4 * q4]) =
+      *reinterpret_cast<float4 *>(&s_acc[j16 * DHP + 16 * n + 4 * q4]) =
           make_float4(o[nn][0], o[nn][1], o[nn][2], o[nn][3]);
     }
     __syncthreads();
@@ -347,7 +350,7 @@ __device__ __forceinline__ void prefix_unit(
           const float sc = fast_exp2(s_ml[w][j][0] - M);
           L = fmaf(s_ml[w][j][1], sc, L);
           const float4 a = *reinterpret_cast<const float4 *>(
-              reinterpret_cast<const float *>(s_wave[w]) + j * DH + d);
+              reinterpret_cast<const float *>(s_wave[w]) + j * DHP + d);
           acc[0] = fmaf(a.x, sc, acc[0]);
           acc[1] = fmaf(a.y, sc, acc[1]);
           acc[2] = fmaf(a.z, sc, acc[2]);
