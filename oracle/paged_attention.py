@@ -1,4 +1,5 @@
-"""CPU oracle for paged decode attention and the KV-cache write.
+"""CPU oracle for paged decode and prefill attention, the KV-cache write and
+the page copy.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this module;
 only the tests, the smoke check and the benchmark's CPU-baseline leg call it.
@@ -16,6 +17,10 @@ What it computes (vLLM / PagedAttention pages):
   in logical order; the only paged part is the gather.  ``decode`` walks each
   sequence's logical pages in order, looks each up in the block table, reads
   that page's tokens, and then applies softmax(q . K^T * scale) . V per head.
+* ``prefill`` is the same attention for several new tokens of a sequence at
+  once (a newly admitted request's prompt, or a chunk of it; tutorial page,
+  chapter 4.3, step 2), each token attending causally to the tokens up to
+  its own position.
 * The tutorial page, chapter 4.3 (step 3 of the iteration), says each forward
   step yields the next token together with the updated KV cache.
   ``reshape_and_cache`` is that update: every new token's K and V rows go to
@@ -30,7 +35,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["widen", "gather_pages", "decode", "reshape_and_cache", "copy_blocks"]
+__all__ = ["widen", "gather_pages", "decode", "prefill", "reshape_and_cache", "copy_blocks"]
 
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -123,6 +128,78 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
             lse[s, h] = m + np.log(z)
     if return_lse:
         return out, lse
+    return out
+
+
+def prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+            block_tables: np.ndarray, context_lens: np.ndarray,
+            query_start: np.ndarray, num_kv_heads: int, scale, block_size: int,
+            dtype: str, rows=None) -> np.ndarray:
+    """Multi-token attention over a paged KV cache (prefill and chunked
+    prefill), in float64.
+
+    q            [T, H, D]        the new tokens of all sequences, packed:
+                                  sequence s owns rows query_start[s] ..
+                                  query_start[s + 1] - 1
+    query_start  [S + 1]          int, 0 = query_start[0] <= ... <= query_start[S] = T
+    context_lens [S]              tokens of sequence s in the cache once this
+                                  chunk is written (earlier tokens + chunk)
+    pools, block_tables           as for ``decode``; the chunk's own K/V rows
+                                  are already in the pool (the cache write
+                                  of the same step)
+
+    Where it comes from: continuous batching admits a new request into the
+    running batch at the next iteration, with pages allocated for it
+    (tutorial page, section 4.3, steps 2-3; pinggu thread, continuous
+    batching); its prompt tokens must attend over the paged cache like every
+    later step, and a long prompt may be cut into chunks.  Reading (the pages
+    give no formula): the chunk is the last n = query_start[s+1] -
+    query_start[s] tokens of the sequence, so its i-th row is the token at
+    position ctx - n + i, and, as in any autoregressive decoder, that token
+    attends to the tokens at positions 0 .. ctx - n + i:
+
+        out[query_start[s] + i, h] = softmax(scale * K[:p+1] q) V[:p+1],
+        p = ctx - n + i,  K, V of kv-head h // (H / Hkv).
+
+    With n = 1 this is ``decode``.  n > ctx is rejected.  ``rows``
+    (optional) limits the computation to those row indices of q; the other
+    output rows are left NaN.  Returns out [T, H, D] float64.
+    """
+    T, H, D = q.shape
+    if H % num_kv_heads:
+        raise ValueError("H must be a multiple of num_kv_heads")
+    group = H // num_kv_heads
+    sc = float(np.float32(scale))
+    qs = np.asarray(query_start, dtype=np.int64)
+    S = len(context_lens)
+    if qs.shape != (S + 1,) or qs[0] != 0 or qs[S] != T or np.any(np.diff(qs) < 0):
+        raise ValueError("query_start must rise from 0 to the number of rows")
+    wanted = np.ones(T, dtype=bool) if rows is None else np.zeros(T, dtype=bool)
+    if rows is not None:
+        wanted[np.asarray(rows, dtype=np.int64)] = True
+    out = np.full((T, H, D), np.nan if rows is not None else 0.0, dtype=np.float64)
+    qf = widen(q, dtype)
+    for s in range(S):
+        L = int(context_lens[s])
+        n = int(qs[s + 1] - qs[s])
+        if n == 0 or not wanted[qs[s]:qs[s + 1]].any():
+            continue
+        if n > L:
+            raise ValueError("more new tokens than context")
+        if (L + block_size - 1) // block_size > block_tables.shape[1]:
+            raise ValueError("context longer than the block table")
+        K = widen(gather_pages(k_pool, block_tables[s], L, block_size), dtype)
+        V = widen(gather_pages(v_pool, block_tables[s], L, block_size), dtype)
+        for i in range(n):
+            row = int(qs[s]) + i
+            if not wanted[row]:
+                continue
+            visible = L - n + i + 1          # positions 0 .. L - n + i
+            for h in range(H):
+                kv = h // group
+                x = sc * (K[kv, :visible] @ qf[row, h])
+                w = np.exp(x - x.max())
+                out[row, h] = (w @ V[kv, :visible]) / w.sum()
     return out
 
 

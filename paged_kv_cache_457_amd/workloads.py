@@ -116,6 +116,10 @@ class Workload:
     # split-K partition size the configuration names, in tokens (0: the
     # library's default)
     partition_size: int = 0
+    # multi-token steps (prefill): rows of q / k_new / v_new / slot_mapping
+    # of sequence s are query_start[s] .. query_start[s+1]-1; None for a
+    # decode step (one row per sequence)
+    query_start: Optional[np.ndarray] = None
 
     @property
     def group(self) -> int:
@@ -129,6 +133,21 @@ class Workload:
         """KV bytes one decode call reads: sum ctx * Hkv * D * 2 * sizeof."""
         return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads \
             * self.head_dim * 2 * self.elem_bytes
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    def prefill_flops(self) -> int:
+        """Multiply-add flops of a prefill step: every chunk row at position p
+        costs 2 * D (q . K) + 2 * D (P . V) per visible token (p + 1 of them),
+        for each of the H query heads."""
+        assert self.query_start is not None
+        n = np.diff(self.query_start.astype(np.int64))
+        ctx = self.context_lens.astype(np.int64)
+        # sum over i < n of (ctx - n + i + 1) = n * (ctx - n) + n (n + 1) / 2
+        visible = n * (ctx - n) + n * (n + 1) // 2
+        return int(visible.sum()) * 4 * self.head_dim * self.num_heads
 
     def unique_kv_bytes(self) -> int:
         """KV bytes counting each physical (page, slot) once (shared prefixes)."""
@@ -157,7 +176,8 @@ def build_workload(name: str, ctx: Sequence[int], num_heads: int, num_kv_heads: 
                    shared_prefix: Optional[List[List[int]]] = None,
                    shared_prefix_len: int = 0,
                    poison: bool = True,
-                   rng: Optional[np.random.Generator] = None) -> Workload:
+                   rng: Optional[np.random.Generator] = None,
+                   new_tokens: Optional[Sequence[int]] = None) -> Workload:
     """Allocate pages for ``ctx`` tokens per sequence and fill the pool.
 
     ``shared_prefix`` lists groups of sequence indices whose first
@@ -165,6 +185,13 @@ def build_workload(name: str, ctx: Sequence[int], num_heads: int, num_kv_heads: 
     physical pages, the parallel-sampling sharing of the tutorial page's 4.2;
     those pages carry a reference count equal to the group size.  The token
     appended in this step always lands on a page the sequence owns alone.
+
+    ``new_tokens`` makes it a multi-token step (a prefill chunk): sequence s
+    appends its last ``new_tokens[s]`` tokens in this step, so the pools hold
+    ``ctx - new_tokens`` live tokens, q / k_new / v_new / slot_mapping have
+    one row per appended token, packed by sequence, and ``query_start``
+    gives each sequence's first row.  Without it each sequence appends one
+    token (none when ctx == 0) and has one row.
     """
     ctx = np.asarray(ctx, dtype=np.int64)
     S = len(ctx)
@@ -218,10 +245,18 @@ def build_workload(name: str, ctx: Sequence[int], num_heads: int, num_kv_heads: 
         bt[s, lo:lo + n] = own
         refcount[own] += 1
 
-    # live slots of the pre-append state: positions 0 .. ctx-2
+    # tokens appended in this step, per sequence
+    if new_tokens is None:
+        appended = np.minimum(ctx, 1)
+    else:
+        appended = np.asarray(new_tokens, dtype=np.int64)
+        if appended.shape != (S,) or np.any(appended < 0) or np.any(appended > ctx):
+            raise ValueError("new_tokens must be between 0 and the context length")
+
+    # live slots of the pre-append state: positions 0 .. ctx - appended - 1
     live = np.zeros((num_blocks, bs), dtype=bool)
     for s in range(S):
-        L = int(ctx[s]) - 1
+        L = int(ctx[s] - appended[s])
         if L <= 0:
             continue
         full = L // bs
@@ -231,12 +266,22 @@ def build_workload(name: str, ctx: Sequence[int], num_heads: int, num_kv_heads: 
         if rem:
             live[bt[s, full], :rem] = True
 
-    # new-token slot for position ctx-1 (none when ctx == 0)
-    slot = np.full(S, -1, dtype=np.int64)
-    for s in range(S):
-        if ctx[s] >= 1:
-            pos = int(ctx[s]) - 1
-            slot[s] = int(bt[s, pos // bs]) * bs + pos % bs
+    # slots of the appended positions ctx - appended .. ctx - 1; a decode
+    # step keeps one row per sequence (slot -1 when ctx == 0)
+    if new_tokens is None:
+        query_start = None
+        slot = np.full(S, -1, dtype=np.int64)
+        for s in range(S):
+            if ctx[s] >= 1:
+                pos = int(ctx[s]) - 1
+                slot[s] = int(bt[s, pos // bs]) * bs + pos % bs
+    else:
+        query_start = np.concatenate([[0], np.cumsum(appended)]).astype(np.int32)
+        slot = np.full(int(appended.sum()), -1, dtype=np.int64)
+        for s in range(S):
+            for i in range(int(appended[s])):
+                pos = int(ctx[s] - appended[s]) + i
+                slot[query_start[s] + i] = int(bt[s, pos // bs]) * bs + pos % bs
     if S and len(set(slot[slot >= 0].tolist())) != int((slot >= 0).sum()):
         raise AssertionError("new-token slots collide")
     for s in range(S):
@@ -255,9 +300,10 @@ def build_workload(name: str, ctx: Sequence[int], num_heads: int, num_kv_heads: 
         nanv = nan_value(dtype)
         k_pool[dead_b, :, dead_o, :] = nanv
         v_pool[dead_b, :, dead_o, :] = nanv
-    q = _normal_fill(q_ss, S * H * D, dtype).reshape(S, H, D)
-    k_new = _normal_fill(kn_ss, S * Hkv * D, dtype).reshape(S, Hkv, D)
-    v_new = _normal_fill(vn_ss, S * Hkv * D, dtype).reshape(S, Hkv, D)
+    T = len(slot)
+    q = _normal_fill(q_ss, T * H * D, dtype).reshape(T, H, D)
+    k_new = _normal_fill(kn_ss, T * Hkv * D, dtype).reshape(T, Hkv, D)
+    v_new = _normal_fill(vn_ss, T * Hkv * D, dtype).reshape(T, Hkv, D)
 
     return Workload(
         name=name, dtype=dtype, num_seqs=S, num_heads=H, num_kv_heads=Hkv,
@@ -266,7 +312,7 @@ def build_workload(name: str, ctx: Sequence[int], num_heads: int, num_kv_heads: 
         scale=np.float32(1.0 / math.sqrt(D)), q=q, k_pool=k_pool, v_pool=v_pool,
         block_tables=bt, context_lens=ctx.astype(np.int32), k_new=k_new,
         v_new=v_new, slot_mapping=slot, refcount=refcount, seed=seed,
-        extra={"live": live})
+        extra={"live": live}, query_start=query_start)
 
 
 def free_slots(w: Workload, count: int, rng: np.random.Generator) -> np.ndarray:
@@ -337,3 +383,34 @@ def make_config(index: int, seed: Optional[int] = None) -> Workload:
         w.extra["prefix_lens"] = np.full(prompts, prefix, dtype=np.int32)
         return w
     raise ValueError(f"no configuration {index}")
+
+
+PREFILL_CONFIG_NAMES = {
+    1: "tiny prefill (4 seqs, cached {0,5,16,40} + new {1,12,33,7}, 4/2 heads, D 64, bs 16, bf16)",
+    2: "Llama-2-7B chunked prefill (8 seqs, 1024 new after U[0,3072] cached, 32/32 heads, D 128, bs 16, bf16)",
+    3: "GQA prompt prefill (16 prompts U[256,2048], nothing cached, 32/8 heads, D 128, bs 16, bf16)",
+}
+
+PREFILL_SEED_BASE = 4580
+
+
+def make_prefill_config(index: int, seed: Optional[int] = None) -> Workload:
+    """Multi-token (prefill) steps, by number (1..3): newly admitted requests
+    whose prompt, or a chunk of it, is appended and attended in one step."""
+    if seed is None:
+        seed = PREFILL_SEED_BASE + index
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if index == 1:
+        cached, new = np.array([0, 5, 16, 40]), np.array([1, 12, 33, 7])
+        return build_workload("p1", cached + new, 4, 2, 64, 16, "bf16", seed, rng=rng,
+                              new_tokens=new)
+    if index == 2:
+        cached = rng.integers(0, 3072, size=8, endpoint=True)
+        new = np.full(8, 1024)
+        return build_workload("p2", cached + new, 32, 32, 128, 16, "bf16", seed,
+                              max_blocks_per_seq=(3072 + 1024) // 16, rng=rng, new_tokens=new)
+    if index == 3:
+        new = rng.integers(256, 2048, size=16, endpoint=True)
+        return build_workload("p3", new, 32, 8, 128, 16, "bf16", seed,
+                              max_blocks_per_seq=2048 // 16, rng=rng, new_tokens=new)
+    raise ValueError(f"no prefill configuration {index}")

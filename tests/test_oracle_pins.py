@@ -440,12 +440,120 @@ def pin_copy_on_write_keeps_attention(o):
     assert back_k.tobytes() == kp.tobytes() and back_v.tobytes() == vp.tobytes()
 
 
+def _prefill_case(rng, prior, chunk, H, Hkv, D, bs, nblocks):
+    """Contiguous K/V for prior + chunk tokens per sequence, scattered into
+    shuffled pages by explicit loops; q for the chunk rows."""
+    ctx = [p + c for p, c in zip(prior, chunk)]
+    Kc = [rng.standard_normal((Hkv, L, D)).astype(np.float32) for L in ctx]
+    Vc = [rng.standard_normal((Hkv, L, D)).astype(np.float32) for L in ctx]
+    kp, vp, table = _scatter_contiguous(Kc, Vc, ctx, bs, nblocks, rng, "f32", np.nan)
+    T = sum(chunk)
+    q = rng.standard_normal((T, H, D)).astype(np.float32)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    return Kc, Vc, kp, vp, table, np.array(ctx, np.int32), q, qs
+
+
+def pin_prefill_brute_force(o):
+    # row i of a chunk that follows `prior` cached tokens is the token at
+    # position prior + i and sees exactly tokens 0 .. prior + i
+    rng = np.random.default_rng(31)
+    prior, chunk = [0, 3, 17, 6], [5, 1, 9, 0]
+    H, Hkv, D, bs = 4, 2, 8, 4
+    Kc, Vc, kp, vp, table, ctx, q, qs = _prefill_case(rng, prior, chunk, H, Hkv, D, bs, 24)
+    sc = np.float32(0.3)
+    got = o.prefill(q, kp, vp, table, ctx, qs, Hkv, sc, bs, "f32")
+    row = 0
+    for s in range(len(prior)):
+        for i in range(chunk[s]):
+            seen = prior[s] + i + 1
+            Kv = [[[float(x) for x in Kc[s][g, t]] for t in range(seen)] for g in range(Hkv)]
+            Vv = [[[float(x) for x in Vc[s][g, t]] for t in range(seen)] for g in range(Hkv)]
+            qv = [[float(x) for x in q[row, h]] for h in range(H)]
+            want = np.array(_brute_force(qv, Kv, Vv, float(sc), H // Hkv))
+            np.testing.assert_allclose(got[row], want, rtol=1e-12, atol=1e-12)
+            row += 1
+    assert row == got.shape[0]
+
+
+def pin_prefill_ramp_closed_form(o):
+    # q = 0: equal weights over the visible tokens; V row t = t: the output of
+    # the token at position p is the mean of 0..p = p / 2
+    prior, chunk = [6, 0, 6], [4, 5, 1]
+    H, Hkv, D, bs = 2, 1, 4, 4
+    rng = np.random.default_rng(5)
+    ctx = [p + c for p, c in zip(prior, chunk)]
+    Kc = [rng.standard_normal((Hkv, L, D)).astype(np.float32) for L in ctx]
+    Vc = [np.broadcast_to(np.arange(L, dtype=np.float32)[None, :, None], (Hkv, L, D)).copy()
+          for L in ctx]
+    kp, vp, table = _scatter_contiguous(Kc, Vc, ctx, bs, 16, rng, "f32", np.nan)
+    q = np.zeros((sum(chunk), H, D), np.float32)
+    qs = np.array([0, 4, 9, 10], np.int32)
+    got = o.prefill(q, kp, vp, table, np.array(ctx, np.int32), qs, Hkv, 1.0, bs, "f32")
+    want = [3.0, 3.5, 4.0, 4.5, 0.0, 0.5, 1.0, 1.5, 2.0, 3.0]
+    for r, w in enumerate(want):
+        assert np.all(got[r] == w), (r, got[r, 0, 0], w)
+
+
+def pin_prefill_single_row_is_decode(o):
+    # one new token per sequence: the chunk is the decode step
+    rng = np.random.default_rng(8)
+    prior, chunk = [0, 9, 30, 2], [1, 1, 1, 1]
+    H, Hkv, D, bs = 6, 3, 16, 8
+    _, _, kp, vp, table, ctx, q, qs = _prefill_case(rng, prior, chunk, H, Hkv, D, bs, 12)
+    got = o.prefill(q, kp, vp, table, ctx, qs, Hkv, 0.25, bs, "f32")
+    want = o.decode(q, kp, vp, table, ctx, Hkv, 0.25, bs, "f32")
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
+
+
+def pin_prefill_chunking_invariance(o):
+    # a prompt computed in one chunk or in two gives the same rows
+    rng = np.random.default_rng(12)
+    L, a = 23, 9
+    H, Hkv, D, bs = 4, 4, 8, 4
+    _, _, kp, vp, table, ctx, q, _ = _prefill_case(rng, [0], [L], H, Hkv, D, bs, 8)
+    whole = o.prefill(q, kp, vp, table, ctx, np.array([0, L], np.int32), Hkv, 0.5, bs, "f32")
+    head = o.prefill(q[:a], kp, vp, table, np.array([a], np.int32), np.array([0, a], np.int32),
+                     Hkv, 0.5, bs, "f32")
+    tail = o.prefill(q[a:], kp, vp, table, ctx, np.array([0, L - a], np.int32), Hkv, 0.5, bs,
+                     "f32")
+    np.testing.assert_allclose(np.concatenate([head, tail]), whole, rtol=1e-13, atol=1e-13)
+
+
+def pin_prefill_sdpa_causal(o):
+    # a prompt with nothing cached before it, identity page table: torch's
+    # causal scaled_dot_product_attention (float64, CPU)
+    rng = np.random.default_rng(21)
+    L, H, Hkv, D, bs = 19, 4, 2, 16, 4
+    G = H // Hkv
+    K = rng.standard_normal((Hkv, L, D)).astype(np.float32)
+    V = rng.standard_normal((Hkv, L, D)).astype(np.float32)
+    q = rng.standard_normal((L, H, D)).astype(np.float32)
+    nb = (L + bs - 1) // bs
+    kp = np.full((nb, Hkv, bs, D), np.nan, np.float32)
+    vp = np.full((nb, Hkv, bs, D), np.nan, np.float32)
+    for t in range(L):
+        kp[t // bs, :, t % bs] = K[:, t]
+        vp[t // bs, :, t % bs] = V[:, t]
+    table = np.arange(nb, dtype=np.int32)[None, :]
+    sc = np.float32(1.0 / math.sqrt(D))
+    got = o.prefill(q, kp, vp, table, np.array([L], np.int32), np.array([0, L], np.int32),
+                    Hkv, sc, bs, "f32")
+    qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)              # [H, L, D]
+    kt = torch.from_numpy(K.astype(np.float64)).repeat_interleave(G, dim=0)   # [H, L, D]
+    vt = torch.from_numpy(V.astype(np.float64)).repeat_interleave(G, dim=0)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, is_causal=True, scale=float(sc)).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
 PINS = [
     pin_widen_bf16_definition, pin_hand_worked_example, pin_page_table_figure,
     pin_brute_force, pin_sdpa_identity_table, pin_ctx1_is_v0, pin_uniform_logits_mean,
     pin_permutation_invariance, pin_gqa_equals_mha, pin_split_combine,
     pin_peaked_softmax, pin_ctx0_and_poison, pin_cache_write, pin_cache_write_then_decode,
     pin_copy_blocks, pin_copy_on_write_keeps_attention,
+    pin_prefill_brute_force, pin_prefill_ramp_closed_form, pin_prefill_single_row_is_decode,
+    pin_prefill_chunking_invariance, pin_prefill_sdpa_causal,
 ]
 
 
@@ -458,6 +566,7 @@ def test_package_exports_pinned_functions():
     assert oracle.decode is oracle_mod.decode
     assert oracle.reshape_and_cache is oracle_mod.reshape_and_cache
     assert oracle.copy_blocks is oracle_mod.copy_blocks
+    assert oracle.prefill is oracle_mod.prefill
 
 
 # ------------------------------------------------------- planted mistakes
@@ -483,6 +592,15 @@ MUTANTS = {
     "page copy direction": ("kd[d_page] = k_src[s_page]", "kd[s_page] = k_src[d_page]"),
     "page copy V from K": ("vd[d_page] = v_src[s_page]", "vd[d_page] = k_src[s_page]"),
     "page copy pair order": ("src, dst = m[:, 0], m[:, 1]", "dst, src = m[:, 0], m[:, 1]"),
+    "prefill diagonal excluded": ("visible = L - n + i + 1", "visible = L - n + i"),
+    "prefill position from chunk start": ("visible = L - n + i + 1", "visible = i + 1"),
+    "prefill sees the whole context": ("visible = L - n + i + 1", "visible = L"),
+    "prefill head map interleaved": ("kv = h // group", "kv = h % num_kv_heads"),
+    "prefill scale dropped": ("x = sc * (K[kv, :visible] @ qf[row, h])",
+                              "x = (K[kv, :visible] @ qf[row, h])"),
+    "prefill V from K": ("out[row, h] = (w @ V[kv, :visible]) / w.sum()",
+                         "out[row, h] = (w @ K[kv, :visible]) / w.sum()"),
+    "prefill rows of sequence 0": ("row = int(qs[s]) + i", "row = i"),
 }
 
 
