@@ -25,6 +25,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
 
 
 def parse():
@@ -45,9 +46,10 @@ def parse():
                     help="HBM bytes per partition-kernel launch measured with rocprofv3 counters "
                          "(default: profiles/traffic_pa_decode_partition_c<config>.json); used "
                          "only while the kernel source still has the hash recorded there")
-    ap.add_argument("--op", choices=["decode-step", "copy", "swap-out", "swap-in"],
+    ap.add_argument("--op", choices=["decode-step", "prefill", "copy", "swap-out", "swap-in"],
                     default="decode-step",
-                    help="decode-step (default): the hot path; copy / swap-out / swap-in: "
+                    help="decode-step (default): the hot path; prefill: a multi-token step "
+                         "(--config picks prefill workload 1..3); copy / swap-out / swap-in: "
                          "copy_blocks within the device pool, to a pinned host pool, back")
     ap.add_argument("--pages", type=int, default=2048,
                     help="pages moved per copy_blocks call (--op copy/swap-*)")
@@ -64,6 +66,7 @@ def parse():
 # valid only while their combined hash is unchanged.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_457_amd", "csrc")
 KERNEL_SOURCES = {
+    "pa_prefill_gqa": ["pagedattn_prefill.hip", "pagedattn_device.h", "pagedattn_internal.h"],
     "pa_decode_prefix_gqa": ["pagedattn_decode_prefix.hip", "pagedattn_device.h",
                              "pagedattn_internal.h"],
     "pa_decode_partition": ["pagedattn_decode.hip", "pagedattn_device.h", "pagedattn_internal.h"],
@@ -88,13 +91,13 @@ def kernel_source_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(args, kernel):
+def measured_traffic(args, kernel, tag=None):
     """HBM bytes per partition-kernel launch from a committed counter run,
     or None when there is none for this workload or the kernel source has
     changed since the counters were taken."""
     path = args.traffic_json or os.path.join(
         os.path.dirname(os.path.abspath(__file__)), "profiles",
-        f"traffic_{kernel}_c{args.config}.json")
+        f"traffic_{kernel}_{tag or 'c%d' % args.config}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -214,6 +217,148 @@ def bench_copy(args):
     print(json.dumps(result), flush=True)
 
 
+def prefill_cpu_baseline(w, budget_s):
+    """The oracle's prefill, as it stands, on this host: eight evenly spaced
+    chunk rows of every sequence (all heads), repeated until the budget is
+    spent (at least once); rows per second."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    qs = w.query_start
+    rows = np.unique(np.concatenate([
+        np.linspace(qs[s], qs[s + 1] - 1, 8).astype(np.int64)
+        for s in range(w.num_seqs) if qs[s + 1] > qs[s]]))
+    kp, vp = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping,
+                                      w.block_size)
+    runs = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            out = oracle.prefill(w.q, kp, vp, w.block_tables, w.context_lens, qs,
+                                 w.num_kv_heads, w.scale, w.block_size, w.dtype, rows=rows)
+            runs += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = (time.perf_counter() - t0) / runs
+    assert np.all(np.isfinite(out[rows]))
+    return {
+        "value": round(len(rows) / dt, 2),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(rows)} chunk rows (8 evenly spaced per sequence, all {w.num_heads} "
+                  f"heads) of the same step, {runs} run(s), {dt:.2f} s per run, fp64 NumPy, "
+                  f"BLAS limited to 1 thread; host has {len(os.sched_getaffinity(0))} usable "
+                  f"cores ({platform.processor() or platform.machine()})",
+    }
+
+
+def bench_prefill(args):
+    """Multi-token step: cache write of every chunk row, then prefill
+    attention.  value = chunk tokens / step time; the roofline prices the
+    attention pass against the dense bf16 matrix-core peak with its
+    algorithmic flops (4 * head_dim per visible (row, key) pair and head)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_457_amd import binding
+    from paged_kv_cache_457_amd.device_inputs import upload
+    from paged_kv_cache_457_amd.workloads import PREFILL_CONFIG_NAMES, make_prefill_config
+
+    w = make_prefill_config(args.config, args.seed)
+    dw = upload(w)
+    stream = torch.cuda.current_stream()
+    ws = torch.empty(max(binding.paged_attention_prefill_workspace_bytes(
+        dw.q, dw.k_pool, dw.block_tables, dw.query_start), 16), dtype=torch.uint8, device="cuda")
+    scale = float(w.scale)
+
+    def step(events=(None, None)):
+        binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
+        binding.paged_attention_prefill(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
+                                        dw.context_lens, dw.query_start, scale=scale,
+                                        workspace=ws, timing_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    flops = w.prefill_flops()
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    kv_bytes = w.kv_bytes()
+    args.effective_partition = 0
+    result = {
+        "metric": "prefill-attn tokens/s + matrix-core TFLOP/s (% of bf16 peak)",
+        "value": round(w.num_tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": PREFILL_CONFIG_NAMES[args.config],
+            "config_index": args.config,
+            "seed": w.seed,
+            "num_seqs": w.num_seqs,
+            "num_tokens": w.num_tokens,
+            "num_heads": w.num_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "sum_context_tokens": int(w.context_lens.sum()),
+            "entry": "paged_attention_prefill",
+            "parallelism": "single GPU",
+        },
+        "flops_per_step": flops,
+        "kv_bytes_per_step": kv_bytes,
+        "prefill_kernel_ms": round(k_ms, 5),
+        "kv_read_gbs_kernel": round(kv_bytes / (k_ms * 1e-3) / 1e9, 1),
+        "wall_s_timed_region": round(t_wall, 4),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "pa_prefill_gqa",
+            "achieved": round(tflops, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(args, "pa_prefill_gqa", f"p{args.config}"),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -231,6 +376,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.op == "prefill":
+        bench_prefill(args)
+        return
     if args.op != "decode-step":
         bench_copy(args)
         return

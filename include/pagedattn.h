@@ -1,6 +1,6 @@
 /*
- * libpagedattn -- paged decode attention and the KV-cache write for AMD
- * Instinct MI355X (gfx950).
+ * libpagedattn -- paged decode and prefill attention, the KV-cache write and
+ * the page copy for AMD Instinct MI355X (gfx950).
  *
  * What is computed (vLLM / PagedAttention pages):
  *   - The KV cache is cut into fixed-size pages of 16 or 32 tokens that sit
@@ -194,6 +194,77 @@ int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k
  */
 size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t block_size,
                                                             const pa_decode_dims *dims);
+
+/* Shapes and launch context of paged_attention_prefill. */
+typedef struct pa_prefill_dims {
+  int32_t num_seqs;            /* >= 0 */
+  int32_t num_tokens;          /* rows of q and out (query_start[num_seqs]), >= 0;
+                                  0 is a no-op */
+  int32_t num_heads;           /* query heads; num_heads / num_kv_heads in {1, 2, 4, 8} */
+  int32_t head_dim;            /* 64 or 128 */
+  int32_t max_blocks_per_seq;  /* columns of block_tables, >= 1 */
+  int32_t num_blocks;          /* pages in each pool, >= 1 */
+  int32_t dtype;               /* PA_DTYPE_BF16 (the only type built) */
+  int32_t reserved;            /* must be 0 */
+  void *workspace;             /* device scratch, caller-owned, 16-byte aligned, at
+                                  least paged_attention_prefill_workspace_bytes();
+                                  required whenever num_tokens > 0 (work plan) */
+  size_t workspace_bytes;
+  void *stream;                /* hipStream_t */
+  void *timing_events[2];      /* optional hipEvent_t pair around the attention pass */
+} pa_prefill_dims;
+
+/*
+ * Multi-token attention over a paged KV cache: the prompt of a newly
+ * admitted request, or a chunk of it, attended in one step (continuous
+ * batching admits new requests into the running batch with pages allocated
+ * for them: tutorial page, section 4.3, step 2; pinggu.org thread,
+ * continuous batching).
+ *
+ * Rows query_start[s] .. query_start[s+1]-1 of q and out belong to sequence
+ * s; with n = their count and L = context_lens[s] (clamped to
+ * [0, max_blocks_per_seq * block_size]), the chunk is the sequence's last n
+ * tokens, and its row i, at position p = L - n + i, attends to the tokens at
+ * positions 0 .. p:
+ *   out[query_start[s] + i, h, :] = sum_{t <= p} w_t V_t,
+ *   w = softmax_{t <= p}(scale * q[query_start[s] + i, h, :] . K_t),
+ * K, V of kv-head h / (num_heads / num_kv_heads), read through
+ * block_tables[s, t / block_size].  The chunk's own K/V rows must already be
+ * in the pools (reshape_and_cache of the same rows, earlier on the stream).
+ * A single row per sequence is the decode step.  A row that sees no token
+ * (p < 0, i.e. more rows than context) is written as zeros; tokens on pages
+ * whose id is outside [0, num_blocks) are skipped.  Slots past L in the last
+ * page are never used in arithmetic.
+ *
+ * Layouts: q, out [num_tokens, num_heads, head_dim] bf16; query_start int32
+ * [num_seqs + 1], non-decreasing from 0 to num_tokens (values are clamped to
+ * [0, num_tokens] on the device); pools, block_tables and context_lens as
+ * for paged_attention_decode.  Rows of out outside every sequence's range are
+ * not written.
+ *
+ * Arithmetic: q.K and P.V on the matrix cores in bf16 with fp32
+ * accumulation; the softmax weights enter P.V rounded to bf16 (8
+ * significant bits), their sum is kept in fp32.  Results are rounded to
+ * nearest even.
+ *
+ * Launches, all on dims->stream: a one-workgroup plan kernel (splits every
+ * chunk into blocks of 128 / group consecutive tokens and orders them by the
+ * keys they read, most first, into the workspace) and the attention pass
+ * (timing_events bracket this one).  The result does not depend on the
+ * order work items run in.
+ */
+int paged_attention_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            const int32_t *query_start, int32_t num_kv_heads, float scale,
+                            int32_t block_size, const pa_prefill_dims *dims);
+
+/*
+ * Workspace bytes of paged_attention_prefill: the work plan,
+ *   4 * (4 + 2 * num_tokens) rounded up to 256.
+ * 0 when num_tokens is 0; SIZE_MAX for invalid shapes.
+ */
+size_t paged_attention_prefill_workspace_bytes(int32_t num_kv_heads, int32_t block_size,
+                                               const pa_prefill_dims *dims);
 
 /* Shapes and launch context of reshape_and_cache. */
 typedef struct pa_cache_dims {

@@ -41,6 +41,23 @@ class DecodeDims(ctypes.Structure):
     ]
 
 
+class PrefillDims(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+        ("timing_events", ctypes.c_void_p * 2),
+    ]
+
+
 class CacheDims(ctypes.Structure):
     _fields_ = [
         ("num_tokens", ctypes.c_int32),
@@ -84,6 +101,12 @@ SIGNATURES = {
         ctypes.POINTER(DecodeDims)]),
     "paged_attention_decode_shared_prefix_workspace_bytes": (ctypes.c_size_t, [
         ctypes.c_int32, ctypes.POINTER(DecodeDims)]),
+    "paged_attention_prefill": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+        ctypes.c_int32, ctypes.POINTER(PrefillDims)]),
+    "paged_attention_prefill_workspace_bytes": (ctypes.c_size_t, [
+        ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(PrefillDims)]),
     "reshape_and_cache": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.POINTER(CacheDims)]),

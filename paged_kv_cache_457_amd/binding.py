@@ -195,6 +195,81 @@ def paged_attention_decode_shared_prefix_workspace_bytes(q, k_pool, block_tables
     return n
 
 
+def prefill_dims(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tensor,
+                 query_start: torch.Tensor) -> _lib.PrefillDims:
+    T, H, D = q.shape
+    d = _lib.PrefillDims()
+    d.num_seqs = query_start.shape[0] - 1
+    d.num_tokens, d.num_heads, d.head_dim = T, H, D
+    d.max_blocks_per_seq = block_tables.shape[1]
+    d.num_blocks = k_pool.shape[0]
+    d.dtype = _DTYPES[q.dtype]
+    return d
+
+
+def paged_attention_prefill_workspace_bytes(q: torch.Tensor, k_pool: torch.Tensor,
+                                            block_tables: torch.Tensor,
+                                            query_start: torch.Tensor) -> int:
+    d = prefill_dims(q, k_pool, block_tables, query_start)
+    n = _lib.load().paged_attention_prefill_workspace_bytes(k_pool.shape[1], k_pool.shape[2],
+                                                            ctypes.byref(d))
+    if n == _lib.SIZE_MAX:
+        raise ValueError("invalid shapes for paged_attention_prefill")
+    return n
+
+
+def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                            v_pool: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, query_start: torch.Tensor,
+                            scale: Optional[float] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None,
+                            timing_events: Sequence = (None, None)) -> torch.Tensor:
+    """out[T,H,D] <- multi-token (prefill / chunked prefill) attention over
+    the paged cache (see paged_attention_prefill in include/pagedattn.h);
+    query_start int32 [S + 1] gives each sequence's first row of q.  A
+    workspace (work plan) is allocated here when none is given."""
+    if q.dtype != torch.bfloat16:
+        raise ValueError("prefill attention is built for bf16")
+    for name, t in (("out", out), ("k_pool", k_pool), ("v_pool", v_pool)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    for name, t in (("block_tables", block_tables), ("context_lens", context_lens),
+                    ("query_start", query_start)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    T, H, D = q.shape
+    S = query_start.shape[0] - 1
+    if query_start.dim() != 1 or S < 0:
+        raise ValueError("query_start must be [S + 1]")
+    if out.shape != q.shape or k_pool.shape != v_pool.shape or k_pool.dim() != 4 \
+            or k_pool.shape[3] != D:
+        raise ValueError("out must match q; pools [num_blocks, num_kv_heads, block_size, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    hkv, bs = k_pool.shape[1], k_pool.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    d = prefill_dims(q, k_pool, block_tables, query_start)
+    lib = _lib.load()
+    need = lib.paged_attention_prefill_workspace_bytes(hkv, bs, ctypes.byref(d))
+    if need == _lib.SIZE_MAX:
+        _check(_lib.PA_ERR_SHAPE, "paged_attention_prefill")
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        d.workspace = _dev(workspace, "workspace")
+        d.workspace_bytes = workspace.numel() * workspace.element_size()
+    d.stream = _stream_ptr(stream)
+    d.timing_events[0] = _event_ptr(timing_events[0])
+    d.timing_events[1] = _event_ptr(timing_events[1])
+    rc = lib.paged_attention_prefill(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        _dev(query_start, "query_start"), hkv, ctypes.c_float(scale), bs, ctypes.byref(d))
+    _check(rc, "paged_attention_prefill")
+    return out
+
+
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, k_pool: torch.Tensor,
                       v_pool: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
     """Write k[i], v[i] ([T, num_kv_heads, head_dim]) to pool slot

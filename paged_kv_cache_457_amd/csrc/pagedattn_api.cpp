@@ -96,6 +96,30 @@ size_t prefix_workspace_bytes(int32_t block_size, const pa_decode_dims *d) {
   return plan + (size_t)d->num_seqs * d->num_heads * ms * (size_t)(d->head_dim + 2) * sizeof(float);
 }
 
+// Shape checks shared by the prefill call and its workspace query.
+int check_prefill_dims(int32_t num_kv_heads, int32_t block_size, const pa_prefill_dims *d) {
+  if (!d) return PA_ERR_NULL;
+  if (d->num_seqs < 0 || d->num_tokens < 0 || d->num_heads < 1 || num_kv_heads < 1 ||
+      d->max_blocks_per_seq < 1 || d->num_blocks < 1 || d->reserved != 0)
+    return PA_ERR_SHAPE;
+  if (d->num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (d->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;  // matrix cores: bf16 only
+  if (!supported_dim(d->head_dim) || !supported_bs(block_size) ||
+      !supported_group(d->num_heads / num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  if ((int64_t)d->max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  // work items (item, kv-head) are int32; there are at most num_tokens items
+  if ((int64_t)d->num_tokens * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
+  // rows of a sequence cannot exist without the sequence
+  if (d->num_tokens > 0 && d->num_seqs == 0) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+size_t prefill_plan_bytes(int num_tokens) {
+  const size_t ints = (size_t)kPlanHeader + 2 * (size_t)num_tokens;
+  return (ints * sizeof(int32_t) + 255) / 256 * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -242,6 +266,54 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool, const v
   a.ev_begin = dims->timing_events[0];
   a.ev_end = dims->timing_events[1];
   return pa_internal::launch_decode(a);
+}
+
+size_t paged_attention_prefill_workspace_bytes(int32_t num_kv_heads, int32_t block_size,
+                                               const pa_prefill_dims *dims) {
+  if (check_prefill_dims(num_kv_heads, block_size, dims) != PA_OK) return SIZE_MAX;
+  if (dims->num_tokens == 0) return 0;
+  return prefill_plan_bytes(dims->num_tokens);
+}
+
+int paged_attention_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            const int32_t *query_start, int32_t num_kv_heads, float scale,
+                            int32_t block_size, const pa_prefill_dims *dims) {
+  if (!dims) return PA_ERR_NULL;
+  int rc = check_prefill_dims(num_kv_heads, block_size, dims);
+  if (rc != PA_OK) return rc;
+  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (dims->num_tokens == 0) return PA_OK;  // no rows: nothing is read or written
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+    return PA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+    return PA_ERR_ALIGN;
+  if (!dims->workspace || dims->workspace_bytes < prefill_plan_bytes(dims->num_tokens) ||
+      !aligned(dims->workspace, 16))
+    return PA_ERR_WORKSPACE;
+  pa_internal::PrefillLaunch a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.plan = static_cast<int32_t *>(dims->workspace);
+  a.num_seqs = dims->num_seqs;
+  a.num_tokens = dims->num_tokens;
+  a.num_heads = dims->num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.block_size = block_size;
+  a.max_blocks = dims->max_blocks_per_seq;
+  a.num_blocks = dims->num_blocks;
+  a.scale = scale;
+  a.stream = dims->stream;
+  a.ev_begin = dims->timing_events[0];
+  a.ev_end = dims->timing_events[1];
+  return pa_internal::launch_prefill(a);
 }
 
 int reshape_and_cache(const void *k, const void *v, void *k_pool, void *v_pool,

@@ -49,6 +49,23 @@ struct PrefixLaunch {
   long long max_units;          // bound on the plan's units
 };
 
+struct PrefillLaunch {
+  void *out;
+  const void *q;
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  const int32_t *query_start;  // [num_seqs + 1]
+  int32_t *plan;               // item list written by the plan kernel
+  int num_seqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size;
+  int max_blocks, num_blocks;
+  float scale;
+  void *stream;
+  void *ev_begin;
+  void *ev_end;
+};
+
 struct CacheLaunch {
   const void *k;
   const void *v;
@@ -86,6 +103,8 @@ unsigned persistent_grid_items(long long items, int per_cu);
 int launch_decode_shared_prefix(const PrefixLaunch &p);
 int launch_prefix_plan(const PrefixLaunch &p);
 int launch_prefix_units(const PrefixLaunch &p, float scale_log2);
+// multi-token attention: plan kernel, then the persistent item pass
+int launch_prefill(const PrefillLaunch &a);
 int launch_reshape_and_cache(const CacheLaunch &a);
 // Also PA_ERR_UNSUPPORTED (3) when a pointer is not device-accessible.
 int launch_copy_pages(const CopyLaunch &a);

@@ -7,6 +7,7 @@ bits.
 from __future__ import annotations
 
 from dataclasses import dataclass
+from typing import Optional
 
 import numpy as np
 import torch
@@ -45,6 +46,7 @@ class DeviceWorkload:
     v_new: torch.Tensor
     slot_mapping: torch.Tensor
     out: torch.Tensor
+    query_start: Optional[torch.Tensor] = None
 
 
 def upload(w: Workload, device="cuda") -> DeviceWorkload:
@@ -59,6 +61,7 @@ def upload(w: Workload, device="cuda") -> DeviceWorkload:
         k_new=to_device(w.k_new, dt, device),
         v_new=to_device(w.v_new, dt, device),
         slot_mapping=torch.from_numpy(np.ascontiguousarray(w.slot_mapping)).to(device),
-        out=torch.empty((w.num_seqs, w.num_heads, w.head_dim), dtype=torch_dtype(dt),
-                        device=device),
+        out=torch.empty(tuple(w.q.shape), dtype=torch_dtype(dt), device=device),
+        query_start=(None if w.query_start is None else
+                     torch.from_numpy(np.ascontiguousarray(w.query_start)).to(device)),
     )

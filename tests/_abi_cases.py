@@ -219,6 +219,61 @@ expect("copy head_dim 96", copy(head_dim=96), _lib.PA_ERR_UNSUPPORTED)
 expect("copy block_size 8", copy(block_size=8), _lib.PA_ERR_UNSUPPORTED)
 expect("copy dtype 3", copy(dtype=3), _lib.PA_ERR_UNSUPPORTED)
 
+# ---- prefill (num_tokens == 0 calls are no-ops)
+def pdims(**kw):
+    d = _lib.PrefillDims()
+    d.num_seqs, d.num_tokens, d.num_heads, d.head_dim = 0, 0, 32, 128
+    d.max_blocks_per_seq, d.num_blocks, d.dtype = 128, 1000, _lib.PA_DTYPE_BF16
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def prefill(d, hkv=8, bs=16, scale=0.088, ptrs=None):
+    p = ptrs or [P] * 7
+    return lib.paged_attention_prefill(*p, hkv, ctypes.c_float(scale), bs, ctypes.byref(d))
+
+
+ROWS = dict(num_seqs=2, num_tokens=100)
+expect("prefill dims NULL",
+       lib.paged_attention_prefill(P, P, P, P, P, P, P, 8, ctypes.c_float(1), 16, None),
+       _lib.PA_ERR_NULL)
+expect("prefill: valid empty step", prefill(pdims()), _lib.PA_OK)
+expect("prefill: empty step accepts NULL pointers", prefill(pdims(), ptrs=[None] * 7), _lib.PA_OK)
+expect("prefill: fp32 unsupported", prefill(pdims(dtype=_lib.PA_DTYPE_F32)), _lib.PA_ERR_UNSUPPORTED)
+expect("prefill: head_dim 96", prefill(pdims(head_dim=96)), _lib.PA_ERR_UNSUPPORTED)
+expect("prefill: block_size 8", prefill(pdims(), bs=8), _lib.PA_ERR_UNSUPPORTED)
+expect("prefill: group 3", prefill(pdims(num_heads=6), hkv=2), _lib.PA_ERR_UNSUPPORTED)
+expect("prefill: heads not a multiple", prefill(pdims(num_heads=30)), _lib.PA_ERR_SHAPE)
+expect("prefill: negative rows", prefill(pdims(num_tokens=-1)), _lib.PA_ERR_SHAPE)
+expect("prefill: negative sequences", prefill(pdims(num_seqs=-1)), _lib.PA_ERR_SHAPE)
+expect("prefill: rows without sequences", prefill(pdims(num_tokens=5)), _lib.PA_ERR_SHAPE)
+expect("prefill: reserved nonzero", prefill(pdims(reserved=1)), _lib.PA_ERR_SHAPE)
+expect("prefill: zero blocks", prefill(pdims(num_blocks=0)), _lib.PA_ERR_SHAPE)
+expect("prefill: zero table columns", prefill(pdims(max_blocks_per_seq=0)), _lib.PA_ERR_SHAPE)
+expect("prefill: zero kv heads", prefill(pdims(), hkv=0), _lib.PA_ERR_SHAPE)
+expect("prefill: NaN scale", prefill(pdims(**ROWS), scale=float("nan")), _lib.PA_ERR_SHAPE)
+for i in range(7):
+    ptrs = [P] * 7
+    ptrs[i] = None
+    expect(f"prefill: pointer {i} NULL", prefill(pdims(**ROWS), ptrs=ptrs), _lib.PA_ERR_NULL)
+for i in range(7):
+    ptrs = [P] * 7
+    ptrs[i] = MIS + 2 if i >= 4 else MIS
+    expect(f"prefill: pointer {i} misaligned", prefill(pdims(**ROWS), ptrs=ptrs), _lib.PA_ERR_ALIGN)
+expect("prefill: workspace missing", prefill(pdims(**ROWS)), _lib.PA_ERR_WORKSPACE)
+pf_need = lib.paged_attention_prefill_workspace_bytes(8, 16, ctypes.byref(pdims(**ROWS)))
+expect("prefill: workspace bytes formula", pf_need, -(-(4 + 2 * 100) * 4 // 256) * 256)
+expect("prefill: workspace too small",
+       prefill(pdims(workspace=P, workspace_bytes=pf_need - 4, **ROWS)), _lib.PA_ERR_WORKSPACE)
+expect("prefill: workspace misaligned",
+       prefill(pdims(workspace=MIS, workspace_bytes=pf_need, **ROWS)), _lib.PA_ERR_WORKSPACE)
+expect("prefill: workspace query, empty step",
+       lib.paged_attention_prefill_workspace_bytes(8, 16, ctypes.byref(pdims())), 0)
+expect("prefill: workspace query rejects bad dims",
+       lib.paged_attention_prefill_workspace_bytes(8, 16, ctypes.byref(pdims(head_dim=80))),
+       _lib.SIZE_MAX)
+
 # ---- probe
 expect("probe NULL buffer", lib.pa_hbm_read_probe(None, 1024, P, None), _lib.PA_ERR_NULL)
 expect("probe size not a multiple of 16", lib.pa_hbm_read_probe(P, 1000, P, None), _lib.PA_ERR_SHAPE)

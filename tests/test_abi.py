@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
                  "paged_attention_decode_shared_prefix",
                  "paged_attention_decode_shared_prefix_workspace_bytes",
                  "paged_attention_decode_workspace_bytes",
-                 "paged_attention_decode_partition_tokens", "pa_status_string"):
+                 "paged_attention_decode_partition_tokens", "paged_attention_prefill",
+                 "paged_attention_prefill_workspace_bytes", "pa_status_string"):
         assert want in names
 
 
@@ -62,16 +63,20 @@ def test_struct_layouts_match_the_header(built):
     os.makedirs(os.path.dirname(src), exist_ok=True)
     with open(src, "w") as f:
         f.write('#include <stdio.h>\n#include <stddef.h>\n#include "pagedattn.h"\n'
-                'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(pa_decode_dims),'
-                ' offsetof(pa_decode_dims, timing_events), sizeof(pa_cache_dims),'
-                ' offsetof(pa_cache_dims, stream), sizeof(pa_copy_dims),'
-                ' offsetof(pa_copy_dims, stream)); return 0;}\n')
+                'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n",'
+                ' sizeof(pa_decode_dims), offsetof(pa_decode_dims, timing_events),'
+                ' sizeof(pa_cache_dims), offsetof(pa_cache_dims, stream),'
+                ' sizeof(pa_copy_dims), offsetof(pa_copy_dims, stream),'
+                ' sizeof(pa_prefill_dims), offsetof(pa_prefill_dims, workspace),'
+                ' offsetof(pa_prefill_dims, timing_events)); return 0;}\n')
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
     vals = list(map(int, subprocess.run([exe], capture_output=True, text=True,
                                         check=True).stdout.split()))
     assert vals == [ctypes.sizeof(_lib.DecodeDims), _lib.DecodeDims.timing_events.offset,
                     ctypes.sizeof(_lib.CacheDims), _lib.CacheDims.stream.offset,
-                    ctypes.sizeof(_lib.CopyDims), _lib.CopyDims.stream.offset]
+                    ctypes.sizeof(_lib.CopyDims), _lib.CopyDims.stream.offset,
+                    ctypes.sizeof(_lib.PrefillDims), _lib.PrefillDims.workspace.offset,
+                    _lib.PrefillDims.timing_events.offset]
 
 
 def test_host_validation_rejects_bad_arguments(built):
