@@ -34,6 +34,12 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpagedattn)")
 
 
+# Per-source extra flags.  The prefill kernel's scores are finite or -inf
+# (masked keys are staged as zeros and masked by selection), never NaN, so
+# its max operations need no NaN quieting.
+EXTRA_FLAGS = {"pagedattn_prefill.hip": ["-fno-honor-nans"]}
+
+
 def compile_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -47,7 +53,8 @@ def build(verbose: bool = False) -> str:
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc, *compile_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *compile_flags(), *EXTRA_FLAGS.get(src, []), *lang, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)

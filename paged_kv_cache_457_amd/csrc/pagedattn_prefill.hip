@@ -48,10 +48,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;           // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // query rows of a work item
 constexpr int kKeys = 64;           // keys per LDS tile
+constexpr float kRescaleLog2 = 8.f; // lazy rescale threshold of the running max
 constexpr int kBuckets = 1024;      // plan size classes (key tiles); the last is open-ended
 constexpr int kPlanThreads = 1024;
 
@@ -131,6 +132,24 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
 }
 
 // ------------------------------------------------------------- work item
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D, int BS, int G>
 __device__ __forceinline__ void prefill_item(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
@@ -167,6 +186,13 @@ __device__ __forceinline__ void prefill_item(
   const int wmin = p0 + t0 + first;  // position of the wave's first token
   const int wmax = p0 + t0 + last;   // and of its last
 
+  // The exponent argument is fma(s, c, -m) with the row max m taken over
+  // raw scores, which needs c > 0: a negative scale negates q instead (exact
+  // in bf16), and c is kept at least FLT_MIN so that masked -inf scores stay
+  // -inf (a zero scale then gives equal weights, as it should).
+  const bool negate = scale_log2 < 0.f;
+  const float c = fmaxf(fabsf(scale_log2), 1.17549435e-38f);
+
   // query rows as MFMA B operands, and each row's position (-1: not a row)
   bf16x8 qf[2][NC];
   int pos[2];
@@ -179,50 +205,61 @@ __device__ __forceinline__ void prefill_item(
     const char *qrow = reinterpret_cast<const char *>(q) +
                        ((size_t)(qa + t0 + (live ? tk : 0)) * num_heads + g * G + row % G) * ROW;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int cc = 0; cc < NC; ++cc) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (live) w = load16(qrow + 64 * c + 16 * q4);
-      qf[t][c] = __builtin_bit_cast(bf16x8, w);
+      if (live) w = load16(qrow + 64 * cc + 16 * q4);
+      if (negate) w ^= 0x80008000u;
+      qf[t][cc] = __builtin_bit_cast(bf16x8, w);
     }
   }
+
+  // LDS offsets of this lane's operand reads; the 16-key sub-tile and the
+  // key pair add whole-row multiples that leave the swizzle unchanged
+  int koff[NC], voff[NN];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) koff[cc] = j16 * ROW + swz<D>(j16, 4 * cc + q4) * 16;
+  const int vr = 4 * q4 + (j16 >> 2);
+#pragma unroll
+  for (int nb = 0; nb < NN; ++nb)
+    voff[nb] = vr * ROW + swz<D>(vr, 2 * nb + ((j16 >> 1) & 1)) * 16 + (j16 & 1) * 8;
 
   // global -> registers -> LDS staging of key tiles
   const size_t page_stride = (size_t)num_kv_heads * BS * ROW;
   const char *kb = reinterpret_cast<const char *>(k_pool) + (size_t)g * BS * ROW;
   const char *vb = reinterpret_cast<const char *>(v_pool) + (size_t)g * BS * ROW;
+  // Load l of a thread takes chunk l * kThreads + tid of the tile, whose
+  // page within the tile is the same for the whole wave (a wave's 64 chunks
+  // lie in one page): the table entry and page base are scalar, the lane
+  // adds its offset inside the page.
+  static_assert(CPR * BS >= 64, "a wave's chunks lie in one page");
+  const int wtid = __builtin_amdgcn_readfirstlane(tid & ~63);
+  int loff[LOADS], lkey[LOADS];
+#pragma unroll
+  for (int l = 0; l < LOADS; ++l) {
+    const int ci = l * kThreads + tid;
+    lkey[l] = ci / CPR;
+    loff[l] = (lkey[l] % BS) * ROW + (ci % CPR) * 16;
+  }
   u32x4 rk[LOADS], rv[LOADS];
   unsigned okbits = 0;
   auto fetch = [&](int kt) {
     okbits = 0;
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
-      const int ci = l * kThreads + tid;
-      const int key = ci / CPR;
-      const int kk = kt * kKeys + key;
-      const int pj = kk / BS;
+      const int pj = kt * PPT + (l * kThreads + wtid) / CPR / BS;  // uniform
       const int bid = pj < npages ? bt[pj] : -1;
-      const bool ok = kk < kv_end && (unsigned)bid < (unsigned)num_blocks;
-      okbits |= (unsigned)ok << l;
-      const size_t off = (size_t)(ok ? bid : 0) * page_stride + (kk % BS) * ROW + (ci % CPR) * 16;
-      rk[l] = load16(kb + off);
-      rv[l] = load16(vb + off);
+      const bool page_ok = (unsigned)bid < (unsigned)num_blocks;
+      const size_t base = (size_t)(page_ok ? bid : 0) * page_stride;
+      okbits |= (unsigned)(page_ok && kt * kKeys + lkey[l] < kv_end) << l;
+      rk[l] = load16(kb + base + loff[l]);
+      rv[l] = load16(vb + base + loff[l]);
     }
   };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int l = 0; l < LOADS; ++l) {
-      const int ci = l * kThreads + tid;
-      const int key = ci / CPR;
-      const bool ok = (okbits >> l) & 1u;
-      const int at = key * ROW + swz<D>(key, ci % CPR) * 16;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4 *>(&s_kv[buf][0][at]) = ok ? rk[l] : z;
-      *reinterpret_cast<u32x4 *>(&s_kv[buf][1][at]) = ok ? rv[l] : z;
-    }
-  };
-  // pages of tile kt that are valid (uniform)
-  auto tile_pages_ok = [&](int kt) {
-    bool ok = true;
+  const int skey = tid / CPR;  // key row of this thread's first chunk
+  const int soff = skey * ROW + swz<D>(skey, tid % CPR) * 16;
+  // tiles that hold a key the item does not see, or a page outside the pool
+  auto tile_clean = [&](int kt) {
+    bool ok = (kt + 1) * kKeys <= kv_end;
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int pj = kt * PPT + j;
@@ -230,7 +267,22 @@ __device__ __forceinline__ void prefill_item(
     }
     return ok;
   };
+  auto stage = [&](int buf, bool clean) {
+    char *kd = s_kv[buf][0] + soff;
+    char *vd = s_kv[buf][1] + soff;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int l = 0; l < LOADS; ++l) {
+      // chunk l * kThreads + tid sits kThreads / CPR rows further per l
+      constexpr int kStep = kThreads / CPR * ROW;
+      const bool ok = clean || ((okbits >> l) & 1u);
+      *reinterpret_cast<u32x4 *>(kd + l * kStep) = ok ? rk[l] : z;
+      *reinterpret_cast<u32x4 *>(vd + l * kStep) = ok ? rv[l] : z;
+    }
+  };
 
+  // softmax state per row tile: running max m (scaled, log2 units), the
+  // lane's partial sum, O^T columns
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
   f32x4 o[2][NN];
 #pragma unroll
@@ -238,110 +290,112 @@ __device__ __forceinline__ void prefill_item(
 #pragma unroll
     for (int nb = 0; nb < NN; ++nb) o[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](auto masked_c, int buf, int kt) {
+  // one 32-key half of a tile: S^T for its two 16-key sub-tiles and both
+  // row tiles, the online softmax over them, then O^T += V^T P^T with the 32
+  // keys as the reduction dimension of one instruction
+  auto half = [&](auto masked_c, const lds_char *ks, const lds_char *vs, int kt, int h) {
     constexpr bool kMasked = decltype(masked_c)::value;
-    const lds_char *ks = (const lds_char *)s_kv[buf][0];
-    const lds_char *vs = (const lds_char *)s_kv[buf][1];
-    // S^T for the tile's four 16-key sub-tiles and both row tiles
-    f32x4 sacc[4][2];
+    f32x4 sacc[2][2];  // [sub-tile][row tile]
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < 2; ++st) {
       sacc[st][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       sacc[st][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int r = 16 * st + j16;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+      for (int cc = 0; cc < NC; ++cc) {
         const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8 *)(
-            ks + r * ROW + swz<D>(r, 4 * c + q4) * 16);
-        sacc[st][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][c], sacc[st][0], 0, 0, 0);
-        sacc[st][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][c], sacc[st][1], 0, 0, 0);
+            ks + (32 * h + 16 * st) * ROW + koff[cc]);
+        sacc[st][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][cc], sacc[st][0], 0, 0, 0);
+        sacc[st][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][cc], sacc[st][1], 0, 0, 0);
       }
     }
-    // page validity of each sub-tile's keys (a sub-tile lies in one page)
-    bool sub_ok[4] = {true, true, true, true};
     if constexpr (kMasked) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int pj = kt * PPT + (16 * st) / BS;
-        sub_ok[st] = pj < npages && (unsigned)bt[pj] < (unsigned)num_blocks;
+      for (int st = 0; st < 2; ++st) {
+        const int k16 = 32 * h + 16 * st;           // first key of the sub-tile in the tile
+        const int pj = kt * PPT + k16 / BS;         // a sub-tile lies in one page
+        const bool page_ok = pj < npages && (unsigned)bt[pj] < (unsigned)num_blocks;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kk = kt * kKeys + k16 + 4 * q4 + r;
+            if (!(page_ok && kk <= pos[t])) sacc[st][t][r] = -INFINITY;
+          }
       }
     }
-    // online softmax, then P as bf16 B operands
-    i16x4 pb[2][4];
+    // the running max moves only when some row's grows by more than
+    // 2^kRescaleLog2 (weights stay below that bound, and the base cancels
+    // between the weighted sum and the sum of weights)
+    float mt[2];
+    bool grow = false;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      float sv[4][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = sacc[st][t][r] * scale_log2;
-          if constexpr (kMasked) {
-            const int kk = kt * kKeys + 16 * st + 4 * q4 + r;
-            if (!(sub_ok[st] && kk <= pos[t])) x = -INFINITY;
-          }
-          sv[st][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[t], mx);
-      const bool none = mn == -INFINITY;  // the row has seen no key yet
-      const float alpha = none ? 1.f : fast_exp2(m[t] - mn);
-      const float base = none ? 0.f : mn;
-      m[t] = mn;
-      lsum[t] *= alpha;
-#pragma unroll
-      for (int nb = 0; nb < NN; ++nb) o[t][nb] *= alpha;
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(sv[st][r] - base);
-          lsum[t] += p;
-          pb[t][st][r] = __builtin_bit_cast(short, (__bf16)p);
-        }
+      const float mx = fmaxf(fmaxf(fmaxf(sacc[0][t][0], sacc[0][t][1]),
+                                   fmaxf(sacc[0][t][2], sacc[0][t][3])),
+                             fmaxf(fmaxf(sacc[1][t][0], sacc[1][t][1]),
+                                   fmaxf(sacc[1][t][2], sacc[1][t][3])));
+      mt[t] = rows_max(mx) * c;
+      grow = grow || mt[t] > m[t] + kRescaleLog2;
     }
-    // O^T += V^T P^T over key pairs of sub-tiles (32 keys per instruction)
-    const int vrow = 4 * q4 + (j16 >> 2);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      const i16x8 b0 = __builtin_shufflevector(pb[0][2 * kp], pb[0][2 * kp + 1], 0, 1, 2, 3, 4,
-                                               5, 6, 7);
-      const i16x8 b1 = __builtin_shufflevector(pb[1][2 * kp], pb[1][2 * kp + 1], 0, 1, 2, 3, 4,
-                                               5, 6, 7);
+      for (int t = 0; t < 2; ++t) {
+        const float mn = fmaxf(m[t], mt[t]);
+        const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[t] - mn);
+        m[t] = mn;
+        lsum[t] *= alpha;
 #pragma unroll
-      for (int nb = 0; nb < NN; ++nb) {
-        const int chunk = 2 * nb + ((j16 >> 1) & 1);
-        const int r0 = 32 * kp + vrow, r1 = r0 + 16;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(vs + r0 * ROW + swz<D>(r0, chunk) * 16 + (j16 & 1) * 8));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(vs + r1 * ROW + swz<D>(r1, chunk) * 16 + (j16 & 1) * 8));
-        const bf16x8 a =
-            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, b0),
-                                                           o[0][nb], 0, 0, 0);
-        o[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, b1),
-                                                           o[1][nb], 0, 0, 0);
+        for (int nb = 0; nb < NN; ++nb) o[t][nb] *= alpha;
       }
     }
+    // weights as bf16 B operands: keys 4*q4 + r of sub-tile 0, then of 1
+    i16x8 pb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float base = m[t] == -INFINITY ? 0.f : m[t];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(fmaf(sacc[st][t][r], c, -base));
+          lsum[t] += p;
+          pb[t][4 * st + r] = __builtin_bit_cast(short, (__bf16)p);
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NN; ++nb) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4 *)(vs + 32 * h * ROW + voff[nb]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4 *)(vs + (32 * h + 16) * ROW + voff[nb]));
+      const bf16x8 a =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pb[0]),
+                                                         o[0][nb], 0, 0, 0);
+      o[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pb[1]),
+                                                         o[1][nb], 0, 0, 0);
+    }
+  };
+  auto compute = [&](auto masked_c, int buf, int kt) {
+    const lds_char *ks = (const lds_char *)s_kv[buf][0];
+    const lds_char *vs = (const lds_char *)s_kv[buf][1];
+    half(masked_c, ks, vs, kt, 0);
+    half(masked_c, ks, vs, kt, 1);
   };
 
   if (ntiles > 0) {
     fetch(0);
-    stage(0);
+    stage(0, tile_clean(0));
     if (ntiles > 1) fetch(1);
     __syncthreads();
     for (int kt = 0; kt < ntiles; ++kt) {
       const int buf = kt & 1;
       if (kt + 1 < ntiles) {
-        stage(buf ^ 1);  // its previous contents were used before the last barrier
+        stage(buf ^ 1, tile_clean(kt + 1));  // its previous contents were used before the last barrier
         if (kt + 2 < ntiles) fetch(kt + 2);
       }
       if (wave_live && kt * kKeys <= wmax) {
-        if (kt * kKeys + kKeys - 1 <= wmin && tile_pages_ok(kt))
+        if (kt * kKeys + kKeys - 1 <= wmin && tile_clean(kt))
           compute(std::integral_constant<bool, false>{}, buf, kt);
         else
           compute(std::integral_constant<bool, true>{}, buf, kt);
@@ -353,12 +407,10 @@ __device__ __forceinline__ void prefill_item(
   // normalise and store: lane (q4, j) writes d = 16n + 4*q4 .. +3 of row j
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
+    const float L = rows_sum(lsum[t]);
     const int row = 32 * wave + 16 * t + j16;
     const int tk = row / G;
     if (tk >= ntok) continue;
-    float L = lsum[t];
-    L += __shfl_xor(L, 16);
-    L += __shfl_xor(L, 32);
     const float inv = L > 0.f ? 1.f / L : 0.f;
     char *orow = reinterpret_cast<char *>(out) +
                  ((size_t)(qa + t0 + tk) * num_heads + g * G + row % G) * ROW;
@@ -373,7 +425,7 @@ __device__ __forceinline__ void prefill_item(
 }
 
 template <int D, int BS, int G>
-__global__ __launch_bounds__(kThreads) void pa_prefill_gqa(
+__global__ __launch_bounds__(kThreads, 2) void pa_prefill_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
