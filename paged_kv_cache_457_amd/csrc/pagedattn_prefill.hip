@@ -53,8 +53,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // query rows of a work item
 constexpr int kKeys = 64;           // keys per LDS tile
 constexpr float kRescaleLog2 = 8.f; // lazy rescale threshold of the running max
-constexpr int kBuckets = 1024;      // plan size classes (key tiles); the last is open-ended
 constexpr int kPlanThreads = 1024;
+constexpr int kBuckets = kPlanThreads - 1;  // plan size classes (key tiles); the last is open-ended
 
 template <int D, int BS, int G>
 struct PrefillShape {
@@ -71,15 +71,19 @@ struct PrefillShape {
 };
 
 // Position of 16-byte chunk c of key row r inside its LDS row.  Rows are
-// unpadded; XOR-ing the chunk index with a function of the row spreads the
-// 16 rows one q.K operand read touches, and the 8 rows each half of a
-// transposing V read touches, over all banks.
+// unpadded; the chunk index is XOR-ed with a function of the row chosen so
+// that, whether the LDS serves 128 or 256 bytes a cycle, the rows a q.K
+// operand read touches (16 rows, one chunk column), the rows a transposing
+// V read touches (8 rows, two chunk columns) and a staging write (whole
+// rows) fall on distinct banks.
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (D == 128)
-    return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
-  else
-    return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+  if constexpr (D == 128) {
+    return c ^ (((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1));
+  } else {
+    const int a = r & 1, b = (r >> 1) & 1, cc = (r >> 2) & 1, d = (r >> 3) & 1;
+    return c ^ (((((b ^ cc) << 1) | (a ^ cc)) << 1) | (cc ^ d));
+  }
 }
 
 // ------------------------------------------------------------------ plan
@@ -111,13 +115,24 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
     for (int t0 = 0; t0 < n; t0 += tok) atomicAdd(&s_count[bucket(n, p0, t0)], 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int at = 0;
-    for (int z = kBuckets; z >= 0; --z) {
-      s_next[z] = at;
-      at += s_count[z];
+  // first slot of each size class, largest class first: an exclusive scan
+  // over thread t <-> class kBuckets - t (lane scan, then one over waves)
+  {
+    __shared__ int s_wave[kPlanThreads / 64];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int v = s_count[kBuckets - t];
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
     }
-    plan[0] = at;
+    if (lane == 63) s_wave[w] = x;
+    __syncthreads();
+    int before = 0;
+    for (int k = 0; k < w; ++k) before += s_wave[k];
+    s_next[kBuckets - t] = before + x - v;
+    if (t == kPlanThreads - 1) plan[0] = before + x;
   }
   __syncthreads();
   for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
@@ -290,12 +305,8 @@ __device__ __forceinline__ void prefill_item(
 #pragma unroll
     for (int nb = 0; nb < NN; ++nb) o[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one 32-key half of a tile: S^T for its two 16-key sub-tiles and both
-  // row tiles, the online softmax over them, then O^T += V^T P^T with the 32
-  // keys as the reduction dimension of one instruction
-  auto half = [&](auto masked_c, const lds_char *ks, const lds_char *vs, int kt, int h) {
-    constexpr bool kMasked = decltype(masked_c)::value;
-    f32x4 sacc[2][2];  // [sub-tile][row tile]
+  // S^T for one 32-key half of a tile (two 16-key sub-tiles, both row tiles)
+  auto scores = [&](const lds_char *ks, int h, f32x4 (&sacc)[2][2]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       sacc[st][0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -308,47 +319,56 @@ __device__ __forceinline__ void prefill_item(
         sacc[st][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][cc], sacc[st][1], 0, 0, 0);
       }
     }
-    if constexpr (kMasked) {
+  };
+  // scores of keys a row does not see (past its position, or on a page
+  // outside the pool) to -inf
+  auto mask = [&](f32x4 (&sacc)[2][2], int kt, int h) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int k16 = 32 * h + 16 * st;           // first key of the sub-tile in the tile
-        const int pj = kt * PPT + k16 / BS;         // a sub-tile lies in one page
-        const bool page_ok = pj < npages && (unsigned)bt[pj] < (unsigned)num_blocks;
+    for (int st = 0; st < 2; ++st) {
+      const int k16 = 32 * h + 16 * st;    // first key of the sub-tile in the tile
+      const int pj = kt * PPT + k16 / BS;  // a sub-tile lies in one page
+      const bool page_ok = pj < npages && (unsigned)bt[pj] < (unsigned)num_blocks;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kk = kt * kKeys + k16 + 4 * q4 + r;
-            if (!(page_ok && kk <= pos[t])) sacc[st][t][r] = -INFINITY;
-          }
-      }
+        for (int r = 0; r < 4; ++r) {
+          const int kk = kt * kKeys + k16 + 4 * q4 + r;
+          if (!(page_ok && kk <= pos[t])) sacc[st][t][r] = -INFINITY;
+        }
     }
-    // the running max moves only when some row's grows by more than
-    // 2^kRescaleLog2 (weights stay below that bound, and the base cancels
-    // between the weighted sum and the sum of weights)
-    float mt[2];
+  };
+  // The running max moves only when some row's grows by more than
+  // 2^kRescaleLog2 (weights stay below that bound, and the base cancels
+  // between the weighted sum and the sum of weights).  The check compares
+  // each lane's raw maximum with its row's threshold (m + kRescaleLog2) / c
+  // and takes one ballot; the row-wide maximum is formed only in the rare
+  // rescale.
+  float thr[2] = {-INFINITY, -INFINITY};
+  auto update_max = [&](const f32x4 (&sacc)[2][2]) {
+    float mx[2];
     bool grow = false;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const float mx = fmaxf(fmaxf(fmaxf(sacc[0][t][0], sacc[0][t][1]),
-                                   fmaxf(sacc[0][t][2], sacc[0][t][3])),
-                             fmaxf(fmaxf(sacc[1][t][0], sacc[1][t][1]),
-                                   fmaxf(sacc[1][t][2], sacc[1][t][3])));
-      mt[t] = rows_max(mx) * c;
-      grow = grow || mt[t] > m[t] + kRescaleLog2;
+      mx[t] = fmaxf(fmaxf(fmaxf(sacc[0][t][0], sacc[0][t][1]), fmaxf(sacc[0][t][2], sacc[0][t][3])),
+                    fmaxf(fmaxf(sacc[1][t][0], sacc[1][t][1]), fmaxf(sacc[1][t][2], sacc[1][t][3])));
+      grow = grow || mx[t] > thr[t];
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const float mn = fmaxf(m[t], mt[t]);
+        const float mn = fmaxf(m[t], rows_max(mx[t]) * c);
         const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[t] - mn);
         m[t] = mn;
+        thr[t] = (mn + kRescaleLog2) / c;
         lsum[t] *= alpha;
 #pragma unroll
         for (int nb = 0; nb < NN; ++nb) o[t][nb] *= alpha;
       }
     }
-    // weights as bf16 B operands: keys 4*q4 + r of sub-tile 0, then of 1
+  };
+  // weights as bf16 B operands (keys 4*q4 + r of sub-tile 0, then of 1),
+  // then O^T += V^T P^T with the half's 32 keys as the reduction dimension
+  auto accumulate = [&](const f32x4 (&sacc)[2][2], const lds_char *vs, int h) {
     i16x8 pb[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -376,31 +396,66 @@ __device__ __forceinline__ void prefill_item(
                                                          o[1][nb], 0, 0, 0);
     }
   };
-  auto compute = [&](auto masked_c, int buf, int kt) {
+  // One tile, in 32-key parts.  Each part's scores are computed before the
+  // previous part's exponentials and P.V, so those matrix instructions can
+  // run beside the vector work.
+  auto compute = [&](auto masked_c, auto buf_c, int kt) {
+    constexpr bool kMasked = decltype(masked_c)::value;
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr int kParts = kKeys / 32;
     const lds_char *ks = (const lds_char *)s_kv[buf][0];
     const lds_char *vs = (const lds_char *)s_kv[buf][1];
-    half(masked_c, ks, vs, kt, 0);
-    half(masked_c, ks, vs, kt, 1);
+    f32x4 sc[2][2][2];  // scores of two parts in flight: [slot][sub-tile][row tile]
+    scores(ks, 0, sc[0]);
+    if constexpr (kMasked) mask(sc[0], kt, 0);
+    update_max(sc[0]);
+#pragma unroll
+    for (int h = 0; h < kParts; ++h) {
+      if (h + 1 < kParts) {
+        scores(ks, h + 1, sc[(h + 1) & 1]);
+        if constexpr (kMasked) mask(sc[(h + 1) & 1], kt, h + 1);
+      }
+      accumulate(sc[h & 1], vs, h);
+      if (h + 1 < kParts) update_max(sc[(h + 1) & 1]);
+    }
   };
+  // one key tile: stage the next tile (fetched one tile ago) into the other
+  // buffer, fetch the one after, use this one; the buffer index is a
+  // compile-time constant so every LDS address is a lane offset plus an
+  // immediate
+  auto step = [&](auto masked_c, auto buf_c, int kt) {
+    constexpr int buf = decltype(buf_c)::value;
+    if (kt + 1 < ntiles) {
+      stage(buf ^ 1, tile_clean(kt + 1));  // its previous contents were used before the last barrier
+      if (kt + 2 < ntiles) fetch(kt + 2);
+    }
+    if (wave_live && kt * kKeys <= wmax) compute(masked_c, buf_c, kt);
+    __syncthreads();
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using Clean = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
 
+  // Each wave first runs the tiles that lie wholly below its first row's
+  // position on valid pages (no per-key mask), then the rest.  Every wave
+  // takes one barrier per tile, so the two loops of different waves stay in
+  // step.
   if (ntiles > 0) {
     fetch(0);
     stage(0, tile_clean(0));
     if (ntiles > 1) fetch(1);
     __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < ntiles) {
-        stage(buf ^ 1, tile_clean(kt + 1));  // its previous contents were used before the last barrier
-        if (kt + 2 < ntiles) fetch(kt + 2);
-      }
-      if (wave_live && kt * kKeys <= wmax) {
-        if (kt * kKeys + kKeys - 1 <= wmin && tile_clean(kt))
-          compute(std::integral_constant<bool, false>{}, buf, kt);
-        else
-          compute(std::integral_constant<bool, true>{}, buf, kt);
-      }
-      __syncthreads();
+    const int clean_end = wave_live ? min(ntiles, max(0, (wmin + 1) / kKeys)) : 0;
+    int kt = 0;
+    for (; kt + 1 < clean_end && tile_clean(kt) && tile_clean(kt + 1); kt += 2) {
+      step(Clean{}, B0{}, kt);
+      step(Clean{}, B1{}, kt + 1);
+    }
+    // kt is even here: the clean loop takes tiles in pairs
+    for (; kt < ntiles; kt += 2) {
+      step(Masked{}, B0{}, kt);
+      if (kt + 1 < ntiles) step(Masked{}, B1{}, kt + 1);
     }
   }
 
