@@ -7,6 +7,7 @@ It shares no code with the HIP path.  Every function is pinned by CPU tests
 (brute force, closed forms, invariants, a library routine, the pages'
 page-table figure); no function is "parity unpinned".
 """
-from .paged_attention import copy_blocks, decode, gather_pages, prefill, reshape_and_cache, widen
+from .paged_attention import (copy_blocks, decode, gather_pages, prefill, reshape_and_cache, rope,
+                              widen)
 
-__all__ = ["copy_blocks", "decode", "gather_pages", "prefill", "reshape_and_cache", "widen"]
+__all__ = ["copy_blocks", "decode", "gather_pages", "prefill", "reshape_and_cache", "rope", "widen"]

@@ -35,7 +35,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["widen", "gather_pages", "decode", "prefill", "reshape_and_cache", "copy_blocks"]
+__all__ = ["widen", "gather_pages", "decode", "prefill", "rope", "reshape_and_cache", "copy_blocks"]
 
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -83,7 +83,7 @@ def gather_pages(pool: np.ndarray, table_row: np.ndarray, ctx: int,
 def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
            block_tables: np.ndarray, context_lens: np.ndarray,
            num_kv_heads: int, scale, block_size: int, dtype: str,
-           return_lse: bool = False):
+           return_lse: bool = False, alibi_slopes=None):
     """Single-token decode attention over a paged KV cache, in float64.
 
     q            [S, H, D]          stored values (float32, or bf16 bits)
@@ -99,6 +99,13 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
     group (grouped-query attention).  ctx == 0 gives a zero row (and
     lse = -inf).  Returns out [S, H, D] float64, and with ``return_lse`` also
     the log-sum-exp of the scaled logits [S, H].
+
+    ``alibi_slopes`` (optional, [H]): the ALiBi model variant (showapi.com
+    article, section 4.1, names ALiBi among the position encodings the
+    engine serves).  Reading: the logit of token t gets slope_h * (t - p)
+    added, p = ctx - 1 being the query's own position, so nearer tokens
+    weigh more for a positive slope.  Slopes are used at their float32
+    values.
     """
     S, H, D = q.shape
     if H % num_kv_heads:
@@ -121,6 +128,8 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         for h in range(H):
             g = h // group
             logits = sc * (K[g] @ qf[s, h])              # [L]
+            if alibi_slopes is not None:
+                logits = logits + float(np.float32(alibi_slopes[h])) * (np.arange(L) - (L - 1))
             m = logits.max()
             p = np.exp(logits - m)
             z = p.sum()
@@ -134,7 +143,7 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
 def prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
             block_tables: np.ndarray, context_lens: np.ndarray,
             query_start: np.ndarray, num_kv_heads: int, scale, block_size: int,
-            dtype: str, rows=None) -> np.ndarray:
+            dtype: str, rows=None, alibi_slopes=None) -> np.ndarray:
     """Multi-token attention over a paged KV cache (prefill and chunked
     prefill), in float64.
 
@@ -161,7 +170,8 @@ def prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         out[query_start[s] + i, h] = softmax(scale * K[:p+1] q) V[:p+1],
         p = ctx - n + i,  K, V of kv-head h // (H / Hkv).
 
-    With n = 1 this is ``decode``.  n > ctx is rejected.  ``rows``
+    With n = 1 this is ``decode``; ``alibi_slopes`` adds slope_h * (t - p)
+    to the logit of token t as there.  n > ctx is rejected.  ``rows``
     (optional) limits the computation to those row indices of q; the other
     output rows are left NaN.  Returns out [T, H, D] float64.
     """
@@ -198,9 +208,50 @@ def prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
             for h in range(H):
                 kv = h // group
                 x = sc * (K[kv, :visible] @ qf[row, h])
+                if alibi_slopes is not None:
+                    x = x + float(np.float32(alibi_slopes[h])) * (np.arange(visible) - (visible - 1))
                 w = np.exp(x - x.max())
                 out[row, h] = (w @ V[kv, :visible]) / w.sum()
     return out
+
+
+def rope(x: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray, rot_dim: int,
+         neox: bool, dtype: str) -> np.ndarray:
+    """Rotary position embedding of rows x [T, heads, D], in float64.
+
+    The showapi.com article (section 4.1) names RoPE among the position
+    encodings the engine serves; the pages give no formula.  Reading (the
+    usual definition): the first rot_dim entries of every head are taken in
+    rot_dim / 2 pairs, pair i of token t is rotated by the angle whose
+    cosine and sine are cos_sin[positions[t], i] and
+    cos_sin[positions[t], rot_dim / 2 + i] (a table the caller fills, e.g.
+    with angle = position * base^(-2i / rot_dim)):
+
+        (a, b) -> (a cos - b sin,  b cos + a sin)
+
+    Pair i is entries (i, i + rot_dim / 2) when ``neox`` (split halves) and
+    entries (2i, 2i + 1) otherwise (interleaved).  Entries past rot_dim are
+    unchanged.  Table values are used at their float32 values.  Returns the
+    rotated rows as float64.
+    """
+    T, nh, D = x.shape
+    if rot_dim % 2 or not 0 < rot_dim <= D:
+        raise ValueError("rot_dim must be even and at most head_dim")
+    xf = widen(x, dtype).copy()
+    half = rot_dim // 2
+    cs = np.asarray(cos_sin, dtype=np.float32).astype(np.float64)
+    for t in range(T):
+        pos = int(positions[t])
+        if not 0 <= pos < cs.shape[0]:
+            raise IndexError(f"position {pos} outside the table")
+        for i in range(half):
+            c, sn = cs[pos, i], cs[pos, half + i]
+            ia, ib = (i, i + half) if neox else (2 * i, 2 * i + 1)
+            a = xf[t, :, ia].copy()
+            b = xf[t, :, ib].copy()
+            xf[t, :, ia] = a * c - b * sn
+            xf[t, :, ib] = b * c + a * sn
+    return xf
 
 
 def reshape_and_cache(k: np.ndarray, v: np.ndarray, k_pool: np.ndarray,

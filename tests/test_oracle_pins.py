@@ -546,6 +546,120 @@ def pin_prefill_sdpa_causal(o):
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
+def pin_alibi_geometric_closed_form(o):
+    # q = 0: the logits are the bias slope * (t - p) alone.  With slope 1 the
+    # weight of the token j places before the query is e^-j / sum_{i<L} e^-i,
+    # so the query's own token gets (1 - e^-1) / (1 - e^-L) and the mean
+    # position is sum_j (L-1-j) e^-j / sum_j e^-j; a zero slope is the plain
+    # average.
+    L, bs = 6, 4
+    Kc = [np.zeros((1, L, 2), np.float32)]
+    V = np.zeros((1, L, 2), np.float32)
+    V[0, L - 1, 0] = 1.0
+    V[0, :, 1] = np.arange(L)
+    rng = np.random.default_rng(3)
+    kp, vp, table = _scatter_contiguous(Kc, [V], [L], bs, 4, rng, "f32", np.nan)
+    q = np.zeros((1, 2, 2), np.float32)
+    got = o.decode(q, kp, vp, table, np.array([L], np.int32), 1, 1.0, bs, "f32",
+                   alibi_slopes=np.array([1.0, 0.0], np.float32))
+    e = math.exp(-1.0)
+    z = (1 - e ** L) / (1 - e)
+    mean_pos = sum((L - 1 - j) * e ** j for j in range(L)) / z
+    assert abs(got[0, 0, 0] - (1 - e) / (1 - e ** L)) < 1e-14
+    assert abs(got[0, 0, 1] - mean_pos) < 1e-13
+    assert abs(got[0, 1, 0] - 1.0 / L) < 1e-15 and abs(got[0, 1, 1] - (L - 1) / 2) < 1e-14
+
+
+def pin_alibi_brute_force(o):
+    rng = np.random.default_rng(41)
+    ctx, H, Hkv, D, bs = [1, 9, 23], 6, 3, 8, 4
+    Kc = [rng.standard_normal((Hkv, L, D)).astype(np.float32) for L in ctx]
+    Vc = [rng.standard_normal((Hkv, L, D)).astype(np.float32) for L in ctx]
+    kp, vp, table = _scatter_contiguous(Kc, Vc, ctx, bs, 16, rng, "f32", np.nan)
+    q = rng.standard_normal((len(ctx), H, D)).astype(np.float32)
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625, 1.0, 0.03125], np.float32)
+    sc = 0.35
+    got = o.decode(q, kp, vp, table, np.array(ctx, np.int32), Hkv, sc, bs, "f32",
+                   alibi_slopes=slopes)
+    G = H // Hkv
+    for s_, L in enumerate(ctx):
+        for h in range(H):
+            g = h // G
+            logits = [float(np.float32(sc)) * sum(float(q[s_, h, d]) * float(Kc[s_][g, t, d])
+                                                  for d in range(D))
+                      + float(slopes[h]) * (t - (L - 1)) for t in range(L)]
+            top = max(logits)
+            w = [math.exp(x - top) for x in logits]
+            want = [sum(w[t] * float(Vc[s_][g, t, d]) for t in range(L)) / sum(w)
+                    for d in range(D)]
+            np.testing.assert_allclose(got[s_, h], want, rtol=1e-12, atol=1e-12)
+
+
+def pin_alibi_prefill_rows(o):
+    # each chunk row with ALiBi is the decode of its own prefix
+    rng = np.random.default_rng(44)
+    prior, chunk = [0, 7], [5, 3]
+    H, Hkv, D, bs = 4, 2, 8, 4
+    Kc, Vc, kp, vp, table, ctx, q, qs = _prefill_case(rng, prior, chunk, H, Hkv, D, bs, 16)
+    slopes = np.array([0.7, 0.2, 0.05, 1.5], np.float32)
+    got = o.prefill(q, kp, vp, table, ctx, qs, Hkv, 0.3, bs, "f32", alibi_slopes=slopes)
+    row = 0
+    for s_ in range(len(prior)):
+        for i in range(chunk[s_]):
+            L = prior[s_] + i + 1
+            want = o.decode(q[row:row + 1], kp, vp, table[s_:s_ + 1], np.array([L], np.int32),
+                            Hkv, 0.3, bs, "f32", alibi_slopes=slopes)
+            np.testing.assert_allclose(got[row], want[0], rtol=1e-13, atol=1e-13)
+            row += 1
+
+
+def pin_rope_worked_pairs(o):
+    # a table row of cos = (0, -1), sin = (1, 0): pair 0 turns a quarter,
+    # pair 1 a half.  x = (1, 2, 3, 4):
+    #   split halves, pairs (0, 2), (1, 3): (1, 3) -> (-3, 1); (2, 4) -> (-2, -4)
+    #   interleaved, pairs (0, 1), (2, 3): (1, 2) -> (-2, 1); (3, 4) -> (-3, -4)
+    table = np.array([[1, 1, 0, 0], [0, -1, 1, 0]], np.float32)
+    x = np.array([[[1, 2, 3, 4]]], np.float32)
+    neox = o.rope(x, np.array([1]), table, 4, True, "f32")
+    inter = o.rope(x, np.array([1]), table, 4, False, "f32")
+    assert neox[0, 0].tolist() == [-3.0, -2.0, 1.0, -4.0]
+    assert inter[0, 0].tolist() == [-2.0, 1.0, -3.0, -4.0]
+    # position 0 of the table is the identity
+    assert o.rope(x, np.array([0]), table, 4, True, "f32")[0, 0].tolist() == [1, 2, 3, 4]
+
+
+def _rope_table(npos, rot_dim, base=10000.0):
+    inv = base ** (-np.arange(0, rot_dim, 2) / rot_dim)
+    ang = np.arange(npos)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def pin_rope_rotation_properties(o):
+    # norms of the rotated pairs are kept; q . k depends only on the
+    # position difference; entries past rot_dim are untouched
+    rng = np.random.default_rng(51)
+    D, rot = 16, 12
+    table = _rope_table(64, rot)
+    for neox in (True, False):
+        x = rng.standard_normal((3, 2, D)).astype(np.float32)
+        pos = np.array([0, 17, 63])
+        y = o.rope(x, pos, table, rot, neox, "f32")
+        np.testing.assert_allclose(np.linalg.norm(y[..., :rot], axis=-1),
+                                   np.linalg.norm(x[..., :rot].astype(np.float64), axis=-1),
+                                   rtol=1e-6)
+        assert np.array_equal(y[..., rot:], x[..., rot:].astype(np.float64))
+        np.testing.assert_array_equal(y[0], x[0].astype(np.float64))
+        qv = rng.standard_normal((1, 1, D)).astype(np.float32)
+        kv = rng.standard_normal((1, 1, D)).astype(np.float32)
+        dots = []
+        for m, n in ((5, 2), (13, 10), (40, 37)):
+            dots.append(float(o.rope(qv, np.array([m]), table, rot, neox, "f32")[0, 0]
+                              @ o.rope(kv, np.array([n]), table, rot, neox, "f32")[0, 0]))
+        # the table holds float32 cosines and sines: the products agree to
+        # float32 rounding of the table
+        assert max(dots) - min(dots) < 2e-5 * (1 + abs(dots[0]))
+
+
 PINS = [
     pin_widen_bf16_definition, pin_hand_worked_example, pin_page_table_figure,
     pin_brute_force, pin_sdpa_identity_table, pin_ctx1_is_v0, pin_uniform_logits_mean,
@@ -554,6 +668,8 @@ PINS = [
     pin_copy_blocks, pin_copy_on_write_keeps_attention,
     pin_prefill_brute_force, pin_prefill_ramp_closed_form, pin_prefill_single_row_is_decode,
     pin_prefill_chunking_invariance, pin_prefill_sdpa_causal,
+    pin_alibi_geometric_closed_form, pin_alibi_brute_force, pin_alibi_prefill_rows,
+    pin_rope_worked_pairs, pin_rope_rotation_properties,
 ]
 
 
@@ -567,6 +683,7 @@ def test_package_exports_pinned_functions():
     assert oracle.reshape_and_cache is oracle_mod.reshape_and_cache
     assert oracle.copy_blocks is oracle_mod.copy_blocks
     assert oracle.prefill is oracle_mod.prefill
+    assert oracle.rope is oracle_mod.rope
 
 
 # ------------------------------------------------------- planted mistakes
@@ -601,6 +718,18 @@ MUTANTS = {
     "prefill V from K": ("out[row, h] = (w @ V[kv, :visible]) / w.sum()",
                          "out[row, h] = (w @ K[kv, :visible]) / w.sum()"),
     "prefill rows of sequence 0": ("row = int(qs[s]) + i", "row = i"),
+    "alibi sign": ("* (np.arange(L) - (L - 1))", "* ((L - 1) - np.arange(L))"),
+    "alibi slope of the kv-head": ("float(np.float32(alibi_slopes[h])) * (np.arange(L)",
+                                   "float(np.float32(alibi_slopes[g])) * (np.arange(L)"),
+    "prefill alibi reversed": ("* (np.arange(visible) - (visible - 1))",
+                               "* ((visible - 1) - np.arange(visible))"),
+    "rope sine sign": ("xf[t, :, ia] = a * c - b * sn", "xf[t, :, ia] = a * c + b * sn"),
+    "rope cos and sin swapped": ("c, sn = cs[pos, i], cs[pos, half + i]",
+                                 "sn, c = cs[pos, i], cs[pos, half + i]"),
+    "rope pairing swapped": ("(i, i + half) if neox else (2 * i, 2 * i + 1)",
+                             "(2 * i, 2 * i + 1) if neox else (i, i + half)"),
+    "rope position ignored": ("pos = int(positions[t])", "pos = t"),
+    "rope past rot_dim": ("half = rot_dim // 2", "half = D // 2"),
 }
 
 
