@@ -46,11 +46,17 @@ def parse():
                     help="HBM bytes per partition-kernel launch measured with rocprofv3 counters "
                          "(default: profiles/traffic_pa_decode_partition_c<config>.json); used "
                          "only while the kernel source still has the hash recorded there")
-    ap.add_argument("--op", choices=["decode-step", "prefill", "copy", "swap-out", "swap-in"],
+    ap.add_argument("--op", choices=["decode-step", "prefill", "cache-rope", "copy", "swap-out",
+                                     "swap-in"],
                     default="decode-step",
                     help="decode-step (default): the hot path; prefill: a multi-token step "
-                         "(--config picks prefill workload 1..3); copy / swap-out / swap-in: "
-                         "copy_blocks within the device pool, to a pinned host pool, back")
+                         "(--config picks prefill workload 1..3); cache-rope: the cache write "
+                         "with rotary embedding fused in, on prefill workload --config; copy / "
+                         "swap-out / swap-in: copy_blocks within the device pool, to a pinned "
+                         "host pool, back")
+    ap.add_argument("--alibi", action="store_true",
+                    help="decode-step / prefill through the ALiBi entry points (the ALiBi "
+                         "paper's geometric slopes)")
     ap.add_argument("--pages", type=int, default=2048,
                     help="pages moved per copy_blocks call (--op copy/swap-*)")
     ap.add_argument("--shared-prefix", action="store_true",
@@ -253,6 +259,73 @@ def prefill_cpu_baseline(w, budget_s):
     }
 
 
+def alibi_slopes(H):
+    """The geometric per-head slopes of the ALiBi paper."""
+    import numpy as np
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], np.float32)
+
+
+def bench_cache_rope(args):
+    """reshape_and_cache_rope over every chunk row of a prefill workload
+    (rotary dimension = head_dim, split-half pairs, positions 0..ctx-1),
+    against the plain cache write of the same rows.  Bytes per call: q read
+    and written, k and v read, K and V written to the pool, the table rows
+    read (H, Hkv, D, T of the workload, 4-byte table entries)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_457_amd import binding
+    from paged_kv_cache_457_amd.device_inputs import upload
+    from paged_kv_cache_457_amd.workloads import PREFILL_CONFIG_NAMES, make_prefill_config
+
+    w = make_prefill_config(args.config, args.seed)
+    dw = upload(w)
+    qs, ctx = w.query_start, w.context_lens
+    pos = np.concatenate([np.arange(ctx[s] - (qs[s + 1] - qs[s]), ctx[s])
+                          for s in range(w.num_seqs)]).astype(np.int64)
+    D = w.head_dim
+    inv = 10000.0 ** (-np.arange(0, D, 2) / D)
+    ang = np.arange(int(pos.max()) + 1)[:, None] * inv[None, :]
+    table = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], 1).astype(np.float32)).cuda()
+    pos_d = torch.from_numpy(pos).cuda()
+    q = dw.q.clone()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms = timed(lambda: binding.reshape_and_cache_rope(q, dw.k_new, dw.v_new, dw.k_pool,
+                                                      dw.v_pool, dw.slot_mapping, pos_d, table,
+                                                      D, True))
+    ms_plain = timed(lambda: binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool,
+                                                       dw.slot_mapping))
+    T, H, Hkv, e = w.num_tokens, w.num_heads, w.num_kv_heads, w.elem_bytes
+    nbytes = T * H * D * e * 2 + T * Hkv * D * e * 4 + T * D * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "cache write with RoPE fused, GB/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": PREFILL_CONFIG_NAMES[args.config] + "; rot_dim = head_dim, "
+                   "split-half pairs", "num_tokens": T, "op": "cache-rope"},
+        "bytes_per_call": nbytes,
+        "plain_cache_write_ms": round(ms_plain, 5),
+        "plain_cache_write_gbs": round(T * Hkv * D * e * 4 / (ms_plain * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "pa_reshape_and_cache_rope",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }), flush=True)
+
+
 def bench_prefill(args):
     """Multi-token step: cache write of every chunk row, then prefill
     attention.  value = chunk tokens / step time; the roofline prices the
@@ -270,12 +343,13 @@ def bench_prefill(args):
     ws = torch.empty(max(binding.paged_attention_prefill_workspace_bytes(
         dw.q, dw.k_pool, dw.block_tables, dw.query_start), 16), dtype=torch.uint8, device="cuda")
     scale = float(w.scale)
+    slopes = torch.from_numpy(alibi_slopes(w.num_heads)).cuda() if args.alibi else None
 
     def step(events=(None, None)):
         binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
         binding.paged_attention_prefill(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
                                         dw.context_lens, dw.query_start, scale=scale,
-                                        workspace=ws, timing_events=events)
+                                        workspace=ws, timing_events=events, alibi_slopes=slopes)
 
     for _ in range(args.warmup):
         step()
@@ -336,7 +410,7 @@ def bench_prefill(args):
             "head_dim": w.head_dim,
             "block_size": w.block_size,
             "sum_context_tokens": int(w.context_lens.sum()),
-            "entry": "paged_attention_prefill",
+            "entry": "paged_attention_prefill_alibi" if args.alibi else "paged_attention_prefill",
             "parallelism": "single GPU",
         },
         "flops_per_step": flops,
@@ -351,7 +425,8 @@ def bench_prefill(args):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(args, "pa_prefill_gqa", f"p{args.config}"),
+            "traffic": None if args.alibi else measured_traffic(args, "pa_prefill_gqa",
+                                                                f"p{args.config}"),
         },
     }
     if not args.no_cpu_baseline:
@@ -379,6 +454,9 @@ def main():
     if args.op == "prefill":
         bench_prefill(args)
         return
+    if args.op == "cache-rope":
+        bench_cache_rope(args)
+        return
     if args.op != "decode-step":
         bench_copy(args)
         return
@@ -397,6 +475,10 @@ def main():
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     scale = float(w.scale)
 
+    slopes = torch.from_numpy(alibi_slopes(w.num_heads)).cuda() if args.alibi else None
+    if args.alibi and args.shared_prefix:
+        print("--alibi has no shared-prefix entry point", file=sys.stderr)
+        sys.exit(2)
     if args.shared_prefix:
         if "group_starts" not in w.extra:
             print("--shared-prefix needs a workload with sharing groups (config 5)",
@@ -419,7 +501,7 @@ def main():
         binding.paged_attention_decode(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
                                        dw.context_lens, scale=scale,
                                        partition_size=args.partition_size, workspace=ws,
-                                       timing_events=events)
+                                       timing_events=events, alibi_slopes=slopes)
 
     for _ in range(args.warmup):
         step()
@@ -452,7 +534,7 @@ def main():
     kernel_bytes = w.unique_kv_bytes() if args.shared_prefix else kv_bytes
     achieved = kernel_bytes / (k1_avg_ms * 1e-3) / 1e9
     kernel = "pa_decode_prefix_gqa" if args.shared_prefix else dominant_kernel(w)
-    traffic = measured_traffic(args, kernel)
+    traffic = None if args.alibi else measured_traffic(args, kernel)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -505,7 +587,7 @@ def main():
             "num_blocks": w.num_blocks,
             "partition_size": args.effective_partition,
             "decode_entry": "paged_attention_decode_shared_prefix" if args.shared_prefix
-            else "paged_attention_decode",
+            else ("paged_attention_decode_alibi" if args.alibi else "paged_attention_decode"),
             "parallelism": "single GPU",
         },
         "kv_bytes_per_step": kv_bytes,

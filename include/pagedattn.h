@@ -129,6 +129,21 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool,
                            const pa_decode_dims *dims);
 
 /*
+ * paged_attention_decode with ALiBi (the showapi.com article, section 4.1,
+ * lists ALiBi among the position encodings the engine serves): the logit of
+ * context token t for query head h gets alibi_slopes[h] * (t - (L - 1))
+ * added, L - 1 being the query's own position, before the softmax.
+ * alibi_slopes: device fp32 [num_heads], 4-byte aligned, required when
+ * num_seqs > 0 (PA_ERR_NULL otherwise).  Everything else, workspace
+ * included, is as for paged_attention_decode.
+ */
+int paged_attention_decode_alibi(void *out, const void *q, const void *k_pool,
+                                 const void *v_pool, const int32_t *block_tables,
+                                 const int32_t *context_lens, int32_t num_kv_heads, float scale,
+                                 int32_t block_size, const float *alibi_slopes,
+                                 const pa_decode_dims *dims);
+
+/*
  * Workspace bytes paged_attention_decode needs for these shapes, with
  * P = ceil(max_blocks_per_seq * block_size / partition_size):
  *   the work plan, 4 * (4 + num_seqs * P) rounded up to 256, plus, when
@@ -259,6 +274,18 @@ int paged_attention_prefill(void *out, const void *q, const void *k_pool, const 
                             int32_t block_size, const pa_prefill_dims *dims);
 
 /*
+ * paged_attention_prefill with ALiBi: the logit of token t for the chunk
+ * row at position p and query head h gets alibi_slopes[h] * (t - p) added.
+ * alibi_slopes: device fp32 [num_heads], 4-byte aligned, required when
+ * num_tokens > 0.  Everything else is as for paged_attention_prefill.
+ */
+int paged_attention_prefill_alibi(void *out, const void *q, const void *k_pool,
+                                  const void *v_pool, const int32_t *block_tables,
+                                  const int32_t *context_lens, const int32_t *query_start,
+                                  int32_t num_kv_heads, float scale, int32_t block_size,
+                                  const float *alibi_slopes, const pa_prefill_dims *dims);
+
+/*
  * Workspace bytes of paged_attention_prefill: the work plan,
  *   4 * (4 + 2 * num_tokens) rounded up to 256.
  * 0 when num_tokens is 0; SIZE_MAX for invalid shapes.
@@ -288,6 +315,39 @@ typedef struct pa_cache_dims {
  */
 int reshape_and_cache(const void *k, const void *v, void *k_pool, void *v_pool,
                       const int64_t *slot_mapping, const pa_cache_dims *dims);
+
+/* Rotary position embedding parameters of reshape_and_cache_rope. */
+typedef struct pa_rope_dims {
+  int32_t num_heads;     /* query heads of q, >= 1 */
+  int32_t rot_dim;       /* rotated entries per head: even, <= head_dim, a multiple
+                            of 16 (bf16) or 8 (fp32); PA_ERR_UNSUPPORTED otherwise */
+  int32_t max_position;  /* rows of cos_sin, >= 1 */
+  int32_t is_neox;       /* 1: pairs (i, i + rot_dim/2); 0: pairs (2i, 2i + 1) */
+  int32_t reserved;      /* must be 0 */
+} pa_rope_dims;
+
+/*
+ * KV-cache write with rotary position embedding fused in (the showapi.com
+ * article, section 4.1, lists RoPE among the position encodings the engine
+ * serves).  For each token i with pos = positions[i] in [0, max_position):
+ *   - every query head of q[i] ([num_tokens, num_heads, head_dim], device,
+ *     same dtype as the pools) is rotated in place;
+ *   - k[i] is rotated the same way and written, with v[i] unchanged, to
+ *     slot_mapping[i] exactly as reshape_and_cache writes it (k itself is
+ *     not modified; negative or out-of-pool slots write nothing).
+ * Rotation of pair (a, b) with c = cos_sin[pos, j], s = cos_sin[pos,
+ * rot_dim/2 + j]: (a c - b s, b c + a s), in fp32, rounded to the element
+ * type (bf16: nearest even).  Pair j is entries (j, j + rot_dim/2) when
+ * is_neox, else (2j, 2j + 1); entries past rot_dim are unchanged.
+ * cos_sin: device fp32 [max_position, rot_dim], filled by the caller (for
+ * example cos and sin of pos * base^(-2j/rot_dim)).  A token whose position
+ * is outside [0, max_position) is skipped entirely (q untouched, nothing
+ * written).  positions: device int64 [num_tokens], 8-byte aligned.
+ */
+int reshape_and_cache_rope(void *q, const void *k, const void *v, void *k_pool, void *v_pool,
+                           const int64_t *slot_mapping, const int64_t *positions,
+                           const float *cos_sin, const pa_rope_dims *rope,
+                           const pa_cache_dims *dims);
 
 /* Shapes and launch context of copy_blocks. */
 typedef struct pa_copy_dims {

@@ -70,6 +70,16 @@ class CacheDims(ctypes.Structure):
     ]
 
 
+class RopeDims(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("rot_dim", ctypes.c_int32),
+        ("max_position", ctypes.c_int32),
+        ("is_neox", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 class CopyDims(ctypes.Structure):
     _fields_ = [
         ("num_pairs", ctypes.c_int32),
@@ -90,6 +100,10 @@ SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
         ctypes.c_int32, ctypes.POINTER(DecodeDims)]),
+    "paged_attention_decode_alibi": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(DecodeDims)]),
     "paged_attention_decode_workspace_bytes": (ctypes.c_size_t, [
         ctypes.c_int32, ctypes.POINTER(DecodeDims)]),
     "paged_attention_decode_partition_tokens": (ctypes.c_int32, [
@@ -105,11 +119,19 @@ SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
         ctypes.c_int32, ctypes.POINTER(PrefillDims)]),
+    "paged_attention_prefill_alibi": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(PrefillDims)]),
     "paged_attention_prefill_workspace_bytes": (ctypes.c_size_t, [
         ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(PrefillDims)]),
     "reshape_and_cache": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.POINTER(CacheDims)]),
+    "reshape_and_cache_rope": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(RopeDims),
+        ctypes.POINTER(CacheDims)]),
     "copy_blocks": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.POINTER(CopyDims)]),

@@ -55,6 +55,11 @@ def _event_ptr(ev) -> Optional[int]:
     return handle
 
 
+def _check_slopes(alibi_slopes: torch.Tensor, H: int) -> None:
+    if alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (H,):
+        raise ValueError(f"alibi_slopes must be float32 [{H}]")
+
+
 def decode_dims(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tensor,
                 partition_size: int = 0) -> _lib.DecodeDims:
     S, H, D = q.shape
@@ -92,12 +97,14 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
                            v_pool: torch.Tensor, block_tables: torch.Tensor,
                            context_lens: torch.Tensor, scale: Optional[float] = None,
                            partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
-                           stream=None, timing_events: Sequence = (None, None)) -> torch.Tensor:
+                           stream=None, timing_events: Sequence = (None, None),
+                           alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[S,H,D] <- paged decode attention (see paged_attention_decode in
     include/pagedattn.h).  Pools are [num_blocks, num_kv_heads, block_size,
     head_dim]; the kv-head count and block size are read off k_pool.
     ``scale`` defaults to 1/sqrt(head_dim).  A workspace (unit plan and
-    split-K partials) is allocated here when none is given."""
+    split-K partials) is allocated here when none is given.  With
+    ``alibi_slopes`` (fp32 [H]) the call is paged_attention_decode_alibi."""
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     for name, t in (("out", out), ("k_pool", k_pool), ("v_pool", v_pool)):
@@ -128,6 +135,14 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     d.stream = _stream_ptr(stream)
     d.timing_events[0] = _event_ptr(timing_events[0])
     d.timing_events[1] = _event_ptr(timing_events[1])
+    if alibi_slopes is not None:
+        _check_slopes(alibi_slopes, H)
+        rc = lib.paged_attention_decode_alibi(
+            _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+            hkv, ctypes.c_float(scale), bs, _dev(alibi_slopes, "alibi_slopes"), ctypes.byref(d))
+        _check(rc, "paged_attention_decode_alibi")
+        return out
     rc = lib.paged_attention_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
         _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
@@ -223,7 +238,8 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Te
                             context_lens: torch.Tensor, query_start: torch.Tensor,
                             scale: Optional[float] = None,
                             workspace: Optional[torch.Tensor] = None, stream=None,
-                            timing_events: Sequence = (None, None)) -> torch.Tensor:
+                            timing_events: Sequence = (None, None),
+                            alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[T,H,D] <- multi-token (prefill / chunked prefill) attention over
     the paged cache (see paged_attention_prefill in include/pagedattn.h);
     query_start int32 [S + 1] gives each sequence's first row of q.  A
@@ -262,6 +278,15 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Te
     d.stream = _stream_ptr(stream)
     d.timing_events[0] = _event_ptr(timing_events[0])
     d.timing_events[1] = _event_ptr(timing_events[1])
+    if alibi_slopes is not None:
+        _check_slopes(alibi_slopes, H)
+        rc = lib.paged_attention_prefill_alibi(
+            _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+            _dev(query_start, "query_start"), hkv, ctypes.c_float(scale), bs,
+            _dev(alibi_slopes, "alibi_slopes"), ctypes.byref(d))
+        _check(rc, "paged_attention_prefill_alibi")
+        return out
     rc = lib.paged_attention_prefill(
         _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
         _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
@@ -305,6 +330,40 @@ def _pool_ptr(t: torch.Tensor, name: str) -> int:
     if not t.is_cuda and not t.is_pinned():
         raise ValueError(f"{name} must be a device tensor or pinned host memory")
     return t.data_ptr()
+
+
+def reshape_and_cache_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           k_pool: torch.Tensor, v_pool: torch.Tensor, slot_mapping: torch.Tensor,
+                           positions: torch.Tensor, cos_sin: torch.Tensor, rot_dim: int,
+                           is_neox: bool = True, stream=None) -> None:
+    """Rotate q ([T, H, D]) in place and write rotated k with v to the pool
+    slots (see reshape_and_cache_rope in include/pagedattn.h); positions
+    int64 [T], cos_sin float32 [max_position, rot_dim] (cosines, then
+    sines)."""
+    for name, t in (("q", q), ("v", v), ("k_pool", k_pool), ("v_pool", v_pool)):
+        if t.dtype != k.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} differs from k dtype {k.dtype}")
+    if k.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k.dtype}")
+    if slot_mapping.dtype != torch.int64 or positions.dtype != torch.int64:
+        raise ValueError("slot_mapping and positions must be int64")
+    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != rot_dim:
+        raise ValueError("cos_sin must be float32 [max_position, rot_dim]")
+    T, hkv, D = k.shape
+    if v.shape != k.shape or q.dim() != 3 or q.shape[0] != T or q.shape[2] != D \
+            or slot_mapping.shape != (T,) or positions.shape != (T,):
+        raise ValueError("q [T, H, D], k and v [T, Hkv, D], slot_mapping and positions [T]")
+    d = _lib.CacheDims()
+    d.num_tokens, d.num_kv_heads, d.head_dim = T, hkv, D
+    d.block_size, d.num_blocks, d.dtype = k_pool.shape[2], k_pool.shape[0], _DTYPES[k.dtype]
+    d.stream = _stream_ptr(stream)
+    r = _lib.RopeDims()
+    r.num_heads, r.rot_dim, r.max_position, r.is_neox = q.shape[1], rot_dim, cos_sin.shape[0], int(is_neox)
+    rc = _lib.load().reshape_and_cache_rope(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(slot_mapping, "slot_mapping"), _dev(positions, "positions"), _dev(cos_sin, "cos_sin"),
+        ctypes.byref(r), ctypes.byref(d))
+    _check(rc, "reshape_and_cache_rope")
 
 
 def copy_blocks(k_src: torch.Tensor, v_src: torch.Tensor, k_dst: torch.Tensor,

@@ -120,6 +120,14 @@ size_t prefill_plan_bytes(int num_tokens) {
   return (ints * sizeof(int32_t) + 255) / 256 * 256;
 }
 
+int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
+                const int32_t *block_tables, const int32_t *context_lens, int32_t num_kv_heads,
+                float scale, int32_t block_size, const float *alibi, const pa_decode_dims *dims);
+int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
+                 const int32_t *block_tables, const int32_t *context_lens,
+                 const int32_t *query_start, int32_t num_kv_heads, float scale,
+                 int32_t block_size, const float *alibi, const pa_prefill_dims *dims);
+
 }  // namespace
 
 extern "C" {
@@ -219,6 +227,31 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool, const v
                            const int32_t *block_tables, const int32_t *context_lens,
                            int32_t num_kv_heads, float scale, int32_t block_size,
                            const pa_decode_dims *dims) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_kv_heads, scale,
+                     block_size, nullptr, dims);
+}
+
+int paged_attention_decode_alibi(void *out, const void *q, const void *k_pool,
+                                 const void *v_pool, const int32_t *block_tables,
+                                 const int32_t *context_lens, int32_t num_kv_heads, float scale,
+                                 int32_t block_size, const float *alibi_slopes,
+                                 const pa_decode_dims *dims) {
+  if (!dims) return PA_ERR_NULL;
+  const int rc = check_decode_dims(num_kv_heads, block_size, dims);
+  if (rc != PA_OK) return rc;
+  if (dims->num_seqs > 0 && !alibi_slopes) return PA_ERR_NULL;
+  if (!aligned(alibi_slopes, 4)) return PA_ERR_ALIGN;
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_kv_heads, scale,
+                     block_size, alibi_slopes, dims);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
+                const int32_t *block_tables, const int32_t *context_lens, int32_t num_kv_heads,
+                float scale, int32_t block_size, const float *alibi, const pa_decode_dims *dims) {
   if (!dims) return PA_ERR_NULL;
   int rc = check_decode_dims(num_kv_heads, block_size, dims);
   if (rc != PA_OK) return rc;
@@ -265,8 +298,13 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool, const v
   a.stream = dims->stream;
   a.ev_begin = dims->timing_events[0];
   a.ev_end = dims->timing_events[1];
+  a.alibi = alibi;
   return pa_internal::launch_decode(a);
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t paged_attention_prefill_workspace_bytes(int32_t num_kv_heads, int32_t block_size,
                                                const pa_prefill_dims *dims) {
@@ -279,6 +317,32 @@ int paged_attention_prefill(void *out, const void *q, const void *k_pool, const 
                             const int32_t *block_tables, const int32_t *context_lens,
                             const int32_t *query_start, int32_t num_kv_heads, float scale,
                             int32_t block_size, const pa_prefill_dims *dims) {
+  return prefill_impl(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                      num_kv_heads, scale, block_size, nullptr, dims);
+}
+
+int paged_attention_prefill_alibi(void *out, const void *q, const void *k_pool,
+                                  const void *v_pool, const int32_t *block_tables,
+                                  const int32_t *context_lens, const int32_t *query_start,
+                                  int32_t num_kv_heads, float scale, int32_t block_size,
+                                  const float *alibi_slopes, const pa_prefill_dims *dims) {
+  if (!dims) return PA_ERR_NULL;
+  const int rc = check_prefill_dims(num_kv_heads, block_size, dims);
+  if (rc != PA_OK) return rc;
+  if (dims->num_tokens > 0 && !alibi_slopes) return PA_ERR_NULL;
+  if (!aligned(alibi_slopes, 4)) return PA_ERR_ALIGN;
+  return prefill_impl(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                      num_kv_heads, scale, block_size, alibi_slopes, dims);
+}
+
+}  // extern "C"
+
+namespace {
+
+int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
+                 const int32_t *block_tables, const int32_t *context_lens,
+                 const int32_t *query_start, int32_t num_kv_heads, float scale,
+                 int32_t block_size, const float *alibi, const pa_prefill_dims *dims) {
   if (!dims) return PA_ERR_NULL;
   int rc = check_prefill_dims(num_kv_heads, block_size, dims);
   if (rc != PA_OK) return rc;
@@ -313,8 +377,13 @@ int paged_attention_prefill(void *out, const void *q, const void *k_pool, const 
   a.stream = dims->stream;
   a.ev_begin = dims->timing_events[0];
   a.ev_end = dims->timing_events[1];
+  a.alibi = alibi;
   return pa_internal::launch_prefill(a);
 }
+
+}  // namespace
+
+extern "C" {
 
 int reshape_and_cache(const void *k, const void *v, void *k_pool, void *v_pool,
                       const int64_t *slot_mapping, const pa_cache_dims *dims) {
@@ -343,6 +412,55 @@ int reshape_and_cache(const void *k, const void *v, void *k_pool, void *v_pool,
   a.elem_bytes = elem_bytes(dims->dtype);
   a.stream = dims->stream;
   return pa_internal::launch_reshape_and_cache(a);
+}
+
+int reshape_and_cache_rope(void *q, const void *k, const void *v, void *k_pool, void *v_pool,
+                           const int64_t *slot_mapping, const int64_t *positions,
+                           const float *cos_sin, const pa_rope_dims *rope,
+                           const pa_cache_dims *dims) {
+  if (!dims || !rope) return PA_ERR_NULL;
+  if (dims->num_tokens < 0 || dims->num_kv_heads < 1 || dims->num_blocks < 1 ||
+      rope->num_heads < 1 || rope->max_position < 1 || rope->reserved != 0)
+    return PA_ERR_SHAPE;
+  if (dims->dtype != PA_DTYPE_F32 && dims->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (!supported_dim(dims->head_dim) || !supported_bs(dims->block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (rope->is_neox != 0 && rope->is_neox != 1) return PA_ERR_SHAPE;
+  // rotary entries: even, within the head, whole 16-byte chunks per half
+  const int per_chunk = 16 / elem_bytes(dims->dtype);
+  if (rope->rot_dim < 2 || rope->rot_dim > dims->head_dim || rope->rot_dim % 2 != 0)
+    return PA_ERR_SHAPE;
+  if (rope->rot_dim % (2 * per_chunk) != 0) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)rope->max_position * rope->rot_dim > INT32_MAX) return PA_ERR_SHAPE;
+  if (dims->num_tokens == 0) return PA_OK;  // nothing to write; pointers may be NULL
+  if (!q || !k || !v || !k_pool || !v_pool || !slot_mapping || !positions || !cos_sin)
+    return PA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) ||
+      !aligned(v_pool, 16) || !aligned(slot_mapping, 8) || !aligned(positions, 8) ||
+      !aligned(cos_sin, 4))
+    return PA_ERR_ALIGN;
+  pa_internal::RopeLaunch r{};
+  pa_internal::CacheLaunch &a = r.cache;
+  a.k = k;
+  a.v = v;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = dims->num_tokens;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.block_size = dims->block_size;
+  a.num_blocks = dims->num_blocks;
+  a.elem_bytes = elem_bytes(dims->dtype);
+  a.stream = dims->stream;
+  r.q = q;
+  r.positions = positions;
+  r.cos_sin = cos_sin;
+  r.num_heads = rope->num_heads;
+  r.rot_dim = rope->rot_dim;
+  r.max_position = rope->max_position;
+  r.neox = rope->is_neox;
+  return pa_internal::launch_reshape_and_cache_rope(r);
 }
 
 int copy_blocks(const void *k_src, const void *v_src, void *k_dst, void *v_dst,

@@ -37,6 +37,89 @@ __global__ __launch_bounds__(256) void pa_reshape_and_cache(
   }
 }
 
+// ------------------------------------------------ cache write with RoPE
+// The position encodings the engine serves include RoPE (showapi.com
+// article, section 4.1): K is rotated by its token's position before it is
+// cached, and q by the same rotation before attention.  This kernel does
+// both in the one pass that writes the cache.  Grid (num_tokens), 256
+// threads; a thread takes 16-byte chunks of the token's rows (q heads
+// first, then kv-heads):
+//   rotary chunks   split halves: chunk j and chunk j + half hold the two
+//                   members of pairs j*E .. j*E + E-1; interleaved: one
+//                   chunk holds E/2 whole pairs.  Rotated in fp32 with the
+//                   table row cos_sin[pos] (cosines, then sines), rounded
+//                   to the element type.
+//   other chunks    K copied as is (q untouched).
+// q is rotated in place; K (rotated) and V go to the page slot.  A token
+// whose position is outside the table is skipped, and one whose slot is
+// negative or past the pool gets its q rotated but writes no K/V.
+template <class T>
+__global__ __launch_bounds__(256) void pa_reshape_and_cache_rope(
+    u32x4 *__restrict__ q, const u32x4 *__restrict__ k, const u32x4 *__restrict__ v,
+    u32x4 *__restrict__ k_pool, u32x4 *__restrict__ v_pool,
+    const int64_t *__restrict__ slot_mapping, const int64_t *__restrict__ positions,
+    const float *__restrict__ cos_sin, int num_heads, int num_kv_heads, int row_chunks,
+    int block_size, int64_t num_slots, int rot_dim, int max_position, int neox) {
+  constexpr int E = T::kPerChunk;
+  const int t = blockIdx.x;
+  const int64_t pos = positions[t];
+  if (pos < 0 || pos >= max_position) return;
+  const int64_t slot = slot_mapping[t];
+  const bool write = slot >= 0 && slot < num_slots;
+  const int64_t page = write ? slot / block_size : 0;
+  const int64_t off = write ? slot - page * block_size : 0;
+  const float *cs = cos_sin + pos * rot_dim;
+  const int half = rot_dim / 2;
+  const int rot_chunks = rot_dim / E;
+  const int rows = num_heads + num_kv_heads;
+  for (int u = threadIdx.x; u < rows * row_chunks; u += blockDim.x) {
+    const int r = u / row_chunks;
+    const int c = u - r * row_chunks;
+    const bool is_q = r < num_heads;
+    const int g = r - num_heads;
+    if (!is_q && !write) continue;
+    u32x4 *qrow = q + ((size_t)t * num_heads + r) * row_chunks;
+    const u32x4 *krow = k + ((size_t)t * num_kv_heads + g) * row_chunks;
+    u32x4 *prow = k_pool + (((size_t)page * num_kv_heads + g) * block_size + off) * row_chunks;
+    if (!is_q) {
+      v_pool[(((size_t)page * num_kv_heads + g) * block_size + off) * row_chunks + c] =
+          v[((size_t)t * num_kv_heads + g) * row_chunks + c];
+    }
+    if (c >= rot_chunks) {
+      if (!is_q) prow[c] = krow[c];
+      continue;
+    }
+    if (neox) {
+      if (c >= rot_chunks / 2) continue;  // the partner of chunk c - rot_chunks / 2
+      const int c2 = c + rot_chunks / 2;
+      float a[E], b[E];
+      T::unpack(is_q ? qrow[c] : krow[c], a);
+      T::unpack(is_q ? qrow[c2] : krow[c2], b);
+      float ra[E], rb[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float co = cs[c * E + e], si = cs[half + c * E + e];
+        ra[e] = a[e] * co - b[e] * si;
+        rb[e] = b[e] * co + a[e] * si;
+      }
+      u32x4 *dst = is_q ? qrow : prow;
+      dst[c] = T::pack(ra);
+      dst[c2] = T::pack(rb);
+    } else {
+      float x[E], y[E];
+      T::unpack(is_q ? qrow[c] : krow[c], x);
+#pragma unroll
+      for (int e = 0; e < E; e += 2) {
+        const int i = (c * E + e) / 2;
+        const float co = cs[i], si = cs[half + i];
+        y[e] = x[e] * co - x[e + 1] * si;
+        y[e + 1] = x[e + 1] * co + x[e] * si;
+      }
+      (is_q ? qrow : prow)[c] = T::pack(y);
+    }
+  }
+}
+
 // ------------------------------------------------------------ page copy
 // Grid (num_pairs, chunks per page), 256 threads.  Workgroup (i, c) copies
 // chunk c (16 KiB) of page mapping[i][0] of the source pools to page
@@ -117,6 +200,20 @@ int launch_reshape_and_cache(const CacheLaunch &a) {
                      reinterpret_cast<u32x4 *>(a.k_pool), reinterpret_cast<u32x4 *>(a.v_pool),
                      a.slot_mapping, a.num_kv_heads, row_chunks, a.block_size,
                      (int64_t)a.num_blocks * a.block_size);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+int launch_reshape_and_cache_rope(const RopeLaunch &r) {
+  const CacheLaunch &a = r.cache;
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const int row_chunks = a.head_dim * a.elem_bytes / 16;
+  auto kernel = a.elem_bytes == 2 ? pa_reshape_and_cache_rope<BF16> : pa_reshape_and_cache_rope<F32>;
+  hipLaunchKernelGGL(kernel, dim3(a.num_tokens), dim3(256), 0, st,
+                     reinterpret_cast<u32x4 *>(r.q), reinterpret_cast<const u32x4 *>(a.k),
+                     reinterpret_cast<const u32x4 *>(a.v), reinterpret_cast<u32x4 *>(a.k_pool),
+                     reinterpret_cast<u32x4 *>(a.v_pool), a.slot_mapping, r.positions, r.cos_sin,
+                     r.num_heads, a.num_kv_heads, row_chunks, a.block_size,
+                     (int64_t)a.num_blocks * a.block_size, r.rot_dim, r.max_position, r.neox);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

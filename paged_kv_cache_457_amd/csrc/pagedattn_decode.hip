@@ -79,14 +79,21 @@ struct WaveSoftmax {
   // token; live: whether the page id was valid; rg: this lane's token-row
   // group.  Tokens at or past ctx get weight exactly 0 and their V is never
   // used in arithmetic (a masked slot may hold NaN).
+  // With ALiBi, slope[h] (log2 units) times the token's distance behind the
+  // query, (token - (ctx - 1)), is added to head h's logit.
+  template <bool AL>
   __device__ __forceinline__ void page(const u32x4 (&qc)[G], const u32x4 (&kc)[S::NLD],
                                        const u32x4 (&vc)[S::NLD], int tok0, int ctx, bool live,
-                                       int rg, float scale_log2) {
+                                       int rg, float scale_log2, const float (&slope)[G]) {
     float lg[S::NLD][G];
 #pragma unroll
     for (int i = 0; i < S::NLD; ++i)
 #pragma unroll
-      for (int h = 0; h < G; ++h) lg[i][h] = row_sum<S::R>(T::dot(qc[h], kc[i])) * scale_log2;
+      for (int h = 0; h < G; ++h) {
+        lg[i][h] = row_sum<S::R>(T::dot(qc[h], kc[i])) * scale_log2;
+        if constexpr (AL)
+          lg[i][h] = fmaf(slope[h], (float)(tok0 + i * S::TPI + rg - (ctx - 1)), lg[i][h]);
+      }
     bool keep[S::NLD];
 #pragma unroll
     for (int i = 0; i < S::NLD; ++i) {
@@ -137,13 +144,14 @@ struct WaveSoftmax {
 
 // One work unit: the G query heads of kv-head g over partition `part` of
 // sequence s.  All threads of the workgroup call it with the same unit.
-template <class T, int D, int BS, int G, int NW>
+template <class T, int D, int BS, int G, int NW, bool AL>
 __device__ __forceinline__ void decode_unit(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, int num_heads, int num_kv_heads, int max_blocks,
-    int num_blocks, int part_pages, int max_parts, float scale_log2, int s, int g, int part) {
+    int num_blocks, int part_pages, int max_parts, float scale_log2,
+    const float *__restrict__ alibi, int s, int g, int part) {
   using S = DecodeShape<T, D, BS, G>;
   constexpr int E = S::E, R = S::R, NLD = S::NLD, PAGE_BYTES = S::PAGE_BYTES;
   __shared__ float s_ml[NW][G][2];
@@ -191,6 +199,9 @@ __device__ __forceinline__ void decode_unit(
 
   WaveSoftmax<T, D, BS, G> st;
   st.init();
+  float slope[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) slope[h] = AL ? alibi[h0 + h] * kLog2e : 0.f;
   const size_t page_stride = (size_t)num_kv_heads * PAGE_BYTES;
   const char *k_b = reinterpret_cast<const char *>(k_pool) + (size_t)g * PAGE_BYTES + lane * 16;
   const char *v_b = reinterpret_cast<const char *>(v_pool) + (size_t)g * PAGE_BYTES + lane * 16;
@@ -219,23 +230,23 @@ __device__ __forceinline__ void decode_unit(
       int j = 0;
       for (; j + 2 < np_w; j += 2) {
         okb = fetch(kb, vb, j + 1);
-        st.page(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2);
+        st.template page<AL>(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2, slope);
         oka = fetch(ka, va, j + 2);
-        st.page(qc, kb, vb, tok0(j + 1), ctx, okb, rg, scale_log2);
+        st.template page<AL>(qc, kb, vb, tok0(j + 1), ctx, okb, rg, scale_log2, slope);
       }
       if (j + 1 < np_w) {
         okb = fetch(kb, vb, j + 1);
-        st.page(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2);
-        st.page(qc, kb, vb, tok0(j + 1), ctx, okb, rg, scale_log2);
+        st.template page<AL>(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2, slope);
+        st.template page<AL>(qc, kb, vb, tok0(j + 1), ctx, okb, rg, scale_log2, slope);
       } else {
-        st.page(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2);
+        st.template page<AL>(qc, ka, va, tok0(j), ctx, oka, rg, scale_log2, slope);
       }
     }
   } else {
     for (int j = 0; j < np_w; ++j) {
       u32x4 kc[NLD], vc[NLD];
       const bool ok = fetch(kc, vc, j);
-      st.page(qc, kc, vc, tok0(j), ctx, ok, rg, scale_log2);
+      st.template page<AL>(qc, kc, vc, tok0(j), ctx, ok, rg, scale_log2, slope);
     }
   }
 
@@ -279,23 +290,23 @@ __device__ __forceinline__ void decode_unit(
 // snake_item.  Kv-head fastest puts the heads of one unit on workgroups
 // that start together on different XCDs (the hardware hands consecutive
 // workgroups to the 8 XCDs in turn).
-template <class T, int D, int BS, int G, int NW>
+template <class T, int D, int BS, int G, int NW, bool AL>
 __global__ __launch_bounds__(64 * NW) void pa_decode_partition(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, const int32_t *__restrict__ plan, int num_heads,
     int num_kv_heads, int max_blocks, int num_blocks, int part_pages, int max_parts,
-    float scale_log2) {
+    float scale_log2, const float *__restrict__ alibi) {
   const int items = plan[0] * num_kv_heads;
   for (int k = 0;; ++k) {
     const int it = snake_item(k);
     if (it >= items) break;
     const int unit = plan[kPlanHeader + it / num_kv_heads];
-    decode_unit<T, D, BS, G, NW>(out, q, k_pool, v_pool, block_tables, context_lens, ws_ml,
-                                 ws_acc, num_heads, num_kv_heads, max_blocks, num_blocks,
-                                 part_pages, max_parts, scale_log2, unit / max_parts,
-                                 it % num_kv_heads, unit % max_parts);
+    decode_unit<T, D, BS, G, NW, AL>(out, q, k_pool, v_pool, block_tables, context_lens, ws_ml,
+                                     ws_acc, num_heads, num_kv_heads, max_blocks, num_blocks,
+                                     part_pages, max_parts, scale_log2, alibi, unit / max_parts,
+                                     it % num_kv_heads, unit % max_parts);
     __syncthreads();  // the next unit reuses the LDS the merge just read
   }
 }
@@ -445,10 +456,10 @@ __global__ __launch_bounds__(64 * kReduceWaves) void pa_decode_reduce(
 
 constexpr int kWavesPerUnit = 4;
 
-template <class T, int D, int BS, int G>
-int launch_valu(const pa_internal::DecodeLaunch &a, float scale_log2) {
+template <class T, int D, int BS, int G, bool AL>
+int launch_valu_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  auto kernel = pa_decode_partition<T, D, BS, G, kWavesPerUnit>;
+  auto kernel = pa_decode_partition<T, D, BS, G, kWavesPerUnit, AL>;
   static const int per_cu = pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel),
                                                        64 * kWavesPerUnit);
   const unsigned grid = pa_internal::persistent_grid(a, per_cu);
@@ -456,8 +467,14 @@ int launch_valu(const pa_internal::DecodeLaunch &a, float scale_log2) {
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.out, a.q,
                      a.k_pool, a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc,
                      a.plan, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
-                     a.part_pages, a.max_parts, scale_log2);
+                     a.part_pages, a.max_parts, scale_log2, a.alibi);
   return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+template <class T, int D, int BS, int G>
+int launch_valu(const pa_internal::DecodeLaunch &a, float scale_log2) {
+  return a.alibi ? launch_valu_al<T, D, BS, G, true>(a, scale_log2)
+                 : launch_valu_al<T, D, BS, G, false>(a, scale_log2);
 }
 
 template <class T, int D, int BS>

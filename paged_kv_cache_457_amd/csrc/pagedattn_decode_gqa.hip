@@ -83,13 +83,14 @@ struct GqaGranule {
   bool ok;
 };
 
-template <int D, int BS, int G, int NW>
+template <int D, int BS, int G, int NW, bool AL>
 __device__ __forceinline__ void decode_unit_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, int num_heads, int num_kv_heads, int max_blocks,
-    int num_blocks, int part_pages, int max_parts, float scale_log2, int s, int g, int part) {
+    int num_blocks, int part_pages, int max_parts, float scale_log2,
+    const float *__restrict__ alibi, int s, int g, int part) {
   using S = GqaShape<D, BS, G>;
   constexpr int GPP = S::GPP, NC = S::NC, NN = S::NN, ROW = S::ROW, NVLD = S::NVLD;
   constexpr int PITCH = S::PITCH;
@@ -121,6 +122,9 @@ __device__ __forceinline__ void decode_unit_gqa(
       qb[c] = __builtin_bit_cast(bf16x8, w);
     }
   }
+
+  // ALiBi: head j16's slope in log2 units (the padding heads past G add 0)
+  const float slope = AL && j16 < G ? alibi[h0 + j16] * kLog2e : 0.f;
 
   ctx = min(max(ctx, 0), max_blocks * BS);
   const int npages = (ctx + BS - 1) / BS;
@@ -184,7 +188,9 @@ __device__ __forceinline__ void decode_unit_gqa(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool keep = gr.ok && tok0 + 4 * q4 + r < ctx;
-      sc[r] = keep ? acc[r] * scale_log2 : -INFINITY;
+      float x = acc[r] * scale_log2;
+      if constexpr (AL) x = fmaf(slope, (float)(tok0 + 4 * q4 + r - (ctx - 1)), x);
+      sc[r] = keep ? x : -INFINITY;
     }
     // online softmax for head j16: granule max over the 4 lane groups
     float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -272,33 +278,33 @@ __device__ __forceinline__ void decode_unit_gqa(
 // Persistent partition kernel over the plan's unit list (largest units
 // first), item i = (list[i / num_kv_heads], kv-head i % num_kv_heads), in
 // the snake order of snake_item.
-template <int D, int BS, int G, int NW>
+template <int D, int BS, int G, int NW, bool AL>
 __global__ __launch_bounds__(64 * NW) void pa_decode_partition_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, const int32_t *__restrict__ plan, int num_heads,
     int num_kv_heads, int max_blocks, int num_blocks, int part_pages, int max_parts,
-    float scale_log2) {
+    float scale_log2, const float *__restrict__ alibi) {
   const int items = plan[0] * num_kv_heads;
   for (int k = 0;; ++k) {
     const int it = snake_item(k);
     if (it >= items) break;
     const int unit = plan[pa_internal::kPlanHeader + it / num_kv_heads];
-    decode_unit_gqa<D, BS, G, NW>(out, q, k_pool, v_pool, block_tables, context_lens, ws_ml,
-                                  ws_acc, num_heads, num_kv_heads, max_blocks, num_blocks,
-                                  part_pages, max_parts, scale_log2, unit / max_parts,
-                                  it % num_kv_heads, unit % max_parts);
+    decode_unit_gqa<D, BS, G, NW, AL>(out, q, k_pool, v_pool, block_tables, context_lens,
+                                      ws_ml, ws_acc, num_heads, num_kv_heads, max_blocks,
+                                      num_blocks, part_pages, max_parts, scale_log2, alibi,
+                                      unit / max_parts, it % num_kv_heads, unit % max_parts);
     __syncthreads();  // the next unit reuses the LDS the merge just read
   }
 }
 
 constexpr int kWavesPerUnit = 4;
 
-template <int D, int BS, int G>
-int launch(const pa_internal::DecodeLaunch &a, float scale_log2) {
+template <int D, int BS, int G, bool AL>
+int launch_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  auto kernel = pa_decode_partition_gqa<D, BS, G, kWavesPerUnit>;
+  auto kernel = pa_decode_partition_gqa<D, BS, G, kWavesPerUnit, AL>;
   static const int per_cu = pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel),
                                                        64 * kWavesPerUnit);
   const unsigned grid = pa_internal::persistent_grid(a, per_cu);
@@ -306,8 +312,14 @@ int launch(const pa_internal::DecodeLaunch &a, float scale_log2) {
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.out, a.q, a.k_pool,
                      a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc, a.plan,
                      a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks, a.part_pages,
-                     a.max_parts, scale_log2);
+                     a.max_parts, scale_log2, a.alibi);
   return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+template <int D, int BS, int G>
+int launch(const pa_internal::DecodeLaunch &a, float scale_log2) {
+  return a.alibi ? launch_al<D, BS, G, true>(a, scale_log2)
+                 : launch_al<D, BS, G, false>(a, scale_log2);
 }
 
 template <int D, int BS>

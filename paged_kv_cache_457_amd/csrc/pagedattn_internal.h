@@ -37,6 +37,7 @@ struct DecodeLaunch {
   void *stream;
   void *ev_begin;
   void *ev_end;
+  const float *alibi = nullptr;  // [num_heads] ALiBi slopes, or none
 };
 
 struct PrefixLaunch {
@@ -64,6 +65,7 @@ struct PrefillLaunch {
   void *stream;
   void *ev_begin;
   void *ev_end;
+  const float *alibi = nullptr;  // [num_heads] ALiBi slopes, or none
 };
 
 struct CacheLaunch {
@@ -74,6 +76,14 @@ struct CacheLaunch {
   const int64_t *slot_mapping;
   int num_tokens, num_kv_heads, head_dim, block_size, num_blocks, elem_bytes;
   void *stream;
+};
+
+struct RopeLaunch {
+  CacheLaunch cache;          // k, v, pools, slots, shapes, stream
+  void *q;                    // [num_tokens, num_heads, head_dim], rotated in place
+  const int64_t *positions;   // [num_tokens]
+  const float *cos_sin;       // [max_position, rot_dim]: cosines, then sines
+  int num_heads, rot_dim, max_position, neox;
 };
 
 struct CopyLaunch {
@@ -106,6 +116,7 @@ int launch_prefix_units(const PrefixLaunch &p, float scale_log2);
 // multi-token attention: plan kernel, then the persistent item pass
 int launch_prefill(const PrefillLaunch &a);
 int launch_reshape_and_cache(const CacheLaunch &a);
+int launch_reshape_and_cache_rope(const RopeLaunch &r);
 // Also PA_ERR_UNSUPPORTED (3) when a pointer is not device-accessible.
 int launch_copy_pages(const CopyLaunch &a);
 int launch_hbm_probe(const void *buf, size_t bytes, void *sink, void *stream);

@@ -165,13 +165,13 @@ __device__ __forceinline__ float rows_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int BS, int G>
+template <int D, int BS, int G, bool AL>
 __device__ __forceinline__ void prefill_item(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
     int num_tokens, int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
-    float scale_log2, int s, int t0, int g) {
+    float scale_log2, const float *__restrict__ alibi, int s, int t0, int g) {
   using Sh = PrefillShape<D, BS, G>;
   constexpr int ROW = Sh::ROW, CPR = Sh::CPR, NC = Sh::NC, NN = Sh::NN, TILE = Sh::TILE;
   constexpr int LOADS = Sh::LOADS, TOK = Sh::TOK, PPT = Sh::PPT;
@@ -207,16 +207,22 @@ __device__ __forceinline__ void prefill_item(
   // -inf (a zero scale then gives equal weights, as it should).
   const bool negate = scale_log2 < 0.f;
   const float c = fmaxf(fabsf(scale_log2), 1.17549435e-38f);
+  // With ALiBi the scores are first turned into scaled logits with the bias
+  // slope * (key - position) added (log2 units), and the rest of the
+  // softmax runs with a unit scale.
+  const float cx = AL ? 1.f : c;
 
   // query rows as MFMA B operands, and each row's position (-1: not a row)
   bf16x8 qf[2][NC];
   int pos[2];
+  float slope[2];  // ALiBi slope of each row tile's head, log2 units
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int row = 32 * wave + 16 * t + j16;
     const int tk = row / G;
     const bool live = tk < ntok;
     pos[t] = live ? p0 + t0 + tk : -1;
+    slope[t] = AL ? alibi[g * G + row % G] * kLog2e : 0.f;
     const char *qrow = reinterpret_cast<const char *>(q) +
                        ((size_t)(qa + t0 + (live ? tk : 0)) * num_heads + g * G + row % G) * ROW;
 #pragma unroll
@@ -337,6 +343,18 @@ __device__ __forceinline__ void prefill_item(
         }
     }
   };
+  // ALiBi: scores -> scaled logits plus slope * (key - position)
+  auto add_bias = [&](f32x4 (&sacc)[2][2], int kt, int h) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float sb = slope[t] * (float)(kt * kKeys + 32 * h + 4 * q4 - pos[t]);
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sacc[st][t][r] = fmaf(sacc[st][t][r], c, fmaf(slope[t], (float)(16 * st + r), sb));
+    }
+  };
   // The running max moves only when some row's grows by more than
   // 2^kRescaleLog2 (weights stay below that bound, and the base cancels
   // between the weighted sum and the sum of weights).  The check compares
@@ -356,10 +374,10 @@ __device__ __forceinline__ void prefill_item(
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const float mn = fmaxf(m[t], rows_max(mx[t]) * c);
+        const float mn = fmaxf(m[t], rows_max(mx[t]) * cx);
         const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[t] - mn);
         m[t] = mn;
-        thr[t] = (mn + kRescaleLog2) / c;
+        thr[t] = (mn + kRescaleLog2) / cx;
         lsum[t] *= alpha;
 #pragma unroll
         for (int nb = 0; nb < NN; ++nb) o[t][nb] *= alpha;
@@ -367,9 +385,12 @@ __device__ __forceinline__ void prefill_item(
     }
   };
   // weights as bf16 B operands (keys 4*q4 + r of sub-tile 0, then of 1),
-  // then O^T += V^T P^T with the half's 32 keys as the reduction dimension
+  // then O^T += V^T P^T with the half's 32 keys as the reduction dimension.
+  // With ALiBi the attention can rest on a handful of nearby keys, so there
+  // the weights enter as a bf16 pair hi + lo (about 16 significant bits) at
+  // the cost of a second instruction per tile.
   auto accumulate = [&](const f32x4 (&sacc)[2][2], const lds_char *vs, int h) {
-    i16x8 pb[2];
+    i16x8 pb[2], pl[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float base = m[t] == -INFINITY ? 0.f : m[t];
@@ -377,9 +398,11 @@ __device__ __forceinline__ void prefill_item(
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(fmaf(sacc[st][t][r], c, -base));
+          const float p = fast_exp2(fmaf(sacc[st][t][r], cx, -base));
           lsum[t] += p;
-          pb[t][4 * st + r] = __builtin_bit_cast(short, (__bf16)p);
+          const __bf16 hi = (__bf16)p;
+          pb[t][4 * st + r] = __builtin_bit_cast(short, hi);
+          if constexpr (AL) pl[t][4 * st + r] = __builtin_bit_cast(short, (__bf16)(p - (float)hi));
         }
     }
 #pragma unroll
@@ -394,6 +417,12 @@ __device__ __forceinline__ void prefill_item(
                                                          o[0][nb], 0, 0, 0);
       o[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pb[1]),
                                                          o[1][nb], 0, 0, 0);
+      if constexpr (AL) {
+        o[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pl[0]),
+                                                           o[0][nb], 0, 0, 0);
+        o[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pl[1]),
+                                                           o[1][nb], 0, 0, 0);
+      }
     }
   };
   // One tile, in 32-key parts.  Each part's scores are computed before the
@@ -407,12 +436,14 @@ __device__ __forceinline__ void prefill_item(
     const lds_char *vs = (const lds_char *)s_kv[buf][1];
     f32x4 sc[2][2][2];  // scores of two parts in flight: [slot][sub-tile][row tile]
     scores(ks, 0, sc[0]);
+    if constexpr (AL) add_bias(sc[0], kt, 0);
     if constexpr (kMasked) mask(sc[0], kt, 0);
     update_max(sc[0]);
 #pragma unroll
     for (int h = 0; h < kParts; ++h) {
       if (h + 1 < kParts) {
         scores(ks, h + 1, sc[(h + 1) & 1]);
+        if constexpr (AL) add_bias(sc[(h + 1) & 1], kt, h + 1);
         if constexpr (kMasked) mask(sc[(h + 1) & 1], kt, h + 1);
       }
       accumulate(sc[h & 1], vs, h);
@@ -479,29 +510,29 @@ __device__ __forceinline__ void prefill_item(
   }
 }
 
-template <int D, int BS, int G>
+template <int D, int BS, int G, bool AL>
 __global__ __launch_bounds__(kThreads, 2) void pa_prefill_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
     const int32_t *__restrict__ plan, int num_tokens, int num_heads, int num_kv_heads,
-    int max_blocks, int num_blocks, float scale_log2) {
+    int max_blocks, int num_blocks, float scale_log2, const float *__restrict__ alibi) {
   const int items = plan[0] * num_kv_heads;
   for (int k = 0;; ++k) {
     const int it = snake_item(k);
     if (it >= items) break;
     const int32_t *u = plan + kPlanHeader + 2 * (it / num_kv_heads);
-    prefill_item<D, BS, G>(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
-                           num_tokens, num_heads, num_kv_heads, max_blocks, num_blocks,
-                           scale_log2, u[0], u[1], it % num_kv_heads);
+    prefill_item<D, BS, G, AL>(out, q, k_pool, v_pool, block_tables, context_lens,
+                               query_start, num_tokens, num_heads, num_kv_heads, max_blocks,
+                               num_blocks, scale_log2, alibi, u[0], u[1], it % num_kv_heads);
     __syncthreads();  // the next item reuses the LDS
   }
 }
 
-template <int D, int BS, int G>
-int launch(const pa_internal::PrefillLaunch &a) {
+template <int D, int BS, int G, bool AL>
+int launch_al(const pa_internal::PrefillLaunch &a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  auto kernel = pa_prefill_gqa<D, BS, G>;
+  auto kernel = pa_prefill_gqa<D, BS, G, AL>;
   static const int per_cu =
       pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel), kThreads);
   // items <= num_tokens (each holds at least one chunk token)
@@ -511,8 +542,13 @@ int launch(const pa_internal::PrefillLaunch &a) {
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, st, a.out, a.q, a.k_pool, a.v_pool,
                      a.block_tables, a.context_lens, a.query_start, a.plan, a.num_tokens,
                      a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
-                     a.scale * kLog2e);
+                     a.scale * kLog2e, a.alibi);
   return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+template <int D, int BS, int G>
+int launch(const pa_internal::PrefillLaunch &a) {
+  return a.alibi ? launch_al<D, BS, G, true>(a) : launch_al<D, BS, G, false>(a);
 }
 
 template <int D, int BS>

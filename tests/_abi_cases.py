@@ -274,6 +274,82 @@ expect("prefill: workspace query rejects bad dims",
        lib.paged_attention_prefill_workspace_bytes(8, 16, ctypes.byref(pdims(head_dim=80))),
        _lib.SIZE_MAX)
 
+# ---- ALiBi entry points
+def decode_alibi(d, slopes=P, ptrs=None):
+    p = ptrs or [P] * 6
+    return lib.paged_attention_decode_alibi(*p, 32, ctypes.c_float(0.088), 16, slopes,
+                                            ctypes.byref(d))
+
+
+expect("decode alibi: empty batch, no slopes", decode_alibi(dims(), slopes=None), _lib.PA_OK)
+expect("decode alibi: slopes NULL", decode_alibi(dims(**ONE), slopes=None), _lib.PA_ERR_NULL)
+expect("decode alibi: slopes misaligned", decode_alibi(dims(**ONE), slopes=P + 2), _lib.PA_ERR_ALIGN)
+expect("decode alibi: bad dims first", decode_alibi(dims(head_dim=96, **ONE), slopes=None),
+       _lib.PA_ERR_UNSUPPORTED)
+expect("decode alibi: workspace missing", decode_alibi(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
+expect("decode alibi: dims NULL",
+       lib.paged_attention_decode_alibi(P, P, P, P, P, P, 32, ctypes.c_float(1), 16, P, None),
+       _lib.PA_ERR_NULL)
+
+
+def prefill_alibi(d, slopes=P):
+    return lib.paged_attention_prefill_alibi(*([P] * 7), 8, ctypes.c_float(0.088), 16, slopes,
+                                             ctypes.byref(d))
+
+
+expect("prefill alibi: empty step, no slopes", prefill_alibi(pdims(), slopes=None), _lib.PA_OK)
+expect("prefill alibi: slopes NULL", prefill_alibi(pdims(**ROWS), slopes=None), _lib.PA_ERR_NULL)
+expect("prefill alibi: slopes misaligned", prefill_alibi(pdims(**ROWS), slopes=P + 1),
+       _lib.PA_ERR_ALIGN)
+expect("prefill alibi: fp32 unsupported", prefill_alibi(pdims(dtype=_lib.PA_DTYPE_F32, **ROWS)),
+       _lib.PA_ERR_UNSUPPORTED)
+expect("prefill alibi: workspace missing", prefill_alibi(pdims(**ROWS)), _lib.PA_ERR_WORKSPACE)
+
+
+# ---- cache write with RoPE (num_tokens == 0: a wrong pass is a no-op)
+def rope_call(ptrs=None, r=None, **kw):
+    d = _lib.CacheDims()
+    d.num_tokens, d.num_kv_heads, d.head_dim, d.block_size = 0, 8, 128, 16
+    d.num_blocks, d.dtype = 100, _lib.PA_DTYPE_BF16
+    for k, v in kw.items():
+        setattr(d, k, v)
+    if r is None:
+        r = _lib.RopeDims()
+        r.num_heads, r.rot_dim, r.max_position, r.is_neox = 32, 128, 4096, 1
+    return lib.reshape_and_cache_rope(*(ptrs or [P] * 8), ctypes.byref(r), ctypes.byref(d))
+
+
+def rdims(**kw):
+    r = _lib.RopeDims()
+    r.num_heads, r.rot_dim, r.max_position, r.is_neox = 32, 128, 4096, 1
+    for k, v in kw.items():
+        setattr(r, k, v)
+    return r
+
+
+expect("rope: valid empty write", rope_call(), _lib.PA_OK)
+expect("rope: empty write accepts NULL pointers", rope_call(ptrs=[None] * 8), _lib.PA_OK)
+expect("rope: rope dims NULL",
+       lib.reshape_and_cache_rope(*([P] * 8), None, ctypes.byref(_lib.CacheDims())), _lib.PA_ERR_NULL)
+expect("rope: odd rot_dim", rope_call(r=rdims(rot_dim=63)), _lib.PA_ERR_SHAPE)
+expect("rope: rot_dim past head_dim", rope_call(r=rdims(rot_dim=256)), _lib.PA_ERR_SHAPE)
+expect("rope: rot_dim 24 (not whole chunks)", rope_call(r=rdims(rot_dim=24)), _lib.PA_ERR_UNSUPPORTED)
+expect("rope: rot_dim 8 fp32 is whole chunks",
+       rope_call(r=rdims(rot_dim=8), dtype=_lib.PA_DTYPE_F32), _lib.PA_OK)
+expect("rope: is_neox 2", rope_call(r=rdims(is_neox=2)), _lib.PA_ERR_SHAPE)
+expect("rope: reserved", rope_call(r=rdims(reserved=3)), _lib.PA_ERR_SHAPE)
+expect("rope: zero positions", rope_call(r=rdims(max_position=0)), _lib.PA_ERR_SHAPE)
+expect("rope: zero query heads", rope_call(r=rdims(num_heads=0)), _lib.PA_ERR_SHAPE)
+expect("rope: head_dim 96", rope_call(head_dim=96), _lib.PA_ERR_UNSUPPORTED)
+for i in range(8):
+    ptrs = [P] * 8
+    ptrs[i] = None
+    expect(f"rope: pointer {i} NULL", rope_call(ptrs=ptrs, num_tokens=1), _lib.PA_ERR_NULL)
+for i, bad in ((0, MIS), (1, MIS), (2, MIS), (3, MIS), (4, MIS), (5, P + 4), (6, P + 4), (7, P + 2)):
+    ptrs = [P] * 8
+    ptrs[i] = bad
+    expect(f"rope: pointer {i} misaligned", rope_call(ptrs=ptrs, num_tokens=1), _lib.PA_ERR_ALIGN)
+
 # ---- probe
 expect("probe NULL buffer", lib.pa_hbm_read_probe(None, 1024, P, None), _lib.PA_ERR_NULL)
 expect("probe size not a multiple of 16", lib.pa_hbm_read_probe(P, 1000, P, None), _lib.PA_ERR_SHAPE)

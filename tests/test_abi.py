@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
                  "paged_attention_decode_shared_prefix_workspace_bytes",
                  "paged_attention_decode_workspace_bytes",
                  "paged_attention_decode_partition_tokens", "paged_attention_prefill",
-                 "paged_attention_prefill_workspace_bytes", "pa_status_string"):
+                 "paged_attention_prefill_workspace_bytes", "paged_attention_decode_alibi",
+                 "paged_attention_prefill_alibi", "reshape_and_cache_rope", "pa_status_string"):
         assert want in names
 
 
@@ -63,12 +64,13 @@ def test_struct_layouts_match_the_header(built):
     os.makedirs(os.path.dirname(src), exist_ok=True)
     with open(src, "w") as f:
         f.write('#include <stdio.h>\n#include <stddef.h>\n#include "pagedattn.h"\n'
-                'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n",'
+                'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n",'
                 ' sizeof(pa_decode_dims), offsetof(pa_decode_dims, timing_events),'
                 ' sizeof(pa_cache_dims), offsetof(pa_cache_dims, stream),'
                 ' sizeof(pa_copy_dims), offsetof(pa_copy_dims, stream),'
                 ' sizeof(pa_prefill_dims), offsetof(pa_prefill_dims, workspace),'
-                ' offsetof(pa_prefill_dims, timing_events)); return 0;}\n')
+                ' offsetof(pa_prefill_dims, timing_events), sizeof(pa_rope_dims),'
+                ' offsetof(pa_rope_dims, reserved)); return 0;}\n')
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
     vals = list(map(int, subprocess.run([exe], capture_output=True, text=True,
                                         check=True).stdout.split()))
@@ -76,7 +78,8 @@ def test_struct_layouts_match_the_header(built):
                     ctypes.sizeof(_lib.CacheDims), _lib.CacheDims.stream.offset,
                     ctypes.sizeof(_lib.CopyDims), _lib.CopyDims.stream.offset,
                     ctypes.sizeof(_lib.PrefillDims), _lib.PrefillDims.workspace.offset,
-                    _lib.PrefillDims.timing_events.offset]
+                    _lib.PrefillDims.timing_events.offset, ctypes.sizeof(_lib.RopeDims),
+                    _lib.RopeDims.reserved.offset]
 
 
 def test_host_validation_rejects_bad_arguments(built):

@@ -1,0 +1,269 @@
+"""GPU parity of the ALiBi attention entry points and the cache write with
+rotary position embedding, through the C ABI, against the CPU oracle.
+
+Bars: attention within max-abs-error 1e-5 (fp32 KV) / 1e-2 (bf16 KV), as
+for plain decode; rotated values within one unit in the last place of the
+element type of the oracle's exact (float64) rotation plus the fp32
+rounding of the rotation (the kernel rotates in fp32 and rounds once);
+everything the rotation does not touch bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_457_amd import binding
+from paged_kv_cache_457_amd.device_inputs import to_device, to_host, upload
+from paged_kv_cache_457_amd.workloads import build_workload, make_config, make_prefill_config
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def alibi_slopes(H):
+    """The geometric slopes of the ALiBi paper for H heads."""
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], np.float32)
+
+
+def max_err(gpu_bits, ref, dtype):
+    g = oracle.widen(gpu_bits, dtype)
+    assert np.all(np.isfinite(g)), "non-finite output"
+    return float(np.max(np.abs(g - ref))) if g.size else 0.0
+
+
+def decode_alibi_step(w, slopes, partition_size=0):
+    dw = upload(w)
+    binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
+    binding.paged_attention_decode(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
+                                   dw.context_lens, scale=float(w.scale),
+                                   partition_size=partition_size,
+                                   alibi_slopes=torch.from_numpy(slopes).cuda())
+    torch.cuda.synchronize()
+    kp, vp = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping,
+                                      w.block_size)
+    ref = oracle.decode(w.q, kp, vp, w.block_tables, w.context_lens, w.num_kv_heads, w.scale,
+                        w.block_size, w.dtype, alibi_slopes=slopes)
+    return to_host(dw.out, w.dtype), ref
+
+
+# ------------------------------------------------------------ ALiBi decode
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_decode_alibi_configs(idx):
+    w = make_config(idx)
+    got, ref = decode_alibi_step(w, alibi_slopes(w.num_heads), w.partition_size)
+    err = max_err(got, ref, w.dtype)
+    say(f"c{idx} ALiBi decode: max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+VARIANTS = [("f32", 64, 16, 1), ("f32", 128, 32, 4), ("bf16", 64, 32, 1), ("bf16", 128, 16, 2),
+            ("bf16", 64, 16, 4), ("bf16", 128, 32, 8)]
+
+
+@pytest.mark.parametrize("dt,D,bs,G", VARIANTS, ids=[f"{a}-D{b}-bs{c}-G{d}" for a, b, c, d in VARIANTS])
+def test_decode_alibi_variants_and_partitions(dt, D, bs, G):
+    ctx = [1, bs - 1, bs + 1, 3 * bs + 5, 300, 777]
+    w = build_workload("al", ctx, 2 * G, 2, D, bs, dt, seed=D + bs + G,
+                       max_blocks_per_seq=(800 + bs - 1) // bs)
+    # steep slopes as well as the paper's: the bias dominates the logits
+    slopes = np.array([0.9, 0.003] * G, np.float32)[:2 * G]
+    for ps in (0, 4 * bs):
+        got, ref = decode_alibi_step(w, slopes, ps)
+        err = max_err(got, ref, dt)
+        say(f"{dt} D{D} bs{bs} G{G} partition {ps}: max abs err {err:.3e}")
+        assert err <= TOL[dt]
+
+
+def test_decode_alibi_zero_slopes_equal_plain_decode_bitwise():
+    w = make_config(3)
+    dw = upload(w)
+    binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
+    binding.paged_attention_decode(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
+                                   dw.context_lens, scale=float(w.scale))
+    torch.cuda.synchronize()
+    plain = to_host(dw.out, "bf16").copy()
+    binding.paged_attention_decode(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
+                                   dw.context_lens, scale=float(w.scale),
+                                   alibi_slopes=torch.zeros(w.num_heads, device="cuda"))
+    torch.cuda.synchronize()
+    assert to_host(dw.out, "bf16").tobytes() == plain.tobytes()
+
+
+# ----------------------------------------------------------- ALiBi prefill
+def prefill_alibi(w, slopes, rows=None):
+    dw = upload(w)
+    binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
+    binding.paged_attention_prefill(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
+                                    dw.context_lens, dw.query_start, scale=float(w.scale),
+                                    alibi_slopes=torch.from_numpy(slopes).cuda())
+    torch.cuda.synchronize()
+    kp, vp = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping,
+                                      w.block_size)
+    ref = oracle.prefill(w.q, kp, vp, w.block_tables, w.context_lens, w.query_start,
+                         w.num_kv_heads, w.scale, w.block_size, w.dtype, rows=rows,
+                         alibi_slopes=slopes)
+    return to_host(dw.out, "bf16"), ref
+
+
+def test_prefill_alibi_tiny():
+    w = make_prefill_config(1)
+    got, ref = prefill_alibi(w, alibi_slopes(w.num_heads))
+    err = max_err(got, ref, "bf16")
+    say(f"p1 ALiBi prefill: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("D,bs,G", [(64, 16, 1), (128, 32, 2), (128, 16, 4), (64, 32, 8)])
+def test_prefill_alibi_variants(D, bs, G):
+    cached, new = np.array([0, 70, 131]), np.array([150, 37, 1])
+    w = build_workload("pal", cached + new, 2 * G, 2, D, bs, "bf16", seed=D + G, new_tokens=new)
+    slopes = np.array([0.5, 0.01] * G, np.float32)[:2 * G]
+    got, ref = prefill_alibi(w, slopes)
+    err = max_err(got, ref, "bf16")
+    say(f"D{D} bs{bs} G{G} ALiBi prefill: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_prefill_alibi_full_size_sampled():
+    w = make_prefill_config(3)
+    qs = w.query_start
+    rng = np.random.default_rng(5)
+    rows = sorted({int(x) for s in range(w.num_seqs) if qs[s + 1] > qs[s]
+                   for x in [qs[s], qs[s + 1] - 1] + list(rng.integers(qs[s], qs[s + 1], 3))})
+    got, ref = prefill_alibi(w, alibi_slopes(w.num_heads), rows=rows)
+    g = oracle.widen(got, "bf16")[rows]
+    err = float(np.max(np.abs(g - ref[rows])))
+    say(f"p3 ALiBi prefill, {len(rows)} rows: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+# ------------------------------------------------- cache write with RoPE
+def rope_table(npos, rot_dim, base=10000.0):
+    inv = base ** (-np.arange(0, rot_dim, 2) / rot_dim)
+    ang = np.arange(npos)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def within_one_ulp(gpu_vals, ref, dtype):
+    """|gpu - ref| <= one unit in the last place of the element type at ref,
+    plus the fp32 rounding of the rotation itself (a few units of 2^-24 of
+    the pair's magnitude, which matters only where a c - b s cancels):
+    2^-21 times the largest magnitude in the head row."""
+    g = oracle.widen(gpu_vals, dtype)
+    mant = 7 if dtype == "bf16" else 23
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - mant)
+    bound = ulp + 2.0 ** -21 * np.max(np.abs(ref), axis=-1, keepdims=True)
+    bad = np.abs(g - ref) > bound
+    return int(bad.sum()), float(np.max(np.abs(g - ref) / bound))
+
+
+def positions_of(w):
+    """Each row's token position: the last appended positions of every
+    sequence (one row per sequence for a decode step)."""
+    if w.query_start is None:
+        return np.maximum(w.context_lens.astype(np.int64) - 1, 0)
+    qs, ctx = w.query_start, w.context_lens
+    pos = np.zeros(w.num_tokens, np.int64)
+    for s in range(w.num_seqs):
+        n = qs[s + 1] - qs[s]
+        pos[qs[s]:qs[s + 1]] = np.arange(ctx[s] - n, ctx[s])
+    return pos
+
+
+def run_rope(w, rot_dim, neox, positions=None, npos=None):
+    pos = positions_of(w) if positions is None else positions
+    table = rope_table(npos or int(pos.max()) + 1, rot_dim)
+    dw = upload(w)
+    q_dev = dw.q.clone()
+    binding.reshape_and_cache_rope(q_dev, dw.k_new, dw.v_new, dw.k_pool, dw.v_pool,
+                                   dw.slot_mapping, torch.from_numpy(pos).cuda(),
+                                   torch.from_numpy(table).cuda(), rot_dim, neox)
+    torch.cuda.synchronize()
+    return dw, q_dev, pos, table
+
+
+def check_rope(w, rot_dim, neox, tag):
+    dw, q_dev, pos, table = run_rope(w, rot_dim, neox)
+    dt = w.dtype
+    q_ref = oracle.rope(w.q, pos, table, rot_dim, neox, dt)
+    nbad, worst = within_one_ulp(to_host(q_dev, dt), q_ref, dt)
+    say(f"{tag}: q worst {worst:.2f} ulp, {nbad} beyond one")
+    assert nbad == 0
+    k_ref = oracle.rope(w.k_new, pos, table, rot_dim, neox, dt)
+    kp = to_host(dw.k_pool, dt)
+    vp = to_host(dw.v_pool, dt)
+    # rotated K at each written slot; V as is; every other slot untouched
+    _, vp_ref = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping,
+                                         w.block_size)
+    assert vp.tobytes() == vp_ref.tobytes()
+    written = np.zeros(kp.shape[0] * w.block_size, bool)
+    for i, slot in enumerate(w.slot_mapping):
+        if slot < 0:
+            continue
+        page, off = divmod(int(slot), w.block_size)
+        nbad, worst = within_one_ulp(kp[page, :, off, :][None], k_ref[i][None], dt)
+        assert nbad == 0, (i, worst)
+        written[slot] = True
+    before = w.k_pool.reshape(w.k_pool.shape[0], w.num_kv_heads, w.block_size, -1)
+    keep = ~written.reshape(-1, w.block_size)
+    for page in np.flatnonzero(keep.any(axis=1)):
+        offs = np.flatnonzero(keep[page])
+        assert kp[page][:, offs].tobytes() == before[page][:, offs].tobytes()
+
+
+@pytest.mark.parametrize("neox", [True, False])
+def test_rope_cache_write_decode_step(neox):
+    check_rope(make_config(3), 128, neox, f"c3 decode step, neox={neox}")
+
+
+@pytest.mark.parametrize("dt,D,rot", [("bf16", 128, 64), ("bf16", 64, 64), ("f32", 128, 128),
+                                      ("f32", 64, 24)])
+def test_rope_cache_write_prefill_rows(dt, D, rot):
+    cached, new = np.array([0, 100, 37]), np.array([60, 25, 90])
+    w = build_workload("rope", cached + new, 8, 4, D, 16, dt, seed=D + rot, new_tokens=new)
+    for neox in (True, False):
+        check_rope(w, rot, neox, f"{dt} D{D} rot {rot} neox={neox}")
+
+
+def test_rope_out_of_table_position_skips_token():
+    w = build_workload("ropeskip", [5, 9, 20, 3], 8, 4, 64, 16, "bf16", seed=23)
+    pos = positions_of(w)
+    pos[1] = 10_000          # past the table: skipped
+    pos[2] = -3              # negative: skipped
+    dw, q_dev, _, table = run_rope(w, 64, True, positions=pos, npos=64)
+    q = to_host(q_dev, "bf16")
+    assert q[1].tobytes() == w.q[1].tobytes() and q[2].tobytes() == w.q[2].tobytes()
+    kp = to_host(dw.k_pool, "bf16")
+    for i in (1, 2):
+        page, off = divmod(int(w.slot_mapping[i]), 16)
+        assert kp[page, :, off].tobytes() == w.k_pool[page, :, off].tobytes()
+    q_ref = oracle.rope(w.q[[0, 3]], pos[[0, 3]], table, 64, True, "bf16")
+    assert within_one_ulp(q[[0, 3]], q_ref, "bf16")[0] == 0
+
+
+def test_rope_then_decode_matches_oracle():
+    """The fused write feeds decode: attention over the rotated cache with
+    the rotated q equals the oracle's."""
+    w = make_config(3)
+    dw, q_dev, pos, table = run_rope(w, 128, True)
+    binding.paged_attention_decode(dw.out, q_dev, dw.k_pool, dw.v_pool, dw.block_tables,
+                                   dw.context_lens, scale=float(w.scale))
+    torch.cuda.synchronize()
+    q_rot = oracle.rope(w.q, pos, table, 128, True, "bf16")
+    # the cached K and q the oracle attends with are the rounded rotations
+    q_bits = to_host(q_dev, "bf16")
+    assert within_one_ulp(q_bits, q_rot, "bf16")[0] == 0
+    kp_bits = to_host(dw.k_pool, "bf16")
+    vp_bits = to_host(dw.v_pool, "bf16")
+    ref = oracle.decode(q_bits, kp_bits, vp_bits, w.block_tables, w.context_lens,
+                        w.num_kv_heads, w.scale, w.block_size, "bf16")
+    err = max_err(to_host(dw.out, "bf16"), ref, "bf16")
+    say(f"c3 RoPE write then decode: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
