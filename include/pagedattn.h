@@ -339,8 +339,8 @@ typedef struct pa_rope_dims {
  * rot_dim/2 + j]: (a c - b s, b c + a s), in fp32, rounded to the element
  * type (bf16: nearest even).  Pair j is entries (j, j + rot_dim/2) when
  * is_neox, else (2j, 2j + 1); entries past rot_dim are unchanged.
- * cos_sin: device fp32 [max_position, rot_dim], filled by the caller (for
- * example cos and sin of pos * base^(-2j/rot_dim)).  A token whose position
+ * cos_sin: device fp32 [max_position, rot_dim], 16-byte aligned, filled by
+ * the caller (for example cos and sin of pos * base^(-2j/rot_dim)).  A token whose position
  * is outside [0, max_position) is skipped entirely (q untouched, nothing
  * written).  positions: device int64 [num_tokens], 8-byte aligned.
  */

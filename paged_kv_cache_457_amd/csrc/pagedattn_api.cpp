@@ -437,7 +437,7 @@ int reshape_and_cache_rope(void *q, const void *k, const void *v, void *k_pool, 
     return PA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) ||
       !aligned(v_pool, 16) || !aligned(slot_mapping, 8) || !aligned(positions, 8) ||
-      !aligned(cos_sin, 4))
+      !aligned(cos_sin, 16))
     return PA_ERR_ALIGN;
   pa_internal::RopeLaunch r{};
   pa_internal::CacheLaunch &a = r.cache;

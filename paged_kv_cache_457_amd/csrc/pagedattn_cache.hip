@@ -53,6 +53,30 @@ __global__ __launch_bounds__(256) void pa_reshape_and_cache(
 // q is rotated in place; K (rotated) and V go to the page slot.  A token
 // whose position is outside the table is skipped, and one whose slot is
 // negative or past the pool gets its q rotated but writes no K/V.
+// n consecutive floats from p, in 16- or 8-byte steps as n and the
+// alignment of p (16 bytes when n is a multiple of 4, else 8) allow
+template <int N>
+__device__ __forceinline__ void load_floats(const float *p, float (&o)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float4 v = *reinterpret_cast<const float4 *>(p + i);
+      o[i] = v.x;
+      o[i + 1] = v.y;
+      o[i + 2] = v.z;
+      o[i + 3] = v.w;
+    }
+  } else {
+    static_assert(N % 2 == 0, "pairs of floats");
+#pragma unroll
+    for (int i = 0; i < N; i += 2) {
+      const float2 v = *reinterpret_cast<const float2 *>(p + i);
+      o[i] = v.x;
+      o[i + 1] = v.y;
+    }
+  }
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void pa_reshape_and_cache_rope(
     u32x4 *__restrict__ q, const u32x4 *__restrict__ k, const u32x4 *__restrict__ v,
@@ -68,55 +92,69 @@ __global__ __launch_bounds__(256) void pa_reshape_and_cache_rope(
   const bool write = slot >= 0 && slot < num_slots;
   const int64_t page = write ? slot / block_size : 0;
   const int64_t off = write ? slot - page * block_size : 0;
+  // the table row: rot_dim / 2 cosines then as many sines (rot_dim is a
+  // multiple of 2 * E and the table 16-byte aligned, so every group of
+  // values a unit reads is aligned to its size)
   const float *cs = cos_sin + pos * rot_dim;
   const int half = rot_dim / 2;
   const int rot_chunks = rot_dim / E;
-  const int rows = num_heads + num_kv_heads;
-  for (int u = threadIdx.x; u < rows * row_chunks; u += blockDim.x) {
-    const int r = u / row_chunks;
-    const int c = u - r * row_chunks;
+  // units of a row: split halves take chunk pairs (j, j + rot_chunks / 2),
+  // interleaved pairs one chunk each; chunks past rot_dim pass through
+  const int units = neox ? row_chunks - rot_chunks / 2 : row_chunks;
+  const int rows = num_heads + (write ? num_kv_heads : 0);
+  for (int u = threadIdx.x; u < rows * units; u += blockDim.x) {
+    const int r = u / units;
+    const int j = u - r * units;
     const bool is_q = r < num_heads;
     const int g = r - num_heads;
-    if (!is_q && !write) continue;
     u32x4 *qrow = q + ((size_t)t * num_heads + r) * row_chunks;
     const u32x4 *krow = k + ((size_t)t * num_kv_heads + g) * row_chunks;
     u32x4 *prow = k_pool + (((size_t)page * num_kv_heads + g) * block_size + off) * row_chunks;
-    if (!is_q) {
-      v_pool[(((size_t)page * num_kv_heads + g) * block_size + off) * row_chunks + c] =
-          v[((size_t)t * num_kv_heads + g) * row_chunks + c];
-    }
-    if (c >= rot_chunks) {
-      if (!is_q) prow[c] = krow[c];
-      continue;
-    }
+    const u32x4 *src = is_q ? qrow : krow;
+    u32x4 *dst = is_q ? qrow : prow;
     if (neox) {
-      if (c >= rot_chunks / 2) continue;  // the partner of chunk c - rot_chunks / 2
-      const int c2 = c + rot_chunks / 2;
-      float a[E], b[E];
-      T::unpack(is_q ? qrow[c] : krow[c], a);
-      T::unpack(is_q ? qrow[c2] : krow[c2], b);
+      if (j >= rot_chunks / 2) {  // past rot_dim
+        if (!is_q) prow[j + rot_chunks / 2] = krow[j + rot_chunks / 2];
+        continue;
+      }
+      const int c2 = j + rot_chunks / 2;
+      float a[E], b[E], co[E], si[E];
+      T::unpack(src[j], a);
+      T::unpack(src[c2], b);
+      load_floats(cs + j * E, co);
+      load_floats(cs + half + j * E, si);
       float ra[E], rb[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float co = cs[c * E + e], si = cs[half + c * E + e];
-        ra[e] = a[e] * co - b[e] * si;
-        rb[e] = b[e] * co + a[e] * si;
+        ra[e] = a[e] * co[e] - b[e] * si[e];
+        rb[e] = b[e] * co[e] + a[e] * si[e];
       }
-      u32x4 *dst = is_q ? qrow : prow;
-      dst[c] = T::pack(ra);
+      dst[j] = T::pack(ra);
       dst[c2] = T::pack(rb);
     } else {
-      float x[E], y[E];
-      T::unpack(is_q ? qrow[c] : krow[c], x);
-#pragma unroll
-      for (int e = 0; e < E; e += 2) {
-        const int i = (c * E + e) / 2;
-        const float co = cs[i], si = cs[half + i];
-        y[e] = x[e] * co - x[e + 1] * si;
-        y[e + 1] = x[e + 1] * co + x[e] * si;
+      if (j >= rot_chunks) {
+        if (!is_q) prow[j] = krow[j];
+        continue;
       }
-      (is_q ? qrow : prow)[c] = T::pack(y);
+      // chunk j holds pairs j*E/2 .. j*E/2 + E/2 - 1
+      float x[E], y[E], co[E / 2], si[E / 2];
+      T::unpack(src[j], x);
+      load_floats(cs + j * (E / 2), co);
+      load_floats(cs + half + j * (E / 2), si);
+#pragma unroll
+      for (int e = 0; e < E / 2; ++e) {
+        y[2 * e] = x[2 * e] * co[e] - x[2 * e + 1] * si[e];
+        y[2 * e + 1] = x[2 * e + 1] * co[e] + x[2 * e] * si[e];
+      }
+      dst[j] = T::pack(y);
     }
+  }
+  if (!write) return;
+  for (int u = threadIdx.x; u < num_kv_heads * row_chunks; u += blockDim.x) {
+    const int g = u / row_chunks;
+    const int c = u - g * row_chunks;
+    v_pool[(((size_t)page * num_kv_heads + g) * block_size + off) * row_chunks + c] =
+        v[((size_t)t * num_kv_heads + g) * row_chunks + c];
   }
 }
 

@@ -345,7 +345,7 @@ for i in range(8):
     ptrs = [P] * 8
     ptrs[i] = None
     expect(f"rope: pointer {i} NULL", rope_call(ptrs=ptrs, num_tokens=1), _lib.PA_ERR_NULL)
-for i, bad in ((0, MIS), (1, MIS), (2, MIS), (3, MIS), (4, MIS), (5, P + 4), (6, P + 4), (7, P + 2)):
+for i, bad in ((0, MIS), (1, MIS), (2, MIS), (3, MIS), (4, MIS), (5, P + 4), (6, P + 4), (7, P + 8)):
     ptrs = [P] * 8
     ptrs[i] = bad
     expect(f"rope: pointer {i} misaligned", rope_call(ptrs=ptrs, num_tokens=1), _lib.PA_ERR_ALIGN)
