@@ -71,7 +71,9 @@ typedef struct pa_decode_dims {
   int32_t partition_size;      /* tokens per split-K partition, a multiple of
                                   block_size, at most 256 pages; 0 = default: no
                                   split when max_blocks_per_seq * block_size
-                                  <= 2048, else 1024 */
+                                  <= 2048, else the largest of 2048, 1024, 512,
+                                  256 that gives num_seqs * partitions >= 128
+                                  (256 when none does) */
   int32_t reserved;            /* must be 0 */
   void *workspace;             /* device scratch, caller-owned, 16-byte aligned, at
                                   least paged_attention_decode_workspace_bytes();

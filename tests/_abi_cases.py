@@ -99,8 +99,10 @@ def plan_bytes(S, parts):
 
 need_d = dims(num_seqs=4, max_blocks_per_seq=256)
 need = lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(need_d))
+# 4 sequences of up to 4096 tokens: the default halves 2048 -> 256 tokens
+# looking for 128 units and stops at 256: 16 partitions
 expect("workspace bytes formula", need,
-       plan_bytes(4, 4) + 4 * 32 * ((256 * 16 + 1023) // 1024) * (128 + 2) * 4)
+       plan_bytes(4, 16) + 4 * 32 * 16 * (128 + 2) * 4)
 expect("workspace missing", decode(dims(num_seqs=4)), _lib.PA_ERR_WORKSPACE)
 expect("workspace missing, one partition", decode(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
 expect("workspace too small",
@@ -129,8 +131,18 @@ expect("workspace query rejects NULL", lib.paged_attention_decode_workspace_byte
 pt = lib.paged_attention_decode_partition_tokens
 expect("default partition: table of 2048 tokens is one partition",
        pt(16, ctypes.byref(dims(max_blocks_per_seq=128))), 2048)
-expect("default partition: larger tables split by 1024", pt(16, ctypes.byref(dims(max_blocks_per_seq=129))), 1024)
-expect("default partition at bs 32", pt(32, ctypes.byref(dims(max_blocks_per_seq=1024))), 1024)
+expect("default partition: large batch, long runs",
+       pt(16, ctypes.byref(dims(num_seqs=256, max_blocks_per_seq=512))), 2048)
+expect("default partition: 8 x 32768 tokens at bs 32 keeps 2048",
+       pt(32, ctypes.byref(dims(num_seqs=8, max_blocks_per_seq=1024))), 2048)
+expect("default partition: 4 x 32768 halves once",
+       pt(32, ctypes.byref(dims(num_seqs=4, max_blocks_per_seq=1024))), 1024)
+expect("default partition: one long sequence goes to the 256-token floor",
+       pt(32, ctypes.byref(dims(num_seqs=1, max_blocks_per_seq=1024))), 256)
+expect("default partition: just past one partition, 64 x 2 units",
+       pt(16, ctypes.byref(dims(num_seqs=64, max_blocks_per_seq=129))), 2048)
+expect("default partition: just past one partition, 16 sequences halve to 256",
+       pt(16, ctypes.byref(dims(num_seqs=16, max_blocks_per_seq=129))), 256)
 expect("explicit partition", pt(32, ctypes.byref(dims(max_blocks_per_seq=1024, partition_size=512))), 512)
 expect("partition query rejects bad dims", pt(16, ctypes.byref(dims(head_dim=80))), -1)
 expect("workspace for a one-partition default table",
