@@ -50,7 +50,7 @@ def parse():
                                      "swap-in"],
                     default="decode-step",
                     help="decode-step (default): the hot path; prefill: a multi-token step "
-                         "(--config picks prefill workload 1..3); cache-rope: the cache write "
+                         "(--config picks prefill workload 1..4); cache-rope: the cache write "
                          "with rotary embedding fused in, on prefill workload --config; copy / "
                          "swap-out / swap-in: copy_blocks within the device pool, to a pinned "
                          "host pool, back")
@@ -340,8 +340,12 @@ def bench_prefill(args):
     w = make_prefill_config(args.config, args.seed)
     dw = upload(w)
     stream = torch.cuda.current_stream()
+    ps = args.partition_size or 0
+    args.effective_partition = binding.paged_attention_prefill_partition_tokens(
+        dw.q, dw.k_pool, dw.block_tables, dw.query_start, ps)
     ws = torch.empty(max(binding.paged_attention_prefill_workspace_bytes(
-        dw.q, dw.k_pool, dw.block_tables, dw.query_start), 16), dtype=torch.uint8, device="cuda")
+        dw.q, dw.k_pool, dw.block_tables, dw.query_start, ps), 16), dtype=torch.uint8,
+        device="cuda")
     scale = float(w.scale)
     slopes = torch.from_numpy(alibi_slopes(w.num_heads)).cuda() if args.alibi else None
 
@@ -349,7 +353,8 @@ def bench_prefill(args):
         binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
         binding.paged_attention_prefill(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
                                         dw.context_lens, dw.query_start, scale=scale,
-                                        workspace=ws, timing_events=events, alibi_slopes=slopes)
+                                        workspace=ws, timing_events=events, alibi_slopes=slopes,
+                                        partition_size=ps)
 
     for _ in range(args.warmup):
         step()
@@ -385,7 +390,6 @@ def bench_prefill(args):
     flops = w.prefill_flops()
     tflops = flops / (k_ms * 1e-3) / 1e12
     kv_bytes = w.kv_bytes()
-    args.effective_partition = 0
     result = {
         "metric": "prefill-attn tokens/s + matrix-core TFLOP/s (% of bf16 peak)",
         "value": round(w.num_tokens / (ms_step * 1e-3), 1),
@@ -411,6 +415,7 @@ def bench_prefill(args):
             "block_size": w.block_size,
             "sum_context_tokens": int(w.context_lens.sum()),
             "entry": "paged_attention_prefill_alibi" if args.alibi else "paged_attention_prefill",
+            "partition_size": args.effective_partition,
             "parallelism": "single GPU",
         },
         "flops_per_step": flops,

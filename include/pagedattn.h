@@ -222,10 +222,17 @@ typedef struct pa_prefill_dims {
   int32_t max_blocks_per_seq;  /* columns of block_tables, >= 1 */
   int32_t num_blocks;          /* pages in each pool, >= 1 */
   int32_t dtype;               /* PA_DTYPE_BF16 (the only type built) */
-  int32_t reserved;            /* must be 0 */
+  int32_t partition_size;      /* keys per split-K partition, a positive multiple
+                                  of 64; 0 = default: no split when the step has
+                                  at least 1024 (block, kv-head) work items, else
+                                  partitions of max(1024, ceil(capacity / parts))
+                                  keys with parts = ceil(1024 / items), capacity =
+                                  max_blocks_per_seq * block_size (no split when
+                                  that is not below the capacity) */
   void *workspace;             /* device scratch, caller-owned, 16-byte aligned, at
                                   least paged_attention_prefill_workspace_bytes();
-                                  required whenever num_tokens > 0 (work plan) */
+                                  required whenever num_tokens > 0 (work plan and,
+                                  with a split, the partials) */
   size_t workspace_bytes;
   void *stream;                /* hipStream_t */
   void *timing_events[2];      /* optional hipEvent_t pair around the attention pass */
@@ -264,11 +271,13 @@ typedef struct pa_prefill_dims {
  * significant bits), their sum is kept in fp32.  Results are rounded to
  * nearest even.
  *
- * Launches, all on dims->stream: a one-workgroup plan kernel (splits every
- * chunk into blocks of 128 / group consecutive tokens and orders them by the
- * keys they read, most first, into the workspace) and the attention pass
- * (timing_events bracket this one).  The result does not depend on the
- * order work items run in.
+ * Launches, all on dims->stream: a one-workgroup plan kernel (cuts every
+ * chunk into blocks of 256 / group consecutive tokens, and with a split each
+ * block's keys into partitions, and orders the items by the keys they read,
+ * most first, into the workspace), the attention pass (timing_events
+ * bracket this one) and, with a split, a reduce kernel that merges each
+ * row's partitions by log-sum-exp.  The result does not depend on the order
+ * work items run in.
  */
 int paged_attention_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
                             const int32_t *block_tables, const int32_t *context_lens,
@@ -288,12 +297,22 @@ int paged_attention_prefill_alibi(void *out, const void *q, const void *k_pool,
                                   const float *alibi_slopes, const pa_prefill_dims *dims);
 
 /*
- * Workspace bytes of paged_attention_prefill: the work plan,
- *   4 * (4 + 2 * num_tokens) rounded up to 256.
+ * Workspace bytes of paged_attention_prefill, with P the partitions of the
+ * capacity (1 without a split):
+ *   plan 4 * (4 + 3 * num_tokens * P + num_tokens) rounded up to 256, plus,
+ *   when P > 1, partials num_tokens * num_heads * P * (head_dim + 2) * 4.
  * 0 when num_tokens is 0; SIZE_MAX for invalid shapes.
  */
 size_t paged_attention_prefill_workspace_bytes(int32_t num_kv_heads, int32_t block_size,
                                                const pa_prefill_dims *dims);
+
+/*
+ * The key partition paged_attention_prefill uses for these shapes
+ * (dims->partition_size, or the default when that is 0; 0 = no split);
+ * -1 for invalid shapes.
+ */
+int32_t paged_attention_prefill_partition_tokens(int32_t num_kv_heads, int32_t block_size,
+                                                 const pa_prefill_dims *dims);
 
 /* Shapes and launch context of reshape_and_cache. */
 typedef struct pa_cache_dims {

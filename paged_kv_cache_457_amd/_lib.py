@@ -50,7 +50,7 @@ class PrefillDims(ctypes.Structure):
         ("max_blocks_per_seq", ctypes.c_int32),
         ("num_blocks", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("partition_size", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
@@ -124,6 +124,8 @@ SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
         ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(PrefillDims)]),
     "paged_attention_prefill_workspace_bytes": (ctypes.c_size_t, [
+        ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(PrefillDims)]),
+    "paged_attention_prefill_partition_tokens": (ctypes.c_int32, [
         ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(PrefillDims)]),
     "reshape_and_cache": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,

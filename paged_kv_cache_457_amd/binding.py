@@ -211,7 +211,7 @@ def paged_attention_decode_shared_prefix_workspace_bytes(q, k_pool, block_tables
 
 
 def prefill_dims(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tensor,
-                 query_start: torch.Tensor) -> _lib.PrefillDims:
+                 query_start: torch.Tensor, partition_size: int = 0) -> _lib.PrefillDims:
     T, H, D = q.shape
     d = _lib.PrefillDims()
     d.num_seqs = query_start.shape[0] - 1
@@ -219,16 +219,32 @@ def prefill_dims(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tens
     d.max_blocks_per_seq = block_tables.shape[1]
     d.num_blocks = k_pool.shape[0]
     d.dtype = _DTYPES[q.dtype]
+    d.partition_size = partition_size
     return d
 
 
 def paged_attention_prefill_workspace_bytes(q: torch.Tensor, k_pool: torch.Tensor,
                                             block_tables: torch.Tensor,
-                                            query_start: torch.Tensor) -> int:
-    d = prefill_dims(q, k_pool, block_tables, query_start)
+                                            query_start: torch.Tensor,
+                                            partition_size: int = 0) -> int:
+    d = prefill_dims(q, k_pool, block_tables, query_start, partition_size)
     n = _lib.load().paged_attention_prefill_workspace_bytes(k_pool.shape[1], k_pool.shape[2],
                                                             ctypes.byref(d))
     if n == _lib.SIZE_MAX:
+        raise ValueError("invalid shapes for paged_attention_prefill")
+    return n
+
+
+def paged_attention_prefill_partition_tokens(q: torch.Tensor, k_pool: torch.Tensor,
+                                             block_tables: torch.Tensor,
+                                             query_start: torch.Tensor,
+                                             partition_size: int = 0) -> int:
+    """Keys per split-K partition that paged_attention_prefill uses for these
+    shapes (0: no split)."""
+    d = prefill_dims(q, k_pool, block_tables, query_start, partition_size)
+    n = _lib.load().paged_attention_prefill_partition_tokens(k_pool.shape[1], k_pool.shape[2],
+                                                             ctypes.byref(d))
+    if n < 0:
         raise ValueError("invalid shapes for paged_attention_prefill")
     return n
 
@@ -239,11 +255,14 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Te
                             scale: Optional[float] = None,
                             workspace: Optional[torch.Tensor] = None, stream=None,
                             timing_events: Sequence = (None, None),
-                            alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
+                            alibi_slopes: Optional[torch.Tensor] = None,
+                            partition_size: int = 0) -> torch.Tensor:
     """out[T,H,D] <- multi-token (prefill / chunked prefill) attention over
     the paged cache (see paged_attention_prefill in include/pagedattn.h);
-    query_start int32 [S + 1] gives each sequence's first row of q.  A
-    workspace (work plan) is allocated here when none is given."""
+    query_start int32 [S + 1] gives each sequence's first row of q.
+    partition_size: keys per split-K partition (0: the library's choice).  A
+    workspace (work plan, split-K partials) is allocated here when none is
+    given."""
     if q.dtype != torch.bfloat16:
         raise ValueError("prefill attention is built for bf16")
     for name, t in (("out", out), ("k_pool", k_pool), ("v_pool", v_pool)):
@@ -265,7 +284,7 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Te
     hkv, bs = k_pool.shape[1], k_pool.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    d = prefill_dims(q, k_pool, block_tables, query_start)
+    d = prefill_dims(q, k_pool, block_tables, query_start, partition_size)
     lib = _lib.load()
     need = lib.paged_attention_prefill_workspace_bytes(hkv, bs, ctypes.byref(d))
     if need == _lib.SIZE_MAX:

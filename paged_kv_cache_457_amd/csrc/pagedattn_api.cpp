@@ -106,11 +106,36 @@ size_t prefix_workspace_bytes(int32_t block_size, const pa_decode_dims *d) {
   return plan + (size_t)d->num_seqs * d->num_heads * ms * (size_t)(d->head_dim + 2) * sizeof(float);
 }
 
+// Prefill split-K default: enough (block, kv-head) items to keep every CU
+// busy several rounds without splitting, else partitions that reach that
+// many, of at least kMinPrefillPartition keys.
+constexpr int64_t kPrefillTargetItems = 1024;
+constexpr int kMinPrefillPartition = 1024;
+
+int prefill_partition_tokens(int32_t num_kv_heads, int32_t block_size, const pa_prefill_dims *d) {
+  const int64_t cap = (int64_t)d->max_blocks_per_seq * block_size;
+  if (d->partition_size != 0) return d->partition_size >= cap ? 0 : d->partition_size;
+  const int tok = pa_internal::kPrefillRows / (d->num_heads / num_kv_heads);
+  const int64_t items = ((int64_t)d->num_tokens + tok - 1) / tok * num_kv_heads;
+  if (items >= kPrefillTargetItems || items == 0) return 0;
+  const int64_t parts = (kPrefillTargetItems + items - 1) / items;
+  int64_t kp = ((cap + parts - 1) / parts + 63) / 64 * 64;
+  if (kp < kMinPrefillPartition) kp = kMinPrefillPartition;
+  return kp >= cap ? 0 : (int)kp;
+}
+
+int prefill_max_parts(int32_t num_kv_heads, int32_t block_size, const pa_prefill_dims *d) {
+  const int pt = prefill_partition_tokens(num_kv_heads, block_size, d);
+  const int64_t cap = (int64_t)d->max_blocks_per_seq * block_size;
+  return pt ? (int)((cap + pt - 1) / pt) : 1;
+}
+
 // Shape checks shared by the prefill call and its workspace query.
 int check_prefill_dims(int32_t num_kv_heads, int32_t block_size, const pa_prefill_dims *d) {
   if (!d) return PA_ERR_NULL;
   if (d->num_seqs < 0 || d->num_tokens < 0 || d->num_heads < 1 || num_kv_heads < 1 ||
-      d->max_blocks_per_seq < 1 || d->num_blocks < 1 || d->reserved != 0)
+      d->max_blocks_per_seq < 1 || d->num_blocks < 1 || d->partition_size < 0 ||
+      d->partition_size % 64 != 0)
     return PA_ERR_SHAPE;
   if (d->num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   if (d->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;  // matrix cores: bf16 only
@@ -118,16 +143,27 @@ int check_prefill_dims(int32_t num_kv_heads, int32_t block_size, const pa_prefil
       !supported_group(d->num_heads / num_kv_heads))
     return PA_ERR_UNSUPPORTED;
   if ((int64_t)d->max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
-  // work items (item, kv-head) are int32; there are at most num_tokens items
-  if ((int64_t)d->num_tokens * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
   // rows of a sequence cannot exist without the sequence
   if (d->num_tokens > 0 && d->num_seqs == 0) return PA_ERR_SHAPE;
+  // work items (block, partition, kv-head) are int32; there are at most
+  // num_tokens * partitions of them
+  const int64_t parts = prefill_max_parts(num_kv_heads, block_size, d);
+  if ((int64_t)d->num_tokens * parts * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
   return PA_OK;
 }
 
-size_t prefill_plan_bytes(int num_tokens) {
-  const size_t ints = (size_t)kPlanHeader + 2 * (size_t)num_tokens;
+size_t prefill_plan_bytes(int num_tokens, int parts) {
+  const size_t ints = (size_t)kPlanHeader +
+                      (size_t)pa_internal::kPrefillPlanRecord * num_tokens * parts + num_tokens;
   return (ints * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+size_t prefill_workspace_bytes(int32_t num_kv_heads, int32_t block_size, const pa_prefill_dims *d) {
+  const int parts = prefill_max_parts(num_kv_heads, block_size, d);
+  size_t b = prefill_plan_bytes(d->num_tokens, parts);
+  if (parts > 1)
+    b += (size_t)d->num_tokens * d->num_heads * parts * (d->head_dim + 2) * sizeof(float);
+  return b;
 }
 
 int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
@@ -320,7 +356,13 @@ size_t paged_attention_prefill_workspace_bytes(int32_t num_kv_heads, int32_t blo
                                                const pa_prefill_dims *dims) {
   if (check_prefill_dims(num_kv_heads, block_size, dims) != PA_OK) return SIZE_MAX;
   if (dims->num_tokens == 0) return 0;
-  return prefill_plan_bytes(dims->num_tokens);
+  return prefill_workspace_bytes(num_kv_heads, block_size, dims);
+}
+
+int32_t paged_attention_prefill_partition_tokens(int32_t num_kv_heads, int32_t block_size,
+                                                 const pa_prefill_dims *dims) {
+  if (check_prefill_dims(num_kv_heads, block_size, dims) != PA_OK) return -1;
+  return prefill_partition_tokens(num_kv_heads, block_size, dims);
 }
 
 int paged_attention_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
@@ -363,9 +405,12 @@ int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_poo
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
     return PA_ERR_ALIGN;
-  if (!dims->workspace || dims->workspace_bytes < prefill_plan_bytes(dims->num_tokens) ||
+  if (!dims->workspace ||
+      dims->workspace_bytes < prefill_workspace_bytes(num_kv_heads, block_size, dims) ||
       !aligned(dims->workspace, 16))
     return PA_ERR_WORKSPACE;
+  const int parts = prefill_max_parts(num_kv_heads, block_size, dims);
+  const size_t pb = prefill_plan_bytes(dims->num_tokens, parts);
   pa_internal::PrefillLaunch a{};
   a.out = out;
   a.q = q;
@@ -375,6 +420,14 @@ int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_poo
   a.context_lens = context_lens;
   a.query_start = query_start;
   a.plan = static_cast<int32_t *>(dims->workspace);
+  a.nparts = a.plan + kPlanHeader +
+             (size_t)pa_internal::kPrefillPlanRecord * dims->num_tokens * parts;
+  a.part_tokens = prefill_partition_tokens(num_kv_heads, block_size, dims);
+  a.max_parts = parts;
+  if (parts > 1) {
+    a.ws_acc = reinterpret_cast<float *>(static_cast<char *>(dims->workspace) + pb);
+    a.ws_ml = a.ws_acc + (size_t)dims->num_tokens * dims->num_heads * parts * dims->head_dim;
+  }
   a.num_seqs = dims->num_seqs;
   a.num_tokens = dims->num_tokens;
   a.num_heads = dims->num_heads;

@@ -18,6 +18,10 @@ constexpr int kMaxDevices = 64;
 // unit serves, and the ints of one unit record in the plan.
 constexpr int kPrefixRows = 32;
 constexpr int kPrefixUnitInts = 5;
+// query rows of a prefill work item (token x head of one kv-head's group),
+// and ints per prefill plan item
+constexpr int kPrefillRows = 256;
+constexpr int kPrefillPlanRecord = 3;
 
 struct DecodeLaunch {
   void *out;
@@ -59,6 +63,11 @@ struct PrefillLaunch {
   const int32_t *context_lens;
   const int32_t *query_start;  // [num_seqs + 1]
   int32_t *plan;               // item list written by the plan kernel
+  int32_t *nparts;             // [num_tokens] key partitions of each row's block
+  float *ws_ml;                // [num_tokens, num_heads, max_parts, 2]
+  float *ws_acc;               // [num_tokens, num_heads, max_parts, head_dim]
+  int part_tokens = 0;         // keys per partition (a multiple of 64), 0: no split
+  int max_parts = 1;
   int num_seqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size;
   int max_blocks, num_blocks;
   float scale;

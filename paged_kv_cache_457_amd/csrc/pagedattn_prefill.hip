@@ -51,9 +51,11 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr int kWaves = 8;           // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // query rows of a work item
+static_assert(kRows == pa_internal::kPrefillRows, "rows per work item");
 constexpr int kKeys = 64;           // keys per LDS tile
 constexpr float kRescaleLog2 = 8.f; // lazy rescale threshold of the running max
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanRecord = pa_internal::kPrefillPlanRecord;  // ints per plan item
 constexpr int kBuckets = kPlanThreads - 1;  // plan size classes (key tiles); the last is open-ended
 
 template <int D, int BS, int G>
@@ -87,32 +89,50 @@ __device__ __forceinline__ int swz(int r, int c) {
 }
 
 // ------------------------------------------------------------------ plan
-// One workgroup.  plan[0] = item count; item k is plan[kPlanHeader + 2k]
-// (sequence) and plan[kPlanHeader + 2k + 1] (first chunk token), items
-// ordered by the key tiles they read, most first.  Every chunk token is in
-// exactly one item, so there are at most num_tokens items.
+// One workgroup.  Every chunk is cut into blocks of `tok` consecutive
+// tokens; with key partitions of kpart tokens (a multiple of kKeys; 0: no
+// split) each block is further cut by its keys, one item per partition
+// that holds keys the block sees.  plan[0] = item count; item k is
+// plan[kPlanHeader + 3k ..] = (sequence, first chunk token, partition),
+// items ordered by the key tiles they read, most first.  With a split,
+// nparts[row] is the number of partitions of the row's block (1: the item
+// writes the row's output itself).  Valid chunks give at most max_items
+// items; with overlapping chunks (an invalid query_start) the surplus is
+// dropped, so nothing is written outside the plan.
 __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
-    int num_seqs, int num_tokens, int ctx_cap, int tok, int32_t *__restrict__ plan) {
+    int num_seqs, int num_tokens, int ctx_cap, int tok, int kpart, int max_items,
+    int32_t *__restrict__ plan, int32_t *__restrict__ nparts) {
   __shared__ int s_count[kBuckets + 1];
   __shared__ int s_next[kBuckets + 1];
   for (int i = threadIdx.x; i <= kBuckets; i += kPlanThreads) s_count[i] = 0;
+  if (kpart)  // rows outside every chunk: nothing to merge
+    for (int i = threadIdx.x; i < num_tokens; i += kPlanThreads) nparts[i] = 1;
   __syncthreads();
-  // chunk length, and the position of its first token
-  auto chunk = [&](int s, int &n, int &p0) {
-    const int a = min(max(query_start[s], 0), num_tokens);
+  // chunk bounds, and the position of its first token
+  auto chunk = [&](int s, int &a, int &n, int &p0) {
+    a = min(max(query_start[s], 0), num_tokens);
     const int b = min(max(query_start[s + 1], a), num_tokens);
     n = b - a;
     p0 = min(max(context_lens[s], 0), ctx_cap) - n;
   };
-  auto bucket = [&](int n, int p0, int t0) {
-    const int kv_end = p0 + min(n, t0 + tok);  // keys the item's last token sees
-    return kv_end <= 0 ? 0 : min((kv_end + kKeys - 1) / kKeys, kBuckets);
+  // keys the block starting at t0 sees, and its partitions
+  auto keys = [&](int n, int p0, int t0) { return max(0, p0 + min(n, t0 + tok)); };
+  auto parts = [&](int kv_end) { return kpart && kv_end > 0 ? (kv_end + kpart - 1) / kpart : 1; };
+  auto bucket = [&](int kv_end, int kp) {
+    const int lo = kpart ? kp * kpart : 0;
+    const int hi = kpart ? min(kv_end, lo + kpart) : kv_end;
+    return hi <= lo ? 0 : min((hi - lo + kKeys - 1) / kKeys, kBuckets);
   };
   for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
-    int n, p0;
-    chunk(s, n, p0);
-    for (int t0 = 0; t0 < n; t0 += tok) atomicAdd(&s_count[bucket(n, p0, t0)], 1);
+    int a, n, p0;
+    chunk(s, a, n, p0);
+    for (int t0 = 0; t0 < n; t0 += tok) {
+      const int ke = keys(n, p0, t0), np = parts(ke);
+      for (int kp = 0; kp < np; ++kp) atomicAdd(&s_count[bucket(ke, kp)], 1);
+      if (kpart)
+        for (int i = t0; i < min(n, t0 + tok); ++i) nparts[a + i] = np;
+    }
   }
   __syncthreads();
   // first slot of each size class, largest class first: an exclusive scan
@@ -132,16 +152,22 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
     int before = 0;
     for (int k = 0; k < w; ++k) before += s_wave[k];
     s_next[kBuckets - t] = before + x - v;
-    if (t == kPlanThreads - 1) plan[0] = before + x;
+    if (t == kPlanThreads - 1) plan[0] = min(before + x, max_items);
   }
   __syncthreads();
   for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
-    int n, p0;
-    chunk(s, n, p0);
+    int a, n, p0;
+    chunk(s, a, n, p0);
     for (int t0 = 0; t0 < n; t0 += tok) {
-      int32_t *r = plan + kPlanHeader + 2 * atomicAdd(&s_next[bucket(n, p0, t0)], 1);
-      r[0] = s;
-      r[1] = t0;
+      const int ke = keys(n, p0, t0), np = parts(ke);
+      for (int kp = 0; kp < np; ++kp) {
+        const int k = atomicAdd(&s_next[bucket(ke, kp)], 1);
+        if (k >= max_items) continue;
+        int32_t *r = plan + kPlanHeader + kPlanRecord * k;
+        r[0] = s;
+        r[1] = t0;
+        r[2] = kp;
+      }
     }
   }
 }
@@ -171,7 +197,8 @@ __device__ __forceinline__ void prefill_item(
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
     int num_tokens, int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
-    float scale_log2, const float *__restrict__ alibi, int s, int t0, int g) {
+    float scale_log2, const float *__restrict__ alibi, int kpart, int max_parts,
+    float *__restrict__ ws_ml, float *__restrict__ ws_acc, int s, int t0, int kp, int g) {
   using Sh = PrefillShape<D, BS, G>;
   constexpr int ROW = Sh::ROW, CPR = Sh::CPR, NC = Sh::NC, NN = Sh::NN, TILE = Sh::TILE;
   constexpr int LOADS = Sh::LOADS, TOK = Sh::TOK, PPT = Sh::PPT;
@@ -189,8 +216,12 @@ __device__ __forceinline__ void prefill_item(
   const int n = qb - qa;
   const int p0 = min(max(context_lens[s], 0), max_blocks * BS) - n;  // position of chunk token 0
   const int ntok = min(TOK, n - t0);                                  // tokens of this item
-  const int kv_end = max(0, p0 + t0 + ntok);                          // keys the item sees
-  const int ntiles = (kv_end + kKeys - 1) / kKeys;
+  const int kv_end = max(0, p0 + t0 + ntok);                          // keys the block sees
+  // this item's key tiles [kt_lo, kt_hi): partition kp of the block's keys
+  const int nparts_item = kpart && kv_end > 0 ? (kv_end + kpart - 1) / kpart : 1;
+  const int kt_lo = kpart ? kp * (kpart / kKeys) : 0;
+  const int kt_hi = kpart ? min((kv_end + kKeys - 1) / kKeys, (kp + 1) * (kpart / kKeys))
+                          : (kv_end + kKeys - 1) / kKeys;
   const int npages = (kv_end + BS - 1) / BS;
   const int32_t *bt = block_tables + (size_t)s * max_blocks;
 
@@ -456,9 +487,9 @@ __device__ __forceinline__ void prefill_item(
   // immediate
   auto step = [&](auto masked_c, auto buf_c, int kt) {
     constexpr int buf = decltype(buf_c)::value;
-    if (kt + 1 < ntiles) {
+    if (kt + 1 < kt_hi) {
       stage(buf ^ 1, tile_clean(kt + 1));  // its previous contents were used before the last barrier
-      if (kt + 2 < ntiles) fetch(kt + 2);
+      if (kt + 2 < kt_hi) fetch(kt + 2);
     }
     if (wave_live && kt * kKeys <= wmax) compute(masked_c, buf_c, kt);
     __syncthreads();
@@ -472,42 +503,90 @@ __device__ __forceinline__ void prefill_item(
   // position on valid pages (no per-key mask), then the rest.  Every wave
   // takes one barrier per tile, so the two loops of different waves stay in
   // step.
-  if (ntiles > 0) {
-    fetch(0);
-    stage(0, tile_clean(0));
-    if (ntiles > 1) fetch(1);
+  // Buffer 0 holds the item's even tiles counted from kt_lo.
+  if (kt_hi > kt_lo) {
+    fetch(kt_lo);
+    stage(0, tile_clean(kt_lo));
+    if (kt_lo + 1 < kt_hi) fetch(kt_lo + 1);
     __syncthreads();
-    const int clean_end = wave_live ? min(ntiles, max(0, (wmin + 1) / kKeys)) : 0;
-    int kt = 0;
+    const int clean_end = wave_live ? min(kt_hi, max(kt_lo, (wmin + 1) / kKeys)) : kt_lo;
+    int kt = kt_lo;
     for (; kt + 1 < clean_end && tile_clean(kt) && tile_clean(kt + 1); kt += 2) {
       step(Clean{}, B0{}, kt);
       step(Clean{}, B1{}, kt + 1);
     }
-    // kt is even here: the clean loop takes tiles in pairs
-    for (; kt < ntiles; kt += 2) {
+    // kt - kt_lo is even here: the clean loop takes tiles in pairs
+    for (; kt < kt_hi; kt += 2) {
       step(Masked{}, B0{}, kt);
-      if (kt + 1 < ntiles) step(Masked{}, B1{}, kt + 1);
+      if (kt + 1 < kt_hi) step(Masked{}, B1{}, kt + 1);
     }
   }
 
-  // normalise and store: lane (q4, j) writes d = 16n + 4*q4 .. +3 of row j
+  // Store: lane (q4, j) holds d = 16n + 4*q4 .. +3 of row j.  A block with
+  // one key partition writes its normalised output; otherwise each item
+  // writes its partition's (max, sum, unnormalised sum of weighted V) for
+  // the reduce kernel.
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const float L = rows_sum(lsum[t]);
     const int row = 32 * wave + 16 * t + j16;
     const int tk = row / G;
     if (tk >= ntok) continue;
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    char *orow = reinterpret_cast<char *>(out) +
-                 ((size_t)(qa + t0 + tk) * num_heads + g * G + row % G) * ROW;
+    const size_t grow = (size_t)(qa + t0 + tk) * num_heads + g * G + row % G;
+    if (nparts_item == 1) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      char *orow = reinterpret_cast<char *>(out) + grow * ROW;
 #pragma unroll
-    for (int nb = 0; nb < NN; ++nb) {
-      float v[4];
+      for (int nb = 0; nb < NN; ++nb) {
+        float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = o[t][nb][r] * inv;
-      BF16::store4(orow + (16 * nb + 4 * q4) * 2, v);
+        for (int r = 0; r < 4; ++r) v[r] = o[t][nb][r] * inv;
+        BF16::store4(orow + (16 * nb + 4 * q4) * 2, v);
+      }
+    } else {
+      const size_t slot = grow * max_parts + kp;
+      float *acc = ws_acc + slot * D;
+#pragma unroll
+      for (int nb = 0; nb < NN; ++nb)
+        *reinterpret_cast<float4 *>(acc + 16 * nb + 4 * q4) =
+            make_float4(o[t][nb][0], o[t][nb][1], o[t][nb][2], o[t][nb][3]);
+      if (q4 == 0) {
+        ws_ml[slot * 2] = m[t];
+        ws_ml[slot * 2 + 1] = L;
+      }
     }
   }
+}
+
+// Merge of the key partitions of the rows whose block was split: one wave
+// per (row, query head), out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+template <int D>
+__global__ __launch_bounds__(256) void pa_prefill_reduce(
+    void *__restrict__ out, const float *__restrict__ ws_ml, const float *__restrict__ ws_acc,
+    const int32_t *__restrict__ nparts, int num_tokens, int num_heads, int max_parts) {
+  constexpr int DPL = D / 64;  // outputs per lane
+  const int lane = threadIdx.x & 63;
+  const long long rh = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head)
+  if (rh >= (long long)num_tokens * num_heads) return;
+  const int np = min(nparts[rh / num_heads], max_parts);
+  if (np <= 1) return;  // written by its item
+  const float *ml = ws_ml + rh * max_parts * 2;
+  float M = -INFINITY;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  float L = 0.f, acc[DPL] = {};
+  if (M != -INFINITY) {
+    for (int p = 0; p < np; ++p) {
+      const float w = fast_exp2(ml[2 * p] - M);
+      L = fmaf(ml[2 * p + 1], w, L);
+      const float *a = ws_acc + (rh * max_parts + p) * D + lane * DPL;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) acc[j] = fmaf(a[j], w, acc[j]);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t *dst = reinterpret_cast<uint16_t *>(out) + rh * D + lane * DPL;
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) dst[j] = (uint16_t)BF16::round_bits(acc[j] * inv);
 }
 
 template <int D, int BS, int G, bool AL>
@@ -516,15 +595,17 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_gqa(
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
     const int32_t *__restrict__ plan, int num_tokens, int num_heads, int num_kv_heads,
-    int max_blocks, int num_blocks, float scale_log2, const float *__restrict__ alibi) {
+    int max_blocks, int num_blocks, float scale_log2, const float *__restrict__ alibi,
+    int kpart, int max_parts, float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
   const int items = plan[0] * num_kv_heads;
   for (int k = 0;; ++k) {
     const int it = snake_item(k);
     if (it >= items) break;
-    const int32_t *u = plan + kPlanHeader + 2 * (it / num_kv_heads);
+    const int32_t *u = plan + kPlanHeader + kPlanRecord * (it / num_kv_heads);
     prefill_item<D, BS, G, AL>(out, q, k_pool, v_pool, block_tables, context_lens,
                                query_start, num_tokens, num_heads, num_kv_heads, max_blocks,
-                               num_blocks, scale_log2, alibi, u[0], u[1], it % num_kv_heads);
+                               num_blocks, scale_log2, alibi, kpart, max_parts, ws_ml, ws_acc,
+                               u[0], u[1], u[2], it % num_kv_heads);
     __syncthreads();  // the next item reuses the LDS
   }
 }
@@ -535,14 +616,14 @@ int launch_al(const pa_internal::PrefillLaunch &a) {
   auto kernel = pa_prefill_gqa<D, BS, G, AL>;
   static const int per_cu =
       pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel), kThreads);
-  // items <= num_tokens (each holds at least one chunk token)
-  const unsigned grid =
-      pa_internal::persistent_grid_items((long long)a.num_tokens * a.num_kv_heads, per_cu);
+  // items <= num_tokens * max_parts (each block holds at least one token)
+  const unsigned grid = pa_internal::persistent_grid_items(
+      (long long)a.num_tokens * a.max_parts * a.num_kv_heads, per_cu);
   if (grid == 0) return 6;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, st, a.out, a.q, a.k_pool, a.v_pool,
                      a.block_tables, a.context_lens, a.query_start, a.plan, a.num_tokens,
                      a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
-                     a.scale * kLog2e, a.alibi);
+                     a.scale * kLog2e, a.alibi, a.part_tokens, a.max_parts, a.ws_ml, a.ws_acc);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
@@ -566,13 +647,12 @@ int by_group(const pa_internal::PrefillLaunch &a) {
 
 namespace pa_internal {
 
-int prefill_tokens_per_item(int group) { return kRows / group; }
-
 int launch_prefill(const PrefillLaunch &a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   hipLaunchKernelGGL(pa_prefill_plan, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens,
                      a.query_start, a.num_seqs, a.num_tokens, a.max_blocks * a.block_size,
-                     prefill_tokens_per_item(a.num_heads / a.num_kv_heads), a.plan);
+                     kPrefillRows / (a.num_heads / a.num_kv_heads), a.part_tokens,
+                     a.num_tokens * a.max_parts, a.plan, a.nparts);
   if (hipGetLastError() != hipSuccess) return 6;
   if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
   int rc;
@@ -582,6 +662,13 @@ int launch_prefill(const PrefillLaunch &a) {
     rc = a.block_size == 16 ? by_group<128, 16>(a) : by_group<128, 32>(a);
   if (rc != 0) return rc;
   if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
+  if (a.max_parts > 1) {
+    const long long rows = (long long)a.num_tokens * a.num_heads;
+    auto reduce = a.head_dim == 64 ? pa_prefill_reduce<64> : pa_prefill_reduce<128>;
+    hipLaunchKernelGGL(reduce, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a.out,
+                       a.ws_ml, a.ws_acc, a.nparts, a.num_tokens, a.num_heads, a.max_parts);
+    if (hipGetLastError() != hipSuccess) return 6;
+  }
   return 0;
 }
 

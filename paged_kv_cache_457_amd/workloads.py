@@ -389,13 +389,15 @@ PREFILL_CONFIG_NAMES = {
     1: "tiny prefill (4 seqs, cached {0,5,16,40} + new {1,12,33,7}, 4/2 heads, D 64, bs 16, bf16)",
     2: "Llama-2-7B chunked prefill (8 seqs, 1024 new after U[0,3072] cached, 32/32 heads, D 128, bs 16, bf16)",
     3: "GQA prompt prefill (16 prompts U[256,2048], nothing cached, 32/8 heads, D 128, bs 16, bf16)",
+    4: "long-context chunked prefill (2 seqs: 512 new after 15872 cached, 256 new after 7680 "
+       "cached; 32/8 heads, D 128, bs 16, bf16)",
 }
 
 PREFILL_SEED_BASE = 4580
 
 
 def make_prefill_config(index: int, seed: Optional[int] = None) -> Workload:
-    """Multi-token (prefill) steps, by number (1..3): newly admitted requests
+    """Multi-token (prefill) steps, by number (1..4): newly admitted requests
     whose prompt, or a chunk of it, is appended and attended in one step."""
     if seed is None:
         seed = PREFILL_SEED_BASE + index
@@ -413,4 +415,9 @@ def make_prefill_config(index: int, seed: Optional[int] = None) -> Workload:
         new = rng.integers(256, 2048, size=16, endpoint=True)
         return build_workload("p3", new, 32, 8, 128, 16, "bf16", seed,
                               max_blocks_per_seq=2048 // 16, rng=rng, new_tokens=new)
+    if index == 4:
+        # the next chunk of two long prompts: few query rows over many cached keys
+        cached, new = np.array([15872, 7680]), np.array([512, 256])
+        return build_workload("p4", cached + new, 32, 8, 128, 16, "bf16", seed,
+                              max_blocks_per_seq=16384 // 16, rng=rng, new_tokens=new)
     raise ValueError(f"no prefill configuration {index}")

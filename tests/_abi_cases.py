@@ -260,7 +260,9 @@ expect("prefill: heads not a multiple", prefill(pdims(num_heads=30)), _lib.PA_ER
 expect("prefill: negative rows", prefill(pdims(num_tokens=-1)), _lib.PA_ERR_SHAPE)
 expect("prefill: negative sequences", prefill(pdims(num_seqs=-1)), _lib.PA_ERR_SHAPE)
 expect("prefill: rows without sequences", prefill(pdims(num_tokens=5)), _lib.PA_ERR_SHAPE)
-expect("prefill: reserved nonzero", prefill(pdims(reserved=1)), _lib.PA_ERR_SHAPE)
+expect("prefill: partition not a multiple of 64", prefill(pdims(partition_size=100)),
+       _lib.PA_ERR_SHAPE)
+expect("prefill: negative partition", prefill(pdims(partition_size=-64)), _lib.PA_ERR_SHAPE)
 expect("prefill: zero blocks", prefill(pdims(num_blocks=0)), _lib.PA_ERR_SHAPE)
 expect("prefill: zero table columns", prefill(pdims(max_blocks_per_seq=0)), _lib.PA_ERR_SHAPE)
 expect("prefill: zero kv heads", prefill(pdims(), hkv=0), _lib.PA_ERR_SHAPE)
@@ -274,8 +276,41 @@ for i in range(7):
     ptrs[i] = MIS + 2 if i >= 4 else MIS
     expect(f"prefill: pointer {i} misaligned", prefill(pdims(**ROWS), ptrs=ptrs), _lib.PA_ERR_ALIGN)
 expect("prefill: workspace missing", prefill(pdims(**ROWS)), _lib.PA_ERR_WORKSPACE)
+# plan ints 4 + 3 * rows * P + rows (rounded to 256 bytes), plus with P > 1
+# partitions the partials rows * heads * P * (head_dim + 2) floats
+def pf_bytes(rows, heads, dh, parts):
+    b = -(-(4 + 3 * rows * parts + rows) * 4 // 256) * 256
+    return b + (rows * heads * parts * (dh + 2) * 4 if parts > 1 else 0)
+
+
+pf_short = lib.paged_attention_prefill_workspace_bytes(
+    8, 16, ctypes.byref(pdims(max_blocks_per_seq=64, **ROWS)))
+expect("prefill: workspace bytes, capacity 1024 keys is never split", pf_short,
+       pf_bytes(100, 32, 128, 1))
 pf_need = lib.paged_attention_prefill_workspace_bytes(8, 16, ctypes.byref(pdims(**ROWS)))
-expect("prefill: workspace bytes formula", pf_need, -(-(4 + 2 * 100) * 4 // 256) * 256)
+# 100 rows, group 4: 2 blocks x 8 kv heads = 16 items; capacity 2048 keys,
+# partitions of max(1024, 2048 / 64) = 1024 keys -> P = 2
+expect("prefill: workspace bytes, default split", pf_need, pf_bytes(100, 32, 128, 2))
+expect("prefill: workspace bytes, explicit partition 192",
+       lib.paged_attention_prefill_workspace_bytes(
+           8, 16, ctypes.byref(pdims(partition_size=192, **ROWS))), pf_bytes(100, 32, 128, 11))
+expect("prefill: too many items for int32",
+       lib.paged_attention_prefill_workspace_bytes(
+           8, 16, ctypes.byref(pdims(num_seqs=1, num_tokens=1 << 24, max_blocks_per_seq=1 << 12,
+                                     partition_size=64))), _lib.SIZE_MAX)
+ppt = lib.paged_attention_prefill_partition_tokens
+expect("prefill partition: default, few items", ppt(8, 16, ctypes.byref(pdims(**ROWS))), 1024)
+expect("prefill partition: default, capacity 1024", ppt(
+    8, 16, ctypes.byref(pdims(max_blocks_per_seq=64, **ROWS))), 0)
+expect("prefill partition: default, long table", ppt(
+    8, 16, ctypes.byref(pdims(num_seqs=1, num_tokens=512, max_blocks_per_seq=2048))), 2048)
+expect("prefill partition: default, 1024 items", ppt(
+    8, 16, ctypes.byref(pdims(num_seqs=2, num_tokens=8192, max_blocks_per_seq=2048))), 0)
+expect("prefill partition: explicit", ppt(8, 16, ctypes.byref(pdims(partition_size=128, **ROWS))),
+       128)
+expect("prefill partition: explicit beyond the capacity",
+       ppt(8, 16, ctypes.byref(pdims(partition_size=4096, **ROWS))), 0)
+expect("prefill partition: bad dims", ppt(8, 16, ctypes.byref(pdims(head_dim=80))), -1)
 expect("prefill: workspace too small",
        prefill(pdims(workspace=P, workspace_bytes=pf_need - 4, **ROWS)), _lib.PA_ERR_WORKSPACE)
 expect("prefill: workspace misaligned",

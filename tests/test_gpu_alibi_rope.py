@@ -97,12 +97,13 @@ def test_decode_alibi_zero_slopes_equal_plain_decode_bitwise():
 
 
 # ----------------------------------------------------------- ALiBi prefill
-def prefill_alibi(w, slopes, rows=None):
+def prefill_alibi(w, slopes, rows=None, partition_size=0):
     dw = upload(w)
     binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
     binding.paged_attention_prefill(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
                                     dw.context_lens, dw.query_start, scale=float(w.scale),
-                                    alibi_slopes=torch.from_numpy(slopes).cuda())
+                                    alibi_slopes=torch.from_numpy(slopes).cuda(),
+                                    partition_size=partition_size)
     torch.cuda.synchronize()
     kp, vp = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping,
                                       w.block_size)
@@ -120,14 +121,19 @@ def test_prefill_alibi_tiny():
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("D,bs,G", [(64, 16, 1), (128, 32, 2), (128, 16, 4), (64, 32, 8)])
-def test_prefill_alibi_variants(D, bs, G):
-    cached, new = np.array([0, 70, 131]), np.array([150, 37, 1])
+PAL = [(64, 16, 1, 0), (128, 32, 2, 0), (128, 16, 4, 0), (64, 32, 8, 0),
+       (64, 16, 1, 64), (128, 32, 2, 192), (128, 16, 4, 128), (64, 32, 8, 64)]
+
+
+@pytest.mark.parametrize("D,bs,G,ps", PAL, ids=[f"D{a}-bs{b}-G{c}-ps{d}" for a, b, c, d in PAL])
+def test_prefill_alibi_variants(D, bs, G, ps):
+    # ps > 0: keys split in partitions of ps, merged by the reduce kernel
+    cached, new = np.array([0, 70, 131, 400]), np.array([150, 37, 1, 90])
     w = build_workload("pal", cached + new, 2 * G, 2, D, bs, "bf16", seed=D + G, new_tokens=new)
     slopes = np.array([0.5, 0.01] * G, np.float32)[:2 * G]
-    got, ref = prefill_alibi(w, slopes)
+    got, ref = prefill_alibi(w, slopes, partition_size=ps)
     err = max_err(got, ref, "bf16")
-    say(f"D{D} bs{bs} G{G} ALiBi prefill: max abs err {err:.3e}")
+    say(f"D{D} bs{bs} G{G} partition {ps} ALiBi prefill: max abs err {err:.3e}")
     assert err <= TOL["bf16"]
 
 

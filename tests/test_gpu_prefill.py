@@ -24,7 +24,7 @@ def say(msg):
     print(msg, flush=True)
 
 
-def gpu_prefill(dw, write=True, context_lens=None, block_tables=None):
+def gpu_prefill(dw, write=True, context_lens=None, block_tables=None, partition_size=0):
     """Cache write of the chunk rows, then prefill attention."""
     if write:
         binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
@@ -32,7 +32,7 @@ def gpu_prefill(dw, write=True, context_lens=None, block_tables=None):
         dw.out, dw.q, dw.k_pool, dw.v_pool,
         dw.block_tables if block_tables is None else block_tables,
         dw.context_lens if context_lens is None else context_lens,
-        dw.query_start, scale=float(dw.w.scale))
+        dw.query_start, scale=float(dw.w.scale), partition_size=partition_size)
     torch.cuda.synchronize()
     return to_host(dw.out, "bf16")
 
@@ -103,18 +103,62 @@ def test_prefill_variants(D, bs, G):
     assert err <= TOL
 
 
-def test_prefill_empty_sequences_and_exact_tile_edges():
+# Split-K: each block's keys in partitions of `ps` (a multiple of the 64-key
+# tile; odd tile counts start partitions on either LDS buffer), merged by the
+# reduce kernel.  Lengths leave partial last partitions and early rows that
+# see none of a late partition's keys.
+SPLIT = [(64, 16, 1, 64), (64, 32, 4, 192), (64, 16, 8, 128), (128, 16, 1, 320),
+         (128, 32, 2, 128), (128, 16, 4, 64), (128, 16, 8, 192), (128, 32, 4, 256)]
+
+
+@pytest.mark.parametrize("D,bs,G,ps", SPLIT, ids=[f"D{a}-bs{b}-G{c}-ps{d}" for a, b, c, d in SPLIT])
+def test_prefill_split_variants(D, bs, G, ps):
+    cached = np.array([0, 70, 5, 331, 1000])
+    new = np.array([150, 37, 200, 1, 70])
+    w = build_workload(f"ps{D}-{bs}-{G}-{ps}", cached + new, 2 * G, 2, D, bs, "bf16",
+                       seed=D + bs + G + ps, new_tokens=new)
+    dw = upload(w)
+    assert binding.paged_attention_prefill_partition_tokens(
+        dw.q, dw.k_pool, dw.block_tables, dw.query_start, ps) == ps
+    got = gpu_prefill(dw, partition_size=ps)
+    err = max_err(got, oracle_prefill(w))
+    say(f"split D{D} bs{bs} G{G} ps{ps}: T={w.num_tokens} max abs err {err:.3e}")
+    assert err <= TOL
+
+
+def test_prefill_long_context_default_split_sampled_rows():
+    """Few chunk rows over long cached contexts: the library splits the keys
+    by default; sampled rows against the oracle, then bitwise repeats."""
+    w = make_prefill_config(4)
+    dw = upload(w)
+    ps = binding.paged_attention_prefill_partition_tokens(dw.q, dw.k_pool, dw.block_tables,
+                                                          dw.query_start)
+    rows = sample_rows(w, 6, np.random.default_rng(4))
+    say(f"prefill p4: T={w.num_tokens}, ctx={w.context_lens.tolist()}, default partition {ps}, "
+        f"{len(rows)} sampled rows")
+    assert ps > 0
+    got = gpu_prefill(dw)
+    err = max_err(got, oracle_prefill(w, rows=rows), rows)
+    say(f"p4 max abs err {err:.3e}")
+    assert err <= TOL
+    for _ in range(2):
+        assert gpu_prefill(dw, write=False).tobytes() == got.tobytes()
+
+
+@pytest.mark.parametrize("ps", [0, 64])
+def test_prefill_empty_sequences_and_exact_tile_edges(ps):
     # a sequence with no rows, chunks ending exactly on 64-key tiles and pages
     cached = np.array([64, 0, 3, 128, 16])
     new = np.array([64, 0, 61, 128, 48])
     w = build_workload("edges", cached + new, 8, 2, 128, 16, "bf16", seed=77, new_tokens=new)
-    got = gpu_prefill(upload(w))
+    got = gpu_prefill(upload(w), partition_size=ps)
     err = max_err(got, oracle_prefill(w))
-    say(f"edges: max abs err {err:.3e}")
+    say(f"edges, partition {ps}: max abs err {err:.3e}")
     assert err <= TOL
 
 
-def test_prefill_rows_outside_every_sequence_untouched():
+@pytest.mark.parametrize("ps", [0, 64])
+def test_prefill_rows_outside_every_sequence_untouched(ps):
     cached, new = np.array([10, 30]), np.array([20, 9])
     w = build_workload("untouched", cached + new, 4, 4, 64, 16, "bf16", seed=5, new_tokens=new)
     dw = upload(w)
@@ -124,14 +168,16 @@ def test_prefill_rows_outside_every_sequence_untouched():
                                      device="cuda")])
     out = torch.full(tuple(q.shape), 3.0, dtype=q.dtype, device="cuda")
     binding.paged_attention_prefill(out, q, dw.k_pool, dw.v_pool, dw.block_tables,
-                                    dw.context_lens, dw.query_start, scale=float(w.scale))
+                                    dw.context_lens, dw.query_start, scale=float(w.scale),
+                                    partition_size=ps)
     torch.cuda.synchronize()
     got = to_host(out, "bf16")
     assert np.all(oracle.widen(got[w.num_tokens:], "bf16") == 3.0)
     assert max_err(got[:w.num_tokens], oracle_prefill(w)) <= TOL
 
 
-def test_prefill_more_rows_than_context():
+@pytest.mark.parametrize("ps", [0, 64])
+def test_prefill_more_rows_than_context(ps):
     """Rows at a position below 0 see nothing and are zeros; the others are
     the oracle over the sequence's last ctx rows."""
     cached, new = np.array([0, 40]), np.array([30, 25])
@@ -140,7 +186,7 @@ def test_prefill_more_rows_than_context():
     dw = upload(w)
     binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
     short = torch.tensor([20, 65], dtype=torch.int32, device="cuda")   # seq 0: 30 rows, ctx 20
-    got = gpu_prefill(dw, write=False, context_lens=short)
+    got = gpu_prefill(dw, write=False, context_lens=short, partition_size=ps)
     # sequence 0 with context 20: its last 20 rows are a plain prompt prefill
     kp, vp = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping, 16)
     ref0 = oracle.prefill(w.q[10:30], kp, vp, w.block_tables[:1], np.array([20]),
@@ -151,7 +197,8 @@ def test_prefill_more_rows_than_context():
     assert float(np.max(np.abs(g[30:] - ref[30:]))) <= TOL
 
 
-def test_prefill_out_of_range_page_id_is_skipped():
+@pytest.mark.parametrize("ps", [0, 64])
+def test_prefill_out_of_range_page_id_is_skipped(ps):
     """A used table entry outside the pool drops that page's tokens, which
     equals the oracle over the sequence without the page (an interior,
     full page below every chunk row)."""
@@ -163,7 +210,7 @@ def test_prefill_out_of_range_page_id_is_skipped():
     bt = w.block_tables.copy()
     bt[0, bad_col] = w.num_blocks + 7
     dw = upload(w)
-    got = gpu_prefill(dw, block_tables=torch.from_numpy(bt).cuda())
+    got = gpu_prefill(dw, block_tables=torch.from_numpy(bt).cuda(), partition_size=ps)
     bt_ref = np.full_like(w.block_tables, -1)
     bt_ref[0, :bt.shape[1] - 1] = np.delete(w.block_tables[0], bad_col)
     bt_ref[1] = w.block_tables[1]
