@@ -99,12 +99,19 @@ __device__ __forceinline__ int swz(int r, int c) {
 // writes the row's output itself).  Valid chunks give at most max_items
 // items; with overlapping chunks (an invalid query_start) the surplus is
 // dropped, so nothing is written outside the plan.
+//
+// A wave takes one sequence at a time and its lanes the sequence's
+// (block, partition) pairs, so a long chunk over a long context costs a
+// few strided passes rather than one lane's serial loop.
 __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
-    int num_seqs, int num_tokens, int ctx_cap, int tok, int kpart, int max_items,
+    int num_seqs, int num_tokens, int ctx_cap, int tok, int kpart, int max_parts, int max_items,
     int32_t *__restrict__ plan, int32_t *__restrict__ nparts) {
+  constexpr int kPlanWaves = kPlanThreads / 64;
   __shared__ int s_count[kBuckets + 1];
   __shared__ int s_next[kBuckets + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int P = kpart ? max_parts : 1;  // partition slots per block
   for (int i = threadIdx.x; i <= kBuckets; i += kPlanThreads) s_count[i] = 0;
   if (kpart)  // rows outside every chunk: nothing to merge
     for (int i = threadIdx.x; i < num_tokens; i += kPlanThreads) nparts[i] = 1;
@@ -124,22 +131,32 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
     const int hi = kpart ? min(kv_end, lo + kpart) : kv_end;
     return hi <= lo ? 0 : min((hi - lo + kKeys - 1) / kKeys, kBuckets);
   };
-  for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
+  // visit(s, block start, partition, keys) for every item of sequence s
+  auto items_of = [&](int s, auto visit) {
     int a, n, p0;
     chunk(s, a, n, p0);
-    for (int t0 = 0; t0 < n; t0 += tok) {
-      const int ke = keys(n, p0, t0), np = parts(ke);
-      for (int kp = 0; kp < np; ++kp) atomicAdd(&s_count[bucket(ke, kp)], 1);
-      if (kpart)
-        for (int i = t0; i < min(n, t0 + tok); ++i) nparts[a + i] = np;
+    const int nb = (n + tok - 1) / tok;
+    for (int j = lane; j < nb * P; j += 64) {
+      const int b = P == 1 ? j : j / P, kp = j - b * P;
+      const int ke = keys(n, p0, b * tok);
+      if (kp < parts(ke)) visit(b * tok, kp, ke);
+    }
+    return a;
+  };
+  for (int s = wave; s < num_seqs; s += kPlanWaves) {
+    const int a = items_of(s, [&](int, int kp, int ke) { atomicAdd(&s_count[bucket(ke, kp)], 1); });
+    if (kpart) {
+      int a2, n, p0;
+      chunk(s, a2, n, p0);
+      for (int i = lane; i < n; i += 64) nparts[a + i] = parts(keys(n, p0, i - i % tok));
     }
   }
   __syncthreads();
   // first slot of each size class, largest class first: an exclusive scan
   // over thread t <-> class kBuckets - t (lane scan, then one over waves)
   {
-    __shared__ int s_wave[kPlanThreads / 64];
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    __shared__ int s_wave[kPlanWaves];
+    const int t = threadIdx.x;
     const int v = s_count[kBuckets - t];
     int x = v;
 #pragma unroll
@@ -147,29 +164,23 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
       const int y = __shfl_up(x, o);
       if (lane >= o) x += y;
     }
-    if (lane == 63) s_wave[w] = x;
+    if (lane == 63) s_wave[wave] = x;
     __syncthreads();
     int before = 0;
-    for (int k = 0; k < w; ++k) before += s_wave[k];
+    for (int k = 0; k < wave; ++k) before += s_wave[k];
     s_next[kBuckets - t] = before + x - v;
     if (t == kPlanThreads - 1) plan[0] = min(before + x, max_items);
   }
   __syncthreads();
-  for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
-    int a, n, p0;
-    chunk(s, a, n, p0);
-    for (int t0 = 0; t0 < n; t0 += tok) {
-      const int ke = keys(n, p0, t0), np = parts(ke);
-      for (int kp = 0; kp < np; ++kp) {
-        const int k = atomicAdd(&s_next[bucket(ke, kp)], 1);
-        if (k >= max_items) continue;
-        int32_t *r = plan + kPlanHeader + kPlanRecord * k;
-        r[0] = s;
-        r[1] = t0;
-        r[2] = kp;
-      }
-    }
-  }
+  for (int s = wave; s < num_seqs; s += kPlanWaves)
+    items_of(s, [&](int t0, int kp, int ke) {
+      const int k = atomicAdd(&s_next[bucket(ke, kp)], 1);
+      if (k >= max_items) return;
+      int32_t *r = plan + kPlanHeader + kPlanRecord * k;
+      r[0] = s;
+      r[1] = t0;
+      r[2] = kp;
+    });
 }
 
 // ------------------------------------------------------------- work item
@@ -560,33 +571,55 @@ __device__ __forceinline__ void prefill_item(
 
 // Merge of the key partitions of the rows whose block was split: one wave
 // per (row, query head), out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// Lanes hold the partitions' (m, l) 64 at a time; each partition's weight
+// is then broadcast while the lanes stream its D accumulator values.
 template <int D>
 __global__ __launch_bounds__(256) void pa_prefill_reduce(
     void *__restrict__ out, const float *__restrict__ ws_ml, const float *__restrict__ ws_acc,
     const int32_t *__restrict__ nparts, int num_tokens, int num_heads, int max_parts) {
   constexpr int DPL = D / 64;  // outputs per lane
+  using Vec = std::conditional_t<DPL == 2, float2, float>;
   const int lane = threadIdx.x & 63;
   const long long rh = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head)
   if (rh >= (long long)num_tokens * num_heads) return;
   const int np = min(nparts[rh / num_heads], max_parts);
   if (np <= 1) return;  // written by its item
-  const float *ml = ws_ml + rh * max_parts * 2;
+  const float2 *ml = reinterpret_cast<const float2 *>(ws_ml) + rh * max_parts;
   float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-  float L = 0.f, acc[DPL] = {};
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[p].x);
+  M = wave_max(M);
+  float acc[DPL] = {}, L = 0.f;
   if (M != -INFINITY) {
-    for (int p = 0; p < np; ++p) {
-      const float w = fast_exp2(ml[2 * p] - M);
-      L = fmaf(ml[2 * p + 1], w, L);
-      const float *a = ws_acc + (rh * max_parts + p) * D + lane * DPL;
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) acc[j] = fmaf(a[j], w, acc[j]);
+    const float *a = ws_acc + rh * max_parts * D + lane * DPL;
+    for (int p0 = 0; p0 < np; p0 += 64) {
+      float w = 0.f;
+      if (p0 + lane < np) {
+        const float2 st = ml[p0 + lane];
+        w = fast_exp2(st.x - M);
+        L = fmaf(st.y, w, L);
+      }
+      const int cnt = min(64, np - p0);
+#pragma unroll 4
+      for (int q = 0; q < cnt; ++q) {
+        const float wq = __shfl(w, q);
+        const Vec v = *reinterpret_cast<const Vec *>(a + (size_t)(p0 + q) * D);
+        if constexpr (DPL == 2) {
+          acc[0] = fmaf(v.x, wq, acc[0]);
+          acc[1] = fmaf(v.y, wq, acc[1]);
+        } else {
+          acc[0] = fmaf(v, wq, acc[0]);
+        }
+      }
     }
+    L = wave_sum(L);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t *dst = reinterpret_cast<uint16_t *>(out) + rh * D + lane * DPL;
-#pragma unroll
-  for (int j = 0; j < DPL; ++j) dst[j] = (uint16_t)BF16::round_bits(acc[j] * inv);
+  if constexpr (DPL == 2)
+    *reinterpret_cast<uint32_t *>(dst) =
+        BF16::round_bits(acc[0] * inv) | (BF16::round_bits(acc[1] * inv) << 16);
+  else
+    dst[0] = (uint16_t)BF16::round_bits(acc[0] * inv);
 }
 
 template <int D, int BS, int G, bool AL>
@@ -651,7 +684,7 @@ int launch_prefill(const PrefillLaunch &a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   hipLaunchKernelGGL(pa_prefill_plan, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens,
                      a.query_start, a.num_seqs, a.num_tokens, a.max_blocks * a.block_size,
-                     kPrefillRows / (a.num_heads / a.num_kv_heads), a.part_tokens,
+                     kPrefillRows / (a.num_heads / a.num_kv_heads), a.part_tokens, a.max_parts,
                      a.num_tokens * a.max_parts, a.plan, a.nparts);
   if (hipGetLastError() != hipSuccess) return 6;
   if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
