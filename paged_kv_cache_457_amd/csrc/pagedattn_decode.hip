@@ -284,11 +284,13 @@ __device__ __forceinline__ void decode_unit(
       ws_ml + (((size_t)s * num_heads + h0) * max_parts + part) * 2, (size_t)max_parts);
 }
 
-// Persistent partition kernel: a grid sized to what the GPU holds at once
-// walks the unit list the plan kernel wrote, largest units first, item i =
-// (list[i / num_kv_heads], kv-head i % num_kv_heads), in the snake order of
-// snake_item.  Kv-head fastest puts the heads of one unit on workgroups
-// that start together on different XCDs (the hardware hands consecutive
+// Partition kernel: a grid of up to kDecodeGridRounds times what the GPU
+// holds at once walks the unit list the plan kernel wrote, largest units
+// first, item i = (list[i / num_kv_heads], kv-head i % num_kv_heads), in the
+// snake order of snake_item.  Workgroups past the resident ones start as
+// earlier ones finish, so the hardware's dispatcher hands the list out
+// greedily.  Kv-head fastest puts the heads of one unit on workgroups that
+// start together on different XCDs (the hardware hands consecutive
 // workgroups to the 8 XCDs in turn).
 template <class T, int D, int BS, int G, int NW, bool AL>
 __global__ __launch_bounds__(64 * NW) void pa_decode_partition(
@@ -462,7 +464,7 @@ int launch_valu_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
   auto kernel = pa_decode_partition<T, D, BS, G, kWavesPerUnit, AL>;
   static const int per_cu = pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel),
                                                        64 * kWavesPerUnit);
-  const unsigned grid = pa_internal::persistent_grid(a, per_cu);
+  const unsigned grid = pa_internal::decode_grid(a, per_cu);
   if (grid == 0) return 6;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.out, a.q,
                      a.k_pool, a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc,
@@ -534,8 +536,9 @@ int blocks_per_cu(const void *kernel, int block_threads) {
   return n > 0 ? n : 1;
 }
 
-unsigned persistent_grid(const DecodeLaunch &a, int per_cu) {
-  return persistent_grid_items((long long)a.num_seqs * a.max_parts * a.num_kv_heads, per_cu);
+unsigned decode_grid(const DecodeLaunch &a, int per_cu) {
+  return persistent_grid_items((long long)a.num_seqs * a.max_parts * a.num_kv_heads,
+                               per_cu * kDecodeGridRounds);
 }
 
 unsigned persistent_grid_items(long long items, int per_cu) {

@@ -275,9 +275,9 @@ __device__ __forceinline__ void decode_unit_gqa(
       ws_ml + (((size_t)s * num_heads + h0) * max_parts + part) * 2, (size_t)max_parts);
 }
 
-// Persistent partition kernel over the plan's unit list (largest units
-// first), item i = (list[i / num_kv_heads], kv-head i % num_kv_heads), in
-// the snake order of snake_item.
+// Partition kernel over the plan's unit list (largest units first), item
+// i = (list[i / num_kv_heads], kv-head i % num_kv_heads), in the snake order
+// of snake_item, on a grid of decode_grid.
 template <int D, int BS, int G, int NW, bool AL>
 __global__ __launch_bounds__(64 * NW) void pa_decode_partition_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
@@ -307,7 +307,7 @@ int launch_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
   auto kernel = pa_decode_partition_gqa<D, BS, G, kWavesPerUnit, AL>;
   static const int per_cu = pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel),
                                                        64 * kWavesPerUnit);
-  const unsigned grid = pa_internal::persistent_grid(a, per_cu);
+  const unsigned grid = pa_internal::decode_grid(a, per_cu);
   if (grid == 0) return 6;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.out, a.q, a.k_pool,
                      a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc, a.plan,
