@@ -369,8 +369,9 @@ __device__ __forceinline__ void prefix_unit(
   }
 }
 
-// Persistent kernel over the plan's units (largest first), item i = (unit
-// i / num_kv_heads, kv-head i % num_kv_heads), snake order.
+// Kernel over the plan's units (largest first), item i = (unit
+// i / num_kv_heads, kv-head i % num_kv_heads), snake order, on a grid of
+// several rounds of resident workgroups.
 template <int D, int BS, int G, int NW>
 __global__ __launch_bounds__(64 * NW) void pa_decode_prefix_gqa(
     const void *__restrict__ q, const void *__restrict__ k_pool, const void *__restrict__ v_pool,
@@ -399,8 +400,9 @@ int launch(const pa_internal::PrefixLaunch &p, float scale_log2) {
   auto kernel = pa_decode_prefix_gqa<D, BS, G, kWavesPerUnit>;
   static const int per_cu = pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel),
                                                        64 * kWavesPerUnit);
+  // several rounds of resident workgroups, as for the partition kernels
   const unsigned grid = pa_internal::persistent_grid_items(p.max_units * (long long)a.num_kv_heads,
-                                                           per_cu);
+                                                           per_cu * pa_internal::kDecodeGridRounds);
   if (grid == 0) return 6;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.q, a.k_pool,
                      a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc, a.plan,
