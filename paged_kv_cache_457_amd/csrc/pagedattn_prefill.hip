@@ -13,8 +13,9 @@
 // tokens) = kRows query rows, row r = token r / G, query head g*G + r % G.
 // Each of the workgroup's waves carries 32 rows as two 16-row MFMA tiles.
 // Keys go through in tiles of kKeys that all waves share: the workgroup
-// stages a tile's K and V rows in LDS (double buffered; the next tile's
-// global loads are in flight in registers while the current tile is used).
+// loads a tile's K and V rows straight from global memory into LDS
+// (global_load_lds_dwordx4, no staging registers), three buffers deep, so
+// the loads of the tile two ahead are in flight while one tile is used.
 //
 //   q.K   S^T = K Q^T, v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 head_dim
 //         (one 16-byte LDS read per lane), B = 16 query rows (registers).
@@ -28,7 +29,7 @@
 //
 // Online softmax per row in log2 units with the scale folded in.  Keys at or
 // past the item's last position, and keys on pages whose id is outside the
-// pool, are staged as zeros (so a poisoned slot never reaches a multiply) and
+// pool, are loaded as zeros (so a poisoned slot never reaches a multiply) and
 // masked to -inf in S; a tile that lies wholly below a wave's first position
 // and on valid pages skips the per-key mask.
 #include <type_traits>
@@ -57,6 +58,30 @@ constexpr float kRescaleLog2 = 8.f; // lazy rescale threshold of the running max
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanRecord = pa_internal::kPrefillPlanRecord;  // ints per plan item
 constexpr int kBuckets = kPlanThreads - 1;  // plan size classes (key tiles); the last is open-ended
+
+// Source of the zero chunks staged for keys an item does not see: one
+// 16-byte chunk per lane of a wave.
+__device__ __attribute__((aligned(16))) uint32_t g_zero_chunks[64 * 4];
+
+// Wait until at most N vector-memory operations of this wave are
+// outstanding and all its LDS operations are done (s_waitcnt vmcnt(N)
+// lgkmcnt(0)).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the tile loop.  A fence would wait for every load
+// still writing LDS, including the tile two ahead; instead each wave waits
+// (wait_vmem) for its loads of the next tile and for its own LDS reads
+// before it arrives, and the empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int D, int BS, int G>
 struct PrefillShape {
@@ -213,7 +238,17 @@ __device__ __forceinline__ void prefill_item(
   using Sh = PrefillShape<D, BS, G>;
   constexpr int ROW = Sh::ROW, CPR = Sh::CPR, NC = Sh::NC, NN = Sh::NN, TILE = Sh::TILE;
   constexpr int LOADS = Sh::LOADS, TOK = Sh::TOK, PPT = Sh::PPT;
-  __shared__ __attribute__((aligned(16))) char s_kv[2][2][TILE];  // [buffer][K, V]
+  // three buffers of [K, V]; separate arrays, so the compiler can tell that
+  // reads of one buffer do not wait for the loads still filling another
+  __shared__ __attribute__((aligned(16))) char s_kv0[2][TILE];
+  __shared__ __attribute__((aligned(16))) char s_kv1[2][TILE];
+  __shared__ __attribute__((aligned(16))) char s_kv2[2][TILE];
+  auto kv_buf = [&](auto buf_c) -> char(*)[TILE] {
+    constexpr int buf = decltype(buf_c)::value;
+    if constexpr (buf == 0) return s_kv0;
+    else if constexpr (buf == 1) return s_kv1;
+    else return s_kv2;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -301,25 +336,30 @@ __device__ __forceinline__ void prefill_item(
   for (int l = 0; l < LOADS; ++l) {
     const int ci = l * kThreads + tid;
     lkey[l] = ci / CPR;
-    loff[l] = (lkey[l] % BS) * ROW + (ci % CPR) * 16;
+    loff[l] = (lkey[l] % BS) * ROW + swz<D>(lkey[l], ci % CPR) * 16;
   }
-  u32x4 rk[LOADS], rv[LOADS];
-  unsigned okbits = 0;
-  auto fetch = [&](int kt) {
-    okbits = 0;
+  const char *zero = reinterpret_cast<const char *>(g_zero_chunks) + 16 * lane;
+  // Tile kt into buffer buf, straight from global memory into LDS: each load
+  // instruction of a wave fills 64 consecutive 16-byte slots, lane i the
+  // slot of chunk column i % CPR in row i / CPR of that span, which holds
+  // the row's chunk swz(row, i % CPR) (the swizzle is an XOR, so it is its
+  // own inverse).  Chunks of keys the item does not see, or on pages
+  // outside the pool, come from a page of zeros.
+  auto fetch = [&](int kt, auto buf_c) {
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
       const int pj = kt * PPT + (l * kThreads + wtid) / CPR / BS;  // uniform
       const int bid = pj < npages ? bt[pj] : -1;
       const bool page_ok = (unsigned)bid < (unsigned)num_blocks;
+      const bool ok = page_ok && kt * kKeys + lkey[l] < kv_end;
       const size_t base = (size_t)(page_ok ? bid : 0) * page_stride;
-      okbits |= (unsigned)(page_ok && kt * kKeys + lkey[l] < kv_end) << l;
-      rk[l] = load16(kb + base + loff[l]);
-      rv[l] = load16(vb + base + loff[l]);
+      const int span = (l * kThreads + wtid) / CPR * ROW;  // uniform LDS offset
+      __builtin_amdgcn_global_load_lds(ok ? kb + base + loff[l] : zero,
+                                       (lds_char *)kv_buf(buf_c)[0] + span, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(ok ? vb + base + loff[l] : zero,
+                                       (lds_char *)kv_buf(buf_c)[1] + span, 16, 0, 0);
     }
   };
-  const int skey = tid / CPR;  // key row of this thread's first chunk
-  const int soff = skey * ROW + swz<D>(skey, tid % CPR) * 16;
   // tiles that hold a key the item does not see, or a page outside the pool
   auto tile_clean = [&](int kt) {
     bool ok = (kt + 1) * kKeys <= kv_end;
@@ -329,19 +369,6 @@ __device__ __forceinline__ void prefill_item(
       if (pj < npages) ok = ok && (unsigned)bt[pj] < (unsigned)num_blocks;
     }
     return ok;
-  };
-  auto stage = [&](int buf, bool clean) {
-    char *kd = s_kv[buf][0] + soff;
-    char *vd = s_kv[buf][1] + soff;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int l = 0; l < LOADS; ++l) {
-      // chunk l * kThreads + tid sits kThreads / CPR rows further per l
-      constexpr int kStep = kThreads / CPR * ROW;
-      const bool ok = clean || ((okbits >> l) & 1u);
-      *reinterpret_cast<u32x4 *>(kd + l * kStep) = ok ? rk[l] : z;
-      *reinterpret_cast<u32x4 *>(vd + l * kStep) = ok ? rv[l] : z;
-    }
   };
 
   // softmax state per row tile: running max m (scaled, log2 units), the
@@ -474,8 +501,8 @@ __device__ __forceinline__ void prefill_item(
     constexpr bool kMasked = decltype(masked_c)::value;
     constexpr int buf = decltype(buf_c)::value;
     constexpr int kParts = kKeys / 32;
-    const lds_char *ks = (const lds_char *)s_kv[buf][0];
-    const lds_char *vs = (const lds_char *)s_kv[buf][1];
+    const lds_char *ks = (const lds_char *)kv_buf(buf_c)[0];
+    const lds_char *vs = (const lds_char *)kv_buf(buf_c)[1];
     f32x4 sc[2][2][2];  // scores of two parts in flight: [slot][sub-tile][row tile]
     scores(ks, 0, sc[0]);
     if constexpr (AL) add_bias(sc[0], kt, 0);
@@ -492,44 +519,54 @@ __device__ __forceinline__ void prefill_item(
       if (h + 1 < kParts) update_max(sc[(h + 1) & 1]);
     }
   };
-  // one key tile: stage the next tile (fetched one tile ago) into the other
-  // buffer, fetch the one after, use this one; the buffer index is a
-  // compile-time constant so every LDS address is a lane offset plus an
-  // immediate
+  // one key tile: start the loads of the tile two ahead into the buffer
+  // that the previous tile left (read before the last barrier), use this
+  // one, then wait for the next tile's loads (the most recent ones may stay
+  // in flight) and meet at the barrier.  The buffer index is a compile-time
+  // constant, so every LDS address is a lane offset plus an immediate.
   auto step = [&](auto masked_c, auto buf_c, int kt) {
     constexpr int buf = decltype(buf_c)::value;
-    if (kt + 1 < kt_hi) {
-      stage(buf ^ 1, tile_clean(kt + 1));  // its previous contents were used before the last barrier
-      if (kt + 2 < kt_hi) fetch(kt + 2);
-    }
+    const bool ahead = kt + 2 < kt_hi;
+    if (ahead) fetch(kt + 2, std::integral_constant<int, (buf + 2) % 3>{});
     if (wave_live && kt * kKeys <= wmax) compute(masked_c, buf_c, kt);
-    __syncthreads();
+    if (ahead)
+      wait_vmem<2 * LOADS>();
+    else
+      wait_vmem<0>();
+    lds_barrier();
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
   using Clean = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, true>;
 
   // Each wave first runs the tiles that lie wholly below its first row's
   // position on valid pages (no per-key mask), then the rest.  Every wave
   // takes one barrier per tile, so the two loops of different waves stay in
-  // step.
-  // Buffer 0 holds the item's even tiles counted from kt_lo.
+  // step.  Buffer (kt - kt_lo) % 3 holds tile kt.
   if (kt_hi > kt_lo) {
-    fetch(kt_lo);
-    stage(0, tile_clean(kt_lo));
-    if (kt_lo + 1 < kt_hi) fetch(kt_lo + 1);
-    __syncthreads();
+    fetch(kt_lo, B0{});
+    if (kt_lo + 1 < kt_hi) {
+      fetch(kt_lo + 1, B1{});
+      wait_vmem<2 * LOADS>();
+    } else {
+      wait_vmem<0>();
+    }
+    lds_barrier();
     const int clean_end = wave_live ? min(kt_hi, max(kt_lo, (wmin + 1) / kKeys)) : kt_lo;
     int kt = kt_lo;
-    for (; kt + 1 < clean_end && tile_clean(kt) && tile_clean(kt + 1); kt += 2) {
+    for (; kt + 2 < clean_end && tile_clean(kt) && tile_clean(kt + 1) && tile_clean(kt + 2);
+         kt += 3) {
       step(Clean{}, B0{}, kt);
       step(Clean{}, B1{}, kt + 1);
+      step(Clean{}, B2{}, kt + 2);
     }
-    // kt - kt_lo is even here: the clean loop takes tiles in pairs
-    for (; kt < kt_hi; kt += 2) {
+    // kt - kt_lo is a multiple of 3 here: the clean loop takes tiles in threes
+    for (; kt < kt_hi; kt += 3) {
       step(Masked{}, B0{}, kt);
       if (kt + 1 < kt_hi) step(Masked{}, B1{}, kt + 1);
+      if (kt + 2 < kt_hi) step(Masked{}, B2{}, kt + 2);
     }
   }
 
