@@ -223,7 +223,8 @@ typedef struct pa_prefill_dims {
   int32_t num_blocks;          /* pages in each pool, >= 1 */
   int32_t dtype;               /* PA_DTYPE_BF16 (the only type built) */
   int32_t partition_size;      /* keys per split-K partition, a positive multiple
-                                  of 64; 0 = default: no split when the step has
+                                  of 128 (the kernel's key tile); 0 = default:
+                                  no split when the step has
                                   at least 1024 (block, kv-head) work items, else
                                   partitions of max(1024, ceil(capacity / parts))
                                   keys with parts = ceil(1024 / items), capacity =

@@ -119,7 +119,8 @@ int prefill_partition_tokens(int32_t num_kv_heads, int32_t block_size, const pa_
   const int64_t items = ((int64_t)d->num_tokens + tok - 1) / tok * num_kv_heads;
   if (items >= kPrefillTargetItems || items == 0) return 0;
   const int64_t parts = (kPrefillTargetItems + items - 1) / items;
-  int64_t kp = ((cap + parts - 1) / parts + 63) / 64 * 64;
+  constexpr int64_t tile = pa_internal::kPrefillKeyTile;
+  int64_t kp = ((cap + parts - 1) / parts + tile - 1) / tile * tile;
   if (kp < kMinPrefillPartition) kp = kMinPrefillPartition;
   return kp >= cap ? 0 : (int)kp;
 }
@@ -135,7 +136,7 @@ int check_prefill_dims(int32_t num_kv_heads, int32_t block_size, const pa_prefil
   if (!d) return PA_ERR_NULL;
   if (d->num_seqs < 0 || d->num_tokens < 0 || d->num_heads < 1 || num_kv_heads < 1 ||
       d->max_blocks_per_seq < 1 || d->num_blocks < 1 || d->partition_size < 0 ||
-      d->partition_size % 64 != 0)
+      d->partition_size % pa_internal::kPrefillKeyTile != 0)
     return PA_ERR_SHAPE;
   if (d->num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   if (d->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;  // matrix cores: bf16 only

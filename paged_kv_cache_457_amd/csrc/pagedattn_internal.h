@@ -22,6 +22,8 @@ constexpr int kPrefixUnitInts = 5;
 // and ints per prefill plan item
 constexpr int kPrefillRows = 256;
 constexpr int kPrefillPlanRecord = 3;
+// keys of a prefill LDS tile; split-K partitions are whole tiles
+constexpr int kPrefillKeyTile = 128;
 
 struct DecodeLaunch {
   void *out;
@@ -66,7 +68,7 @@ struct PrefillLaunch {
   int32_t *nparts;             // [num_tokens] key partitions of each row's block
   float *ws_ml;                // [num_tokens, num_heads, max_parts, 2]
   float *ws_acc;               // [num_tokens, num_heads, max_parts, head_dim]
-  int part_tokens = 0;         // keys per partition (a multiple of 64), 0: no split
+  int part_tokens = 0;         // keys per partition (whole key tiles), 0: no split
   int max_parts = 1;
   int num_seqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size;
   int max_blocks, num_blocks;

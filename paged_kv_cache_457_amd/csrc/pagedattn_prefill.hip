@@ -14,8 +14,8 @@
 // Each of the workgroup's waves carries 32 rows as two 16-row MFMA tiles.
 // Keys go through in tiles of kKeys that all waves share: the workgroup
 // loads a tile's K and V rows straight from global memory into LDS
-// (global_load_lds_dwordx4, no staging registers), three buffers deep, so
-// the loads of the tile two ahead are in flight while one tile is used.
+// (global_load_lds_dwordx4, no staging registers), double buffered: the
+// next tile's loads are in flight while one tile is used.
 //
 //   q.K   S^T = K Q^T, v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 head_dim
 //         (one 16-byte LDS read per lane), B = 16 query rows (registers).
@@ -53,35 +53,15 @@ constexpr int kWaves = 8;           // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // query rows of a work item
 static_assert(kRows == pa_internal::kPrefillRows, "rows per work item");
-constexpr int kKeys = 64;           // keys per LDS tile
+constexpr int kKeys = pa_internal::kPrefillKeyTile;  // keys per LDS tile
 constexpr float kRescaleLog2 = 8.f; // lazy rescale threshold of the running max
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanRecord = pa_internal::kPrefillPlanRecord;  // ints per plan item
 constexpr int kBuckets = kPlanThreads - 1;  // plan size classes (key tiles); the last is open-ended
 
-// Source of the zero chunks staged for keys an item does not see: one
+// Source of the zero chunks loaded for keys an item does not see: one
 // 16-byte chunk per lane of a wave.
 __device__ __attribute__((aligned(16))) uint32_t g_zero_chunks[64 * 4];
-
-// Wait until at most N vector-memory operations of this wave are
-// outstanding and all its LDS operations are done (s_waitcnt vmcnt(N)
-// lgkmcnt(0)).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier for the tile loop.  A fence would wait for every load
-// still writing LDS, including the tile two ahead; instead each wave waits
-// (wait_vmem) for its loads of the next tile and for its own LDS reads
-// before it arrives, and the empty asm statements keep the compiler from
-// moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 template <int D, int BS, int G>
 struct PrefillShape {
@@ -238,16 +218,13 @@ __device__ __forceinline__ void prefill_item(
   using Sh = PrefillShape<D, BS, G>;
   constexpr int ROW = Sh::ROW, CPR = Sh::CPR, NC = Sh::NC, NN = Sh::NN, TILE = Sh::TILE;
   constexpr int LOADS = Sh::LOADS, TOK = Sh::TOK, PPT = Sh::PPT;
-  // three buffers of [K, V]; separate arrays, so the compiler can tell that
-  // reads of one buffer do not wait for the loads still filling another
+  // two buffers of [K, V]; separate arrays, so the compiler can tell that
+  // reads of one buffer need not wait for the loads filling the other
   __shared__ __attribute__((aligned(16))) char s_kv0[2][TILE];
   __shared__ __attribute__((aligned(16))) char s_kv1[2][TILE];
-  __shared__ __attribute__((aligned(16))) char s_kv2[2][TILE];
   auto kv_buf = [&](auto buf_c) -> char(*)[TILE] {
-    constexpr int buf = decltype(buf_c)::value;
-    if constexpr (buf == 0) return s_kv0;
-    else if constexpr (buf == 1) return s_kv1;
-    else return s_kv2;
+    if constexpr (decltype(buf_c)::value == 0) return s_kv0;
+    else return s_kv1;
   };
 
   const int tid = threadIdx.x;
@@ -519,54 +496,38 @@ __device__ __forceinline__ void prefill_item(
       if (h + 1 < kParts) update_max(sc[(h + 1) & 1]);
     }
   };
-  // one key tile: start the loads of the tile two ahead into the buffer
-  // that the previous tile left (read before the last barrier), use this
-  // one, then wait for the next tile's loads (the most recent ones may stay
-  // in flight) and meet at the barrier.  The buffer index is a compile-time
-  // constant, so every LDS address is a lane offset plus an immediate.
+  // one key tile: start the loads of the next tile into the other buffer
+  // (read before the last barrier), use this one; the barrier's fence waits
+  // for the loads.  The buffer index is a compile-time constant, so every
+  // LDS address is a lane offset plus an immediate.
   auto step = [&](auto masked_c, auto buf_c, int kt) {
     constexpr int buf = decltype(buf_c)::value;
-    const bool ahead = kt + 2 < kt_hi;
-    if (ahead) fetch(kt + 2, std::integral_constant<int, (buf + 2) % 3>{});
+    if (kt + 1 < kt_hi) fetch(kt + 1, std::integral_constant<int, buf ^ 1>{});
     if (wave_live && kt * kKeys <= wmax) compute(masked_c, buf_c, kt);
-    if (ahead)
-      wait_vmem<2 * LOADS>();
-    else
-      wait_vmem<0>();
-    lds_barrier();
+    __syncthreads();
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  using B2 = std::integral_constant<int, 2>;
   using Clean = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, true>;
 
   // Each wave first runs the tiles that lie wholly below its first row's
   // position on valid pages (no per-key mask), then the rest.  Every wave
   // takes one barrier per tile, so the two loops of different waves stay in
-  // step.  Buffer (kt - kt_lo) % 3 holds tile kt.
+  // step.  Buffer 0 holds the item's even tiles counted from kt_lo.
   if (kt_hi > kt_lo) {
     fetch(kt_lo, B0{});
-    if (kt_lo + 1 < kt_hi) {
-      fetch(kt_lo + 1, B1{});
-      wait_vmem<2 * LOADS>();
-    } else {
-      wait_vmem<0>();
-    }
-    lds_barrier();
+    __syncthreads();
     const int clean_end = wave_live ? min(kt_hi, max(kt_lo, (wmin + 1) / kKeys)) : kt_lo;
     int kt = kt_lo;
-    for (; kt + 2 < clean_end && tile_clean(kt) && tile_clean(kt + 1) && tile_clean(kt + 2);
-         kt += 3) {
+    for (; kt + 1 < clean_end && tile_clean(kt) && tile_clean(kt + 1); kt += 2) {
       step(Clean{}, B0{}, kt);
       step(Clean{}, B1{}, kt + 1);
-      step(Clean{}, B2{}, kt + 2);
     }
-    // kt - kt_lo is a multiple of 3 here: the clean loop takes tiles in threes
-    for (; kt < kt_hi; kt += 3) {
+    // kt - kt_lo is even here: the clean loop takes tiles in pairs
+    for (; kt < kt_hi; kt += 2) {
       step(Masked{}, B0{}, kt);
       if (kt + 1 < kt_hi) step(Masked{}, B1{}, kt + 1);
-      if (kt + 2 < kt_hi) step(Masked{}, B2{}, kt + 2);
     }
   }
 

@@ -260,9 +260,9 @@ expect("prefill: heads not a multiple", prefill(pdims(num_heads=30)), _lib.PA_ER
 expect("prefill: negative rows", prefill(pdims(num_tokens=-1)), _lib.PA_ERR_SHAPE)
 expect("prefill: negative sequences", prefill(pdims(num_seqs=-1)), _lib.PA_ERR_SHAPE)
 expect("prefill: rows without sequences", prefill(pdims(num_tokens=5)), _lib.PA_ERR_SHAPE)
-expect("prefill: partition not a multiple of 64", prefill(pdims(partition_size=100)),
-       _lib.PA_ERR_SHAPE)
-expect("prefill: negative partition", prefill(pdims(partition_size=-64)), _lib.PA_ERR_SHAPE)
+expect("prefill: partition not a multiple of the 128-key tile",
+       prefill(pdims(partition_size=192)), _lib.PA_ERR_SHAPE)
+expect("prefill: negative partition", prefill(pdims(partition_size=-128)), _lib.PA_ERR_SHAPE)
 expect("prefill: zero blocks", prefill(pdims(num_blocks=0)), _lib.PA_ERR_SHAPE)
 expect("prefill: zero table columns", prefill(pdims(max_blocks_per_seq=0)), _lib.PA_ERR_SHAPE)
 expect("prefill: zero kv heads", prefill(pdims(), hkv=0), _lib.PA_ERR_SHAPE)
@@ -291,13 +291,13 @@ pf_need = lib.paged_attention_prefill_workspace_bytes(8, 16, ctypes.byref(pdims(
 # 100 rows, group 4: 2 blocks x 8 kv heads = 16 items; capacity 2048 keys,
 # partitions of max(1024, 2048 / 64) = 1024 keys -> P = 2
 expect("prefill: workspace bytes, default split", pf_need, pf_bytes(100, 32, 128, 2))
-expect("prefill: workspace bytes, explicit partition 192",
+expect("prefill: workspace bytes, explicit partition 384",
        lib.paged_attention_prefill_workspace_bytes(
-           8, 16, ctypes.byref(pdims(partition_size=192, **ROWS))), pf_bytes(100, 32, 128, 11))
+           8, 16, ctypes.byref(pdims(partition_size=384, **ROWS))), pf_bytes(100, 32, 128, 6))
 expect("prefill: too many items for int32",
        lib.paged_attention_prefill_workspace_bytes(
            8, 16, ctypes.byref(pdims(num_seqs=1, num_tokens=1 << 24, max_blocks_per_seq=1 << 12,
-                                     partition_size=64))), _lib.SIZE_MAX)
+                                     partition_size=128))), _lib.SIZE_MAX)
 ppt = lib.paged_attention_prefill_partition_tokens
 expect("prefill partition: default, few items", ppt(8, 16, ctypes.byref(pdims(**ROWS))), 1024)
 expect("prefill partition: default, capacity 1024", ppt(

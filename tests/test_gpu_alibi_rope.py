@@ -122,7 +122,7 @@ def test_prefill_alibi_tiny():
 
 
 PAL = [(64, 16, 1, 0), (128, 32, 2, 0), (128, 16, 4, 0), (64, 32, 8, 0),
-       (64, 16, 1, 64), (128, 32, 2, 192), (128, 16, 4, 128), (64, 32, 8, 64)]
+       (64, 16, 1, 128), (128, 32, 2, 384), (128, 16, 4, 128), (64, 32, 8, 256)]
 
 
 @pytest.mark.parametrize("D,bs,G,ps", PAL, ids=[f"D{a}-bs{b}-G{c}-ps{d}" for a, b, c, d in PAL])

@@ -103,12 +103,12 @@ def test_prefill_variants(D, bs, G):
     assert err <= TOL
 
 
-# Split-K: each block's keys in partitions of `ps` (a multiple of the 64-key
+# Split-K: each block's keys in partitions of `ps` (a multiple of the 128-key
 # tile; odd tile counts start partitions on either LDS buffer), merged by the
 # reduce kernel.  Lengths leave partial last partitions and early rows that
 # see none of a late partition's keys.
-SPLIT = [(64, 16, 1, 64), (64, 32, 4, 192), (64, 16, 8, 128), (128, 16, 1, 320),
-         (128, 32, 2, 128), (128, 16, 4, 64), (128, 16, 8, 192), (128, 32, 4, 256)]
+SPLIT = [(64, 16, 1, 128), (64, 32, 4, 384), (64, 16, 8, 256), (128, 16, 1, 640),
+         (128, 32, 2, 128), (128, 16, 4, 384), (128, 16, 8, 128), (128, 32, 4, 256)]
 
 
 @pytest.mark.parametrize("D,bs,G,ps", SPLIT, ids=[f"D{a}-bs{b}-G{c}-ps{d}" for a, b, c, d in SPLIT])
@@ -145,9 +145,9 @@ def test_prefill_long_context_default_split_sampled_rows():
         assert gpu_prefill(dw, write=False).tobytes() == got.tobytes()
 
 
-@pytest.mark.parametrize("ps", [0, 64])
+@pytest.mark.parametrize("ps", [0, 128])
 def test_prefill_empty_sequences_and_exact_tile_edges(ps):
-    # a sequence with no rows, chunks ending exactly on 64-key tiles and pages
+    # a sequence with no rows, chunks ending exactly on 64- and 128-key tiles and pages
     cached = np.array([64, 0, 3, 128, 16])
     new = np.array([64, 0, 61, 128, 48])
     w = build_workload("edges", cached + new, 8, 2, 128, 16, "bf16", seed=77, new_tokens=new)
@@ -157,7 +157,7 @@ def test_prefill_empty_sequences_and_exact_tile_edges(ps):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("ps", [0, 64])
+@pytest.mark.parametrize("ps", [0, 128])
 def test_prefill_rows_outside_every_sequence_untouched(ps):
     cached, new = np.array([10, 30]), np.array([20, 9])
     w = build_workload("untouched", cached + new, 4, 4, 64, 16, "bf16", seed=5, new_tokens=new)
@@ -176,7 +176,7 @@ def test_prefill_rows_outside_every_sequence_untouched(ps):
     assert max_err(got[:w.num_tokens], oracle_prefill(w)) <= TOL
 
 
-@pytest.mark.parametrize("ps", [0, 64])
+@pytest.mark.parametrize("ps", [0, 128])
 def test_prefill_more_rows_than_context(ps):
     """Rows at a position below 0 see nothing and are zeros; the others are
     the oracle over the sequence's last ctx rows."""
@@ -197,7 +197,7 @@ def test_prefill_more_rows_than_context(ps):
     assert float(np.max(np.abs(g[30:] - ref[30:]))) <= TOL
 
 
-@pytest.mark.parametrize("ps", [0, 64])
+@pytest.mark.parametrize("ps", [0, 128])
 def test_prefill_out_of_range_page_id_is_skipped(ps):
     """A used table entry outside the pool drops that page's tokens, which
     equals the oracle over the sequence without the page (an interior,
