@@ -72,7 +72,8 @@ def parse():
 # valid only while their combined hash is unchanged.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_457_amd", "csrc")
 KERNEL_SOURCES = {
-    "pa_prefill_gqa": ["pagedattn_prefill.hip", "pagedattn_device.h", "pagedattn_internal.h"],
+    "pa_prefill_gqa": ["pagedattn_prefill.hip", "pagedattn_device.h", "pagedattn_internal.h",
+                       "pagedattn_prefill_launch.h"],
     "pa_decode_prefix_gqa": ["pagedattn_decode_prefix.hip", "pagedattn_device.h",
                              "pagedattn_internal.h"],
     "pa_decode_partition": ["pagedattn_decode.hip", "pagedattn_device.h", "pagedattn_internal.h"],

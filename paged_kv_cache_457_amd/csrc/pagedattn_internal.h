@@ -18,12 +18,6 @@ constexpr int kMaxDevices = 64;
 // unit serves, and the ints of one unit record in the plan.
 constexpr int kPrefixRows = 32;
 constexpr int kPrefixUnitInts = 5;
-// query rows of a prefill work item (token x head of one kv-head's group),
-// and ints per prefill plan item
-constexpr int kPrefillRows = 256;
-constexpr int kPrefillPlanRecord = 3;
-// keys of a prefill LDS tile; split-K partitions are whole tiles
-constexpr int kPrefillKeyTile = 128;
 
 struct DecodeLaunch {
   void *out;
@@ -54,29 +48,6 @@ struct PrefixLaunch {
   int32_t *nslots;              // [num_seqs] slots each sequence fills
   int32_t *seq_pre;             // [num_seqs] shared prefix pages of its group
   long long max_units;          // bound on the plan's units
-};
-
-struct PrefillLaunch {
-  void *out;
-  const void *q;
-  const void *k_pool;
-  const void *v_pool;
-  const int32_t *block_tables;
-  const int32_t *context_lens;
-  const int32_t *query_start;  // [num_seqs + 1]
-  int32_t *plan;               // item list written by the plan kernel
-  int32_t *nparts;             // [num_tokens] key partitions of each row's block
-  float *ws_ml;                // [num_tokens, num_heads, max_parts, 2]
-  float *ws_acc;               // [num_tokens, num_heads, max_parts, head_dim]
-  int part_tokens = 0;         // keys per partition (whole key tiles), 0: no split
-  int max_parts = 1;
-  int num_seqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size;
-  int max_blocks, num_blocks;
-  float scale;
-  void *stream;
-  void *ev_begin;
-  void *ev_end;
-  const float *alibi = nullptr;  // [num_heads] ALiBi slopes, or none
 };
 
 struct CacheLaunch {
@@ -132,8 +103,6 @@ unsigned decode_grid(const DecodeLaunch &a, int per_cu);
 int launch_decode_shared_prefix(const PrefixLaunch &p);
 int launch_prefix_plan(const PrefixLaunch &p);
 int launch_prefix_units(const PrefixLaunch &p, float scale_log2);
-// multi-token attention: plan kernel, then the persistent item pass
-int launch_prefill(const PrefillLaunch &a);
 int launch_reshape_and_cache(const CacheLaunch &a);
 int launch_reshape_and_cache_rope(const RopeLaunch &r);
 // Also PA_ERR_UNSUPPORTED (3) when a pointer is not device-accessible.

@@ -36,6 +36,7 @@
 
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
+#include "pagedattn_prefill_launch.h"
 
 namespace {
 
