@@ -330,8 +330,10 @@ __device__ __forceinline__ void prefill_item(
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
       const int pj = kt * PPT + (l * kThreads + wtid) / CPR / BS;  // uniform
-      const int bid = pj < npages ? bt[pj] : -1;
-      const bool page_ok = (unsigned)bid < (unsigned)num_blocks;
+      // unconditional scalar loads (the index is clamped to the row), so
+      // the compiler issues them together and waits once
+      const int bid = bt[min(pj, max_blocks - 1)];
+      const bool page_ok = pj < npages && (unsigned)bid < (unsigned)num_blocks;
       const bool ok = page_ok && kt * kKeys + lkey[l] < kv_end;
       const size_t base = (size_t)(page_ok ? bid : 0) * page_stride;
       const int span = (l * kThreads + wtid) / CPR * ROW;  // uniform LDS offset
@@ -341,13 +343,16 @@ __device__ __forceinline__ void prefill_item(
                                        (lds_char *)kv_buf(buf_c)[1] + span, 16, 0, 0);
     }
   };
-  // tiles that hold a key the item does not see, or a page outside the pool
+  // tiles that hold no key the item does not see and no page outside the
+  // pool; the table reads are unconditional (index clamped to the row) so
+  // they issue together with one wait
   auto tile_clean = [&](int kt) {
     bool ok = (kt + 1) * kKeys <= kv_end;
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int pj = kt * PPT + j;
-      if (pj < npages) ok = ok && (unsigned)bt[pj] < (unsigned)num_blocks;
+      const int id = bt[min(pj, max_blocks - 1)];
+      ok = ok & (pj >= npages || (unsigned)id < (unsigned)num_blocks);
     }
     return ok;
   };
@@ -362,17 +367,26 @@ __device__ __forceinline__ void prefill_item(
     for (int nb = 0; nb < NN; ++nb) o[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // S^T for one 32-key half of a tile (two 16-key sub-tiles, both row tiles)
-  auto scores = [&](const lds_char *ks, int h, f32x4 (&sacc)[2][2]) {
+  // K operands of one 32-key part: two 16-key sub-tiles x NC head_dim slabs
+  auto load_k = [&](const lds_char *ks, int h, bf16x8 (&ka)[2][NC]) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+        ka[st][cc] = *(const __attribute__((address_space(3))) bf16x8 *)(
+            ks + (32 * h + 16 * st) * ROW + koff[cc]);
+  };
+  auto scores = [&](const bf16x8 (&ka)[2][NC], f32x4 (&sacc)[2][2]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       sacc[st][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       sacc[st][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
-        const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8 *)(
-            ks + (32 * h + 16 * st) * ROW + koff[cc]);
-        sacc[st][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][cc], sacc[st][0], 0, 0, 0);
-        sacc[st][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][cc], sacc[st][1], 0, 0, 0);
+        sacc[st][0] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[st][cc], qf[0][cc], sacc[st][0], 0, 0, 0);
+        sacc[st][1] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[st][cc], qf[1][cc], sacc[st][1], 0, 0, 0);
       }
     }
   };
@@ -484,15 +498,21 @@ __device__ __forceinline__ void prefill_item(
     constexpr int kParts = kKeys / 32;
     const lds_char *ks = (const lds_char *)kv_buf(buf_c)[0];
     const lds_char *vs = (const lds_char *)kv_buf(buf_c)[1];
-    f32x4 sc[2][2][2];  // scores of two parts in flight: [slot][sub-tile][row tile]
-    scores(ks, 0, sc[0]);
+    f32x4 sc[2][2][2];     // scores of two parts in flight: [slot][sub-tile][row tile]
+    bf16x8 ka[2][NC];      // K operands of one part
+    load_k(ks, 0, ka);
+    scores(ka, sc[0]);
     if constexpr (AL) add_bias(sc[0], kt, 0);
     if constexpr (kMasked) mask(sc[0], kt, 0);
     update_max(sc[0]);
 #pragma unroll
     for (int h = 0; h < kParts; ++h) {
+      // keep the scheduler from hoisting one part's LDS reads into another's
+      // work, which would raise register pressure past the budget
+      __builtin_amdgcn_sched_barrier(0);
       if (h + 1 < kParts) {
-        scores(ks, h + 1, sc[(h + 1) & 1]);
+        load_k(ks, h + 1, ka);
+        scores(ka, sc[(h + 1) & 1]);
         if constexpr (AL) add_bias(sc[(h + 1) & 1], kt, h + 1);
         if constexpr (kMasked) mask(sc[(h + 1) & 1], kt, h + 1);
       }
