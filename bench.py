@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--shared-prefix", action="store_true",
                     help="decode through paged_attention_decode_shared_prefix, using the "
                          "workload's groups of samples that share prompt pages (config 5)")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode-step: also capture one step (cache write + attention) in a HIP "
+                         "graph and time --steps replays (graph_ms_per_step; value stays the "
+                         "eager rate)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run a plain device copy of this many MiB "
                          "5 times, so a counter run can scale FETCH_SIZE / WRITE_SIZE")
@@ -534,6 +538,31 @@ def main():
     k1_ms = [a.elapsed_time(b) for a, b in evs]
     k1_avg_ms = float(np.mean(k1_ms))
 
+    graph_ms = None
+    if args.graph:
+        # the same step, captured once and replayed: launches leave the host path
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ga = torch.cuda.Event(enable_timing=True)
+        gb = torch.cuda.Event(enable_timing=True)
+        ga.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        gb.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = ga.elapsed_time(gb) / args.steps
+        del g
+
     kv_bytes = w.kv_bytes()
     # the shared-prefix pass must read each physical page once: its
     # algorithmic bytes are the unique bytes
@@ -601,6 +630,8 @@ def main():
         "kv_read_gbs_step": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
         "kv_read_frac_of_peak_step": round(kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "partition_kernel_ms": round(k1_avg_ms, 5),
+        **({"graph_ms_per_step": round(graph_ms, 5),
+            "graph_tokens_per_s": round(w.num_seqs / (graph_ms * 1e-3), 1)} if graph_ms else {}),
         "wall_s_timed_region": round(t_wall, 4),
         "roofline": {
             "bound": "hbm",
