@@ -364,22 +364,26 @@ def bench_prefill(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+    # the attention pass alone: K more steps with an event pair around it
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for a, b in evs:
         a.record(stream)
         b.record(stream)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record(stream)
     for i in range(args.steps):
         step(evs[i])
-    end.record(stream)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_step = start.elapsed_time(end) / args.steps
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     if args.copy_calibration_mib:
@@ -517,24 +521,30 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # one event pair per timed step, recorded by the library on its stream
-    # right before and after the partition kernel
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:
-        a.record(stream)
-        b.record(stream)
+    # the timed region: K plain steps, nothing recorded inside them
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(end) / args.steps
+
+    # then K more steps with one event pair each, recorded by the library on
+    # its stream right before and after the partition kernel
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     k1_ms = [a.elapsed_time(b) for a, b in evs]
     k1_avg_ms = float(np.mean(k1_ms))
 

@@ -15,25 +15,52 @@ namespace {
 using namespace pa_dev;
 
 // ------------------------------------------------------------ cache write
-// Grid (num_tokens), 256 threads.  Copies token t's K and V rows, all
-// kv-heads, 16 bytes per lane, to page slot / bs at offset slot % bs.
-__global__ __launch_bounds__(256) void pa_reshape_and_cache(
+// Grid (num_tokens), kCacheThreads threads.  Copies token t's K and V rows,
+// all kv-heads, 16 bytes per lane, to page slot / bs at offset slot % bs.
+// The first kCacheHeld chunks per thread (8 KiB of K and of V per token:
+// 32 kv-heads of 128 bf16) are loaded before the slot is known, so the
+// source reads and the slot read are in flight together.
+constexpr int kCacheThreads = 256;
+constexpr int kCacheHeld = 2;
+
+__global__ __launch_bounds__(kCacheThreads) void pa_reshape_and_cache(
     const u32x4 *__restrict__ k, const u32x4 *__restrict__ v, u32x4 *__restrict__ k_pool,
     u32x4 *__restrict__ v_pool, const int64_t *__restrict__ slot_mapping, int num_kv_heads,
     int row_chunks, int block_size, int64_t num_slots) {
   const int t = blockIdx.x;
+  const int total = num_kv_heads * row_chunks;
+  const u32x4 *k_row = k + (size_t)t * total;
+  const u32x4 *v_row = v + (size_t)t * total;
+  u32x4 kh[kCacheHeld], vh[kCacheHeld];
+#pragma unroll
+  for (int i = 0; i < kCacheHeld; ++i) {
+    const int c = threadIdx.x + i * kCacheThreads;
+    if (c < total) {
+      kh[i] = k_row[c];
+      vh[i] = v_row[c];
+    }
+  }
   const int64_t slot = slot_mapping[t];
   if (slot < 0 || slot >= num_slots) return;
   const int64_t page = slot / block_size;
   const int64_t off = slot - page * block_size;
-  const int total = num_kv_heads * row_chunks;
-  for (int c = threadIdx.x; c < total; c += blockDim.x) {
+  // chunk c of the token (kv-head c / row_chunks) to its slot row in that head's page
+  auto dst = [&](int c) {
     const int g = c / row_chunks;
     const int dc = c - g * row_chunks;
-    const size_t src = ((size_t)t * num_kv_heads + g) * row_chunks + dc;
-    const size_t dst = (((size_t)page * num_kv_heads + g) * block_size + off) * row_chunks + dc;
-    k_pool[dst] = k[src];
-    v_pool[dst] = v[src];
+    return (((size_t)page * num_kv_heads + g) * block_size + off) * row_chunks + dc;
+  };
+#pragma unroll
+  for (int i = 0; i < kCacheHeld; ++i) {
+    const int c = threadIdx.x + i * kCacheThreads;
+    if (c < total) {
+      k_pool[dst(c)] = kh[i];
+      v_pool[dst(c)] = vh[i];
+    }
+  }
+  for (int c = threadIdx.x + kCacheHeld * kCacheThreads; c < total; c += kCacheThreads) {
+    k_pool[dst(c)] = k_row[c];
+    v_pool[dst(c)] = v_row[c];
   }
 }
 
@@ -233,7 +260,7 @@ namespace pa_internal {
 int launch_reshape_and_cache(const CacheLaunch &a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   const int row_chunks = a.head_dim * a.elem_bytes / 16;
-  hipLaunchKernelGGL(pa_reshape_and_cache, dim3(a.num_tokens), dim3(256), 0, st,
+  hipLaunchKernelGGL(pa_reshape_and_cache, dim3(a.num_tokens), dim3(kCacheThreads), 0, st,
                      reinterpret_cast<const u32x4 *>(a.k), reinterpret_cast<const u32x4 *>(a.v),
                      reinterpret_cast<u32x4 *>(a.k_pool), reinterpret_cast<u32x4 *>(a.v_pool),
                      a.slot_mapping, a.num_kv_heads, row_chunks, a.block_size,
