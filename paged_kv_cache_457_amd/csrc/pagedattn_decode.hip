@@ -297,14 +297,16 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_partition(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
-    float *__restrict__ ws_acc, const int32_t *__restrict__ plan, int num_heads,
+    float *__restrict__ ws_acc, const int32_t *__restrict__ plan, int num_seqs, int num_heads,
     int num_kv_heads, int max_blocks, int num_blocks, int part_pages, int max_parts,
     float scale_log2, const float *__restrict__ alibi) {
-  const int items = plan[0] * num_kv_heads;
+  // the list holds num_seqs * max_parts entries, -1 past the last unit
+  const long long bound = (long long)num_seqs * max_parts * num_kv_heads;
   for (int k = 0;; ++k) {
     const int it = snake_item(k);
-    if (it >= items) break;
+    if (it >= bound) break;
     const int unit = plan[kPlanHeader + it / num_kv_heads];
+    if (unit < 0) break;
     decode_unit<T, D, BS, G, NW, AL>(out, q, k_pool, v_pool, block_tables, context_lens, ws_ml,
                                      ws_acc, num_heads, num_kv_heads, max_blocks, num_blocks,
                                      part_pages, max_parts, scale_log2, alibi, unit / max_parts,
@@ -314,15 +316,17 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_partition(
 }
 
 // ----------------------------------------------------------- decode, plan
-// One workgroup orders the (sequence, partition) units for the persistent
-// partition kernels: a counting sort by page count, largest first, so the
-// shortest units finish the pass and no workgroup starts a long unit at the
-// end.  A sequence with context 0 gets one unit of size 0 (its output rows
-// are written as zeros).  Layout: plan[0] = unit count, plan[kPlanHeader +
-// k] = sequence * max_parts + partition.  Threads take candidate units
-// (sequence, partition) in turn, so short batches of long sequences spread
-// over the workgroup too.  Units of equal size are placed in
-// arbitrary order; results do not depend on the order units run in.
+// One workgroup orders the (sequence, partition) units for the partition
+// kernels: a counting sort by page count, largest first, so the shortest
+// units finish the pass and no workgroup starts a long unit at the end.  A
+// sequence with context 0 gets one unit of size 0 (its output rows are
+// written as zeros).  Layout: plan[0] = unit count, plan[kPlanHeader + k] =
+// sequence * max_parts + partition for k below the count, -1 from there to
+// num_seqs * max_parts, so a partition workgroup finds its unit, or that it
+// has none, with one load.  Threads take candidate units (sequence,
+// partition) in turn, so short batches of long sequences spread over the
+// workgroup too.  Units of equal size are placed in arbitrary order; results
+// do not depend on the order units run in.
 constexpr int kPlanThreads = 1024;
 
 __global__ __launch_bounds__(kPlanThreads) void pa_decode_plan(
@@ -330,6 +334,7 @@ __global__ __launch_bounds__(kPlanThreads) void pa_decode_plan(
     int ctx_cap, int block_size, int part_pages, int max_parts) {
   __shared__ int s_count[kMaxPartitionPages + 1];  // units per size 0..part_pages
   __shared__ int s_next[kMaxPartitionPages + 1];   // next free slot per size
+  __shared__ int s_total;
   // size of candidate unit u = (sequence u / max_parts, partition u % max_parts):
   // its page count, 0 for the single unit of an empty sequence, -1 if none
   auto unit_size = [&](int u) {
@@ -348,19 +353,42 @@ __global__ __launch_bounds__(kPlanThreads) void pa_decode_plan(
     if (z >= 0) atomicAdd(&s_count[z], 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int at = 0;
-    for (int z = part_pages; z >= 0; --z) {
-      s_next[z] = at;
-      at += s_count[z];
+  if (threadIdx.x < 64) {
+    // first list position of each size, sizes taken from part_pages down to
+    // 0: lane l owns positions l*per .. l*per + per - 1 of that walk
+    const int lane = threadIdx.x;
+    const int per = (part_pages + 64) / 64;
+    int mine = 0;
+    for (int k = 0; k < per; ++k) {
+      const int i = lane * per + k;
+      if (i <= part_pages) mine += s_count[part_pages - i];
     }
-    plan[0] = at;
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    int at = incl - mine;
+    for (int k = 0; k < per; ++k) {
+      const int i = lane * per + k;
+      if (i <= part_pages) {
+        s_next[part_pages - i] = at;
+        at += s_count[part_pages - i];
+      }
+    }
+    if (lane == 63) {
+      plan[0] = incl;
+      s_total = incl;
+    }
   }
   __syncthreads();
   for (int u = threadIdx.x; u < candidates; u += kPlanThreads) {
     const int z = unit_size(u);
     if (z >= 0) plan[kPlanHeader + atomicAdd(&s_next[z], 1)] = u;
   }
+  for (int k = s_total + threadIdx.x; k < candidates; k += kPlanThreads)
+    plan[kPlanHeader + k] = -1;
 }
 
 // ------------------------------------------------- decode, log-sum-exp merge
@@ -468,8 +496,8 @@ int launch_valu_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
   if (grid == 0) return 6;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.out, a.q,
                      a.k_pool, a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc,
-                     a.plan, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
-                     a.part_pages, a.max_parts, scale_log2, a.alibi);
+                     a.plan, a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks,
+                     a.num_blocks, a.part_pages, a.max_parts, scale_log2, a.alibi);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

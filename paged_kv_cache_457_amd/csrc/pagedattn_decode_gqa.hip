@@ -283,14 +283,16 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_partition_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
-    float *__restrict__ ws_acc, const int32_t *__restrict__ plan, int num_heads,
+    float *__restrict__ ws_acc, const int32_t *__restrict__ plan, int num_seqs, int num_heads,
     int num_kv_heads, int max_blocks, int num_blocks, int part_pages, int max_parts,
     float scale_log2, const float *__restrict__ alibi) {
-  const int items = plan[0] * num_kv_heads;
+  // the list holds num_seqs * max_parts entries, -1 past the last unit
+  const long long bound = (long long)num_seqs * max_parts * num_kv_heads;
   for (int k = 0;; ++k) {
     const int it = snake_item(k);
-    if (it >= items) break;
+    if (it >= bound) break;
     const int unit = plan[pa_internal::kPlanHeader + it / num_kv_heads];
+    if (unit < 0) break;
     decode_unit_gqa<D, BS, G, NW, AL>(out, q, k_pool, v_pool, block_tables, context_lens,
                                       ws_ml, ws_acc, num_heads, num_kv_heads, max_blocks,
                                       num_blocks, part_pages, max_parts, scale_log2, alibi,
@@ -311,8 +313,8 @@ int launch_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
   if (grid == 0) return 6;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.out, a.q, a.k_pool,
                      a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc, a.plan,
-                     a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks, a.part_pages,
-                     a.max_parts, scale_log2, a.alibi);
+                     a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
+                     a.part_pages, a.max_parts, scale_log2, a.alibi);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
