@@ -548,6 +548,27 @@ def main():
     k1_ms = [a.elapsed_time(b) for a, b in evs]
     k1_avg_ms = float(np.mean(k1_ms))
 
+    # the decode access pattern without its arithmetic, on the same inputs:
+    # the read rate the partition kernel's loads can reach on this device
+    pattern_ms = None
+    if not args.shared_prefix:
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in pev:
+            a.record(stream)
+            b.record(stream)
+        for _ in range(3):
+            binding.paged_attention_decode_read_probe(
+                dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables, dw.context_lens,
+                partition_size=args.partition_size, workspace=ws)
+        torch.cuda.synchronize()
+        for a, b in pev:
+            binding.paged_attention_decode_read_probe(
+                dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables, dw.context_lens,
+                partition_size=args.partition_size, workspace=ws, timing_events=(a, b))
+        torch.cuda.synchronize()
+        pattern_ms = float(np.mean([a.elapsed_time(b) for a, b in pev]))
+
     graph_ms = None
     if args.graph:
         # the same step, captured once and replayed: launches leave the host path
@@ -653,6 +674,13 @@ def main():
             "traffic": traffic,
         },
     }
+    if pattern_ms:
+        pattern_gbs = kv_bytes / (pattern_ms * 1e-3) / 1e9
+        result["decode_pattern_probe"] = {
+            "kernel_ms": round(pattern_ms, 5),
+            "read_gbs": round(pattern_gbs, 1),
+            "partition_kernel_frac_of_probe": round(achieved / pattern_gbs, 4),
+        }
     if w.unique_kv_bytes() != kv_bytes:
         result["unique_kv_read_gbs_step"] = round(w.unique_kv_bytes() / (ms_step * 1e-3) / 1e9, 1)
     if probe_gbs is not None:

@@ -423,6 +423,28 @@ const char *pa_status_string(int status);
 int pa_hbm_read_probe(const void *buf, size_t bytes, void *sink, void *stream);
 size_t pa_hbm_read_probe_sink_bytes(void);
 
+/*
+ * Measurement kernel: the access pattern of paged_attention_decode without
+ * its arithmetic.  Takes the same arguments, checks and workspace, runs the
+ * same plan kernel, and then reads exactly the K and V pages the partition
+ * kernels would read, in their order and with their load shapes: items
+ * (unit, kv-head) largest unit first, one workgroup of 4 wavefronts per
+ * item, the unit's pages dealt to the wavefronts in turn, each (page,
+ * kv-head) run as 16-byte non-temporal loads.  Instead of attention it
+ * stores, for each item, the XOR of every 16-byte word it loaded in the
+ * first 16 bytes of the output row of the item's first query head
+ * (h = kv-head * num_heads / num_kv_heads); nothing else in `out` is
+ * written, and a sequence's partitions overwrite each other's word.
+ * timing_events bracket the read kernel.  Its rate, the decode call's KV
+ * bytes over its duration, is the read bandwidth the decode access pattern
+ * reaches on the device: the ceiling for the partition kernels.
+ */
+int paged_attention_decode_read_probe(void *out, const void *q, const void *k_pool,
+                                      const void *v_pool, const int32_t *block_tables,
+                                      const int32_t *context_lens, int32_t num_kv_heads,
+                                      float scale, int32_t block_size,
+                                      const pa_decode_dims *dims);
+
 #ifdef __cplusplus
 }
 #endif

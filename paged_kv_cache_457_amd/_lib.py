@@ -141,6 +141,10 @@ SIGNATURES = {
     "pa_hbm_read_probe": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "pa_hbm_read_probe_sink_bytes": (ctypes.c_size_t, []),
+    "paged_attention_decode_read_probe": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+        ctypes.c_int32, ctypes.POINTER(DecodeDims)]),
 }
 
 _lib = None

@@ -98,7 +98,8 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
                            context_lens: torch.Tensor, scale: Optional[float] = None,
                            partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
                            stream=None, timing_events: Sequence = (None, None),
-                           alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
+                           alibi_slopes: Optional[torch.Tensor] = None,
+                           _entry: str = "paged_attention_decode") -> torch.Tensor:
     """out[S,H,D] <- paged decode attention (see paged_attention_decode in
     include/pagedattn.h).  Pools are [num_blocks, num_kv_heads, block_size,
     head_dim]; the kv-head count and block size are read off k_pool.
@@ -143,12 +144,27 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
             hkv, ctypes.c_float(scale), bs, _dev(alibi_slopes, "alibi_slopes"), ctypes.byref(d))
         _check(rc, "paged_attention_decode_alibi")
         return out
-    rc = lib.paged_attention_decode(
+    rc = getattr(lib, _entry)(
         _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
         _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
         hkv, ctypes.c_float(scale), bs, ctypes.byref(d))
-    _check(rc, "paged_attention_decode")
+    _check(rc, _entry)
     return out
+
+
+def paged_attention_decode_read_probe(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                                      v_pool: torch.Tensor, block_tables: torch.Tensor,
+                                      context_lens: torch.Tensor, partition_size: int = 0,
+                                      workspace: Optional[torch.Tensor] = None, stream=None,
+                                      timing_events: Sequence = (None, None)) -> torch.Tensor:
+    """The decode access pattern without its arithmetic (see
+    paged_attention_decode_read_probe in include/pagedattn.h): same
+    arguments as paged_attention_decode; ``out`` receives one XOR word per
+    item, not attention."""
+    return paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
+                                  partition_size=partition_size, workspace=workspace,
+                                  stream=stream, timing_events=timing_events,
+                                  _entry="paged_attention_decode_read_probe")
 
 
 def paged_attention_decode_shared_prefix(

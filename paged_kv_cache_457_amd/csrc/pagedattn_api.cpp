@@ -170,7 +170,8 @@ size_t prefill_workspace_bytes(int32_t num_kv_heads, int32_t block_size, const p
 
 int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                 const int32_t *block_tables, const int32_t *context_lens, int32_t num_kv_heads,
-                float scale, int32_t block_size, const float *alibi, const pa_decode_dims *dims);
+                float scale, int32_t block_size, const float *alibi, const pa_decode_dims *dims,
+                bool read_probe = false);
 int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                  const int32_t *block_tables, const int32_t *context_lens,
                  const int32_t *query_start, int32_t num_kv_heads, float scale,
@@ -293,13 +294,23 @@ int paged_attention_decode_alibi(void *out, const void *q, const void *k_pool,
                      block_size, alibi_slopes, dims);
 }
 
+int paged_attention_decode_read_probe(void *out, const void *q, const void *k_pool,
+                                      const void *v_pool, const int32_t *block_tables,
+                                      const int32_t *context_lens, int32_t num_kv_heads,
+                                      float scale, int32_t block_size,
+                                      const pa_decode_dims *dims) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_kv_heads, scale,
+                     block_size, nullptr, dims, true);
+}
+
 }  // extern "C"
 
 namespace {
 
 int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                 const int32_t *block_tables, const int32_t *context_lens, int32_t num_kv_heads,
-                float scale, int32_t block_size, const float *alibi, const pa_decode_dims *dims) {
+                float scale, int32_t block_size, const float *alibi, const pa_decode_dims *dims,
+                bool read_probe) {
   if (!dims) return PA_ERR_NULL;
   int rc = check_decode_dims(num_kv_heads, block_size, dims);
   if (rc != PA_OK) return rc;
@@ -347,7 +358,7 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
   a.ev_begin = dims->timing_events[0];
   a.ev_end = dims->timing_events[1];
   a.alibi = alibi;
-  return pa_internal::launch_decode(a);
+  return read_probe ? pa_internal::launch_decode_read_probe(a) : pa_internal::launch_decode(a);
 }
 
 }  // namespace

@@ -1,4 +1,4 @@
-// KV-cache write, whole-page copies, and the HBM read probe.
+// KV-cache write, whole-page copies, and the read-bandwidth probes.
 //
 // Each decode step produces the next token together with the updated KV
 // cache (tutorial page, section 4.3, step 3 of the iteration): the new
@@ -253,6 +253,107 @@ __global__ __launch_bounds__(kProbeThreads) void pa_hbm_probe(const u32x4 *__res
   }
   sink[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = x;
 }
+// ------------------------------------------ decode access-pattern probe
+// Reads the K and V bytes a decode call reads, in the order the partition
+// kernels read them: items (unit, kv-head) of the plan's list, largest units
+// first, kv-head fastest, in the snake rounds of snake_item; one workgroup
+// of 4 waves per item; the unit's pages dealt to the waves in turn; each
+// (page, kv-head) run as 1 KiB wave loads (16 bytes per lane), non-temporal;
+// two pages in flight per wave where a run is at most 4 KiB.  In place of
+// the attention arithmetic the loaded words are XORed, and each item stores
+// its 16-byte XOR in the first chunk of its first query head's output row,
+// which keeps every load live (out receives no attention result; items of
+// one sequence's different partitions overwrite each other's word).  The
+// rate it reaches is the read bandwidth of the decode access pattern on the
+// device, the ceiling the partition kernels work against.
+template <int NLD>
+__global__ __launch_bounds__(256) void pa_decode_read_probe(
+    char *__restrict__ out, const char *__restrict__ k_pool, const char *__restrict__ v_pool,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+    const int32_t *__restrict__ plan, int num_seqs, int num_heads, int num_kv_heads,
+    int max_blocks, int num_blocks, int block_size, int part_pages, int max_parts,
+    int head_row_bytes) {
+  constexpr int kRun = NLD * 1024;  // bytes of one (page, kv-head) run
+  constexpr int PF = NLD <= 4 ? 2 : 1;
+  constexpr int NW = 4;
+  __shared__ u32x4 s_x[NW];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long bound = (long long)num_seqs * max_parts * num_kv_heads;
+  const size_t page_stride = (size_t)num_kv_heads * kRun;
+  for (int k = 0;; ++k) {
+    const int it = snake_item(k);
+    if (it >= bound) break;
+    const int unit = plan[pa_internal::kPlanHeader + it / num_kv_heads];
+    if (unit < 0) break;
+    const int s = unit / max_parts;
+    const int part = unit - s * max_parts;
+    const int g = it % num_kv_heads;
+    const int ctx = min(max(context_lens[s], 0), max_blocks * block_size);
+    const int npages = (ctx + block_size - 1) / block_size;
+    const int p_begin = part * part_pages;
+    const int np = max(0, min(npages - p_begin, part_pages));
+    const int np_w = wave < np ? (np - wave + NW - 1) / NW : 0;  // this wave's pages
+    const int col = p_begin + wave + NW * lane;
+    int my_bid = -1;
+    if (wave + NW * lane < part_pages && col < max_blocks)
+      my_bid = block_tables[(size_t)s * max_blocks + col];
+    const char *kb = k_pool + (size_t)g * kRun + lane * 16;
+    const char *vb = v_pool + (size_t)g * kRun + lane * 16;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    auto fetch = [&](u32x4 (&c)[2 * NLD], int j) {
+      const int bid = __builtin_amdgcn_readlane(my_bid, j);
+      const size_t off = (size_t)((unsigned)bid < (unsigned)num_blocks ? bid : 0) * page_stride;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) c[i] = load_kv16(kb + off + i * 1024);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) c[NLD + i] = load_kv16(vb + off + i * 1024);
+    };
+    auto fold = [&](const u32x4 (&c)[2 * NLD]) {
+#pragma unroll
+      for (int i = 0; i < 2 * NLD; ++i) x ^= c[i];
+    };
+    if constexpr (PF == 2) {
+      if (np_w > 0) {
+        u32x4 a[2 * NLD], b[2 * NLD];
+        fetch(a, 0);
+        int j = 0;
+        for (; j + 2 < np_w; j += 2) {
+          fetch(b, j + 1);
+          fold(a);
+          fetch(a, j + 2);
+          fold(b);
+        }
+        if (j + 1 < np_w) {
+          fetch(b, j + 1);
+          fold(a);
+          fold(b);
+        } else {
+          fold(a);
+        }
+      }
+    } else {
+      for (int j = 0; j < np_w; ++j) {
+        u32x4 c[2 * NLD];
+        fetch(c, j);
+        fold(c);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x[w] ^= (uint32_t)__shfl_xor((int)x[w], o);
+    if (lane == 0) s_x[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const u32x4 r = s_x[0] ^ s_x[1] ^ s_x[2] ^ s_x[3];
+      const int h0 = g * (num_heads / num_kv_heads);
+      *reinterpret_cast<u32x4 *>(out + ((size_t)s * num_heads + h0) * head_row_bytes) = r;
+    }
+    __syncthreads();  // s_x is reused by the next item
+  }
+}
+
 }  // namespace
 
 namespace pa_internal {
@@ -325,6 +426,38 @@ int launch_copy_pages(const CopyLaunch &a) {
 }
 
 size_t hbm_probe_sink_bytes() { return (size_t)kProbeBlocks * kProbeThreads * 4; }
+
+template <int NLD>
+int launch_read_probe_nld(const DecodeLaunch &a) {
+  auto kernel = pa_decode_read_probe<NLD>;
+  static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(kernel), 256);
+  const unsigned grid = decode_grid(a, per_cu);
+  if (grid == 0) return 6;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(a.stream),
+                     reinterpret_cast<char *>(a.out), reinterpret_cast<const char *>(a.k_pool),
+                     reinterpret_cast<const char *>(a.v_pool), a.block_tables, a.context_lens,
+                     a.plan, a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
+                     a.block_size, a.part_pages, a.max_parts,
+                     a.head_dim * (a.dtype == 0 ? 4 : 2));
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+int launch_decode_read_probe(const DecodeLaunch &a) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  if (launch_decode_plan(a) != 0) return 6;
+  if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
+  const int run_bytes = a.block_size * a.head_dim * (a.dtype == 0 ? 4 : 2);
+  int rc = 3;
+  switch (run_bytes / 1024) {
+    case 2: rc = launch_read_probe_nld<2>(a); break;
+    case 4: rc = launch_read_probe_nld<4>(a); break;
+    case 8: rc = launch_read_probe_nld<8>(a); break;
+    case 16: rc = launch_read_probe_nld<16>(a); break;
+  }
+  if (rc != 0) return rc;
+  if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
+  return 0;
+}
 
 int launch_hbm_probe(const void *buf, size_t bytes, void *sink, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -529,10 +529,7 @@ template <class T, int D>
 int run_decode(const pa_internal::DecodeLaunch &a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   const float scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL(pa_decode_plan, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens, a.plan,
-                     a.num_seqs, a.max_blocks * a.block_size, a.block_size, a.part_pages,
-                     a.max_parts);
-  if (hipGetLastError() != hipSuccess) return 6;
+  if (pa_internal::launch_decode_plan(a) != 0) return 6;
   if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
   const int rc = a.block_size == 16 ? partition_pass<T, D, 16>(a, scale_log2)
                                     : partition_pass<T, D, 32>(a, scale_log2);
@@ -598,6 +595,13 @@ int launch_decode_shared_prefix(const PrefixLaunch &p) {
   hipLaunchKernelGGL(reduce, dim3(a.num_heads, a.num_seqs), dim3(64 * kReduceWaves), 0, st,
                      a.out, a.ws_ml, a.ws_acc, a.context_lens, p.nslots, a.num_heads,
                      a.max_blocks * a.block_size, a.part_pages * a.block_size, a.max_parts);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+int launch_decode_plan(const DecodeLaunch &a) {
+  hipLaunchKernelGGL(pa_decode_plan, dim3(1), dim3(kPlanThreads), 0,
+                     reinterpret_cast<hipStream_t>(a.stream), a.context_lens, a.plan, a.num_seqs,
+                     a.max_blocks * a.block_size, a.block_size, a.part_pages, a.max_parts);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

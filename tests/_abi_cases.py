@@ -397,6 +397,28 @@ for i, bad in ((0, MIS), (1, MIS), (2, MIS), (3, MIS), (4, MIS), (5, P + 4), (6,
     ptrs[i] = bad
     expect(f"rope: pointer {i} misaligned", rope_call(ptrs=ptrs, num_tokens=1), _lib.PA_ERR_ALIGN)
 
+# ---- decode access-pattern probe: the decode call's checks
+def read_probe(d, hkv=32, bs=16, ptrs=None):
+    p = ptrs or [P] * 6
+    return lib.paged_attention_decode_read_probe(*p, hkv, ctypes.c_float(0.088), bs,
+                                                 ctypes.byref(d))
+
+
+expect("read probe dims NULL",
+       lib.paged_attention_decode_read_probe(P, P, P, P, P, P, 32, ctypes.c_float(1), 16, None),
+       _lib.PA_ERR_NULL)
+for i in range(6):
+    ptrs = [P] * 6
+    ptrs[i] = None
+    expect(f"read probe pointer {i} NULL", read_probe(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_NULL)
+expect("read probe empty batch is a no-op", read_probe(dims()), _lib.PA_OK)
+expect("read probe group 3 unsupported", read_probe(dims(num_heads=24), hkv=8),
+       _lib.PA_ERR_UNSUPPORTED)
+expect("read probe block_size 8 unsupported", read_probe(dims(), bs=8), _lib.PA_ERR_UNSUPPORTED)
+expect("read probe misaligned k_pool", read_probe(dims(**ONE), ptrs=[P, P, MIS, P, P, P]),
+       _lib.PA_ERR_ALIGN)
+expect("read probe without workspace", read_probe(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
+
 # ---- probe
 expect("probe NULL buffer", lib.pa_hbm_read_probe(None, 1024, P, None), _lib.PA_ERR_NULL)
 expect("probe size not a multiple of 16", lib.pa_hbm_read_probe(P, 1000, P, None), _lib.PA_ERR_SHAPE)

@@ -287,6 +287,51 @@ def test_hundreds_of_partitions(dt, G):
         assert err <= TOL[dt]
 
 
+def _probe_workload(case):
+    if isinstance(case, int):
+        return make_config(case)
+    dt, D, bs, G = case
+    ctx = [0, 1, bs - 1, bs, bs + 1, 300, 777, 256 * bs]
+    return build_workload("probe", ctx, 2 * G, 2, D, bs, dt, seed=31 + D + bs + G,
+                          max_blocks_per_seq=256)
+
+
+# configurations whose tables fit one partition (at most 256 pages), and
+# every (page, kv-head) run size: 2, 4, 8 and 16 KiB
+PROBE_CASES = [1, 2, 5, ("bf16", 64, 16, 4), ("bf16", 128, 32, 4), ("f32", 128, 32, 2),
+               ("f32", 64, 16, 1)]
+
+
+@pytest.mark.parametrize("case", PROBE_CASES, ids=[str(c) for c in PROBE_CASES])
+def test_decode_read_probe_reads_exactly_the_decode_pages(case):
+    """The access-pattern probe stores, per (sequence, kv-head) item, the XOR
+    of every 16-byte word of the K and V runs it loaded.  With one partition
+    per sequence that must equal the XOR of the runs of pages 0 ..
+    ceil(ctx / bs) - 1 of the sequence's table row for that kv-head, bit for
+    bit: a page missed, read twice, or read from the wrong kv-head or table
+    entry changes the word (the pools hold random bits)."""
+    w = _probe_workload(case)
+    S, mb = w.block_tables.shape
+    dw = upload(w)
+    binding.paged_attention_decode_read_probe(dw.out, dw.q, dw.k_pool, dw.v_pool,
+                                              dw.block_tables, dw.context_lens,
+                                              partition_size=mb * w.block_size)
+    torch.cuda.synchronize()
+    got = dw.out.view(torch.uint8).cpu().numpy().reshape(S, w.num_heads, -1)[:, :, :16]
+    kp = np.ascontiguousarray(w.k_pool).view(np.uint8).reshape(w.num_blocks, w.num_kv_heads, -1)
+    vp = np.ascontiguousarray(w.v_pool).view(np.uint8).reshape(w.num_blocks, w.num_kv_heads, -1)
+    G = w.num_heads // w.num_kv_heads
+    say(f"{case}: {S} sequences x {w.num_kv_heads} kv-heads, runs of {kp.shape[2]} bytes")
+    for s in range(S):
+        n = -(-int(w.context_lens[s]) // w.block_size)
+        ids = w.block_tables[s, :n]
+        for g in range(w.num_kv_heads):
+            words = np.concatenate([kp[ids, g].reshape(-1, 16), vp[ids, g].reshape(-1, 16)])
+            want = np.bitwise_xor.reduce(words.view(np.uint32).reshape(-1, 4), axis=0) \
+                if len(words) else np.zeros(4, np.uint32)
+            assert got[s, g * G].view(np.uint32).tolist() == want.tolist(), (s, g)
+
+
 def test_repeated_calls_are_bitwise_identical():
     w = make_config(3)
     dw = upload(w)
