@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "pagedattn_internal.h"
+#include "pagedattn_probe_launch.h"
 #include "pagedattn_prefill_launch.h"
 
 namespace {

@@ -9,6 +9,7 @@
 // come back (sections 4.4 and 4.5).
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
+#include "pagedattn_probe_launch.h"
 
 namespace {
 

@@ -26,6 +26,7 @@
 
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
+#include "pagedattn_probe_launch.h"
 
 namespace {
 

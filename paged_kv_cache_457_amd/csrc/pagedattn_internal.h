@@ -82,10 +82,6 @@ struct CopyLaunch {
 
 // Each returns 0 on success or the PA_ERR_HIP code on a launch error.
 int launch_decode(const DecodeLaunch &a);
-// The plan kernel alone (the unit list of a decode call, into a.plan).
-int launch_decode_plan(const DecodeLaunch &a);
-// The plan kernel, then the decode access-pattern read probe.
-int launch_decode_read_probe(const DecodeLaunch &a);
 // The partition pass for bf16 with 2, 4 or 8 query heads per kv-head, on
 // the matrix cores; called by launch_decode.
 int launch_partition_gqa(const DecodeLaunch &a, float scale_log2);
