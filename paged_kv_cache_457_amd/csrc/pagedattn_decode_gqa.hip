@@ -83,7 +83,11 @@ struct GqaGranule {
   bool ok;
 };
 
-template <int D, int BS, int G, int NW, bool AL>
+// WPI: wavefronts per item.  WPI == NW: the workgroup's NW waves deal the
+// unit's pages among them and merge their states in LDS.  WPI == 1: each
+// wave takes a whole item of its own (at most 64 pages, one id per lane)
+// and writes its result from its registers, with no workgroup barrier.
+template <int D, int BS, int G, int NW, int WPI, bool AL>
 __device__ __forceinline__ void decode_unit_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
@@ -98,7 +102,8 @@ __device__ __forceinline__ void decode_unit_gqa(
   __shared__ float s_ml[NW][G][2];
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // LDS region
+  const int iw = WPI == 1 ? 0 : wave;  // this wave's place among the item's waves
   const int q4 = lane >> 4;
   const int j16 = lane & 15;
   const int h0 = g * G;
@@ -108,9 +113,9 @@ __device__ __forceinline__ void decode_unit_gqa(
   // lane; columns past the context are loaded but never used) and q as the
   // B operand of the q.K tiles.
   int ctx = context_lens[s];
-  const int col = p_begin + wave + NW * lane;
+  const int col = p_begin + iw + WPI * lane;
   int my_bid = -1;
-  if (wave + NW * lane < part_pages && col < max_blocks)
+  if (iw + WPI * lane < part_pages && col < max_blocks)
     my_bid = block_tables[(size_t)s * max_blocks + col];
   bf16x8 qb[NC];
   {
@@ -131,7 +136,7 @@ __device__ __forceinline__ void decode_unit_gqa(
   char *out_b = reinterpret_cast<char *>(out);
   if (ctx == 0) {
     // the G output rows (contiguous) become zeros, 16 bytes per lane and step
-    if (part == 0 && wave == 0) {
+    if (part == 0 && iw == 0) {
       const u32x4 z = {0u, 0u, 0u, 0u};
       for (int off = lane * 16; off < G * ROW; off += 64 * 16)
         *reinterpret_cast<u32x4 *>(out_b + ((size_t)s * num_heads + h0) * ROW + off) = z;
@@ -140,7 +145,7 @@ __device__ __forceinline__ void decode_unit_gqa(
   }
   if (p_begin >= npages) return;
   const int np = min(npages - p_begin, part_pages);
-  const int np_w = wave < np ? (np - wave + NW - 1) / NW : 0;
+  const int np_w = iw < np ? (np - iw + WPI - 1) / WPI : 0;
 
   // running state for head j16 (lanes j16 >= G carry a padding column)
   float m = -INFINITY;  // max of the logits so far, log2 units, same in all 4 lane groups
@@ -169,7 +174,7 @@ __device__ __forceinline__ void decode_unit_gqa(
   };
 
   auto process = [&](const GqaGranule<D, BS, G> &gr, int jg) {
-    const int tok0 = (p_begin + wave + NW * (jg / GPP)) * BS + 16 * (jg % GPP);
+    const int tok0 = (p_begin + iw + WPI * (jg / GPP)) * BS + 16 * (jg % GPP);
     // stage V row-major in LDS; masked rows as zeros
 #pragma unroll
     for (int i = 0; i < NVLD; ++i) {
@@ -251,6 +256,33 @@ __device__ __forceinline__ void decode_unit_gqa(
   // already summed over tokens by the MFMAs
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+  if constexpr (WPI == 1) {
+    // the wave holds the item's whole state: lane (q4, j16) has
+    // O^T[16n + 4*q4 + r][head j16]; out rows when the sequence is one
+    // partition, else the partition's (max, sum, unnormalised O)
+    if (j16 < G) {
+      const size_t row = (size_t)s * num_heads + h0 + j16;
+      if (npages <= part_pages) {
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) {
+          float v[4] = {o[n][0] * inv, o[n][1] * inv, o[n][2] * inv, o[n][3] * inv};
+          BF16::store4(out_b + row * ROW + (16 * n + 4 * q4) * 2, v);
+        }
+      } else {
+        float *acc = ws_acc + (row * max_parts + part) * D;
+#pragma unroll
+        for (int n = 0; n < NN; ++n)
+          *reinterpret_cast<float4 *>(acc + 16 * n + 4 * q4) =
+              make_float4(o[n][0], o[n][1], o[n][2], o[n][3]);
+        if (q4 == 0) {
+          ws_ml[(row * max_parts + part) * 2] = m;
+          ws_ml[(row * max_parts + part) * 2 + 1] = l;
+        }
+      }
+    }
+    return;
+  }
   // the V staging area becomes this wave's partial O (its own region)
   float *s_acc = reinterpret_cast<float *>(vs);
   if (j16 < G) {
@@ -277,8 +309,11 @@ __device__ __forceinline__ void decode_unit_gqa(
 
 // Partition kernel over the plan's unit list (largest units first), item
 // i = (list[i / num_kv_heads], kv-head i % num_kv_heads), in the snake order
-// of snake_item, on a grid of decode_grid.
-template <int D, int BS, int G, int NW, bool AL>
+// of snake_item.  WPI == NW: one item per workgroup step, on a grid of
+// decode_grid.  WPI == 1: wave w of the workgroup's k-th step takes item
+// NW * snake_item(k) + w, so the NW waves run consecutive items (the kv-heads
+// of one unit) independently.
+template <int D, int BS, int G, int NW, int WPI, bool AL>
 __global__ __launch_bounds__(64 * NW) void pa_decode_partition_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
@@ -288,28 +323,61 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_partition_gqa(
     float scale_log2, const float *__restrict__ alibi) {
   // the list holds num_seqs * max_parts entries, -1 past the last unit
   const long long bound = (long long)num_seqs * max_parts * num_kv_heads;
-  for (int k = 0;; ++k) {
-    const int it = snake_item(k);
-    if (it >= bound) break;
-    const int unit = plan[pa_internal::kPlanHeader + it / num_kv_heads];
-    if (unit < 0) break;
-    decode_unit_gqa<D, BS, G, NW, AL>(out, q, k_pool, v_pool, block_tables, context_lens,
-                                      ws_ml, ws_acc, num_heads, num_kv_heads, max_blocks,
-                                      num_blocks, part_pages, max_parts, scale_log2, alibi,
-                                      unit / max_parts, it % num_kv_heads, unit % max_parts);
-    __syncthreads();  // the next unit reuses the LDS the merge just read
+  if constexpr (WPI == 1) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int k = 0;; ++k) {
+      const long long it = (long long)snake_item(k) * NW + wave;
+      if (it >= bound) break;
+      const int unit = plan[pa_internal::kPlanHeader + it / num_kv_heads];
+      if (unit < 0) break;
+      decode_unit_gqa<D, BS, G, NW, 1, AL>(out, q, k_pool, v_pool, block_tables, context_lens,
+                                           ws_ml, ws_acc, num_heads, num_kv_heads, max_blocks,
+                                           num_blocks, part_pages, max_parts, scale_log2, alibi,
+                                           unit / max_parts, (int)(it % num_kv_heads),
+                                           unit % max_parts);
+    }
+  } else {
+    static_assert(WPI == NW, "an item takes one wave or the whole workgroup");
+    for (int k = 0;; ++k) {
+      const int it = snake_item(k);
+      if (it >= bound) break;
+      const int unit = plan[pa_internal::kPlanHeader + it / num_kv_heads];
+      if (unit < 0) break;
+      decode_unit_gqa<D, BS, G, NW, NW, AL>(out, q, k_pool, v_pool, block_tables, context_lens,
+                                            ws_ml, ws_acc, num_heads, num_kv_heads, max_blocks,
+                                            num_blocks, part_pages, max_parts, scale_log2, alibi,
+                                            unit / max_parts, it % num_kv_heads, unit % max_parts);
+      __syncthreads();  // the next unit reuses the LDS the merge just read
+    }
   }
 }
 
 constexpr int kWavesPerUnit = 4;
 
-template <int D, int BS, int G, bool AL>
+// One item per wave when a partition is at most kWaveItemPages pages and
+// the table holds at least kWaveItemMinParts partitions: long sequences cut
+// into many partitions, where each wave then streams a whole partition and
+// no workgroup merge or barrier separates the items.  Measured on MI355X:
+// 8 x 32768 tokens at 512-token partitions 187.7 -> 180.4 us a step, at
+// 2048 171.3 -> 166.8 us.  Ragged batches whose tables hold few partitions
+// keep the four-wave items, whose finer steps the dispatcher balances
+// better (256 lognormal lengths at 1024-token partitions: 165.7 us against
+// 180.2 us one item per wave; 128 shared-prefix samples at 512: 83.3 us
+// against 95.5).
+constexpr int kWaveItemPages = 64;
+constexpr int kWaveItemMinParts = 16;
+
+template <int D, int BS, int G, int WPI, bool AL>
 int launch_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  auto kernel = pa_decode_partition_gqa<D, BS, G, kWavesPerUnit, AL>;
+  auto kernel = pa_decode_partition_gqa<D, BS, G, kWavesPerUnit, WPI, AL>;
   static const int per_cu = pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel),
                                                        64 * kWavesPerUnit);
-  const unsigned grid = pa_internal::decode_grid(a, per_cu);
+  const long long items = (long long)a.num_seqs * a.max_parts * a.num_kv_heads;
+  const unsigned grid =
+      WPI == 1 ? pa_internal::persistent_grid_items((items + kWavesPerUnit - 1) / kWavesPerUnit,
+                                                    per_cu * pa_internal::kDecodeGridRounds)
+               : pa_internal::decode_grid(a, per_cu);
   if (grid == 0) return 6;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.out, a.q, a.k_pool,
                      a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc, a.plan,
@@ -318,10 +386,17 @@ int launch_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
+template <int D, int BS, int G, bool AL>
+int launch_wpi(const pa_internal::DecodeLaunch &a, float scale_log2) {
+  return a.part_pages <= kWaveItemPages && a.max_parts >= kWaveItemMinParts
+             ? launch_al<D, BS, G, 1, AL>(a, scale_log2)
+             : launch_al<D, BS, G, kWavesPerUnit, AL>(a, scale_log2);
+}
+
 template <int D, int BS, int G>
 int launch(const pa_internal::DecodeLaunch &a, float scale_log2) {
-  return a.alibi ? launch_al<D, BS, G, true>(a, scale_log2)
-                 : launch_al<D, BS, G, false>(a, scale_log2);
+  return a.alibi ? launch_wpi<D, BS, G, true>(a, scale_log2)
+                 : launch_wpi<D, BS, G, false>(a, scale_log2);
 }
 
 template <int D, int BS>
