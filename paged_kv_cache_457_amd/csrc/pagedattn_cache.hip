@@ -257,17 +257,20 @@ __global__ __launch_bounds__(kProbeThreads) void pa_hbm_probe(const u32x4 *__res
 // ------------------------------------------ decode access-pattern probe
 // Reads the K and V bytes a decode call reads, in the order the partition
 // kernels read them: items (unit, kv-head) of the plan's list, largest units
-// first, kv-head fastest, in the snake rounds of snake_item; one workgroup
-// of 4 waves per item; the unit's pages dealt to the waves in turn; each
-// (page, kv-head) run as 1 KiB wave loads (16 bytes per lane), non-temporal;
-// two pages in flight per wave where a run is at most 4 KiB.  In place of
-// the attention arithmetic the loaded words are XORed, and each item stores
-// its 16-byte XOR in the first chunk of its first query head's output row,
-// which keeps every load live (out receives no attention result; items of
-// one sequence's different partitions overwrite each other's word).  The
-// rate it reaches is the read bandwidth of the decode access pattern on the
-// device, the ceiling the partition kernels work against.
-template <int NLD>
+// first, kv-head fastest, in the snake rounds of snake_item.  WPI == 4: one
+// workgroup of 4 waves per item, the unit's pages dealt to the waves in
+// turn.  WPI == 1 (what the grouped-query kernel does for long tables of
+// short partitions): wave w of the workgroup's k-th step takes item
+// 4 * snake_item(k) + w whole.  Each (page, kv-head) run is read as 1 KiB
+// wave loads (16 bytes per lane), non-temporal, two pages in flight per
+// wave where a run is at most 4 KiB.  In place of the attention arithmetic
+// the loaded words are XORed, and each item stores its 16-byte XOR in the
+// first chunk of its first query head's output row, which keeps every load
+// live (out receives no attention result; items of one sequence's different
+// partitions overwrite each other's word).  The rate it reaches is the read
+// bandwidth of the decode access pattern on the device, the ceiling the
+// partition kernels work against.
+template <int NLD, int WPI>
 __global__ __launch_bounds__(256) void pa_decode_read_probe(
     char *__restrict__ out, const char *__restrict__ k_pool, const char *__restrict__ v_pool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
@@ -277,27 +280,26 @@ __global__ __launch_bounds__(256) void pa_decode_read_probe(
   constexpr int kRun = NLD * 1024;  // bytes of one (page, kv-head) run
   constexpr int PF = NLD <= 4 ? 2 : 1;
   constexpr int NW = 4;
+  static_assert(WPI == 1 || WPI == NW, "an item takes one wave or the whole workgroup");
   __shared__ u32x4 s_x[NW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int iw = WPI == 1 ? 0 : wave;  // this wave's place among the item's waves
   const long long bound = (long long)num_seqs * max_parts * num_kv_heads;
   const size_t page_stride = (size_t)num_kv_heads * kRun;
-  for (int k = 0;; ++k) {
-    const int it = snake_item(k);
-    if (it >= bound) break;
-    const int unit = plan[pa_internal::kPlanHeader + it / num_kv_heads];
-    if (unit < 0) break;
+
+  // this wave's share of item (unit, kv-head g): the XOR over the whole wave
+  auto item_xor = [&](int unit, int g) -> u32x4 {
     const int s = unit / max_parts;
     const int part = unit - s * max_parts;
-    const int g = it % num_kv_heads;
     const int ctx = min(max(context_lens[s], 0), max_blocks * block_size);
     const int npages = (ctx + block_size - 1) / block_size;
     const int p_begin = part * part_pages;
     const int np = max(0, min(npages - p_begin, part_pages));
-    const int np_w = wave < np ? (np - wave + NW - 1) / NW : 0;  // this wave's pages
-    const int col = p_begin + wave + NW * lane;
+    const int np_w = iw < np ? (np - iw + WPI - 1) / WPI : 0;  // this wave's pages
+    const int col = p_begin + iw + WPI * lane;
     int my_bid = -1;
-    if (wave + NW * lane < part_pages && col < max_blocks)
+    if (iw + WPI * lane < part_pages && col < max_blocks)
       my_bid = block_tables[(size_t)s * max_blocks + col];
     const char *kb = k_pool + (size_t)g * kRun + lane * 16;
     const char *vb = v_pool + (size_t)g * kRun + lane * 16;
@@ -344,14 +346,37 @@ __global__ __launch_bounds__(256) void pa_decode_read_probe(
     for (int o = 32; o >= 1; o >>= 1)
 #pragma unroll
       for (int w = 0; w < 4; ++w) x[w] ^= (uint32_t)__shfl_xor((int)x[w], o);
-    if (lane == 0) s_x[wave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const u32x4 r = s_x[0] ^ s_x[1] ^ s_x[2] ^ s_x[3];
-      const int h0 = g * (num_heads / num_kv_heads);
-      *reinterpret_cast<u32x4 *>(out + ((size_t)s * num_heads + h0) * head_row_bytes) = r;
+    return x;
+  };
+  auto word = [&](int unit, int g) {
+    const int s = unit / max_parts;
+    const int h0 = g * (num_heads / num_kv_heads);
+    return reinterpret_cast<u32x4 *>(out + ((size_t)s * num_heads + h0) * head_row_bytes);
+  };
+
+  if constexpr (WPI == 1) {
+    for (int k = 0;; ++k) {
+      const long long it = (long long)snake_item(k) * NW + wave;
+      if (it >= bound) break;
+      const int unit = plan[pa_internal::kPlanHeader + it / num_kv_heads];
+      if (unit < 0) break;
+      const int g = (int)(it % num_kv_heads);
+      const u32x4 x = item_xor(unit, g);
+      if (lane == 0) *word(unit, g) = x;
     }
-    __syncthreads();  // s_x is reused by the next item
+  } else {
+    for (int k = 0;; ++k) {
+      const int it = snake_item(k);
+      if (it >= bound) break;
+      const int unit = plan[pa_internal::kPlanHeader + it / num_kv_heads];
+      if (unit < 0) break;
+      const int g = it % num_kv_heads;
+      const u32x4 x = item_xor(unit, g);
+      if (lane == 0) s_x[wave] = x;
+      __syncthreads();
+      if (threadIdx.x == 0) *word(unit, g) = s_x[0] ^ s_x[1] ^ s_x[2] ^ s_x[3];
+      __syncthreads();  // s_x is reused by the next item
+    }
   }
 }
 
@@ -428,11 +453,13 @@ int launch_copy_pages(const CopyLaunch &a) {
 
 size_t hbm_probe_sink_bytes() { return (size_t)kProbeBlocks * kProbeThreads * 4; }
 
-template <int NLD>
-int launch_read_probe_nld(const DecodeLaunch &a) {
-  auto kernel = pa_decode_read_probe<NLD>;
+template <int NLD, int WPI>
+int launch_read_probe_wpi(const DecodeLaunch &a) {
+  auto kernel = pa_decode_read_probe<NLD, WPI>;
   static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(kernel), 256);
-  const unsigned grid = decode_grid(a, per_cu);
+  const long long items = (long long)a.num_seqs * a.max_parts * a.num_kv_heads;
+  const unsigned grid = WPI == 1 ? persistent_grid_items((items + 3) / 4, per_cu * kDecodeGridRounds)
+                                 : decode_grid(a, per_cu);
   if (grid == 0) return 6;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(a.stream),
                      reinterpret_cast<char *>(a.out), reinterpret_cast<const char *>(a.k_pool),
@@ -441,6 +468,15 @@ int launch_read_probe_nld(const DecodeLaunch &a) {
                      a.block_size, a.part_pages, a.max_parts,
                      a.head_dim * (a.dtype == 0 ? 4 : 2));
   return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+// the partition kernels' item shape: one wave per item where the grouped-
+// query kernel runs that way, else four
+template <int NLD>
+int launch_read_probe_nld(const DecodeLaunch &a) {
+  const bool gqa = a.dtype == 1 && a.num_heads / a.num_kv_heads >= 2;
+  return gqa && gqa_wave_items(a) ? launch_read_probe_wpi<NLD, 1>(a)
+                                  : launch_read_probe_wpi<NLD, 4>(a);
 }
 
 int launch_decode_read_probe(const DecodeLaunch &a) {

@@ -43,6 +43,7 @@
 // (NaN) never reaches a multiply.
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
+#include "pagedattn_probe_launch.h"
 
 namespace {
 
@@ -388,7 +389,7 @@ int launch_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
 
 template <int D, int BS, int G, bool AL>
 int launch_wpi(const pa_internal::DecodeLaunch &a, float scale_log2) {
-  return a.part_pages <= kWaveItemPages && a.max_parts >= kWaveItemMinParts
+  return pa_internal::gqa_wave_items(a)
              ? launch_al<D, BS, G, 1, AL>(a, scale_log2)
              : launch_al<D, BS, G, kWavesPerUnit, AL>(a, scale_log2);
 }
@@ -417,6 +418,10 @@ int by_block(const pa_internal::DecodeLaunch &a, float scale_log2) {
 }  // namespace
 
 namespace pa_internal {
+
+bool gqa_wave_items(const DecodeLaunch &a) {
+  return a.part_pages <= kWaveItemPages && a.max_parts >= kWaveItemMinParts;
+}
 
 int launch_partition_gqa(const DecodeLaunch &a, float scale_log2) {
   return a.head_dim == 64 ? by_block<64>(a, scale_log2) : by_block<128>(a, scale_log2);

@@ -11,5 +11,8 @@ namespace pa_internal {
 int launch_decode_plan(const DecodeLaunch &a);
 // The plan kernel, then the decode access-pattern read probe.
 int launch_decode_read_probe(const DecodeLaunch &a);
+// Whether the grouped-query (matrix-core) partition kernel runs one item
+// per wavefront for this call (partition and table sizes only).
+bool gqa_wave_items(const DecodeLaunch &a);
 
 }  // namespace pa_internal

@@ -290,16 +290,24 @@ def test_hundreds_of_partitions(dt, G):
 def _probe_workload(case):
     if isinstance(case, int):
         return make_config(case)
-    dt, D, bs, G = case
-    ctx = [0, 1, bs - 1, bs, bs + 1, 300, 777, 256 * bs]
+    dt, D, bs, G = case[:4]
+    if len(case) > 4:
+        # a 256-page table cut into 16-page partitions, every sequence
+        # within the first: the one-wave-per-item shape of the grouped-query
+        # kernel, still one partition per sequence
+        ctx = [0, 1, bs - 1, bs, bs + 1, 7 * bs + 3, 16 * bs - 1, 16 * bs] * 8
+    else:
+        ctx = [0, 1, bs - 1, bs, bs + 1, 300, 777, 256 * bs]
     return build_workload("probe", ctx, 2 * G, 2, D, bs, dt, seed=31 + D + bs + G,
                           max_blocks_per_seq=256)
 
 
-# configurations whose tables fit one partition (at most 256 pages), and
-# every (page, kv-head) run size: 2, 4, 8 and 16 KiB
+# configurations whose sequences fit one partition, with every (page,
+# kv-head) run size: 2, 4, 8 and 16 KiB; the cases marked "wave" run the
+# probe's one-wave-per-item form
 PROBE_CASES = [1, 2, 5, ("bf16", 64, 16, 4), ("bf16", 128, 32, 4), ("f32", 128, 32, 2),
-               ("f32", 64, 16, 1)]
+               ("f32", 64, 16, 1), ("bf16", 128, 16, 4, "wave"), ("bf16", 128, 32, 8, "wave"),
+               ("bf16", 64, 16, 2, "wave")]
 
 
 @pytest.mark.parametrize("case", PROBE_CASES, ids=[str(c) for c in PROBE_CASES])
@@ -312,10 +320,11 @@ def test_decode_read_probe_reads_exactly_the_decode_pages(case):
     entry changes the word (the pools hold random bits)."""
     w = _probe_workload(case)
     S, mb = w.block_tables.shape
+    pages = 16 if isinstance(case, tuple) and len(case) > 4 else mb
     dw = upload(w)
     binding.paged_attention_decode_read_probe(dw.out, dw.q, dw.k_pool, dw.v_pool,
                                               dw.block_tables, dw.context_lens,
-                                              partition_size=mb * w.block_size)
+                                              partition_size=pages * w.block_size)
     torch.cuda.synchronize()
     got = dw.out.view(torch.uint8).cpu().numpy().reshape(S, w.num_heads, -1)[:, :, :16]
     kp = np.ascontiguousarray(w.k_pool).view(np.uint8).reshape(w.num_blocks, w.num_kv_heads, -1)
