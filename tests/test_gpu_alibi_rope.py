@@ -74,7 +74,8 @@ def test_decode_alibi_variants_and_partitions(dt, D, bs, G):
                        max_blocks_per_seq=(800 + bs - 1) // bs)
     # steep slopes as well as the paper's: the bias dominates the logits
     slopes = np.array([0.9, 0.003] * G, np.float32)[:2 * G]
-    for ps in (0, 4 * bs):
+    # one-page partitions: the grouped-query kernel's one-item-per-wave form
+    for ps in (0, bs, 4 * bs):
         got, ref = decode_alibi_step(w, slopes, ps)
         err = max_err(got, ref, dt)
         say(f"{dt} D{D} bs{bs} G{G} partition {ps}: max abs err {err:.3e}")

@@ -366,20 +366,22 @@ def test_context_clamped_to_table_capacity():
 
 
 @pytest.mark.parametrize("dt,G", [("bf16", 1), ("bf16", 4), ("f32", 1)])
-def test_out_of_range_page_id_is_skipped(dt, G):
+@pytest.mark.parametrize("ps", [0, 16])
+def test_out_of_range_page_id_is_skipped(dt, G, ps):
     """A used table entry outside the pool is a precondition violation; the
     kernel must not read it and its tokens drop out, which equals the
-    oracle over the sequence without that (full, interior) page."""
+    oracle over the sequence without that (full, interior) page.  One-page
+    partitions of the 16-page table run the grouped-query kernel one item
+    per wave."""
     L, bs = 200, 16
-    w = build_workload("badid", [L, L], 2 * G, 2, 64, bs, dt, seed=31,
-                       max_blocks_per_seq=(L + bs - 1) // bs)
+    w = build_workload("badid", [L, L], 2 * G, 2, 64, bs, dt, seed=31, max_blocks_per_seq=16)
     kp, vp = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping, bs)
     bad_col = 5
     bt = w.block_tables.copy()
     bt[0, bad_col] = w.num_blocks + 1000
     dw = upload(w)
     dw.block_tables.copy_(torch.from_numpy(bt))
-    got = gpu_step(dw)
+    got = gpu_step(dw, partition_size=ps)
     # expected: sequence 0 without page bad_col (a full page), sequence 1 as is
     bt_ref = np.full_like(w.block_tables, -1)
     bt_ref[0, :bt.shape[1] - 1] = np.delete(w.block_tables[0], bad_col)
