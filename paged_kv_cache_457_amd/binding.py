@@ -93,19 +93,11 @@ def paged_attention_decode_partition_tokens(q: torch.Tensor, k_pool: torch.Tenso
     return n
 
 
-def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
-                           v_pool: torch.Tensor, block_tables: torch.Tensor,
-                           context_lens: torch.Tensor, scale: Optional[float] = None,
-                           partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
-                           stream=None, timing_events: Sequence = (None, None),
-                           alibi_slopes: Optional[torch.Tensor] = None,
-                           _entry: str = "paged_attention_decode") -> torch.Tensor:
-    """out[S,H,D] <- paged decode attention (see paged_attention_decode in
-    include/pagedattn.h).  Pools are [num_blocks, num_kv_heads, block_size,
-    head_dim]; the kv-head count and block size are read off k_pool.
-    ``scale`` defaults to 1/sqrt(head_dim).  A workspace (unit plan and
-    split-K partials) is allocated here when none is given.  With
-    ``alibi_slopes`` (fp32 [H]) the call is paged_attention_decode_alibi."""
+def _decode_call(entry: str, out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                 partition_size, workspace, stream, timing_events, alibi_slopes):
+    """Marshal one call of the decode family: paged_attention_decode,
+    paged_attention_decode_alibi (with slopes) or
+    paged_attention_decode_read_probe, which share arguments and checks."""
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     for name, t in (("out", out), ("k_pool", k_pool), ("v_pool", v_pool)):
@@ -127,7 +119,7 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     lib = _lib.load()
     need = lib.paged_attention_decode_workspace_bytes(bs, ctypes.byref(d))
     if need == _lib.SIZE_MAX:
-        _check(_lib.PA_ERR_SHAPE, "paged_attention_decode")
+        _check(_lib.PA_ERR_SHAPE, entry)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
@@ -136,20 +128,33 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     d.stream = _stream_ptr(stream)
     d.timing_events[0] = _event_ptr(timing_events[0])
     d.timing_events[1] = _event_ptr(timing_events[1])
+    ptrs = (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+            hkv, ctypes.c_float(scale), bs)
     if alibi_slopes is not None:
         _check_slopes(alibi_slopes, H)
-        rc = lib.paged_attention_decode_alibi(
-            _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
-            hkv, ctypes.c_float(scale), bs, _dev(alibi_slopes, "alibi_slopes"), ctypes.byref(d))
-        _check(rc, "paged_attention_decode_alibi")
-        return out
-    rc = getattr(lib, _entry)(
-        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
-        hkv, ctypes.c_float(scale), bs, ctypes.byref(d))
-    _check(rc, _entry)
+        rc = getattr(lib, entry)(*ptrs, _dev(alibi_slopes, "alibi_slopes"), ctypes.byref(d))
+    else:
+        rc = getattr(lib, entry)(*ptrs, ctypes.byref(d))
+    _check(rc, entry)
     return out
+
+
+def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                           v_pool: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, scale: Optional[float] = None,
+                           partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
+                           stream=None, timing_events: Sequence = (None, None),
+                           alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[S,H,D] <- paged decode attention (see paged_attention_decode in
+    include/pagedattn.h).  Pools are [num_blocks, num_kv_heads, block_size,
+    head_dim]; the kv-head count and block size are read off k_pool.
+    ``scale`` defaults to 1/sqrt(head_dim).  A workspace (unit plan and
+    split-K partials) is allocated here when none is given.  With
+    ``alibi_slopes`` (fp32 [H]) the call is paged_attention_decode_alibi."""
+    entry = "paged_attention_decode" if alibi_slopes is None else "paged_attention_decode_alibi"
+    return _decode_call(entry, out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                        partition_size, workspace, stream, timing_events, alibi_slopes)
 
 
 def paged_attention_decode_read_probe(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
@@ -161,10 +166,9 @@ def paged_attention_decode_read_probe(out: torch.Tensor, q: torch.Tensor, k_pool
     paged_attention_decode_read_probe in include/pagedattn.h): same
     arguments as paged_attention_decode; ``out`` receives one XOR word per
     item, not attention."""
-    return paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
-                                  partition_size=partition_size, workspace=workspace,
-                                  stream=stream, timing_events=timing_events,
-                                  _entry="paged_attention_decode_read_probe")
+    return _decode_call("paged_attention_decode_read_probe", out, q, k_pool, v_pool,
+                        block_tables, context_lens, None, partition_size, workspace, stream,
+                        timing_events, None)
 
 
 def paged_attention_decode_shared_prefix(
