@@ -485,6 +485,91 @@ __global__ __launch_bounds__(64 * kReduceWaves) void pa_decode_reduce(
   }
 }
 
+// The same merge when every sequence has at most kFewParts partials (the
+// host knows it from the table width and partition size): one wavefront
+// per (sequence, query head), four heads per workgroup, each lane loading
+// every partial's (max, sum) and its D/64 accumulator values at once; no
+// LDS and no barrier.  Partials past nparts count as (-inf, 0, 0).
+constexpr int kFewParts = 8;
+constexpr int kFewHeadsPerBlock = 4;
+
+template <class T, int D>
+__global__ __launch_bounds__(64 * kFewHeadsPerBlock) void pa_decode_reduce_few(
+    void *__restrict__ out, const float *__restrict__ ws_ml, const float *__restrict__ ws_acc,
+    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ nslots,
+    int num_heads, int ctx_cap, int part_tokens, int max_parts) {
+  constexpr int DPL = D / 64;  // output elements per lane
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * kFewHeadsPerBlock + (threadIdx.x >> 6);
+  const int s = blockIdx.y;
+  if (h >= num_heads) return;
+  int nparts;
+  if (nslots) {
+    nparts = min(nslots[s], max_parts);
+  } else {
+    const int ctx = min(max(context_lens[s], 0), ctx_cap);
+    nparts = (ctx + part_tokens - 1) / part_tokens;
+    if (nparts <= 1) return;  // the partition pass wrote the output itself
+  }
+  const size_t row0 = ((size_t)s * num_heads + h) * max_parts;
+  const float *ml = ws_ml + row0 * 2;
+  const float *acc = ws_acc + row0 * D + lane * DPL;
+  float mp[kFewParts], lp[kFewParts], a[kFewParts][DPL];
+#pragma unroll
+  for (int p = 0; p < kFewParts; ++p) {
+    const bool in = p < nparts;
+    mp[p] = in ? ml[2 * p] : -INFINITY;
+    lp[p] = in ? ml[2 * p + 1] : 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) a[p][j] = in ? acc[(size_t)p * D + j] : 0.f;
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kFewParts; ++p) M = fmaxf(M, mp[p]);
+  float L = 0.f, o[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) o[j] = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int p = 0; p < kFewParts; ++p) {
+      const float sc = fast_exp2(mp[p] - M);
+      L = fmaf(lp[p], sc, L);
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o[j] = fmaf(a[p][j], sc, o[j]);
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const size_t o0 = ((size_t)s * num_heads + h) * D + lane * DPL;
+  if constexpr (T::kBytes == 4) {
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) reinterpret_cast<float *>(out)[o0 + j] = o[j] * inv;
+  } else {
+#pragma unroll
+    for (int j = 0; j < DPL; ++j)
+      reinterpret_cast<uint16_t *>(out)[o0 + j] = (uint16_t)BF16::round_bits(o[j] * inv);
+  }
+}
+
+// The split-K merge of a decode call: the few-partials form when every
+// sequence has at most kFewParts partials, else the four-wave form.
+template <class T, int D>
+int launch_reduce(const pa_internal::DecodeLaunch &a, const int32_t *nslots) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const int ctx_cap = a.max_blocks * a.block_size;
+  const int part_tokens = a.part_pages * a.block_size;
+  if (a.max_parts <= kFewParts) {
+    const dim3 grid((a.num_heads + kFewHeadsPerBlock - 1) / kFewHeadsPerBlock, a.num_seqs);
+    hipLaunchKernelGGL((pa_decode_reduce_few<T, D>), grid, dim3(64 * kFewHeadsPerBlock), 0, st,
+                       a.out, a.ws_ml, a.ws_acc, a.context_lens, nslots, a.num_heads, ctx_cap,
+                       part_tokens, a.max_parts);
+  } else {
+    hipLaunchKernelGGL((pa_decode_reduce<T, D>), dim3(a.num_heads, a.num_seqs),
+                       dim3(64 * kReduceWaves), 0, st, a.out, a.ws_ml, a.ws_acc, a.context_lens,
+                       nslots, a.num_heads, ctx_cap, part_tokens, a.max_parts);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
 constexpr int kWavesPerUnit = 4;
 
 template <class T, int D, int BS, int G, bool AL>
@@ -536,13 +621,7 @@ int run_decode(const pa_internal::DecodeLaunch &a) {
                                     : partition_pass<T, D, 32>(a, scale_log2);
   if (rc != 0) return rc;
   if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
-  if (a.max_parts > 1) {
-    hipLaunchKernelGGL((pa_decode_reduce<T, D>), dim3(a.num_heads, a.num_seqs),
-                       dim3(64 * kReduceWaves), 0, st,
-                       a.out, a.ws_ml, a.ws_acc, a.context_lens, nullptr, a.num_heads,
-                       a.max_blocks * a.block_size, a.part_pages * a.block_size, a.max_parts);
-    if (hipGetLastError() != hipSuccess) return 6;
-  }
+  if (a.max_parts > 1) return launch_reduce<T, D>(a, nullptr);
   return 0;
 }
 
@@ -592,11 +671,8 @@ int launch_decode_shared_prefix(const PrefixLaunch &p) {
   rc = launch_prefix_units(p, a.scale * kLog2e);
   if (rc != 0) return rc;
   if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
-  auto reduce = a.head_dim == 64 ? pa_decode_reduce<BF16, 64> : pa_decode_reduce<BF16, 128>;
-  hipLaunchKernelGGL(reduce, dim3(a.num_heads, a.num_seqs), dim3(64 * kReduceWaves), 0, st,
-                     a.out, a.ws_ml, a.ws_acc, a.context_lens, p.nslots, a.num_heads,
-                     a.max_blocks * a.block_size, a.part_pages * a.block_size, a.max_parts);
-  return hipGetLastError() == hipSuccess ? 0 : 6;
+  return a.head_dim == 64 ? launch_reduce<BF16, 64>(a, p.nslots)
+                          : launch_reduce<BF16, 128>(a, p.nslots);
 }
 
 int launch_decode_plan(const DecodeLaunch &a) {
