@@ -429,8 +429,11 @@ size_t pa_hbm_read_probe_sink_bytes(void);
  * same plan kernel, and then reads exactly the K and V pages the partition
  * kernels would read, in their order and with their load shapes: items
  * (unit, kv-head) largest unit first, one workgroup of 4 wavefronts per
- * item, the unit's pages dealt to the wavefronts in turn, each (page,
- * kv-head) run as 16-byte non-temporal loads.  Instead of attention it
+ * item with the unit's pages dealt to the wavefronts in turn (or one
+ * wavefront per item where the grouped-query kernel works that way: bf16
+ * with 2-8 query heads per kv-head, partitions of at most 64 pages and a
+ * table of at least 16 partitions), each (page, kv-head) run as 16-byte
+ * non-temporal loads.  Instead of attention it
  * stores, for each item, the XOR of every 16-byte word it loaded in the
  * first 16 bytes of the output row of the item's first query head
  * (h = kv-head * num_heads / num_kv_heads); nothing else in `out` is
