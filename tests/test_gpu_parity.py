@@ -341,6 +341,41 @@ def test_decode_read_probe_reads_exactly_the_decode_pages(case):
             assert got[s, g * G].view(np.uint32).tolist() == want.tolist(), (s, g)
 
 
+# (dtype, G, block_size, partition pages, table width in pages): each side of
+# the host's size rules -- the grouped-query kernel runs one item per wave
+# for partitions of at most 64 pages in tables of at least 16 partitions,
+# and the split-K merge takes its few-partials form for at most 8 partials
+DISPATCH_CASES = [
+    ("bf16", 4, 16, 64, 16 * 64),    # one wave per item; 16 partials
+    ("bf16", 4, 16, 65, 16 * 64),    # 65-page partitions: four waves per item
+    ("bf16", 4, 16, 64, 15 * 64),    # 15 partitions: four waves per item
+    ("bf16", 4, 32, 64, 16 * 64),    # 32-token pages, one wave per item
+    ("bf16", 4, 16, 16, 8 * 16),     # 8 partials: few-partials merge
+    ("bf16", 4, 16, 16, 8 * 16 + 1),  # 9 partials: four-wave merge
+    ("bf16", 1, 16, 16, 8 * 16),
+    ("bf16", 1, 16, 16, 8 * 16 + 1),
+    ("f32", 2, 16, 16, 8 * 16),
+    ("f32", 2, 16, 16, 8 * 16 + 1),
+]
+
+
+@pytest.mark.parametrize("dt,G,bs,pp,mb", DISPATCH_CASES,
+                         ids=[f"{a}-G{b}-bs{c}-p{d}-w{e}" for a, b, c, d, e in DISPATCH_CASES])
+def test_dispatch_boundaries(dt, G, bs, pp, mb):
+    """Contexts that fill the table, end inside a partition, on a partition
+    edge, or are tiny, at partition and table sizes on both sides of each
+    size rule; every form must match the oracle."""
+    cap = mb * bs
+    ctx = [cap, cap - 1, 2 * pp * bs, 2 * pp * bs + 1, pp * bs - 1, 17, 1, 0]
+    w = build_workload("dispatch", ctx, 2 * G, 2, 128 if dt == "bf16" else 64, bs, dt,
+                       seed=7 + G + bs + pp + mb, max_blocks_per_seq=mb)
+    ref, _, _ = oracle_step(w)
+    got = gpu_step(upload(w), partition_size=pp * bs)
+    err = max_err(got, ref, dt)
+    say(f"{dt} G{G} bs{bs} partition {pp} pages, table {mb} pages: max abs err {err:.3e}")
+    assert err <= TOL[dt]
+
+
 def test_repeated_calls_are_bitwise_identical():
     w = make_config(3)
     dw = upload(w)
