@@ -452,7 +452,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the kernel shards by sequence or kv-head with no exchange; see DESIGN.md)",
+              "(the decode kernel shards by sequence or by kv-head with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
