@@ -428,8 +428,9 @@ size_t pa_hbm_read_probe_sink_bytes(void);
  * its arithmetic.  Takes the same arguments, checks and workspace, runs the
  * same plan kernel, and then reads exactly the K and V pages the partition
  * kernels would read, in their order and with their load shapes: items
- * (unit, kv-head) largest unit first, one workgroup of 4 wavefronts per
- * item with the unit's pages dealt to the wavefronts in turn (or one
+ * (unit, kv-head) largest unit first, one workgroup of 4 wavefronts (8 for
+ * bf16 with one query head per kv-head) per item with the unit's pages
+ * dealt to the wavefronts in turn (or one
  * wavefront per item where the grouped-query kernel works that way: bf16
  * with 2-8 query heads per kv-head, partitions of at most 64 pages and a
  * table of at least 16 partitions), each (page, kv-head) run as 16-byte

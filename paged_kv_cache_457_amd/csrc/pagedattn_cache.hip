@@ -257,11 +257,12 @@ __global__ __launch_bounds__(kProbeThreads) void pa_hbm_probe(const u32x4 *__res
 // ------------------------------------------ decode access-pattern probe
 // Reads the K and V bytes a decode call reads, in the order the partition
 // kernels read them: items (unit, kv-head) of the plan's list, largest units
-// first, kv-head fastest, in the snake rounds of snake_item.  WPI == 4: one
-// workgroup of 4 waves per item, the unit's pages dealt to the waves in
+// first, kv-head fastest, in the snake rounds of snake_item.  WPI == NW: one
+// workgroup of NW waves per item (8 where the VALU kernel runs bf16 with one
+// query head per kv-head, else 4), the unit's pages dealt to the waves in
 // turn.  WPI == 1 (what the grouped-query kernel does for long tables of
 // short partitions): wave w of the workgroup's k-th step takes item
-// 4 * snake_item(k) + w whole.  Each (page, kv-head) run is read as 1 KiB
+// NW * snake_item(k) + w whole.  Each (page, kv-head) run is read as 1 KiB
 // wave loads (16 bytes per lane), non-temporal, two pages in flight per
 // wave where a run is at most 4 KiB.  In place of the attention arithmetic
 // the loaded words are XORed, and each item stores its 16-byte XOR in the
@@ -270,8 +271,8 @@ __global__ __launch_bounds__(kProbeThreads) void pa_hbm_probe(const u32x4 *__res
 // partitions overwrite each other's word).  The rate it reaches is the read
 // bandwidth of the decode access pattern on the device, the ceiling the
 // partition kernels work against.
-template <int NLD, int WPI>
-__global__ __launch_bounds__(256) void pa_decode_read_probe(
+template <int NLD, int NW, int WPI>
+__global__ __launch_bounds__(64 * NW) void pa_decode_read_probe(
     char *__restrict__ out, const char *__restrict__ k_pool, const char *__restrict__ v_pool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     const int32_t *__restrict__ plan, int num_seqs, int num_heads, int num_kv_heads,
@@ -279,7 +280,6 @@ __global__ __launch_bounds__(256) void pa_decode_read_probe(
     int head_row_bytes) {
   constexpr int kRun = NLD * 1024;  // bytes of one (page, kv-head) run
   constexpr int PF = NLD <= 4 ? 2 : 1;
-  constexpr int NW = 4;
   static_assert(WPI == 1 || WPI == NW, "an item takes one wave or the whole workgroup");
   __shared__ u32x4 s_x[NW];
   const int lane = threadIdx.x & 63;
@@ -374,7 +374,12 @@ __global__ __launch_bounds__(256) void pa_decode_read_probe(
       const u32x4 x = item_xor(unit, g);
       if (lane == 0) s_x[wave] = x;
       __syncthreads();
-      if (threadIdx.x == 0) *word(unit, g) = s_x[0] ^ s_x[1] ^ s_x[2] ^ s_x[3];
+      if (threadIdx.x == 0) {
+        u32x4 x_all = s_x[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) x_all ^= s_x[w];
+        *word(unit, g) = x_all;
+      }
       __syncthreads();  // s_x is reused by the next item
     }
   }
@@ -453,15 +458,16 @@ int launch_copy_pages(const CopyLaunch &a) {
 
 size_t hbm_probe_sink_bytes() { return (size_t)kProbeBlocks * kProbeThreads * 4; }
 
-template <int NLD, int WPI>
+template <int NLD, int NW, int WPI>
 int launch_read_probe_wpi(const DecodeLaunch &a) {
-  auto kernel = pa_decode_read_probe<NLD, WPI>;
-  static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(kernel), 256);
+  auto kernel = pa_decode_read_probe<NLD, NW, WPI>;
+  static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(kernel), 64 * NW);
   const long long items = (long long)a.num_seqs * a.max_parts * a.num_kv_heads;
-  const unsigned grid = WPI == 1 ? persistent_grid_items((items + 3) / 4, per_cu * kDecodeGridRounds)
+  const unsigned grid = WPI == 1 ? persistent_grid_items((items + NW - 1) / NW,
+                                                         per_cu * kDecodeGridRounds)
                                  : decode_grid(a, per_cu);
   if (grid == 0) return 6;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(a.stream),
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * NW), 0, reinterpret_cast<hipStream_t>(a.stream),
                      reinterpret_cast<char *>(a.out), reinterpret_cast<const char *>(a.k_pool),
                      reinterpret_cast<const char *>(a.v_pool), a.block_tables, a.context_lens,
                      a.plan, a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
@@ -470,13 +476,17 @@ int launch_read_probe_wpi(const DecodeLaunch &a) {
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
-// the partition kernels' item shape: one wave per item where the grouped-
-// query kernel runs that way, else four
+// the partition kernels' item shape: the grouped-query kernel's one wave
+// per item or four waves per item; the VALU kernel's eight waves for bf16
+// with one query head per kv-head, else four
 template <int NLD>
 int launch_read_probe_nld(const DecodeLaunch &a) {
-  const bool gqa = a.dtype == 1 && a.num_heads / a.num_kv_heads >= 2;
-  return gqa && gqa_wave_items(a) ? launch_read_probe_wpi<NLD, 1>(a)
-                                  : launch_read_probe_wpi<NLD, 4>(a);
+  const int group = a.num_heads / a.num_kv_heads;
+  if (a.dtype == 1 && group >= 2)
+    return gqa_wave_items(a) ? launch_read_probe_wpi<NLD, 4, 1>(a)
+                             : launch_read_probe_wpi<NLD, 4, 4>(a);
+  return a.dtype == 1 && group == 1 ? launch_read_probe_wpi<NLD, 8, 8>(a)
+                                    : launch_read_probe_wpi<NLD, 4, 4>(a);
 }
 
 int launch_decode_read_probe(const DecodeLaunch &a) {

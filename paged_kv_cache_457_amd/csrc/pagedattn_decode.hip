@@ -570,17 +570,26 @@ int launch_reduce(const pa_internal::DecodeLaunch &a, const int32_t *nslots) {
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
-constexpr int kWavesPerUnit = 4;
+// Wavefronts per workgroup of the VALU partition kernel: 8 for bf16 with
+// one query head per kv-head (measured on MI355X at the Llama-2-7B decode
+// shape: 179.2 -> 178.0 us a step; 2 waves: 187.2 us), 4 for fp32 and for
+// head groups, whose registers leave no room for two waves per SIMD without
+// spilling.
+template <class T, int G>
+constexpr int valu_waves() {
+  return T::kBytes == 2 && G == 1 ? 8 : 4;
+}
 
 template <class T, int D, int BS, int G, bool AL>
 int launch_valu_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  auto kernel = pa_decode_partition<T, D, BS, G, kWavesPerUnit, AL>;
+  constexpr int NW = valu_waves<T, G>();
+  auto kernel = pa_decode_partition<T, D, BS, G, NW, AL>;
   static const int per_cu = pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel),
-                                                       64 * kWavesPerUnit);
+                                                       64 * NW);
   const unsigned grid = pa_internal::decode_grid(a, per_cu);
   if (grid == 0) return 6;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.out, a.q,
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * NW), 0, st, a.out, a.q,
                      a.k_pool, a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc,
                      a.plan, a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks,
                      a.num_blocks, a.part_pages, a.max_parts, scale_log2, a.alibi);
