@@ -213,11 +213,17 @@ __device__ __forceinline__ void prefix_unit(
 #pragma unroll
   for (int o2 = 32; o2 >= 1; o2 >>= 1) ctx_max = max(ctx_max, __shfl_xor(ctx_max, o2));
 
-  // this wave's page ids: unit pages wslot, wslot + wpt, ... (one per lane)
+  // this wave's page ids: unit pages wslot, wslot + wpt, ..., one per lane
+  // in two registers (its pages 0-63, then 64-127): with two tiles, wpt is
+  // NW / 2 = 2 and a partition of up to kMaxPartitionPages = 256 pages gives
+  // a wave up to 128 pages
+  static_assert(kMaxPartitionPages <= 2 * 64 * (NW / 2), "two page ids per lane suffice");
   const int np = pe - pb;
-  int my_bid = -1;
+  int my_bid = -1, my_bid_hi = -1;
   if (wslot + wpt * lane < np)
     my_bid = block_tables[(size_t)seq0 * max_blocks + pb + wslot + wpt * lane];
+  if (wslot + wpt * (64 + lane) < np)
+    my_bid_hi = block_tables[(size_t)seq0 * max_blocks + pb + wslot + wpt * (64 + lane)];
   const int np_w = wslot < np ? (np - wslot + wpt - 1) / wpt : 0;
   __syncthreads();  // s_q is written by wave 0 and read by all
 
@@ -233,7 +239,8 @@ __device__ __forceinline__ void prefix_unit(
   const u32x4 *qt = &s_q[tile][0][lane];
 
   auto fetch = [&](PrefixGranule<D> &gr, int jg) {
-    const int bid = __builtin_amdgcn_readlane(my_bid, jg / GPP);
+    const int jp = jg / GPP;  // this wave's page, uniform
+    const int bid = __builtin_amdgcn_readlane(jp < 64 ? my_bid : my_bid_hi, jp & 63);
     gr.ok = (unsigned)bid < (unsigned)num_blocks;
     const size_t off = (size_t)(gr.ok ? bid : 0) * page_stride + (jg % GPP) * S::GBYTES;
 #pragma unroll

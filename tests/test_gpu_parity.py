@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import _bounds
 import oracle
 from paged_kv_cache_457_amd import binding
 from paged_kv_cache_457_amd.device_inputs import to_device, to_host, torch_dtype, upload
@@ -101,6 +102,10 @@ def test_cache_write_skips_negative_and_out_of_range_slots():
 # ------------------------------------------------------- decode parity
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
 def test_decode_step_parity(idx):
+    """The step's cache write bit-exact, attention within the tolerance; for
+    bf16 also every element within 1 bf16 ulp of the oracle plus the fp32
+    error bound of tests/_bounds.py (about ten times tighter than 1e-2 at
+    long contexts, where outputs are about 1e-2 in size)."""
     w = make_config(idx)
     say(f"decode step c{idx}: S={w.num_seqs} H={w.num_heads}/{w.num_kv_heads} "
         f"D={w.head_dim} bs={w.block_size} {w.dtype}")
@@ -109,8 +114,25 @@ def test_decode_step_parity(idx):
     ref, kp, vp = oracle_step(w)
     assert to_host(dw.k_pool, w.dtype).tobytes() == kp.tobytes()
     err = max_err(got, ref, w.dtype)
-    say(f"  max abs err {err:.3e} (tolerance {TOL[w.dtype]})")
+    g = oracle.widen(got, w.dtype)
+    i = np.unravel_index(int(np.argmax(np.abs(g - ref))), ref.shape)
+    say(f"  max abs err {err:.3e} at {tuple(int(x) for x in i)} (tolerance {TOL[w.dtype]}), "
+        f"mean abs err {float(np.mean(np.abs(g - ref))):.3e}")
     assert err <= TOL[w.dtype]
+    if w.dtype != "bf16":
+        return
+    part = binding.paged_attention_decode_partition_tokens(dw.q, dw.k_pool, dw.block_tables,
+                                                           w.partition_size)
+    delta = _bounds.fp32_delta(
+        m_v=_bounds.max_abs_live(vp, w.dtype),
+        a_dot=_bounds.max_abs_dot(w.q, kp, w.block_tables, w.context_lens, w.num_kv_heads,
+                                  w.block_size, w.dtype),
+        scale=float(w.scale), head_dim=w.head_dim, part_tokens=part,
+        parts=-(-w.max_blocks_per_seq * w.block_size // part), matrix_cores=w.group >= 2)
+    ratio, at = _bounds.check_ulp_bound(got, ref, delta)
+    say(f"  fp32 bound delta {delta:.3e}; worst |err| / (ulp(|ref|) + delta) = {ratio:.3f} "
+        f"at {tuple(int(x) for x in at)}")
+    assert ratio <= 1.0
 
 
 @pytest.mark.parametrize("idx,sizes", [(1, [16, 32, 64, 1024]), (3, [16, 64, 128, 512, 1024]),
