@@ -55,7 +55,9 @@ enum {
   PA_ERR_UNSUPPORTED = 3, /* valid but not built: dtype, head_dim, block_size, group */
   PA_ERR_ALIGN = 4,       /* a pointer is not 16-byte (tables: 4/8-byte) aligned */
   PA_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
-  PA_ERR_HIP = 6          /* the HIP runtime reported a launch error */
+  PA_ERR_HIP = 6,         /* the HIP runtime reported a launch error */
+  PA_ERR_SCRATCH_LIMIT = 7 /* paged_attention_decode_noalloc: the call needs more
+                              than PA_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
@@ -129,6 +131,42 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool,
                            const int32_t *context_lens, int32_t num_kv_heads,
                            float scale, int32_t block_size,
                            const pa_decode_dims *dims);
+
+/* Bytes of the static device scratch of paged_attention_decode_noalloc. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * paged_attention_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The work plan and the split-K partials go to a static device
+ * buffer of PA_NOALLOC_SCRATCH_BYTES (32 MiB) instead of a caller's
+ * workspace; the library allocates nothing and calls no allocating routine.
+ * Every device the library runs on holds one such buffer from the first
+ * call on it until the process ends.
+ *
+ * Arguments, layouts, results and launches are those of
+ * paged_attention_decode, except:
+ *   - dims->workspace must be NULL and dims->workspace_bytes 0
+ *     (PA_ERR_WORKSPACE otherwise);
+ *   - a call whose paged_attention_decode_workspace_bytes() exceeds
+ *     PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_SCRATCH_LIMIT before any HIP
+ *     call (for example 256 sequences x 32 heads x 4 partitions of
+ *     head_dim 128 need 17 MB and fit; 8 x 32 heads x 64 partitions need
+ *     8.5 MB);
+ *   - the first call on a device looks up the buffer's device address
+ *     (hipGetSymbolAddress) with that device current; a failure there
+ *     returns PA_ERR_HIP.
+ * Every call on one device uses that device's one buffer, which keeps the
+ * last call's contents; each call writes every plan entry and partial it
+ * reads, so nothing needs clearing between calls.  Calls that overlap on one
+ * device -- launched on different streams without ordering, or from several
+ * host threads -- race on the buffer and give undefined results.  Calls
+ * ordered on one stream are safe.
+ */
+int paged_attention_decode_noalloc(void *out, const void *q, const void *k_pool,
+                                   const void *v_pool, const int32_t *block_tables,
+                                   const int32_t *context_lens, int32_t num_kv_heads,
+                                   float scale, int32_t block_size, const pa_decode_dims *dims);
 
 /*
  * paged_attention_decode with ALiBi (the showapi.com article, section 4.1,

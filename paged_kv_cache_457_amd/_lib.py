@@ -18,10 +18,12 @@ PA_ERR_UNSUPPORTED = 3
 PA_ERR_ALIGN = 4
 PA_ERR_WORKSPACE = 5
 PA_ERR_HIP = 6
+PA_ERR_SCRATCH_LIMIT = 7
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 
 SIZE_MAX = ctypes.c_size_t(-1).value
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class DecodeDims(ctypes.Structure):
@@ -97,6 +99,10 @@ class CopyDims(ctypes.Structure):
 # name -> (restype, argtypes); every symbol include/pagedattn.h declares
 SIGNATURES = {
     "paged_attention_decode": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+        ctypes.c_int32, ctypes.POINTER(DecodeDims)]),
+    "paged_attention_decode_noalloc": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
         ctypes.c_int32, ctypes.POINTER(DecodeDims)]),

@@ -120,7 +120,11 @@ def _decode_call(entry: str, out, q, k_pool, v_pool, block_tables, context_lens,
     need = lib.paged_attention_decode_workspace_bytes(bs, ctypes.byref(d))
     if need == _lib.SIZE_MAX:
         _check(_lib.PA_ERR_SHAPE, entry)
-    if need and workspace is None:
+    if entry == "paged_attention_decode_noalloc":
+        # the library's static scratch stands in for the workspace
+        if workspace is not None:
+            raise ValueError(f"{entry} takes no workspace")
+    elif need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         d.workspace = _dev(workspace, "workspace")
@@ -155,6 +159,18 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     entry = "paged_attention_decode" if alibi_slopes is None else "paged_attention_decode_alibi"
     return _decode_call(entry, out, q, k_pool, v_pool, block_tables, context_lens, scale,
                         partition_size, workspace, stream, timing_events, alibi_slopes)
+
+
+def paged_attention_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                                   v_pool: torch.Tensor, block_tables: torch.Tensor,
+                                   context_lens: torch.Tensor, scale: Optional[float] = None,
+                                   partition_size: int = 0, stream=None,
+                                   timing_events: Sequence = (None, None)) -> torch.Tensor:
+    """paged_attention_decode with the library's static device scratch in
+    place of a workspace (see paged_attention_decode_noalloc in
+    include/pagedattn.h): nothing is allocated, here or in the library."""
+    return _decode_call("paged_attention_decode_noalloc", out, q, k_pool, v_pool, block_tables,
+                        context_lens, scale, partition_size, None, stream, timing_events, None)
 
 
 def paged_attention_decode_read_probe(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,

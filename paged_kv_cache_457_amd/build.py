@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["pagedattn_decode.hip", "pagedattn_decode_gqa.hip", "pagedattn_decode_prefix.hip",
-           "pagedattn_prefill.hip", "pagedattn_cache.hip", "pagedattn_api.cpp"]
+           "pagedattn_prefill.hip", "pagedattn_cache.hip", "pagedattn_runtime.hip",
+           "pagedattn_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -9,6 +9,7 @@
 #include "pagedattn_internal.h"
 #include "pagedattn_probe_launch.h"
 #include "pagedattn_prefill_launch.h"
+#include "pagedattn_runtime.h"
 
 namespace {
 
@@ -24,6 +25,8 @@ constexpr int kMinDefaultPartitionTokens = 256;
 constexpr int64_t kMinUnits = 128;
 using pa_internal::kMaxPartitionPages;
 using pa_internal::kPlanHeader;
+static_assert(pa_internal::kNoallocScratchBytes == PA_NOALLOC_SCRATCH_BYTES,
+              "the static scratch is the size the header states");
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -169,10 +172,14 @@ size_t prefill_workspace_bytes(int32_t num_kv_heads, int32_t block_size, const p
   return b;
 }
 
+// Where a decode call's work plan and split-K partials go: the caller's
+// workspace, or the library's static device scratch.
+enum class Workspace { kCaller, kStatic };
+
 int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                 const int32_t *block_tables, const int32_t *context_lens, int32_t num_kv_heads,
                 float scale, int32_t block_size, const float *alibi, const pa_decode_dims *dims,
-                bool read_probe = false);
+                bool read_probe = false, Workspace where = Workspace::kCaller);
 int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                  const int32_t *block_tables, const int32_t *context_lens,
                  const int32_t *query_start, int32_t num_kv_heads, float scale,
@@ -281,6 +288,14 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool, const v
                      block_size, nullptr, dims);
 }
 
+int paged_attention_decode_noalloc(void *out, const void *q, const void *k_pool,
+                                   const void *v_pool, const int32_t *block_tables,
+                                   const int32_t *context_lens, int32_t num_kv_heads, float scale,
+                                   int32_t block_size, const pa_decode_dims *dims) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_kv_heads, scale,
+                     block_size, nullptr, dims, false, Workspace::kStatic);
+}
+
 int paged_attention_decode_alibi(void *out, const void *q, const void *k_pool,
                                  const void *v_pool, const int32_t *block_tables,
                                  const int32_t *context_lens, int32_t num_kv_heads, float scale,
@@ -311,11 +326,14 @@ namespace {
 int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                 const int32_t *block_tables, const int32_t *context_lens, int32_t num_kv_heads,
                 float scale, int32_t block_size, const float *alibi, const pa_decode_dims *dims,
-                bool read_probe) {
+                bool read_probe, Workspace where) {
   if (!dims) return PA_ERR_NULL;
   int rc = check_decode_dims(num_kv_heads, block_size, dims);
   if (rc != PA_OK) return rc;
   if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  // the static scratch replaces the workspace: a caller's one is an error
+  if (where == Workspace::kStatic && (dims->workspace || dims->workspace_bytes))
+    return PA_ERR_WORKSPACE;
   if (dims->num_seqs == 0) return PA_OK;  // nothing is read or written; pointers may be NULL
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
@@ -323,10 +341,19 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
     return PA_ERR_ALIGN;
   const int mp = max_partitions(block_size, dims);
   const size_t pb = plan_bytes(dims->num_seqs, mp);
-  if (!dims->workspace || dims->workspace_bytes < pb + partial_bytes(dims, mp) ||
-      !aligned(dims->workspace, 16))
-    return PA_ERR_WORKSPACE;
-  char *ws = static_cast<char *>(dims->workspace);
+  const size_t need = pb + partial_bytes(dims, mp);
+  char *ws = nullptr;
+  if (where == Workspace::kStatic) {
+    if (need > pa_internal::kNoallocScratchBytes) return PA_ERR_SCRATCH_LIMIT;
+    // the first HIP call of the path, after every argument check
+    void *p = nullptr;
+    if (pa_internal::noalloc_scratch(&p) != 0) return PA_ERR_HIP;
+    ws = static_cast<char *>(p);
+  } else {
+    if (!dims->workspace || dims->workspace_bytes < need || !aligned(dims->workspace, 16))
+      return PA_ERR_WORKSPACE;
+    ws = static_cast<char *>(dims->workspace);
+  }
   float *ws_acc = nullptr;
   float *ws_ml = nullptr;
   if (mp > 1) {
@@ -578,6 +605,9 @@ const char *pa_status_string(int status) {
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a pointer is misaligned";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: split-K workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported a launch error";
+    case PA_ERR_SCRATCH_LIMIT:
+      return "PA_ERR_SCRATCH_LIMIT: the call needs more than the library's static scratch "
+             "(PA_NOALLOC_SCRATCH_BYTES); use paged_attention_decode with a workspace";
   }
   return "unknown status";
 }

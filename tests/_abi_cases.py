@@ -419,13 +419,48 @@ expect("read probe misaligned k_pool", read_probe(dims(**ONE), ptrs=[P, P, MIS, 
        _lib.PA_ERR_ALIGN)
 expect("read probe without workspace", read_probe(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
 
+# ---- decode without a workspace (the library's static scratch); every
+# case is rejected before the scratch is looked up, or is an empty batch
+def noalloc(d, hkv=32, bs=16, ptrs=None):
+    p = ptrs or [P] * 6
+    return lib.paged_attention_decode_noalloc(*p, hkv, ctypes.c_float(0.088), bs, ctypes.byref(d))
+
+
+expect("noalloc dims NULL",
+       lib.paged_attention_decode_noalloc(P, P, P, P, P, P, 32, ctypes.c_float(1), 16, None),
+       _lib.PA_ERR_NULL)
+expect("noalloc empty batch is a no-op", noalloc(dims()), _lib.PA_OK)
+expect("noalloc empty batch accepts NULL pointers", noalloc(dims(), ptrs=[None] * 6), _lib.PA_OK)
+expect("noalloc rejects a workspace",
+       noalloc(dims(**ONE, workspace=P, workspace_bytes=1 << 20)), _lib.PA_ERR_WORKSPACE)
+expect("noalloc rejects workspace bytes without a pointer",
+       noalloc(dims(**ONE, workspace_bytes=256)), _lib.PA_ERR_WORKSPACE)
+for i in range(6):
+    ptrs = [P] * 6
+    ptrs[i] = None
+    expect(f"noalloc pointer {i} NULL", noalloc(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_NULL)
+expect("noalloc misaligned q", noalloc(dims(**ONE), ptrs=[P, MIS, P, P, P, P]), _lib.PA_ERR_ALIGN)
+expect("noalloc head_dim 96 unsupported", noalloc(dims(**ONE, head_dim=96)), _lib.PA_ERR_UNSUPPORTED)
+# 8192 sequences x 4 heads of 64 dims in 64 one-page partitions: 70 MB of
+# partials, over the 32 MiB scratch
+big = dims(num_seqs=8192, num_heads=4, head_dim=64, max_blocks_per_seq=64, partition_size=16)
+big_need = lib.paged_attention_decode_workspace_bytes(16, ctypes.byref(big))
+expect("oversized call needs more than the scratch",
+       big_need > _lib.PA_NOALLOC_SCRATCH_BYTES, True)
+expect("noalloc oversized call", noalloc(big, hkv=4), _lib.PA_ERR_SCRATCH_LIMIT)
+# the largest batch of that shape that fits is not rejected for size: with
+# num_blocks = 0 it stops at the shape check instead, which runs first
+fit = dims(num_seqs=3000, num_heads=4, head_dim=64, max_blocks_per_seq=64, partition_size=16,
+           num_blocks=0)
+expect("noalloc shape errors come before the size limit", noalloc(fit, hkv=4), _lib.PA_ERR_SHAPE)
+
 # ---- probe
 expect("probe NULL buffer", lib.pa_hbm_read_probe(None, 1024, P, None), _lib.PA_ERR_NULL)
 expect("probe size not a multiple of 16", lib.pa_hbm_read_probe(P, 1000, P, None), _lib.PA_ERR_SHAPE)
 expect("probe misaligned", lib.pa_hbm_read_probe(MIS, 1024, P, None), _lib.PA_ERR_ALIGN)
 
 # ---- status strings
-for rc in range(7):
+for rc in range(8):
     s = lib.pa_status_string(rc).decode()
     expect(f"status string {rc}", s.split(":")[0].startswith("PA_"), True)
 expect("unknown status", lib.pa_status_string(99).decode(), "unknown status")
