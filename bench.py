@@ -39,8 +39,13 @@ def parse():
                     help="split-K partition in tokens (default: the workload's own, else the "
                          "library default of 1024 tokens)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU-baseline budget: oracle steps are repeated until this is spent")
+                    help="CPU-baseline budget per leg (all cores, then one core): oracle steps "
+                         "are repeated until this is spent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="decode-step: after the timed region, this many steps each preceded "
+                         "by a 1 GiB read that evicts the pools from the caches; reports the "
+                         "partition kernel's cold-cache duration (0: skip)")
     ap.add_argument("--probe", action="store_true", help="also measure achievable read GB/s")
     ap.add_argument("--traffic-json", default=None,
                     help="HBM bytes per partition-kernel launch measured with rocprofv3 counters "
@@ -86,6 +91,14 @@ KERNEL_SOURCES = {
 }
 
 
+def _percentiles(ms):
+    """p10, p50 and p90 of a list of durations in ms."""
+    import numpy as np
+    p = np.percentile(np.asarray(ms, dtype=np.float64), [10, 50, 90])
+    return {"p10": round(float(p[0]), 5), "p50": round(float(p[1]), 5),
+            "p90": round(float(p[2]), 5)}
+
+
 def dominant_kernel(w) -> str:
     """The partition kernel the library runs for this workload: bf16 with a
     group of query heads per kv-head goes to the matrix-core kernel."""
@@ -119,6 +132,76 @@ def measured_traffic(args, kernel, tag=None):
             args.effective_partition or rec.get("seed") != args.seed:
         return None
     return rec.get("bytes_per_launch")
+
+
+# State the all-core leg's worker processes read (inherited through fork,
+# before this process touches the GPU).
+_CPU_STATE = {}
+# Worker processes of the all-core leg: the host's CPU share for one GPU.
+CPU_WORKERS_MAX = 16
+
+
+def _oracle_unit(unit):
+    """oracle.decode on one (sequence, kv-head) unit: that kv-head's query
+    heads over the sequence's pages, in the pools after the step's write."""
+    s, g = unit
+    st = _CPU_STATE
+    w = st["w"]
+    G = w.group
+    import oracle
+    return oracle.decode(w.q[s:s + 1, g * G:(g + 1) * G], st["kp"][:, g:g + 1],
+                         st["vp"][:, g:g + 1], w.block_tables[s:s + 1],
+                         w.context_lens[s:s + 1], 1, w.scale, w.block_size, w.dtype).shape
+
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)      # one BLAS thread per worker process
+
+
+def cpu_baseline_all_cores(w, budget_s):
+    """The oracle, as it stands, on every host core this process may use (at
+    most CPU_WORKERS_MAX): each step runs the oracle's cache write here and
+    oracle.decode over the (sequence, kv-head) units in a pool of worker
+    processes, one BLAS thread each, largest units first.  Must run before
+    this process initialises the GPU (the workers are forked)."""
+    import multiprocessing as mp
+    import oracle
+    from threadpoolctl import threadpool_limits
+    n = max(1, min(CPU_WORKERS_MAX, len(os.sched_getaffinity(0))))
+    kp, vp = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping,
+                                      w.block_size)
+    _CPU_STATE.update(w=w, kp=kp, vp=vp)
+    units = sorted(((s, g) for s in range(w.num_seqs) for g in range(w.num_kv_heads)),
+                   key=lambda u: -int(w.context_lens[u[0]]))
+    chunk = max(1, len(units) // (8 * n))
+    runs = 0
+    with mp.get_context("fork").Pool(n, initializer=_worker_init) as pool, \
+            threadpool_limits(limits=1):
+        list(pool.imap_unordered(_oracle_unit, units[:n], chunksize=1))   # workers up
+        t0 = time.perf_counter()
+        while True:
+            oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping,
+                                     w.block_size)
+            for _ in pool.imap_unordered(_oracle_unit, units, chunksize=chunk):
+                pass
+            runs += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = (time.perf_counter() - t0) / runs
+    _CPU_STATE.clear()
+    return {
+        "value": round(w.num_seqs / dt, 2),
+        "unit": "tokens/s",
+        "cores": n,
+        "kind": "oracle",
+        "sample": f"the whole batch ({w.num_seqs} sequences): per step the oracle's cache "
+                  f"write in one process, then oracle.decode over {len(units)} (sequence, "
+                  f"kv-head) units in {n} worker processes, one BLAS thread each; {runs} "
+                  f"step(s), {dt:.3f} s/step, fp64 NumPy; host has "
+                  f"{len(os.sched_getaffinity(0))} usable cores "
+                  f"({platform.processor() or platform.machine()})",
+    }
 
 
 def cpu_baseline(w, budget_s):
@@ -462,6 +545,13 @@ def main():
     from paged_kv_cache_457_amd.device_inputs import upload
     from paged_kv_cache_457_amd.workloads import CONFIG_NAMES, make_config
 
+    cpu_legs, w = None, None
+    if args.op == "decode-step" and not args.no_cpu_baseline:
+        # the oracle on the host first: the all-core leg forks worker
+        # processes, which must happen before this process touches the GPU
+        w = make_config(args.config, args.seed)
+        cpu_legs = (cpu_baseline_all_cores(w, args.cpu_seconds),
+                    cpu_baseline(w, args.cpu_seconds))
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
@@ -474,7 +564,8 @@ def main():
     if args.op != "decode-step":
         bench_copy(args)
         return
-    w = make_config(args.config, args.seed)
+    if w is None:
+        w = make_config(args.config, args.seed)
     if args.partition_size is None:
         args.partition_size = w.partition_size
     dw = upload(w)
@@ -535,18 +626,42 @@ def main():
     ms_step = start.elapsed_time(end) / args.steps
 
     # then K more steps with one event pair each, recorded by the library on
-    # its stream right before and after the partition kernel
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:
-        a.record(stream)
-        b.record(stream)
+    # its stream right before and after the partition kernel, and one event
+    # at every step boundary (the per-step distribution)
+    def event_pairs(n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            b.record(stream)
+        return evs
+
+    evs = event_pairs(args.steps)
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     for i in range(args.steps):
+        bounds[i].record(stream)
         step(evs[i])
+    bounds[-1].record(stream)
     torch.cuda.synchronize()
     k1_ms = [a.elapsed_time(b) for a, b in evs]
     k1_avg_ms = float(np.mean(k1_ms))
+    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]
+
+    # cold caches: before each of these steps a read of a 1 GiB buffer
+    # evicts the pools from L2 and the 256 MB last-level cache; only the
+    # partition kernel is timed (the library's events)
+    cold_ms = None
+    if args.cold_steps:
+        flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        cev = event_pairs(args.cold_steps)
+        torch.cuda.synchronize()
+        for i in range(args.cold_steps):
+            flush.sum()
+            step(cev[i])
+        torch.cuda.synchronize()
+        cold_ms = [a.elapsed_time(b) for a, b in cev]
+        del flush
 
     # the decode access pattern without its arithmetic, on the same inputs:
     # the read rate the partition kernel's loads can reach on this device
@@ -661,6 +776,8 @@ def main():
         "kv_read_gbs_step": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
         "kv_read_frac_of_peak_step": round(kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "partition_kernel_ms": round(k1_avg_ms, 5),
+        "step_ms_percentiles": _percentiles(step_ms),
+        "partition_kernel_ms_percentiles": _percentiles(k1_ms),
         **({"graph_ms_per_step": round(graph_ms, 5),
             "graph_tokens_per_s": round(w.num_seqs / (graph_ms * 1e-3), 1)} if graph_ms else {}),
         "wall_s_timed_region": round(t_wall, 4),
@@ -681,12 +798,22 @@ def main():
             "read_gbs": round(pattern_gbs, 1),
             "partition_kernel_frac_of_probe": round(achieved / pattern_gbs, 4),
         }
+    if cold_ms:
+        cold_p50 = float(np.median(cold_ms))
+        cold_gbs = kernel_bytes / (cold_p50 * 1e-3) / 1e9
+        result["cold_cache"] = {
+            "flush": "1 GiB read before each step (L2 and the 256 MB last-level cache)",
+            "steps": args.cold_steps,
+            "partition_kernel_ms_percentiles": _percentiles(cold_ms),
+            "achieved_gbs_p50": round(cold_gbs, 1),
+            "frac_of_peak_p50": round(cold_gbs / HBM_PEAK_GBS, 4),
+        }
     if w.unique_kv_bytes() != kv_bytes:
         result["unique_kv_read_gbs_step"] = round(w.unique_kv_bytes() / (ms_step * 1e-3) / 1e9, 1)
     if probe_gbs is not None:
         result["probe_read_gbs"] = round(probe_gbs, 1)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if cpu_legs:
+        result["cpu_baseline"], result["cpu_baseline_one_core"] = cpu_legs
     print(json.dumps(result), flush=True)
 
 

@@ -37,6 +37,25 @@
  * rejected call returns a nonzero PA_ERR_* code and touches nothing.  A
  * failed launch returns PA_ERR_HIP.  Faults inside a kernel surface, as with
  * any HIP call, at the caller's next synchronisation.
+ *
+ * Device-side preconditions (the contents of tables in device memory) are
+ * not checked by default: the kernels skip out-of-pool page ids and slots
+ * and clamp context lengths instead, as each call states.  With the
+ * environment variable PA_DEBUG_CHECKS=1 every call first copies the device
+ * tables it reads to host memory, waits for its stream, and returns
+ * PA_ERR_PRECONDITION without launching anything when a precondition fails:
+ *   - context lengths in [0, max_blocks_per_seq * block_size];
+ *   - the page ids a context uses (its first ceil(L / block_size) table
+ *     entries) in [0, num_blocks);
+ *   - slots negative or in [0, num_blocks * block_size), the non-negative
+ *     ones distinct;
+ *   - query_start from 0 to num_tokens without decreasing; sharing groups
+ *     from 0 to num_seqs without decreasing, prefix lengths within the
+ *     table, members' prefix page ids equal and in the pool;
+ *   - page copies: no repeated destination, and within one pool no
+ *     destination that is also a source.
+ * That pass synchronises and allocates host memory: it is for debugging,
+ * not for graph capture or timing.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -56,8 +75,10 @@ enum {
   PA_ERR_ALIGN = 4,       /* a pointer is not 16-byte (tables: 4/8-byte) aligned */
   PA_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
   PA_ERR_HIP = 6,         /* the HIP runtime reported a launch error */
-  PA_ERR_SCRATCH_LIMIT = 7 /* paged_attention_decode_noalloc: the call needs more
-                              than PA_NOALLOC_SCRATCH_BYTES of scratch */
+  PA_ERR_SCRATCH_LIMIT = 7, /* paged_attention_decode_noalloc: the call needs more
+                               than PA_NOALLOC_SCRATCH_BYTES of scratch */
+  PA_ERR_PRECONDITION = 8   /* PA_DEBUG_CHECKS=1 found a device-side precondition
+                               violated (see the file header) */
 };
 
 enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
@@ -89,7 +110,12 @@ typedef struct pa_decode_dims {
 } pa_decode_dims;
 
 /*
- * Single-token decode attention over a paged KV cache.
+ * Single-token decode attention over a paged KV cache: the attention step of
+ * each decode iteration, reading the sequence's KV pages through its page
+ * table in place, with no gather copy and no padding (showapi.com article,
+ * section 2.1; tutorial page, section 4.2 and its page-table figure, and
+ * section 4.3, step 3 of the iteration).  The formula is not on the pages;
+ * the one below is standard softmax attention per query head.
  *
  * For sequence s with L = context_lens[s] (clamped to
  * [0, max_blocks_per_seq * block_size]) and every query head h:
@@ -121,10 +147,17 @@ typedef struct pa_decode_dims {
  * depend on the order units run in: each output element is computed by one
  * fixed sequence of operations on its sequence's tokens.
  *
- * Device-side preconditions (not checked on the host, which cannot read
- * device memory): the first ceil(L / block_size) entries of each used table
- * row lie in [0, num_blocks).  A page id outside that range is skipped by
- * the kernel (its tokens drop out of the softmax) instead of being read.
+ * The workspace is required for every call with num_seqs > 0, also when no
+ * sequence is split: besides the split-K partials it holds the work plan,
+ * which the plan kernel writes on the device so the host never reads
+ * context_lens.  block_size is a separate argument, as in the call's
+ * published argument list; the pools' other dimensions are in dims.
+ *
+ * Device-side preconditions (checked only with PA_DEBUG_CHECKS=1): the
+ * first ceil(L / block_size) entries of each used table row lie in
+ * [0, num_blocks), and 0 <= L <= max_blocks_per_seq * block_size.  Without
+ * the check, a page id outside that range is skipped by the kernel (its
+ * tokens drop out of the softmax) instead of being read, and L is clamped.
  */
 int paged_attention_decode(void *out, const void *q, const void *k_pool,
                            const void *v_pool, const int32_t *block_tables,
@@ -188,7 +221,9 @@ int paged_attention_decode_alibi(void *out, const void *q, const void *k_pool,
  * P = ceil(max_blocks_per_seq * block_size / partition_size):
  *   the work plan, 4 * (4 + num_seqs * P) rounded up to 256, plus, when
  *   P > 1, the split-K partials num_seqs * num_heads * P * (head_dim + 2) * 4.
- * 0 when num_seqs is 0.  Returns SIZE_MAX when the shapes are invalid.
+ * 0 when num_seqs is 0.  Returns SIZE_MAX when the shapes are invalid.  The
+ * size does not depend on the kv-head count, which is not an argument; the
+ * call itself checks the head group and its count of work items.
  */
 size_t paged_attention_decode_workspace_bytes(int32_t block_size,
                                               const pa_decode_dims *dims);
@@ -365,13 +400,23 @@ typedef struct pa_cache_dims {
 } pa_cache_dims;
 
 /*
- * KV-cache write: for each token i with slot = slot_mapping[i] >= 0,
+ * KV-cache write: each decode iteration yields the next token together with
+ * the updated KV cache (tutorial page, section 4.3, step 3), and a token's
+ * K/V lives in its sequence's page at the slot the page table maps its
+ * position to (tutorial page, section 4.2, page-table figure; showapi.com
+ * article, section 2.1).  The slot encoding is not on the pages; here
+ * slot = physical_page * block_size + offset.
+ *
+ * For each token i with slot = slot_mapping[i] >= 0,
  *   k_pool[slot / block_size, :, slot % block_size, :] = k[i, :, :]
  *   v_pool[slot / block_size, :, slot % block_size, :] = v[i, :, :]
  * bit for bit (no conversion).  A negative slot means "no token" and is
  * skipped.  A slot at or past num_blocks * block_size is also skipped
  * rather than written.  Two tokens naming the same slot is a precondition
- * violation (the surviving value is unspecified).
+ * violation (the surviving value is unspecified); PA_DEBUG_CHECKS=1 reports
+ * both as PA_ERR_PRECONDITION instead.  Pointers: k, v [num_tokens,
+ * num_kv_heads, head_dim] and the pools 16-byte aligned, slot_mapping
+ * 8-byte aligned, all device memory owned by the caller.
  */
 int reshape_and_cache(const void *k, const void *v, void *k_pool, void *v_pool,
                       const int64_t *slot_mapping, const pa_cache_dims *dims);

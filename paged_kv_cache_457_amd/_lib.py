@@ -19,6 +19,7 @@ PA_ERR_ALIGN = 4
 PA_ERR_WORKSPACE = 5
 PA_ERR_HIP = 6
 PA_ERR_SCRATCH_LIMIT = 7
+PA_ERR_PRECONDITION = 8
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 
@@ -172,12 +173,17 @@ def load() -> ctypes.CDLL:
         import torch  # noqa: F401
     except ImportError:
         pass
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Set the argument and return types of every declared entry point on
+    a loaded library."""
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
 
 

@@ -3,8 +3,11 @@
 // workspace sizing, and hand-off to the launch code.
 #include "pagedattn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <vector>
 
 #include "pagedattn_internal.h"
 #include "pagedattn_probe_launch.h"
@@ -48,22 +51,30 @@ int partition_tokens(const pa_decode_dims *d, int32_t block_size) {
   return pt;
 }
 
-// Shape checks shared by the decode call and the workspace query.
-int check_decode_dims(int32_t num_kv_heads, int32_t block_size, const pa_decode_dims *d) {
+// Shape checks that do not involve the kv-head count (the workspace and
+// partition queries, which do not take it, apply only these).
+int check_decode_shape(int32_t block_size, const pa_decode_dims *d) {
   if (!d) return PA_ERR_NULL;
-  if (d->num_seqs < 0 || d->num_heads < 1 || num_kv_heads < 1 || d->max_blocks_per_seq < 1 ||
-      d->num_blocks < 1 || d->reserved != 0 || d->partition_size < 0)
+  if (d->num_seqs < 0 || d->num_heads < 1 || d->max_blocks_per_seq < 1 || d->num_blocks < 1 ||
+      d->reserved != 0 || d->partition_size < 0)
     return PA_ERR_SHAPE;
-  if (d->num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   if (d->dtype != PA_DTYPE_F32 && d->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
-  if (!supported_dim(d->head_dim) || !supported_bs(block_size) ||
-      !supported_group(d->num_heads / num_kv_heads))
-    return PA_ERR_UNSUPPORTED;
-  const int pt = partition_tokens(d, block_size);
-  if (pt % block_size != 0 || pt / block_size > kMaxPartitionPages) return PA_ERR_SHAPE;
+  if (!supported_dim(d->head_dim) || !supported_bs(block_size)) return PA_ERR_UNSUPPORTED;
   // context capacity must fit in int32 token counts
   if ((int64_t)d->max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
-  // units (sequence, partition) and work items (unit, kv-head) are int32
+  const int pt = partition_tokens(d, block_size);
+  if (pt % block_size != 0 || pt / block_size > kMaxPartitionPages) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+// Shape checks of a decode call: the above, the head group, and the int32
+// count of (sequence, partition, kv-head) work items.
+int check_decode_dims(int32_t num_kv_heads, int32_t block_size, const pa_decode_dims *d) {
+  const int rc = check_decode_shape(block_size, d);
+  if (rc != PA_OK) return rc;
+  if (num_kv_heads < 1 || d->num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (!supported_group(d->num_heads / num_kv_heads)) return PA_ERR_UNSUPPORTED;
+  const int pt = partition_tokens(d, block_size);
   const int64_t parts = ((int64_t)d->max_blocks_per_seq * block_size + pt - 1) / pt;
   if ((int64_t)d->num_seqs * parts * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
   return PA_OK;
@@ -172,6 +183,123 @@ size_t prefill_workspace_bytes(int32_t num_kv_heads, int32_t block_size, const p
   return b;
 }
 
+// ---------------------------------------------------------------------------
+// PA_DEBUG_CHECKS=1: the device-side preconditions the kernels do not check
+// (they skip or clamp instead), read back and checked on the host.  Debug
+// only: each check copies the tables it needs to pageable host memory and
+// waits for the stream, so it is not for graph capture or timing.  A
+// violation returns PA_ERR_PRECONDITION and nothing is launched.
+bool debug_checks() {
+  const char *e = std::getenv("PA_DEBUG_CHECKS");
+  return e && e[0] == '1' && e[1] == '\0';
+}
+
+template <class T>
+bool read_back(std::vector<T> &dst, const T *src, size_t n, void *stream) {
+  dst.resize(n);
+  return pa_internal::copy_to_host_sync(dst.data(), src, n * sizeof(T), stream) == 0;
+}
+
+// Context lengths in [0, max_blocks * block_size]; the page ids a context
+// uses (its first ceil(ctx / block_size) table entries) in [0, num_blocks).
+int check_tables(const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                 int max_blocks, int num_blocks, int block_size, void *stream) {
+  std::vector<int32_t> ctx, bt;
+  if (!read_back(ctx, context_lens, num_seqs, stream) ||
+      !read_back(bt, block_tables, (size_t)num_seqs * max_blocks, stream))
+    return PA_ERR_HIP;
+  const int64_t cap = (int64_t)max_blocks * block_size;
+  for (int s = 0; s < num_seqs; ++s) {
+    if (ctx[s] < 0 || ctx[s] > cap) return PA_ERR_PRECONDITION;
+    const int64_t used = ((int64_t)ctx[s] + block_size - 1) / block_size;
+    for (int64_t j = 0; j < used; ++j) {
+      const int32_t b = bt[(size_t)s * max_blocks + j];
+      if (b < 0 || b >= num_blocks) return PA_ERR_PRECONDITION;
+    }
+  }
+  return PA_OK;
+}
+
+// Slots negative (no token) or in [0, num_blocks * block_size), and the
+// non-negative ones distinct.
+int check_slots(const int64_t *slot_mapping, int num_tokens, int num_blocks, int block_size,
+                void *stream) {
+  std::vector<int64_t> sl;
+  if (!read_back(sl, slot_mapping, num_tokens, stream)) return PA_ERR_HIP;
+  const int64_t slots = (int64_t)num_blocks * block_size;
+  std::vector<int64_t> used;
+  used.reserve(sl.size());
+  for (const int64_t x : sl) {
+    if (x < 0) continue;
+    if (x >= slots) return PA_ERR_PRECONDITION;
+    used.push_back(x);
+  }
+  std::sort(used.begin(), used.end());
+  return std::adjacent_find(used.begin(), used.end()) == used.end() ? PA_OK
+                                                                     : PA_ERR_PRECONDITION;
+}
+
+// Sharing groups: group_starts runs from 0 to num_seqs without decreasing;
+// prefix_lens in [0, max_blocks * block_size]; the members of a group hold
+// the same page ids in the prefix's whole pages, and those ids are in the
+// pool (the prefix units read them through the group's first member).
+int check_groups(const int32_t *group_starts, const int32_t *prefix_lens, int num_groups,
+                 const int32_t *block_tables, int num_seqs, int max_blocks, int num_blocks,
+                 int block_size, void *stream) {
+  std::vector<int32_t> gs, pl, bt;
+  if (!read_back(gs, group_starts, (size_t)num_groups + 1, stream) ||
+      !read_back(pl, prefix_lens, num_groups, stream) ||
+      !read_back(bt, block_tables, (size_t)num_seqs * max_blocks, stream))
+    return PA_ERR_HIP;
+  if (gs[0] != 0 || gs[num_groups] != num_seqs) return PA_ERR_PRECONDITION;
+  for (int i = 0; i < num_groups; ++i) {
+    if (gs[i + 1] < gs[i]) return PA_ERR_PRECONDITION;
+    if (pl[i] < 0 || (int64_t)pl[i] > (int64_t)max_blocks * block_size)
+      return PA_ERR_PRECONDITION;
+    if (gs[i + 1] == gs[i]) continue;
+    const int pages = pl[i] / block_size;
+    const int32_t *first = &bt[(size_t)gs[i] * max_blocks];
+    for (int j = 0; j < pages; ++j)
+      if (first[j] < 0 || first[j] >= num_blocks) return PA_ERR_PRECONDITION;
+    for (int m = gs[i] + 1; m < gs[i + 1]; ++m)
+      if (!std::equal(first, first + pages, &bt[(size_t)m * max_blocks]))
+        return PA_ERR_PRECONDITION;
+  }
+  return PA_OK;
+}
+
+// query_start runs from 0 to num_tokens without decreasing.
+int check_query_start(const int32_t *query_start, int num_seqs, int num_tokens, void *stream) {
+  std::vector<int32_t> qs;
+  if (!read_back(qs, query_start, (size_t)num_seqs + 1, stream)) return PA_ERR_HIP;
+  if (qs[0] != 0 || qs[num_seqs] != num_tokens) return PA_ERR_PRECONDITION;
+  for (int s = 0; s < num_seqs; ++s)
+    if (qs[s + 1] < qs[s]) return PA_ERR_PRECONDITION;
+  return PA_OK;
+}
+
+// Page copies: no two pairs that are carried out (both pages inside their
+// pools) name the same destination; within one pool no destination is also
+// a source.
+int check_copy_pairs(const int64_t *mapping, int num_pairs, int src_blocks, int dst_blocks,
+                     bool same_pool, void *stream) {
+  std::vector<int64_t> m;
+  if (!read_back(m, mapping, (size_t)num_pairs * 2, stream)) return PA_ERR_HIP;
+  std::vector<int64_t> src, dst;
+  for (int i = 0; i < num_pairs; ++i) {
+    const int64_t a = m[2 * (size_t)i], b = m[2 * (size_t)i + 1];
+    if (a < 0 || a >= src_blocks || b < 0 || b >= dst_blocks) continue;  // skipped pair
+    src.push_back(a);
+    dst.push_back(b);
+  }
+  std::sort(dst.begin(), dst.end());
+  if (std::adjacent_find(dst.begin(), dst.end()) != dst.end()) return PA_ERR_PRECONDITION;
+  if (same_pool)
+    for (const int64_t a : src)
+      if (std::binary_search(dst.begin(), dst.end(), a)) return PA_ERR_PRECONDITION;
+  return PA_OK;
+}
+
 // Where a decode call's work plan and split-K partials go: the caller's
 // workspace, or the library's static device scratch.
 enum class Workspace { kCaller, kStatic };
@@ -190,10 +318,9 @@ int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_poo
 extern "C" {
 
 size_t paged_attention_decode_workspace_bytes(int32_t block_size, const pa_decode_dims *dims) {
-  // The size does not depend on the kv-head count; checking with
-  // num_kv_heads = num_heads (group 1, always built) validates the rest.
-  if (!dims || dims->num_heads < 1) return SIZE_MAX;
-  if (check_decode_dims(dims->num_heads, block_size, dims) != PA_OK) return SIZE_MAX;
+  // The size does not depend on the kv-head count, which the query does
+  // not take; the call itself checks the head group and the item count.
+  if (check_decode_shape(block_size, dims) != PA_OK) return SIZE_MAX;
   if (dims->num_seqs == 0) return 0;
   const int mp = max_partitions(block_size, dims);
   return plan_bytes(dims->num_seqs, mp) + partial_bytes(dims, mp);
@@ -201,10 +328,7 @@ size_t paged_attention_decode_workspace_bytes(int32_t block_size, const pa_decod
 
 size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t block_size,
                                                             const pa_decode_dims *dims) {
-  if (!dims || dims->num_heads < 1) return SIZE_MAX;
-  if (check_decode_dims(dims->num_heads, block_size, dims) != PA_OK) return SIZE_MAX;
-  if ((int64_t)dims->num_seqs * prefix_slots(block_size, dims) * dims->num_heads > INT32_MAX)
-    return SIZE_MAX;
+  if (check_decode_shape(block_size, dims) != PA_OK) return SIZE_MAX;
   if (dims->num_seqs == 0) return 0;
   return prefix_workspace_bytes(block_size, dims);
 }
@@ -235,6 +359,14 @@ int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k
   if (!dims->workspace || dims->workspace_bytes < prefix_workspace_bytes(block_size, dims) ||
       !aligned(dims->workspace, 16))
     return PA_ERR_WORKSPACE;
+  if (debug_checks()) {
+    rc = check_tables(block_tables, context_lens, dims->num_seqs, dims->max_blocks_per_seq,
+                      dims->num_blocks, block_size, dims->stream);
+    if (rc == PA_OK)
+      rc = check_groups(group_starts, prefix_lens, num_groups, block_tables, dims->num_seqs,
+                        dims->max_blocks_per_seq, dims->num_blocks, block_size, dims->stream);
+    if (rc != PA_OK) return rc;
+  }
   int32_t *plan = static_cast<int32_t *>(dims->workspace);
   const size_t plan_ints = prefix_plan_ints(dims->num_seqs, ms);
   const size_t plan_bytes = (plan_ints * sizeof(int32_t) + 255) / 256 * 256;
@@ -275,8 +407,7 @@ int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k
 }
 
 int32_t paged_attention_decode_partition_tokens(int32_t block_size, const pa_decode_dims *dims) {
-  if (!dims || dims->num_heads < 1) return -1;
-  if (check_decode_dims(dims->num_heads, block_size, dims) != PA_OK) return -1;
+  if (check_decode_shape(block_size, dims) != PA_OK) return -1;
   return partition_tokens(dims, block_size);
 }
 
@@ -342,16 +473,24 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
   const int mp = max_partitions(block_size, dims);
   const size_t pb = plan_bytes(dims->num_seqs, mp);
   const size_t need = pb + partial_bytes(dims, mp);
+  if (where == Workspace::kStatic && need > pa_internal::kNoallocScratchBytes)
+    return PA_ERR_SCRATCH_LIMIT;
+  if (where == Workspace::kCaller &&
+      (!dims->workspace || dims->workspace_bytes < need || !aligned(dims->workspace, 16)))
+    return PA_ERR_WORKSPACE;
+  if (debug_checks()) {
+    rc = check_tables(block_tables, context_lens, dims->num_seqs, dims->max_blocks_per_seq,
+                      dims->num_blocks, block_size, dims->stream);
+    if (rc != PA_OK) return rc;
+  }
   char *ws = nullptr;
   if (where == Workspace::kStatic) {
-    if (need > pa_internal::kNoallocScratchBytes) return PA_ERR_SCRATCH_LIMIT;
-    // the first HIP call of the path, after every argument check
+    // the scratch's address: the first HIP call of the path (the debug
+    // pass aside), after every argument check
     void *p = nullptr;
     if (pa_internal::noalloc_scratch(&p) != 0) return PA_ERR_HIP;
     ws = static_cast<char *>(p);
   } else {
-    if (!dims->workspace || dims->workspace_bytes < need || !aligned(dims->workspace, 16))
-      return PA_ERR_WORKSPACE;
     ws = static_cast<char *>(dims->workspace);
   }
   float *ws_acc = nullptr;
@@ -450,6 +589,13 @@ int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_poo
       dims->workspace_bytes < prefill_workspace_bytes(num_kv_heads, block_size, dims) ||
       !aligned(dims->workspace, 16))
     return PA_ERR_WORKSPACE;
+  if (debug_checks()) {
+    rc = check_query_start(query_start, dims->num_seqs, dims->num_tokens, dims->stream);
+    if (rc == PA_OK)
+      rc = check_tables(block_tables, context_lens, dims->num_seqs, dims->max_blocks_per_seq,
+                        dims->num_blocks, block_size, dims->stream);
+    if (rc != PA_OK) return rc;
+  }
   const int parts = prefill_max_parts(num_kv_heads, block_size, dims);
   const size_t pb = prefill_plan_bytes(dims->num_tokens, parts);
   pa_internal::PrefillLaunch a{};
@@ -502,6 +648,11 @@ int reshape_and_cache(const void *k, const void *v, void *k_pool, void *v_pool,
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(slot_mapping, 8))
     return PA_ERR_ALIGN;
+  if (debug_checks()) {
+    const int rc = check_slots(slot_mapping, dims->num_tokens, dims->num_blocks,
+                               dims->block_size, dims->stream);
+    if (rc != PA_OK) return rc;
+  }
   pa_internal::CacheLaunch a{};
   a.k = k;
   a.v = v;
@@ -543,6 +694,11 @@ int reshape_and_cache_rope(void *q, const void *k, const void *v, void *k_pool, 
       !aligned(v_pool, 16) || !aligned(slot_mapping, 8) || !aligned(positions, 8) ||
       !aligned(cos_sin, 16))
     return PA_ERR_ALIGN;
+  if (debug_checks()) {
+    const int rc = check_slots(slot_mapping, dims->num_tokens, dims->num_blocks,
+                               dims->block_size, dims->stream);
+    if (rc != PA_OK) return rc;
+  }
   pa_internal::RopeLaunch r{};
   pa_internal::CacheLaunch &a = r.cache;
   a.k = k;
@@ -580,6 +736,12 @@ int copy_blocks(const void *k_src, const void *v_src, void *k_dst, void *v_dst,
   if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(k_dst, 16) || !aligned(v_dst, 16) ||
       !aligned(block_mapping, 8))
     return PA_ERR_ALIGN;
+  if (debug_checks()) {
+    const int rc = check_copy_pairs(block_mapping, dims->num_pairs, dims->src_num_blocks,
+                                    dims->dst_num_blocks, k_src == k_dst && v_src == v_dst,
+                                    dims->stream);
+    if (rc != PA_OK) return rc;
+  }
   pa_internal::CopyLaunch a{};
   a.k_src = k_src;
   a.v_src = v_src;
@@ -605,6 +767,9 @@ const char *pa_status_string(int status) {
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a pointer is misaligned";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: split-K workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported a launch error";
+    case PA_ERR_PRECONDITION:
+      return "PA_ERR_PRECONDITION: a device-side precondition does not hold (found by "
+             "PA_DEBUG_CHECKS=1)";
     case PA_ERR_SCRATCH_LIMIT:
       return "PA_ERR_SCRATCH_LIMIT: the call needs more than the library's static scratch "
              "(PA_NOALLOC_SCRATCH_BYTES); use paged_attention_decode with a workspace";

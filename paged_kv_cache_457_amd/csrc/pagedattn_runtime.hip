@@ -1,5 +1,6 @@
 // Host-side runtime helpers of libpagedattn: the static device scratch of
-// the allocation-free decode entry point.
+// the allocation-free decode entry point, and the synchronous copy the
+// optional precondition checks read device tables with.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -35,6 +36,13 @@ int noalloc_scratch(void **ptr) {
   }
   *ptr = g_scratch_ptr[dev];
   return 0;
+}
+
+int copy_to_host_sync(void *dst, const void *src, size_t bytes, void *stream) {
+  if (bytes == 0) return 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(dst, src, bytes, hipMemcpyDefault, st) != hipSuccess) return 6;
+  return hipStreamSynchronize(st) == hipSuccess ? 0 : 6;
 }
 
 }  // namespace pa_internal

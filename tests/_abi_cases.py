@@ -4,6 +4,13 @@ tests/test_abi.py runs this file with every GPU hidden from the HIP runtime,
 so even a check that wrongly passed could not reach a device.  Each case
 passes stand-in (non-NULL, never dereferenced) pointers and expects a given
 status code.  Prints one line per case and exits nonzero on any mismatch.
+
+With a library path as its argument it runs against that build instead: the
+host code built with the address and undefined-behaviour sanitizers over
+stand-in launches (tests/host_check/pa_stubs.cpp).  There, calls that pass
+validation "launch" harmlessly, so further cases check the workspace layout
+against the sizes the queries report, and the PA_DEBUG_CHECKS=1 pass on
+tables held in host memory.
 """
 import ctypes
 import os
@@ -14,7 +21,8 @@ sys.path.insert(0, ROOT)
 
 from paged_kv_cache_457_amd import _lib  # noqa: E402
 
-lib = _lib.load()
+STUB = len(sys.argv) > 1
+lib = _lib.bind(ctypes.CDLL(sys.argv[1])) if STUB else _lib.load()
 P = 0x10000          # a 64 KiB-aligned stand-in address; never dereferenced
 MIS = P + 4          # misaligned for 16-byte data
 
@@ -460,10 +468,14 @@ expect("probe size not a multiple of 16", lib.pa_hbm_read_probe(P, 1000, P, None
 expect("probe misaligned", lib.pa_hbm_read_probe(MIS, 1024, P, None), _lib.PA_ERR_ALIGN)
 
 # ---- status strings
-for rc in range(8):
+for rc in range(9):
     s = lib.pa_status_string(rc).decode()
     expect(f"status string {rc}", s.split(":")[0].startswith("PA_"), True)
 expect("unknown status", lib.pa_status_string(99).decode(), "unknown status")
+
+if STUB:
+    import _abi_stub_cases
+    _abi_stub_cases.run(lib, expect)
 
 print(f"{failures} failures", flush=True)
 sys.exit(1 if failures else 0)

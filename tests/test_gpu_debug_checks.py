@@ -1,0 +1,107 @@
+"""PA_DEBUG_CHECKS=1 on the device: the call reads its device tables back,
+and a violated precondition raises PA_ERR_PRECONDITION with nothing
+launched (out keeps its contents); valid inputs give the same bits as
+without the checks.  Every rejected input here is also one the kernels
+handle safely without the check (out-of-pool page ids and slots are
+skipped, context lengths clamped), so no case can reach memory out of
+bounds either way.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_457_amd import _lib, binding
+from paged_kv_cache_457_amd.device_inputs import to_host, upload
+from paged_kv_cache_457_amd.workloads import build_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture
+def debug_checks():
+    os.environ["PA_DEBUG_CHECKS"] = "1"
+    yield
+    os.environ.pop("PA_DEBUG_CHECKS", None)
+
+
+def _decode(dw):
+    binding.paged_attention_decode(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
+                                   dw.context_lens, scale=float(dw.w.scale))
+    torch.cuda.synchronize()
+
+
+def _rejected(fn):
+    with pytest.raises(binding.PagedAttnError) as e:
+        fn()
+    torch.cuda.synchronize()
+    return e.value.rc == _lib.PA_ERR_PRECONDITION
+
+
+def test_debug_checks_pass_valid_inputs_bitwise(debug_checks):
+    w = build_workload("dbg", [1, 40, 300, 0, 17], 16, 4, 128, 16, "bf16", seed=5)
+    dw = upload(w)
+    binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
+    _decode(dw)
+    checked = to_host(dw.out, "bf16").copy()
+    os.environ.pop("PA_DEBUG_CHECKS")
+    _decode(dw)
+    assert to_host(dw.out, "bf16").tobytes() == checked.tobytes()
+
+
+def test_debug_checks_reject_bad_tables(debug_checks):
+    w = build_workload("dbg", [40, 300, 17], 16, 4, 128, 16, "bf16", seed=6)
+    dw = upload(w)
+    dw.out.fill_(3.0)
+    good_bt = dw.block_tables.clone()
+    dw.block_tables[1, 4] = w.num_blocks            # a used column, out of the pool
+    assert _rejected(lambda: _decode(dw))
+    dw.block_tables.copy_(good_bt)
+    dw.block_tables[2, 1] = -5                      # ctx 17 uses columns 0 and 1
+    assert _rejected(lambda: _decode(dw))
+    dw.block_tables.copy_(good_bt)
+    dw.context_lens[0] = w.block_tables.shape[1] * 16 + 1   # past the table's capacity
+    assert _rejected(lambda: _decode(dw))
+    # nothing ran: out still holds the fill
+    assert np.all(to_host(dw.out, "bf16") == np.uint16(0x4040))
+    dw.context_lens.copy_(torch.from_numpy(w.context_lens))
+    dw.block_tables[0, w.block_tables.shape[1] - 1] = 999_999   # unused column: allowed
+    _decode(dw)
+
+
+def test_debug_checks_reject_bad_slots(debug_checks):
+    w = build_workload("dbg", [40, 300, 17], 16, 4, 128, 16, "bf16", seed=7)
+    dw = upload(w)
+    slots = w.slot_mapping.copy()
+    slots[2] = slots[0]                             # two tokens, one slot
+    dup = torch.from_numpy(slots).cuda()
+    assert _rejected(lambda: binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool,
+                                                       dw.v_pool, dup))
+    slots = w.slot_mapping.copy()
+    slots[1] = w.num_blocks * w.block_size          # one past the pool
+    past = torch.from_numpy(slots).cuda()
+    assert _rejected(lambda: binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool,
+                                                       dw.v_pool, past))
+    # the pools are untouched by the rejected calls
+    assert to_host(dw.k_pool, "bf16").tobytes() == w.k_pool.tobytes()
+
+
+def test_debug_checks_reject_bad_sharing_groups(debug_checks):
+    bs, prefix = 16, 64
+    ctx = [prefix + 5, prefix + 9, prefix + 1]
+    w = build_workload("dbg", ctx, 16, 4, 128, bs, "bf16", seed=8,
+                       shared_prefix=[[0, 1, 2]], shared_prefix_len=prefix)
+    dw = upload(w)
+
+    def shared(starts, prefixes):
+        binding.paged_attention_decode_shared_prefix(
+            dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables, dw.context_lens,
+            torch.tensor(starts, dtype=torch.int32, device="cuda"),
+            torch.tensor(prefixes, dtype=torch.int32, device="cuda"), scale=float(w.scale))
+        torch.cuda.synchronize()
+
+    shared([0, 3], [prefix])
+    assert _rejected(lambda: shared([0, 2], [prefix]))          # does not end at num_seqs
+    dw.block_tables[2, 1] = int(w.block_tables[2, 0])           # member 2 leaves the prefix
+    assert _rejected(lambda: shared([0, 3], [prefix]))
