@@ -243,11 +243,21 @@ __device__ __forceinline__ void prefix_unit(
     const int bid = __builtin_amdgcn_readlane(jp < 64 ? my_bid : my_bid_hi, jp & 63);
     gr.ok = (unsigned)bid < (unsigned)num_blocks;
     const size_t off = (size_t)(gr.ok ? bid : 0) * page_stride + (jg % GPP) * S::GBYTES;
+    if (ntiles == 2) {
+      // both row tiles' waves read each page: cached loads, so the second
+      // read of a line finds it in the caches
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      gr.k[c] = __builtin_bit_cast(bf16x8, load_kv16(k_b + off + j16 * ROW + 64 * c + 16 * q4));
+      for (int c = 0; c < NC; ++c)
+        gr.k[c] = __builtin_bit_cast(bf16x8, load16(k_b + off + j16 * ROW + 64 * c + 16 * q4));
 #pragma unroll
-    for (int i = 0; i < NVLD; ++i) gr.v[i] = load_kv16(v_b + off + i * 1024 + 16 * lane);
+      for (int i = 0; i < NVLD; ++i) gr.v[i] = load16(v_b + off + i * 1024 + 16 * lane);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        gr.k[c] = __builtin_bit_cast(bf16x8, load_kv16(k_b + off + j16 * ROW + 64 * c + 16 * q4));
+#pragma unroll
+      for (int i = 0; i < NVLD; ++i) gr.v[i] = load_kv16(v_b + off + i * 1024 + 16 * lane);
+    }
   };
 
   auto process = [&](const PrefixGranule<D> &gr, int jg) {
