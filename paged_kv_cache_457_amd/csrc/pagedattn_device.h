@@ -58,10 +58,13 @@ struct BF16 {
     }
   }
   // fp32 -> bf16, round to nearest even; NaN stays a quiet NaN
+  // (a select, not a branch: the compiler would otherwise give every value
+  // its own masked block)
   __device__ static uint32_t round_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x40u;
+    return (u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded;
   }
   __device__ static u32x4 pack(const float *f) {
     u32x4 c;

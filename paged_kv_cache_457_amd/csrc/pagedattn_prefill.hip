@@ -60,9 +60,6 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanRecord = pa_internal::kPrefillPlanRecord;  // ints per plan item
 constexpr int kBuckets = kPlanThreads - 1;  // plan size classes (key tiles); the last is open-ended
 
-// Source of the zero chunks loaded for keys an item does not see: one
-// 16-byte chunk per lane of a wave.
-__device__ __attribute__((aligned(16))) uint32_t g_zero_chunks[64 * 4];
 
 template <int D, int BS, int G>
 struct PrefillShape {
@@ -101,9 +98,13 @@ __device__ __forceinline__ int swz(int r, int c) {
 // One workgroup.  Every chunk is cut into blocks of `tok` consecutive
 // tokens; with key partitions of kpart tokens (a multiple of kKeys; 0: no
 // split) each block is further cut by its keys, one item per partition
-// that holds keys the block sees.  plan[0] = item count; item k is
-// plan[kPlanHeader + 3k ..] = (sequence, first chunk token, partition),
-// items ordered by the key tiles they read, most first.  With a split,
+// that holds keys the block sees.  plan[0] = item count; item k is the
+// kPlanRecord ints at plan[kPlanHeader + kPlanRecord * k] (their order is
+// given beside kPrefillPlanRecord), items ordered by the key tiles they
+// read, most first.  An item's page flag is set when no page it reads lies
+// outside the pool: the wave that writes a sequence's items first finds
+// the sequence's first such page (a flag left clear only sends the item
+// down the per-key mask path).  With a split,
 // nparts[row] is the number of partitions of the row's block (1: the item
 // writes the row's output itself).  Valid chunks give at most max_items
 // items; with overlapping chunks (an invalid query_start) the surplus is
@@ -114,6 +115,7 @@ __device__ __forceinline__ int swz(int r, int c) {
 // few strided passes rather than one lane's serial loop.
 __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
+    const int32_t *__restrict__ block_tables, int max_blocks, int num_blocks, int block_size,
     int num_seqs, int num_tokens, int ctx_cap, int tok, int kpart, int max_parts, int max_items,
     int32_t *__restrict__ plan, int32_t *__restrict__ nparts) {
   constexpr int kPlanWaves = kPlanThreads / 64;
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
     const int hi = kpart ? min(kv_end, lo + kpart) : kv_end;
     return hi <= lo ? 0 : min((hi - lo + kKeys - 1) / kKeys, kBuckets);
   };
-  // visit(s, block start, partition, keys) for every item of sequence s
+  // visit(block start, partition, keys) for every item of sequence s
   auto items_of = [&](int s, auto visit) {
     int a, n, p0;
     chunk(s, a, n, p0);
@@ -181,18 +183,47 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
     if (t == kPlanThreads - 1) plan[0] = min(before + x, max_items);
   }
   __syncthreads();
-  for (int s = wave; s < num_seqs; s += kPlanWaves)
+  for (int s = wave; s < num_seqs; s += kPlanWaves) {
+    int a, n, p0;
+    chunk(s, a, n, p0);
+    // first page of the sequence's keys whose id lies outside the pool
+    const int npg = (max(0, p0 + n) + block_size - 1) / block_size;
+    int first_bad = 0x7fffffff;
+    for (int p = lane; p < npg; p += 64)
+      if ((unsigned)block_tables[(size_t)s * max_blocks + p] >= (unsigned)num_blocks)
+        first_bad = min(first_bad, p);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) first_bad = min(first_bad, __shfl_xor(first_bad, o));
     items_of(s, [&](int t0, int kp, int ke) {
       const int k = atomicAdd(&s_next[bucket(ke, kp)], 1);
       if (k >= max_items) return;
+      // pages the item's key tiles span
+      const int kt_hi = kpart ? min((ke + kKeys - 1) / kKeys, (kp + 1) * (kpart / kKeys))
+                              : (ke + kKeys - 1) / kKeys;
+      const int p_hi = min(kt_hi * (kKeys / block_size), (ke + block_size - 1) / block_size);
       int32_t *r = plan + kPlanHeader + kPlanRecord * k;
       r[0] = s;
       r[1] = t0;
       r[2] = kp;
+      r[3] = a;
+      r[4] = n;
+      r[5] = p0;
+      r[6] = first_bad >= p_hi;
+      r[7] = 0;
     });
+  }
 }
 
 // ------------------------------------------------------------- work item
+// Four outputs as bf16 bits through the hardware conversion (round to
+// nearest even, one instruction per pair).
+__device__ __forceinline__ uint2 bf16x4_bits(float a, float b, float c, float d) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 lo = {(__bf16)a, (__bf16)b};
+  const bf16x2 hi = {(__bf16)c, (__bf16)d};
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
 __device__ __forceinline__ float rows_max(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                   false);
@@ -214,11 +245,10 @@ __device__ __forceinline__ float rows_sum(float v) {
 template <int D, int BS, int G, bool AL>
 __device__ __forceinline__ void prefill_item(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
-    const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
-    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
-    int num_tokens, int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
-    float scale_log2, const float *__restrict__ alibi, int kpart, int max_parts,
-    float *__restrict__ ws_ml, float *__restrict__ ws_acc, int s, int t0, int kp, int g) {
+    const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables, int num_heads,
+    int num_kv_heads, int max_blocks, int num_blocks, float scale_log2,
+    const float *__restrict__ alibi, int kpart, int max_parts, float *__restrict__ ws_ml,
+    float *__restrict__ ws_acc, int rec, int g) {
   using Sh = PrefillShape<D, BS, G>;
   constexpr int ROW = Sh::ROW, CPR = Sh::CPR, NC = Sh::NC, NN = Sh::NN, TILE = Sh::TILE;
   constexpr int LOADS = Sh::LOADS, TOK = Sh::TOK, PPT = Sh::PPT;
@@ -237,11 +267,14 @@ __device__ __forceinline__ void prefill_item(
   const int q4 = lane >> 4;
   const int j16 = lane & 15;
 
-  // the sequence's chunk (uniform)
-  const int qa = min(max(query_start[s], 0), num_tokens);
-  const int qb = min(max(query_start[s + 1], qa), num_tokens);
-  const int n = qb - qa;
-  const int p0 = min(max(context_lens[s], 0), max_blocks * BS) - n;  // position of chunk token 0
+  // the item's plan record (lane j holds field j; uniform once read out)
+  const int s = __builtin_amdgcn_readlane(rec, 0);
+  const int t0 = __builtin_amdgcn_readlane(rec, 1);    // first chunk token of the block
+  const int kp = __builtin_amdgcn_readlane(rec, 2);    // key partition
+  const int qa = __builtin_amdgcn_readlane(rec, 3);    // the chunk's first row of q
+  const int n = __builtin_amdgcn_readlane(rec, 4);     // chunk length
+  const int p0 = __builtin_amdgcn_readlane(rec, 5);    // position of chunk token 0
+  const bool pages_ok = __builtin_amdgcn_readlane(rec, 6) != 0;  // no page outside the pool
   const int ntok = min(TOK, n - t0);                                  // tokens of this item
   const int kv_end = max(0, p0 + t0 + ntok);                          // keys the block sees
   // this item's key tiles [kt_lo, kt_hi): partition kp of the block's keys
@@ -269,6 +302,15 @@ __device__ __forceinline__ void prefill_item(
   // slope * (key - position) added (log2 units), and the rest of the
   // softmax runs with a unit scale.
   const float cx = AL ? 1.f : c;
+
+  // Page ids of key tile kt, lane j holding the tile's page j (other lanes
+  // load in-row entries that go unused): one vector load, issued a tile
+  // ahead of the loads that use it, so a tile's loads never wait on the
+  // block table.  The first two tiles' ids are loaded before the query rows,
+  // so that the first tile's loads wait on them alone.
+  auto tile_ids = [&](int kt) { return bt[min(kt * PPT + lane, max_blocks - 1)]; };
+  const int ids_first = tile_ids(kt_lo);
+  int ids_next = tile_ids(kt_lo + 1);  // page ids of tile kt + 1 while tile kt is used
 
   // query rows as MFMA B operands, and each row's position (-1: not a row)
   bf16x8 qf[2][NC];
@@ -319,43 +361,44 @@ __device__ __forceinline__ void prefill_item(
     lkey[l] = ci / CPR;
     loff[l] = (lkey[l] % BS) * ROW + swz<D>(lkey[l], ci % CPR) * 16;
   }
-  const char *zero = reinterpret_cast<const char *>(g_zero_chunks) + 16 * lane;
+  // Buffer-resource loads straight into LDS (buffer_load ... lds).  Unlike
+  // the global form, the compiler does not treat them as possibly touching
+  // LDS through a flat address, so its LDS-read waits inside the compute
+  // below stay partial while a tile's loads are in flight.  The buffer's
+  // range check supplies the zeros: a lane whose offset lies past the
+  // resource's size receives zeros, with no branch.
+  constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw 32-bit dwords, no swizzle
+  constexpr int kOutOfRange = 0x7ffffff0;
   // Tile kt into buffer buf, straight from global memory into LDS: each load
   // instruction of a wave fills 64 consecutive 16-byte slots, lane i the
   // slot of chunk column i % CPR in row i / CPR of that span, which holds
   // the row's chunk swz(row, i % CPR) (the swizzle is an XOR, so it is its
-  // own inverse).  Chunks of keys the item does not see, or on pages
-  // outside the pool, come from a page of zeros.
-  auto fetch = [&](int kt, auto buf_c) {
-#pragma unroll
-    for (int l = 0; l < LOADS; ++l) {
-      const int pj = kt * PPT + (l * kThreads + wtid) / CPR / BS;  // uniform
-      // unconditional scalar loads (the index is clamped to the row), so
-      // the compiler issues them together and waits once
-      const int bid = bt[min(pj, max_blocks - 1)];
-      const bool page_ok = pj < npages && (unsigned)bid < (unsigned)num_blocks;
-      const bool ok = page_ok && kt * kKeys + lkey[l] < kv_end;
-      const size_t base = (size_t)(page_ok ? bid : 0) * page_stride;
-      const int span = (l * kThreads + wtid) / CPR * ROW;  // uniform LDS offset
-      __builtin_amdgcn_global_load_lds(ok ? kb + base + loff[l] : zero,
-                                       (lds_char *)kv_buf(buf_c)[0] + span, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(ok ? vb + base + loff[l] : zero,
-                                       (lds_char *)kv_buf(buf_c)[1] + span, 16, 0, 0);
-    }
+  // own inverse).  ids holds the tile's page ids (tile_ids); fetch_one
+  // issues load l of the LOADS a thread makes per tile.  Chunks of keys the
+  // item does not see, or on pages outside the pool, are loaded as zeros
+  // through the range check.
+  auto fetch_one = [&](int kt, auto buf_c, int ids, int l) {
+    const int pt = (l * kThreads + wtid) / CPR / BS;  // page within the tile (uniform)
+    const int pj = kt * PPT + pt;
+    const int bid = __builtin_amdgcn_readlane(ids, pt);
+    const bool page_ok = pj < npages && (unsigned)bid < (unsigned)num_blocks;
+    const bool ok = page_ok && kt * kKeys + lkey[l] < kv_end;
+    const size_t base = (size_t)(page_ok ? bid : 0) * page_stride;
+    const int span = (l * kThreads + wtid) / CPR * ROW;  // uniform LDS offset
+    // the resource spans the head's rows of one page; an offset past it
+    // reads zeros
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kb + base), 0, BS * ROW, kRsrcWord3);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vb + base), 0, BS * ROW, kRsrcWord3);
+    const int off = ok ? loff[l] : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_char *)kv_buf(buf_c)[0] + span, 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_char *)kv_buf(buf_c)[1] + span, 16, off, 0, 0, 0);
   };
-  // tiles that hold no key the item does not see and no page outside the
-  // pool; the table reads are unconditional (index clamped to the row) so
-  // they issue together with one wait
-  auto tile_clean = [&](int kt) {
-    bool ok = (kt + 1) * kKeys <= kv_end;
+  auto fetch = [&](int kt, auto buf_c, int ids) {
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int pj = kt * PPT + j;
-      const int id = bt[min(pj, max_blocks - 1)];
-      ok = ok & (pj >= npages || (unsigned)id < (unsigned)num_blocks);
-    }
-    return ok;
+    for (int l = 0; l < LOADS; ++l) fetch_one(kt, buf_c, ids, l);
   };
+  // tiles that hold no key the item does not see and no page outside the pool
+  auto tile_clean = [&](int kt) { return pages_ok && (kt + 1) * kKeys <= kv_end; };
 
   // softmax state per row tile: running max m (scaled, log2 units), the
   // lane's partial sum, O^T columns
@@ -397,7 +440,8 @@ __device__ __forceinline__ void prefill_item(
     for (int st = 0; st < 2; ++st) {
       const int k16 = 32 * h + 16 * st;    // first key of the sub-tile in the tile
       const int pj = kt * PPT + k16 / BS;  // a sub-tile lies in one page
-      const bool page_ok = pj < npages && (unsigned)bt[pj] < (unsigned)num_blocks;
+      const bool page_ok =
+          pj < npages && (pages_ok || (unsigned)bt[pj] < (unsigned)num_blocks);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -448,13 +492,11 @@ __device__ __forceinline__ void prefill_item(
       }
     }
   };
-  // weights as bf16 B operands (keys 4*q4 + r of sub-tile 0, then of 1),
-  // then O^T += V^T P^T with the half's 32 keys as the reduction dimension.
+  // weights as bf16 B operands (keys 4*q4 + r of sub-tile 0, then of 1).
   // With ALiBi the attention can rest on a handful of nearby keys, so there
   // the weights enter as a bf16 pair hi + lo (about 16 significant bits) at
   // the cost of a second instruction per tile.
-  auto accumulate = [&](const f32x4 (&sacc)[2][2], const lds_char *vs, int h) {
-    i16x8 pb[2], pl[2];
+  auto weights = [&](const f32x4 (&sacc)[2][2], i16x8 (&pb)[2], i16x8 (&pl)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float base = m[t] == -INFINITY ? 0.f : m[t];
@@ -469,54 +511,71 @@ __device__ __forceinline__ void prefill_item(
           if constexpr (AL) pl[t][4 * st + r] = __builtin_bit_cast(short, (__bf16)(p - (float)hi));
         }
     }
+  };
+  // V^T operands of one 32-key part: two transposing reads per 16 columns
+  auto load_v = [&](const lds_char *vs, int h, bf16x8 (&va)[NN]) {
 #pragma unroll
     for (int nb = 0; nb < NN; ++nb) {
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_i16x4 *)(vs + 32 * h * ROW + voff[nb]));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_i16x4 *)(vs + (32 * h + 16) * ROW + voff[nb]));
-      const bf16x8 a =
-          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pb[0]),
+      va[nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  // O^T += V^T P^T with the part's 32 keys as the reduction dimension
+  auto pv = [&](const bf16x8 (&va)[NN], const i16x8 (&pb)[2], const i16x8 (&pl)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < NN; ++nb) {
+      o[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[nb], __builtin_bit_cast(bf16x8, pb[0]),
                                                          o[0][nb], 0, 0, 0);
-      o[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pb[1]),
+      o[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[nb], __builtin_bit_cast(bf16x8, pb[1]),
                                                          o[1][nb], 0, 0, 0);
       if constexpr (AL) {
-        o[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pl[0]),
-                                                           o[0][nb], 0, 0, 0);
-        o[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pl[1]),
-                                                           o[1][nb], 0, 0, 0);
+        o[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            va[nb], __builtin_bit_cast(bf16x8, pl[0]), o[0][nb], 0, 0, 0);
+        o[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            va[nb], __builtin_bit_cast(bf16x8, pl[1]), o[1][nb], 0, 0, 0);
       }
     }
   };
-  // One tile, in 32-key parts.  Each part's scores are computed before the
-  // previous part's exponentials and P.V, so those matrix instructions can
-  // run beside the vector work.
+  // One tile, in 32-key parts, software pipelined over the LDS reads: a
+  // part's V operands are read at its start and used at its end, and the K
+  // operands are read one part ahead.  Each part's scores are computed
+  // before the previous part's exponentials and P.V, so those matrix
+  // instructions can run beside the vector work.
   auto compute = [&](auto masked_c, auto buf_c, int kt) {
     constexpr bool kMasked = decltype(masked_c)::value;
-    constexpr int buf = decltype(buf_c)::value;
     constexpr int kParts = kKeys / 32;
     const lds_char *ks = (const lds_char *)kv_buf(buf_c)[0];
     const lds_char *vs = (const lds_char *)kv_buf(buf_c)[1];
     f32x4 sc[2][2][2];     // scores of two parts in flight: [slot][sub-tile][row tile]
     bf16x8 ka[2][NC];      // K operands of one part
+    bf16x8 va[NN];         // V^T operands of one part
+    i16x8 pb[2], pl[2];
+    // ALiBi's second weight operand leaves no registers for K one part ahead
+    constexpr bool kAhead = !AL;
     load_k(ks, 0, ka);
     scores(ka, sc[0]);
     if constexpr (AL) add_bias(sc[0], kt, 0);
     if constexpr (kMasked) mask(sc[0], kt, 0);
+    if constexpr (kAhead) load_k(ks, 1, ka);
     update_max(sc[0]);
 #pragma unroll
     for (int h = 0; h < kParts; ++h) {
       // keep the scheduler from hoisting one part's LDS reads into another's
       // work, which would raise register pressure past the budget
       __builtin_amdgcn_sched_barrier(0);
+      load_v(vs, h, va);
       if (h + 1 < kParts) {
-        load_k(ks, h + 1, ka);
+        if constexpr (!kAhead) load_k(ks, h + 1, ka);
         scores(ka, sc[(h + 1) & 1]);
         if constexpr (AL) add_bias(sc[(h + 1) & 1], kt, h + 1);
         if constexpr (kMasked) mask(sc[(h + 1) & 1], kt, h + 1);
       }
-      accumulate(sc[h & 1], vs, h);
+      weights(sc[h & 1], pb, pl);
+      if (kAhead && h + 2 < kParts) load_k(ks, h + 2, ka);
+      pv(va, pb, pl);
       if (h + 1 < kParts) update_max(sc[(h + 1) & 1]);
     }
   };
@@ -526,7 +585,11 @@ __device__ __forceinline__ void prefill_item(
   // LDS address is a lane offset plus an immediate.
   auto step = [&](auto masked_c, auto buf_c, int kt) {
     constexpr int buf = decltype(buf_c)::value;
-    if (kt + 1 < kt_hi) fetch(kt + 1, std::integral_constant<int, buf ^ 1>{});
+    using Next = std::integral_constant<int, buf ^ 1>;
+    if (kt + 1 < kt_hi) {
+      fetch(kt + 1, Next{}, ids_next);
+      ids_next = tile_ids(kt + 2);
+    }
     if (wave_live && kt * kKeys <= wmax) compute(masked_c, buf_c, kt);
     __syncthreads();
   };
@@ -540,7 +603,7 @@ __device__ __forceinline__ void prefill_item(
   // takes one barrier per tile, so the two loops of different waves stay in
   // step.  Buffer 0 holds the item's even tiles counted from kt_lo.
   if (kt_hi > kt_lo) {
-    fetch(kt_lo, B0{});
+    fetch(kt_lo, B0{}, ids_first);
     __syncthreads();
     const int clean_end = wave_live ? min(kt_hi, max(kt_lo, (wmin + 1) / kKeys)) : kt_lo;
     int kt = kt_lo;
@@ -570,12 +633,10 @@ __device__ __forceinline__ void prefill_item(
       const float inv = L > 0.f ? 1.f / L : 0.f;
       char *orow = reinterpret_cast<char *>(out) + grow * ROW;
 #pragma unroll
-      for (int nb = 0; nb < NN; ++nb) {
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = o[t][nb][r] * inv;
-        BF16::store4(orow + (16 * nb + 4 * q4) * 2, v);
-      }
+      for (int nb = 0; nb < NN; ++nb)
+        *reinterpret_cast<uint2 *>(orow + (16 * nb + 4 * q4) * 2) =
+            bf16x4_bits(o[t][nb][0] * inv, o[t][nb][1] * inv, o[t][nb][2] * inv,
+                        o[t][nb][3] * inv);
     } else {
       const size_t slot = grow * max_parts + kp;
       float *acc = ws_acc + slot * D;
@@ -648,20 +709,29 @@ template <int D, int BS, int G, bool AL>
 __global__ __launch_bounds__(kThreads, 2) void pa_prefill_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
-    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
-    const int32_t *__restrict__ plan, int num_tokens, int num_heads, int num_kv_heads,
-    int max_blocks, int num_blocks, float scale_log2, const float *__restrict__ alibi,
-    int kpart, int max_parts, float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
+    const int32_t *__restrict__ plan, int num_heads, int num_kv_heads, int max_blocks,
+    int num_blocks, float scale_log2, const float *__restrict__ alibi, int kpart,
+    int max_parts, float *__restrict__ ws_ml, float *__restrict__ ws_acc) {
   const int items = plan[0] * num_kv_heads;
-  for (int k = 0;; ++k) {
-    const int it = snake_item(k);
-    if (it >= items) break;
-    const int32_t *u = plan + kPlanHeader + kPlanRecord * (it / num_kv_heads);
-    prefill_item<D, BS, G, AL>(out, q, k_pool, v_pool, block_tables, context_lens,
-                               query_start, num_tokens, num_heads, num_kv_heads, max_blocks,
-                               num_blocks, scale_log2, alibi, kpart, max_parts, ws_ml, ws_acc,
-                               u[0], u[1], u[2], it % num_kv_heads);
+  // an item's plan record, lane j holding field j; loaded one item ahead, so
+  // an item starts without waiting on the plan (past the last item: the
+  // first record, unused)
+  auto record = [&](int it) {
+    const int r = it < items ? it / num_kv_heads : 0;
+    return plan[kPlanHeader + kPlanRecord * r + (int)(threadIdx.x & (kPlanRecord - 1))];
+  };
+  static_assert((kPlanRecord & (kPlanRecord - 1)) == 0, "record fields by lane mask");
+  int it = snake_item(0);
+  int rec = record(it);
+  for (int k = 0; it < items; ++k) {
+    const int it_next = snake_item(k + 1);
+    const int rec_next = record(it_next);
+    prefill_item<D, BS, G, AL>(out, q, k_pool, v_pool, block_tables, num_heads, num_kv_heads,
+                               max_blocks, num_blocks, scale_log2, alibi, kpart, max_parts,
+                               ws_ml, ws_acc, rec, it % num_kv_heads);
     __syncthreads();  // the next item reuses the LDS
+    it = it_next;
+    rec = rec_next;
   }
 }
 
@@ -676,9 +746,9 @@ int launch_al(const pa_internal::PrefillLaunch &a) {
       (long long)a.num_tokens * a.max_parts * a.num_kv_heads, per_cu);
   if (grid == 0) return 6;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, st, a.out, a.q, a.k_pool, a.v_pool,
-                     a.block_tables, a.context_lens, a.query_start, a.plan, a.num_tokens,
-                     a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
-                     a.scale * kLog2e, a.alibi, a.part_tokens, a.max_parts, a.ws_ml, a.ws_acc);
+                     a.block_tables, a.plan, a.num_heads, a.num_kv_heads, a.max_blocks,
+                     a.num_blocks, a.scale * kLog2e, a.alibi, a.part_tokens, a.max_parts,
+                     a.ws_ml, a.ws_acc);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
@@ -705,7 +775,8 @@ namespace pa_internal {
 int launch_prefill(const PrefillLaunch &a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   hipLaunchKernelGGL(pa_prefill_plan, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens,
-                     a.query_start, a.num_seqs, a.num_tokens, a.max_blocks * a.block_size,
+                     a.query_start, a.block_tables, a.max_blocks, a.num_blocks, a.block_size,
+                     a.num_seqs, a.num_tokens, a.max_blocks * a.block_size,
                      kPrefillRows / (a.num_heads / a.num_kv_heads), a.part_tokens, a.max_parts,
                      a.num_tokens * a.max_parts, a.plan, a.nparts);
   if (hipGetLastError() != hipSuccess) return 6;

@@ -9,9 +9,11 @@
 namespace pa_internal {
 
 // query rows of a prefill work item (token x head of one kv-head's group),
-// and ints per prefill plan item
+// and ints per prefill plan item: (sequence, first chunk token, partition,
+// chunk's first row, chunk length, position of chunk token 0, whether every
+// page the item reads lies in the pool, unused)
 constexpr int kPrefillRows = 256;
-constexpr int kPrefillPlanRecord = 3;
+constexpr int kPrefillPlanRecord = 8;
 // keys of a prefill LDS tile; split-K partitions are whole tiles
 constexpr int kPrefillKeyTile = 128;
 

@@ -284,10 +284,10 @@ for i in range(7):
     ptrs[i] = MIS + 2 if i >= 4 else MIS
     expect(f"prefill: pointer {i} misaligned", prefill(pdims(**ROWS), ptrs=ptrs), _lib.PA_ERR_ALIGN)
 expect("prefill: workspace missing", prefill(pdims(**ROWS)), _lib.PA_ERR_WORKSPACE)
-# plan ints 4 + 3 * rows * P + rows (rounded to 256 bytes), plus with P > 1
+# plan ints 4 + 8 * rows * P + rows (rounded to 256 bytes), plus with P > 1
 # partitions the partials rows * heads * P * (head_dim + 2) floats
 def pf_bytes(rows, heads, dh, parts):
-    b = -(-(4 + 3 * rows * parts + rows) * 4 // 256) * 256
+    b = -(-(4 + 8 * rows * parts + rows) * 4 // 256) * 256
     return b + (rows * heads * parts * (dh + 2) * 4 if parts > 1 else 0)
 
 
