@@ -14,7 +14,7 @@
 // Each of the workgroup's waves carries 32 rows as two 16-row MFMA tiles.
 // Keys go through in tiles of kKeys that all waves share: the workgroup
 // loads a tile's K and V rows straight from global memory into LDS
-// (global_load_lds_dwordx4, no staging registers), double buffered: the
+// (buffer_load_dwordx4 ... lds, no staging registers), double buffered: the
 // next tile's loads are in flight while one tile is used.
 //
 //   q.K   S^T = K Q^T, v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 head_dim
