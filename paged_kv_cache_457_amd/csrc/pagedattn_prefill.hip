@@ -544,7 +544,7 @@ __device__ __forceinline__ void prefill_item(
   // operands are read one part ahead.  Each part's scores are computed
   // before the previous part's exponentials and P.V, so those matrix
   // instructions can run beside the vector work.
-  auto compute = [&](auto masked_c, auto buf_c, int kt) {
+  auto compute = [&](auto masked_c, auto buf_c, int kt, auto after_first_part) {
     constexpr bool kMasked = decltype(masked_c)::value;
     constexpr int kParts = kKeys / 32;
     const lds_char *ks = (const lds_char *)kv_buf(buf_c)[0];
@@ -566,6 +566,10 @@ __device__ __forceinline__ void prefill_item(
       // keep the scheduler from hoisting one part's LDS reads into another's
       // work, which would raise register pressure past the budget
       __builtin_amdgcn_sched_barrier(0);
+      if (h == 1) {
+        after_first_part();
+        __builtin_amdgcn_sched_barrier(0);
+      }
       load_v(vs, h, va);
       if (h + 1 < kParts) {
         if constexpr (!kAhead) load_k(ks, h + 1, ka);
@@ -586,11 +590,21 @@ __device__ __forceinline__ void prefill_item(
   auto step = [&](auto masked_c, auto buf_c, int kt) {
     constexpr int buf = decltype(buf_c)::value;
     using Next = std::integral_constant<int, buf ^ 1>;
-    if (kt + 1 < kt_hi) {
-      fetch(kt + 1, Next{}, ids_next);
-      ids_next = tile_ids(kt + 2);
-    }
-    if (wave_live && kt * kKeys <= wmax) compute(masked_c, buf_c, kt);
+    // The two waves of a SIMD issue the next tile's loads at different
+    // times: the first four waves right away, the other four after their
+    // first 32-key part (or right away when they skip the tile), so that
+    // while one waits for the load unit to take its loads the other
+    // computes.
+    const bool more = kt + 1 < kt_hi;
+    const bool run = wave_live && kt * kKeys <= wmax;
+    const bool early = wave < 4 || !run;
+    const int ids = ids_next;
+    if (more && early) fetch(kt + 1, Next{}, ids);
+    if (more) ids_next = tile_ids(kt + 2);
+    if (run)
+      compute(masked_c, buf_c, kt, [&] {
+        if (more && !early) fetch(kt + 1, Next{}, ids);
+      });
     __syncthreads();
   };
   using B0 = std::integral_constant<int, 0>;
