@@ -104,9 +104,10 @@ typedef struct pa_decode_dims {
                                   work plan and the split-K partials) */
   size_t workspace_bytes;
   void *stream;                /* hipStream_t */
-  void *timing_events[2];      /* optional hipEvent_t pair (or NULLs): recorded on
-                                  the stream immediately before and after the
-                                  partition kernel, for measuring it alone */
+  void *timing_events[2];      /* optional hipEvent_t pair (or NULLs): recorded at
+                                  the partition kernel's own start and end (the
+                                  kernel is launched through hipExtLaunchKernel),
+                                  for measuring it alone */
 } pa_decode_dims;
 
 /*
@@ -309,7 +310,8 @@ typedef struct pa_prefill_dims {
                                   with a split, the partials) */
   size_t workspace_bytes;
   void *stream;                /* hipStream_t */
-  void *timing_events[2];      /* optional hipEvent_t pair around the attention pass */
+  void *timing_events[2];      /* optional hipEvent_t pair, recorded at the
+                                  attention kernel's own start and end */
 } pa_prefill_dims;
 
 /*

@@ -10,6 +10,7 @@
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
 #include "pagedattn_probe_launch.h"
+#include "pagedattn_timed_launch.h"
 
 namespace {
 
@@ -467,8 +468,9 @@ int launch_read_probe_wpi(const DecodeLaunch &a) {
                                                          per_cu * kDecodeGridRounds)
                                  : decode_grid(a, per_cu);
   if (grid == 0) return 6;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * NW), 0, reinterpret_cast<hipStream_t>(a.stream),
-                     reinterpret_cast<char *>(a.out), reinterpret_cast<const char *>(a.k_pool),
+  pa_internal::launch_timed(kernel, dim3(grid), dim3(64 * NW),
+                            reinterpret_cast<hipStream_t>(a.stream), a.ev_begin, a.ev_end,
+                            reinterpret_cast<char *>(a.out), reinterpret_cast<const char *>(a.k_pool),
                      reinterpret_cast<const char *>(a.v_pool), a.block_tables, a.context_lens,
                      a.plan, a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
                      a.block_size, a.part_pages, a.max_parts,
@@ -492,7 +494,7 @@ int launch_read_probe_nld(const DecodeLaunch &a) {
 int launch_decode_read_probe(const DecodeLaunch &a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   if (launch_decode_plan(a) != 0) return 6;
-  if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
+  // the probe kernel's launch records the timing events, if any
   const int run_bytes = a.block_size * a.head_dim * (a.dtype == 0 ? 4 : 2);
   int rc = 3;
   switch (run_bytes / 1024) {
@@ -501,9 +503,7 @@ int launch_decode_read_probe(const DecodeLaunch &a) {
     case 8: rc = launch_read_probe_nld<8>(a); break;
     case 16: rc = launch_read_probe_nld<16>(a); break;
   }
-  if (rc != 0) return rc;
-  if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
-  return 0;
+  return rc;
 }
 
 int launch_hbm_probe(const void *buf, size_t bytes, void *sink, void *stream) {

@@ -27,6 +27,7 @@
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
 #include "pagedattn_probe_launch.h"
+#include "pagedattn_timed_launch.h"
 
 namespace {
 
@@ -589,8 +590,9 @@ int launch_valu_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
                                                        64 * NW);
   const unsigned grid = pa_internal::decode_grid(a, per_cu);
   if (grid == 0) return 6;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * NW), 0, st, a.out, a.q,
-                     a.k_pool, a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc,
+  pa_internal::launch_timed(kernel, dim3(grid), dim3(64 * NW), st, a.ev_begin, a.ev_end, a.out,
+                            a.q, a.k_pool, a.v_pool, a.block_tables, a.context_lens, a.ws_ml,
+                            a.ws_acc,
                      a.plan, a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks,
                      a.num_blocks, a.part_pages, a.max_parts, scale_log2, a.alibi);
   return hipGetLastError() == hipSuccess ? 0 : 6;
@@ -625,11 +627,10 @@ int run_decode(const pa_internal::DecodeLaunch &a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   const float scale_log2 = a.scale * kLog2e;
   if (pa_internal::launch_decode_plan(a) != 0) return 6;
-  if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
+  // the partition kernel's launch records the timing events, if any
   const int rc = a.block_size == 16 ? partition_pass<T, D, 16>(a, scale_log2)
                                     : partition_pass<T, D, 32>(a, scale_log2);
   if (rc != 0) return rc;
-  if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
   if (a.max_parts > 1) return launch_reduce<T, D>(a, nullptr);
   return 0;
 }
@@ -676,10 +677,9 @@ int launch_decode_shared_prefix(const PrefixLaunch &p) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   int rc = launch_prefix_plan(p);
   if (rc != 0) return rc;
-  if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
+  // the unit kernel's launch records the timing events, if any
   rc = launch_prefix_units(p, a.scale * kLog2e);
   if (rc != 0) return rc;
-  if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
   return a.head_dim == 64 ? launch_reduce<BF16, 64>(a, p.nslots)
                           : launch_reduce<BF16, 128>(a, p.nslots);
 }

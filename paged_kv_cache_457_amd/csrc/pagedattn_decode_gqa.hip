@@ -44,6 +44,7 @@
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
 #include "pagedattn_probe_launch.h"
+#include "pagedattn_timed_launch.h"
 
 namespace {
 
@@ -380,8 +381,9 @@ int launch_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
                                                     per_cu * pa_internal::kDecodeGridRounds)
                : pa_internal::decode_grid(a, per_cu);
   if (grid == 0) return 6;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.out, a.q, a.k_pool,
-                     a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc, a.plan,
+  pa_internal::launch_timed(kernel, dim3(grid), dim3(64 * kWavesPerUnit), st, a.ev_begin,
+                            a.ev_end, a.out, a.q, a.k_pool, a.v_pool, a.block_tables,
+                            a.context_lens, a.ws_ml, a.ws_acc, a.plan,
                      a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
                      a.part_pages, a.max_parts, scale_log2, a.alibi);
   return hipGetLastError() == hipSuccess ? 0 : 6;

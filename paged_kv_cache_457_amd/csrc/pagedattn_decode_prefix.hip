@@ -28,6 +28,7 @@
 // row's other masked tokens only multiply finite, live values by 0.
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
+#include "pagedattn_timed_launch.h"
 
 namespace {
 
@@ -421,8 +422,9 @@ int launch(const pa_internal::PrefixLaunch &p, float scale_log2) {
   const unsigned grid = pa_internal::persistent_grid_items(p.max_units * (long long)a.num_kv_heads,
                                                            per_cu * pa_internal::kDecodeGridRounds);
   if (grid == 0) return 6;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWavesPerUnit), 0, st, a.q, a.k_pool,
-                     a.v_pool, a.block_tables, a.context_lens, a.ws_ml, a.ws_acc, a.plan,
+  pa_internal::launch_timed(kernel, dim3(grid), dim3(64 * kWavesPerUnit), st, a.ev_begin,
+                            a.ev_end, a.q, a.k_pool, a.v_pool, a.block_tables, a.context_lens,
+                            a.ws_ml, a.ws_acc, a.plan,
                      a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks, a.max_parts,
                      scale_log2);
   return hipGetLastError() == hipSuccess ? 0 : 6;

@@ -37,6 +37,7 @@
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
 #include "pagedattn_prefill_launch.h"
+#include "pagedattn_timed_launch.h"
 
 namespace {
 
@@ -759,7 +760,8 @@ int launch_al(const pa_internal::PrefillLaunch &a) {
   const unsigned grid = pa_internal::persistent_grid_items(
       (long long)a.num_tokens * a.max_parts * a.num_kv_heads, per_cu);
   if (grid == 0) return 6;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, st, a.out, a.q, a.k_pool, a.v_pool,
+  pa_internal::launch_timed(kernel, dim3(grid), dim3(kThreads), st, a.ev_begin, a.ev_end, a.out,
+                            a.q, a.k_pool, a.v_pool,
                      a.block_tables, a.plan, a.num_heads, a.num_kv_heads, a.max_blocks,
                      a.num_blocks, a.scale * kLog2e, a.alibi, a.part_tokens, a.max_parts,
                      a.ws_ml, a.ws_acc);
@@ -794,14 +796,13 @@ int launch_prefill(const PrefillLaunch &a) {
                      kPrefillRows / (a.num_heads / a.num_kv_heads), a.part_tokens, a.max_parts,
                      a.num_tokens * a.max_parts, a.plan, a.nparts);
   if (hipGetLastError() != hipSuccess) return 6;
-  if (a.ev_begin) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_begin), st);
+  // the attention kernel's launch records the timing events, if any
   int rc;
   if (a.head_dim == 64)
     rc = a.block_size == 16 ? by_group<64, 16>(a) : by_group<64, 32>(a);
   else
     rc = a.block_size == 16 ? by_group<128, 16>(a) : by_group<128, 32>(a);
   if (rc != 0) return rc;
-  if (a.ev_end) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a.ev_end), st);
   if (a.max_parts > 1) {
     const long long rows = (long long)a.num_tokens * a.num_heads;
     auto reduce = a.head_dim == 64 ? pa_prefill_reduce<64> : pa_prefill_reduce<128>;
