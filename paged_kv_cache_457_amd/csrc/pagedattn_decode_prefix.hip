@@ -49,6 +49,7 @@ constexpr int kTiles = kPrefixRows / 16;
 // ------------------------------------------------------------------ plan
 // One workgroup.  Layout of the plan area:
 //   plan[0]                          unit count
+//   plan[1]                          prefix units (they come first)
 //   plan[kPlanHeader + 5k .. +4]     unit k: seq0, nmem, pb, pe, slot
 //   nslots[s]                        partial slots sequence s fills
 //   seq_pre[s]                       shared prefix pages of s's group
@@ -59,11 +60,12 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefix_plan(
     const int32_t *__restrict__ prefix_lens, int num_groups, int num_seqs, int group_size,
     int ctx_cap, int block_size, int part_pages, int32_t *__restrict__ plan,
     int32_t *__restrict__ nslots, int32_t *__restrict__ seq_pre) {
-  __shared__ int s_count[kMaxPartitionPages + 1];
-  __shared__ int s_next[kMaxPartitionPages + 1];
+  // size classes (pages per unit) of prefix units [0] and own units [1]
+  __shared__ int s_count[2][kMaxPartitionPages + 1];
+  __shared__ int s_next[2][kMaxPartitionPages + 1];
   const int members_per_chunk = kPrefixRows / group_size;
   const int max_pages = ctx_cap / block_size;
-  for (int i = threadIdx.x; i <= part_pages; i += kPlanThreads) s_count[i] = 0;
+  for (int i = threadIdx.x; i <= part_pages; i += kPlanThreads) s_count[0][i] = s_count[1][i] = 0;
   for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) seq_pre[s] = 0;
   __syncthreads();
   for (int gi = threadIdx.x; gi < num_groups; gi += kPlanThreads) {
@@ -86,26 +88,30 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefix_plan(
     const int pre = seq_pre[b];
     const int chunks = (e - b + members_per_chunk - 1) / members_per_chunk;
     for (int p0 = 0; p0 < pre; p0 += part_pages)
-      atomicAdd(&s_count[min(part_pages, pre - p0)], chunks);
+      atomicAdd(&s_count[0][min(part_pages, pre - p0)], chunks);
   }
   for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
     const int own = own_pages(s);
-    for (int p0 = 0; p0 < own; p0 += part_pages) atomicAdd(&s_count[min(part_pages, own - p0)], 1);
+    for (int p0 = 0; p0 < own; p0 += part_pages)
+      atomicAdd(&s_count[1][min(part_pages, own - p0)], 1);
     nslots[s] = (seq_pre[s] + part_pages - 1) / part_pages + (own + part_pages - 1) / part_pages;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     int at = 0;
-    for (int z = part_pages; z >= 1; --z) {
-      s_next[z] = at;
-      at += s_count[z];
+    for (int kind = 0; kind < 2; ++kind) {
+      for (int z = part_pages; z >= 1; --z) {
+        s_next[kind][z] = at;
+        at += s_count[kind][z];
+      }
+      if (kind == 0) plan[1] = at;
     }
     plan[0] = at;
   }
   __syncthreads();
-  // pass 2: write the records, largest first
-  auto put = [&](int seq0, int nmem, int pb, int pe, int slot) {
-    int32_t *r = plan + kPlanHeader + kPrefixUnitInts * atomicAdd(&s_next[pe - pb], 1);
+  // pass 2: write the records, prefix units first, each kind largest first
+  auto put = [&](int kind, int seq0, int nmem, int pb, int pe, int slot) {
+    int32_t *r = plan + kPlanHeader + kPrefixUnitInts * atomicAdd(&s_next[kind][pe - pb], 1);
     r[0] = seq0;
     r[1] = nmem;
     r[2] = pb;
@@ -119,14 +125,14 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefix_plan(
     const int pre = seq_pre[b];
     for (int s0 = b; s0 < e; s0 += members_per_chunk)
       for (int p0 = 0, k = 0; p0 < pre; p0 += part_pages, ++k)
-        put(s0, min(members_per_chunk, e - s0), p0, min(pre, p0 + part_pages), k);
+        put(0, s0, min(members_per_chunk, e - s0), p0, min(pre, p0 + part_pages), k);
   }
   for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
     const int pre = seq_pre[s];
     const int own = own_pages(s);
     const int slot0 = (pre + part_pages - 1) / part_pages;
     for (int p0 = 0, k = 0; p0 < own; p0 += part_pages, ++k)
-      put(s, 1, pre + p0, pre + min(own, p0 + part_pages), slot0 + k);
+      put(1, s, 1, pre + p0, pre + min(own, p0 + part_pages), slot0 + k);
   }
 }
 
@@ -164,47 +170,56 @@ struct PrefixGranule {
 // holds the state of one 16-row tile and a granule of K/V is loaded once
 // per tile (the second load of a page by the other tile's waves, at about
 // the same time in the same workgroup, is served by the caches).
+// solo: each wave carries a unit of its own (a sequence's pages past its
+// prefix: one tile), streams all of that unit's pages and writes its
+// partial rows directly; the workgroup's waves then share no state beyond
+// their barriers.  A wave with no unit passes nmem = 0 and pb = pe.
 template <int D, int BS, int G, int NW>
 __device__ __forceinline__ void prefix_unit(
     const void *__restrict__ q, const void *__restrict__ k_pool, const void *__restrict__ v_pool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     float *__restrict__ ws_ml, float *__restrict__ ws_acc, int num_heads, int num_kv_heads,
     int max_blocks, int num_blocks, int max_slots, float scale_log2, int seq0, int nmem, int pb,
-    int pe, int slot, int g) {
+    int pe, int slot, int g, bool solo) {
   using S = PrefixShape<D, BS>;
   constexpr int GPP = S::GPP, NC = S::NC, NN = S::NN, ROW = S::ROW, NVLD = S::NVLD;
   constexpr int PITCH = S::PITCH, DH = S::DH, DHP = S::DHP;
   __shared__ __attribute__((aligned(16))) char s_wave[NW][S::VBYTES];
   __shared__ float s_ml[NW][16][2];
-  // the unit's query rows as MFMA B operands: [tile][slab][lane] 16 bytes
-  __shared__ __attribute__((aligned(16))) u32x4 s_q[kTiles][NC][64];
+  // the unit's query rows as MFMA B operands: [tile (solo: wave)][slab][lane]
+  // 16 bytes
+  __shared__ __attribute__((aligned(16))) u32x4 s_q[NW][NC][64];
+  static_assert(kTiles <= NW, "a query slot per tile");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q4 = lane >> 4;
   const int j16 = lane & 15;
   const int rows = nmem * G;                       // query rows of this unit (<= 32)
-  const int ntiles = (rows + 15) / 16;             // 1 or 2, same for the whole workgroup
-  const int wpt = ntiles == 2 ? NW / 2 : NW;       // waves per tile
-  const int tile = wave / wpt;                     // this wave's tile
-  const int wslot = wave % wpt;                    // its place among the tile's waves
+  const int ntiles = solo ? 1 : (rows + 15) / 16;  // 1 or 2, same for the whole workgroup
+  const int wpt = solo ? 1 : ntiles == 2 ? NW / 2 : NW;  // waves per tile
+  const int tile = solo ? 0 : wave / wpt;           // this wave's tile
+  const int wslot = solo ? 0 : wave % wpt;          // its place among the tile's waves
+  const int qslot = solo ? wave : tile;             // its query rows in s_q
   const int ctx_cap = max_blocks * BS;
 
-  // q of both tiles to LDS (wave 0), each row's context length, the longest
+  // q of both tiles to LDS (wave 0; solo: each wave its own), each row's
+  // context length, the longest
   int ctx_max = 0, my_ctx = 0;
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
+    if (solo && t > 0) break;
     const int r = 16 * t + j16;
     const bool live = r < rows;
     const int s = seq0 + (live ? r / G : 0);
-    if (wave == 0) {
+    if (solo || wave == 0) {
       const char *qrow =
           reinterpret_cast<const char *>(q) + ((size_t)s * num_heads + g * G + r % G) * ROW;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         u32x4 w = {0u, 0u, 0u, 0u};
         if (live) w = load16(qrow + 64 * c + 16 * q4);
-        s_q[t][c][lane] = w;
+        s_q[solo ? wave : t][c][lane] = w;
       }
     }
     const int c = live ? min(max(context_lens[s], 0), ctx_cap) : 0;
@@ -237,7 +252,7 @@ __device__ __forceinline__ void prefix_unit(
   const char *k_b = reinterpret_cast<const char *>(k_pool) + (size_t)g * BS * ROW;
   const char *v_b = reinterpret_cast<const char *>(v_pool) + (size_t)g * BS * ROW;
   char *vs = s_wave[wave];
-  const u32x4 *qt = &s_q[tile][0][lane];
+  const u32x4 *qt = &s_q[qslot][0][lane];
 
   auto fetch = [&](PrefixGranule<D> &gr, int jg) {
     const int jp = jg / GPP;  // this wave's page, uniform
@@ -334,10 +349,27 @@ __device__ __forceinline__ void prefix_unit(
     }
   }
 
-  // Merge: each tile's waves by log-sum-exp, through LDS, in head_dim slices
-  // of DH columns (a wave's slice of its partial O fits its staging area).
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+  if (solo) {
+    // the wave's own partial rows: lane (q4, j) holds d = 16n + 4*q4 .. +3
+    // of row j
+    if (j16 < rows) {
+      const size_t wrow =
+          ((size_t)(seq0 + j16 / G) * num_heads + g * G + j16 % G) * max_slots + slot;
+#pragma unroll
+      for (int n = 0; n < NN; ++n)
+        *reinterpret_cast<float4 *>(ws_acc + wrow * D + 16 * n + 4 * q4) =
+            make_float4(o[n][0], o[n][1], o[n][2], o[n][3]);
+      if (q4 == 0) {
+        ws_ml[wrow * 2] = m;
+        ws_ml[wrow * 2 + 1] = l;
+      }
+    }
+    return;
+  }
+  // Merge: each tile's waves by log-sum-exp, through LDS, in head_dim slices
+  // of DH columns (a wave's slice of its partial O fits its staging area).
   if (q4 == 0) {
     s_ml[wave][j16][0] = m;
     s_ml[wave][j16][1] = l;
@@ -387,24 +419,38 @@ __device__ __forceinline__ void prefix_unit(
   }
 }
 
-// Kernel over the plan's units (largest first), item i = (unit
-// i / num_kv_heads, kv-head i % num_kv_heads), snake order, on a grid of
-// several rounds of resident workgroups.
+// Kernel over the plan's units, snake order, on a grid of several rounds of
+// resident workgroups.  Prefix units first, item i = (unit i / num_kv_heads,
+// kv-head i % num_kv_heads), all NW waves on one unit; then the own units
+// NW at a time, one per wave (solo), item = (NW consecutive units,
+// kv-head).
 template <int D, int BS, int G, int NW>
 __global__ __launch_bounds__(64 * NW) void pa_decode_prefix_gqa(
     const void *__restrict__ q, const void *__restrict__ k_pool, const void *__restrict__ v_pool,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     float *__restrict__ ws_ml, float *__restrict__ ws_acc, const int32_t *__restrict__ plan,
     int num_heads, int num_kv_heads, int max_blocks, int num_blocks, int max_slots,
-    float scale_log2) {
-  const int items = plan[0] * num_kv_heads;
+    float scale_log2, int solo_own) {
+  const int units = plan[0];
+  // own units run solo unless a unit can exceed the 128 page ids a single
+  // wave holds (partitions of more than 128 pages)
+  const int npre = solo_own ? plan[1] : units;
+  const int pre_items = npre * num_kv_heads;
+  const int items = pre_items + (units - npre + NW - 1) / NW * num_kv_heads;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   for (int k = 0;; ++k) {
     const int it = snake_item(k);
     if (it >= items) break;
-    const int32_t *u = plan + kPlanHeader + (size_t)kPrefixUnitInts * (it / num_kv_heads);
+    const bool solo = it >= pre_items;
+    const int i = solo ? it - pre_items : it;
+    const int unit = solo ? npre + NW * (i / num_kv_heads) + wave : i / num_kv_heads;
+    const bool has = unit < units;  // the last group of own units may be short
+    // (index clamped: the record of a missing unit is not read past the list)
+    const int32_t *u = plan + kPlanHeader + (size_t)kPrefixUnitInts * min(unit, units - 1);
     prefix_unit<D, BS, G, NW>(q, k_pool, v_pool, block_tables, context_lens, ws_ml, ws_acc,
                               num_heads, num_kv_heads, max_blocks, num_blocks, max_slots,
-                              scale_log2, u[0], u[1], u[2], u[3], u[4], it % num_kv_heads);
+                              scale_log2, has ? u[0] : 0, has ? u[1] : 0, has ? u[2] : 0,
+                              has ? u[3] : 0, has ? u[4] : 0, i % num_kv_heads, solo);
     __syncthreads();  // the next unit reuses the LDS
   }
 }
@@ -424,9 +470,9 @@ int launch(const pa_internal::PrefixLaunch &p, float scale_log2) {
   if (grid == 0) return 6;
   pa_internal::launch_timed(kernel, dim3(grid), dim3(64 * kWavesPerUnit), st, a.ev_begin,
                             a.ev_end, a.q, a.k_pool, a.v_pool, a.block_tables, a.context_lens,
-                            a.ws_ml, a.ws_acc, a.plan,
-                     a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks, a.max_parts,
-                     scale_log2);
+                            a.ws_ml, a.ws_acc, a.plan, a.num_heads, a.num_kv_heads,
+                            a.max_blocks, a.num_blocks, a.max_parts, scale_log2,
+                            a.part_pages <= 128 ? 1 : 0);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

@@ -654,6 +654,21 @@ def test_shared_prefix_short_members_and_partial_pages():
         assert np.all(got[3] == 0)
 
 
+def test_shared_prefix_long_own_parts_one_wave_and_four_wave_units():
+    """Own parts of up to 1900 tokens.  At a 2048-token partition (128
+    pages) an own unit of up to 119 pages runs on one wave, which holds the
+    unit's page ids in two registers; at 4096 tokens (256 pages) own units
+    can exceed that and run on all four waves of a workgroup."""
+    bs, prefix = 16, 256
+    w = _shared_workload([3, 2], prefix, [[1900, 1000, 70], [1500, 5]], 8, 2, 128, bs, seed=91)
+    ref, _, _ = oracle_step(w)
+    for ps in (2048, 4096, 0):
+        got = shared_step(upload(w), [0, 3, 5], [prefix, prefix], partition_size=ps)
+        err = max_err(got, ref, "bf16")
+        say(f"partition {ps}: max abs err {err:.3e}")
+        assert err <= TOL["bf16"]
+
+
 def test_shared_prefix_matches_plain_decode_on_unshared_batch():
     """Every sequence its own group with no prefix: the own-page units only."""
     w = make_config(3)
