@@ -87,7 +87,7 @@ int max_partitions(int32_t block_size, const pa_decode_dims *d) {
 
 // Workspace layout: the unit plan (int32, rounded up to 256 bytes), then,
 // when a sequence can span more than one partition, the partials:
-// fp32 accumulators [S, H, P, D] followed by (max, sum) pairs [S, H, P, 2].
+// fp32 accumulators [S, P, H, D] followed by (max, sum) pairs [S, P, H, 2].
 size_t plan_bytes(int num_seqs, int parts) {
   const size_t b = ((size_t)kPlanHeader + (size_t)num_seqs * parts) * sizeof(int32_t);
   return (b + 255) / 256 * 256;

@@ -463,7 +463,9 @@ template <int NLD, int NW, int WPI>
 int launch_read_probe_wpi(const DecodeLaunch &a) {
   auto kernel = pa_decode_read_probe<NLD, NW, WPI>;
   static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(kernel), 64 * NW);
-  const long long items = (long long)a.num_seqs * a.max_parts * a.num_kv_heads;
+  // an item covers a.chain partitions (one unless WPI == 1)
+  const int units = (a.max_parts + a.chain - 1) / a.chain;
+  const long long items = (long long)a.num_seqs * units * a.num_kv_heads;
   const unsigned grid = WPI == 1 ? persistent_grid_items((items + NW - 1) / NW,
                                                          per_cu * kDecodeGridRounds)
                                  : decode_grid(a, per_cu);
@@ -473,7 +475,7 @@ int launch_read_probe_wpi(const DecodeLaunch &a) {
                             reinterpret_cast<char *>(a.out), reinterpret_cast<const char *>(a.k_pool),
                      reinterpret_cast<const char *>(a.v_pool), a.block_tables, a.context_lens,
                      a.plan, a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
-                     a.block_size, a.part_pages, a.max_parts,
+                     a.block_size, a.part_pages * a.chain, units,
                      a.head_dim * (a.dtype == 0 ? 4 : 2));
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
@@ -491,8 +493,10 @@ int launch_read_probe_nld(const DecodeLaunch &a) {
                                     : launch_read_probe_wpi<NLD, 4, 4>(a);
 }
 
-int launch_decode_read_probe(const DecodeLaunch &a) {
-  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+int launch_decode_read_probe(const DecodeLaunch &call) {
+  // items of the partition kernels' shape, runs of partitions included
+  DecodeLaunch a = call;
+  a.chain = decode_chain(call);
   if (launch_decode_plan(a) != 0) return 6;
   // the probe kernel's launch records the timing events, if any
   const int run_bytes = a.block_size * a.head_dim * (a.dtype == 0 ? 4 : 2);

@@ -282,8 +282,8 @@ __device__ __forceinline__ void decode_unit(
       },
       [&](int w, int h) { return s_ml[w][h][0]; }, [&](int w, int h) { return s_ml[w][h][1]; },
       npages <= part_pages, out_b + ((size_t)s * num_heads + h0) * head_row_bytes,
-      ws_acc + (((size_t)s * num_heads + h0) * max_parts + part) * D,
-      ws_ml + (((size_t)s * num_heads + h0) * max_parts + part) * 2, (size_t)max_parts);
+      ws_acc + (((size_t)s * max_parts + part) * num_heads + h0) * D,
+      ws_ml + (((size_t)s * max_parts + part) * num_heads + h0) * 2);
 }
 
 // Partition kernel: a grid of up to kDecodeGridRounds times what the GPU
@@ -426,12 +426,14 @@ __global__ __launch_bounds__(64 * kReduceWaves) void pa_decode_reduce(
     nparts = (ctx + part_tokens - 1) / part_tokens;
     if (nparts <= 1) return;  // the partition pass wrote the output itself
   }
-  const size_t row0 = ((size_t)s * num_heads + h) * max_parts;
+  // partial p of head h is row (s * max_parts + p) * num_heads + h
+  const size_t row0 = (size_t)s * max_parts * num_heads + h;
+  const size_t pstride = num_heads;  // rows between consecutive partials
   const float *ml = ws_ml + row0 * 2;
   const float *acc = ws_acc + row0 * D + lane * DPL;
 
   float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ml[2 * p]);
+  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ml[2 * p * pstride]);
   M = wave_max(M);
 
   float L = 0.f, o[DPL];
@@ -444,10 +446,10 @@ __global__ __launch_bounds__(64 * kReduceWaves) void pa_decode_reduce(
       for (int u = 0; u < kReduceUnroll; ++u) {
         const int p = p0 + u * kReduceWaves;
         const bool in = p < nparts;
-        w[u] = in ? ml[2 * p] : -INFINITY;
-        lp[u] = in ? ml[2 * p + 1] : 0.f;
+        w[u] = in ? ml[2 * p * pstride] : -INFINITY;
+        lp[u] = in ? ml[2 * p * pstride + 1] : 0.f;
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) a[u][j] = in ? acc[(size_t)p * D + j] : 0.f;
+        for (int j = 0; j < DPL; ++j) a[u][j] = in ? acc[p * pstride * D + j] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < kReduceUnroll; ++u) {
@@ -512,17 +514,19 @@ __global__ __launch_bounds__(64 * kFewHeadsPerBlock) void pa_decode_reduce_few(
     nparts = (ctx + part_tokens - 1) / part_tokens;
     if (nparts <= 1) return;  // the partition pass wrote the output itself
   }
-  const size_t row0 = ((size_t)s * num_heads + h) * max_parts;
+  // partial p of head h is row (s * max_parts + p) * num_heads + h
+  const size_t row0 = (size_t)s * max_parts * num_heads + h;
+  const size_t pstride = num_heads;  // rows between consecutive partials
   const float *ml = ws_ml + row0 * 2;
   const float *acc = ws_acc + row0 * D + lane * DPL;
   float mp[kFewParts], lp[kFewParts], a[kFewParts][DPL];
 #pragma unroll
   for (int p = 0; p < kFewParts; ++p) {
     const bool in = p < nparts;
-    mp[p] = in ? ml[2 * p] : -INFINITY;
-    lp[p] = in ? ml[2 * p + 1] : 0.f;
+    mp[p] = in ? ml[2 * p * pstride] : -INFINITY;
+    lp[p] = in ? ml[2 * p * pstride + 1] : 0.f;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) a[p][j] = in ? acc[(size_t)p * D + j] : 0.f;
+    for (int j = 0; j < DPL; ++j) a[p][j] = in ? acc[p * pstride * D + j] : 0.f;
   }
   float M = -INFINITY;
 #pragma unroll
@@ -685,13 +689,18 @@ int launch_decode_shared_prefix(const PrefixLaunch &p) {
 }
 
 int launch_decode_plan(const DecodeLaunch &a) {
+  // units of a.chain partitions (one, except in the grouped-query kernel's
+  // one-wave form)
   hipLaunchKernelGGL(pa_decode_plan, dim3(1), dim3(kPlanThreads), 0,
                      reinterpret_cast<hipStream_t>(a.stream), a.context_lens, a.plan, a.num_seqs,
-                     a.max_blocks * a.block_size, a.block_size, a.part_pages, a.max_parts);
+                     a.max_blocks * a.block_size, a.block_size, a.part_pages * a.chain,
+                     (a.max_parts + a.chain - 1) / a.chain);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
-int launch_decode(const DecodeLaunch &a) {
+int launch_decode(const DecodeLaunch &call) {
+  DecodeLaunch a = call;
+  a.chain = decode_chain(call);
   return a.dtype == 0 ? dispatch_dim<F32>(a) : dispatch_dim<BF16>(a);
 }
 

@@ -85,23 +85,43 @@ struct GqaGranule {
   bool ok;
 };
 
+// In the one-wave-per-item form (below) one wave streams a run of
+// consecutive partitions of its sequence and kv-head, up to kChainPages
+// pages (one page id per lane) and kChainMax partitions, so the loads of
+// the next partition are in flight while the last granules of one are
+// used, and per-item startup is paid once per run.  The partials of all
+// but the run's last partition wait in LDS until the run is streamed.
+constexpr int kChainPages = 64;
+constexpr int kChainMax = 4;
+
 // WPI: wavefronts per item.  WPI == NW: the workgroup's NW waves deal the
-// unit's pages among them and merge their states in LDS.  WPI == 1: each
-// wave takes a whole item of its own (at most 64 pages, one id per lane)
-// and writes its result from its registers, with no workgroup barrier.
+// unit's pages among them and merge their states in LDS; the item is
+// partition `item` of the sequence.  WPI == 1: each wave takes a whole item
+// of its own, partitions chain * item .. chain * item + chain - 1 (at most
+// 64 pages, one id per lane), streams their pages as one run with the
+// granule prefetch crossing the partition edges, keeps each partition's
+// result as it passes the partition's last page and writes them all at the
+// end of the run, with no workgroup barrier.  Each partition's state
+// starts afresh at its first page, so the results are those of one item
+// per partition.
 template <int D, int BS, int G, int NW, int WPI, bool AL>
 __device__ __forceinline__ void decode_unit_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, int num_heads, int num_kv_heads, int max_blocks,
-    int num_blocks, int part_pages, int max_parts, float scale_log2,
-    const float *__restrict__ alibi, int s, int g, int part) {
+    int num_blocks, int part_pages, int max_parts, int chain, float scale_log2,
+    const float *__restrict__ alibi, int s, int g, int item) {
   using S = GqaShape<D, BS, G>;
   constexpr int GPP = S::GPP, NC = S::NC, NN = S::NN, ROW = S::ROW, NVLD = S::NVLD;
   constexpr int PITCH = S::PITCH;
   __shared__ __attribute__((aligned(16))) char s_wave[NW][S::WAVE_LDS];
   __shared__ float s_ml[NW][G][2];
+  // WPI == 1: partials of the run's earlier partitions, and (slot kPend)
+  // the last partition's (max, sum)
+  constexpr int kPend = WPI == 1 ? kChainMax - 1 : 0;
+  __shared__ __attribute__((aligned(16))) float s_pend[WPI == 1 ? NW : 1][kPend > 0 ? kPend : 1][G * D];
+  __shared__ float s_pend_ml[WPI == 1 ? NW : 1][kPend + 1][G][2];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // LDS region
@@ -109,7 +129,8 @@ __device__ __forceinline__ void decode_unit_gqa(
   const int q4 = lane >> 4;
   const int j16 = lane & 15;
   const int h0 = g * G;
-  const int p_begin = part * part_pages;
+  const int item_pages = WPI == 1 ? chain * part_pages : part_pages;
+  const int p_begin = item * item_pages;
 
   // Independent loads first: context length, this wave's page ids (one per
   // lane; columns past the context are loaded but never used) and q as the
@@ -117,7 +138,7 @@ __device__ __forceinline__ void decode_unit_gqa(
   int ctx = context_lens[s];
   const int col = p_begin + iw + WPI * lane;
   int my_bid = -1;
-  if (iw + WPI * lane < part_pages && col < max_blocks)
+  if (iw + WPI * lane < item_pages && col < max_blocks)
     my_bid = block_tables[(size_t)s * max_blocks + col];
   bf16x8 qb[NC];
   {
@@ -138,7 +159,7 @@ __device__ __forceinline__ void decode_unit_gqa(
   char *out_b = reinterpret_cast<char *>(out);
   if (ctx == 0) {
     // the G output rows (contiguous) become zeros, 16 bytes per lane and step
-    if (part == 0 && iw == 0) {
+    if (item == 0 && iw == 0) {
       const u32x4 z = {0u, 0u, 0u, 0u};
       for (int off = lane * 16; off < G * ROW; off += 64 * 16)
         *reinterpret_cast<u32x4 *>(out_b + ((size_t)s * num_heads + h0) * ROW + off) = z;
@@ -146,7 +167,7 @@ __device__ __forceinline__ void decode_unit_gqa(
     return;
   }
   if (p_begin >= npages) return;
-  const int np = min(npages - p_begin, part_pages);
+  const int np = min(npages - p_begin, item_pages);
   const int np_w = iw < np ? (np - iw + WPI - 1) / WPI : 0;
 
   // running state for head j16 (lanes j16 >= G carry a padding column)
@@ -231,60 +252,140 @@ __device__ __forceinline__ void decode_unit_gqa(
     }
   };
 
+  // WPI == 1: one wave holds a partition's whole state; lane (q4, j16) has
+  // O^T[16n + 4*q4 + r][head j16] (O already summed over tokens by the
+  // MFMAs) and its share of the sum of weights, first summed over the 4
+  // lane groups.  The partials of the run's partitions before its last one
+  // wait in LDS and all of the run's partials are written when the wave has
+  // streamed the run: on MI355X writes issued while the pass streams its
+  // reads cost about 1.3 us per MB written (8 x 32768 tokens at 512-token
+  // partitions: 169 -> 159 us with the writes deferred), and few writes
+  // come at the end of a run.
+  auto hold_partials = [&](int k) {  // k-th partition of the run
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (j16 < G) {
+#pragma unroll
+      for (int n = 0; n < NN; ++n)
+        *reinterpret_cast<float4 *>(&s_pend[wave][k][j16 * D + 16 * n + 4 * q4]) =
+            make_float4(o[n][0], o[n][1], o[n][2], o[n][3]);
+      if (q4 == 0) {
+        s_pend_ml[wave][k][j16][0] = m;
+        s_pend_ml[wave][k][j16][1] = lt;
+      }
+    }
+  };
+  // [G][D] floats of LDS to the G heads' partial rows of partition `part`
+  // (adjacent in the workspace), 16 bytes per lane and store, so that each
+  // store instruction writes up to 1 KiB of whole rows
+  auto write_rows = [&](const float *src, const float *src_ml, int part) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const size_t row0 = ((size_t)s * max_parts + part) * num_heads + h0;
+    float *rows = ws_acc + row0 * D;
+    constexpr int kChunks = G * D / 4;  // 16-byte chunks of the [G][D] block
+#pragma unroll
+    for (int i = 0; i < (kChunks + 63) / 64; ++i) {
+      const int c = 64 * i + lane;
+      if (kChunks % 64 == 0 || c < kChunks)
+        *reinterpret_cast<float4 *>(rows + 4 * c) = *reinterpret_cast<const float4 *>(&src[4 * c]);
+    }
+    if (lane < 2 * G) ws_ml[row0 * 2 + lane] = src_ml[lane];
+  };
+  // The wave's final state: out rows when the sequence is one partition,
+  // else the run's partials, the last partition's through the wave's
+  // staging area ([head][d]; the V granule staged there has been read).
+  const int part_first = p_begin / part_pages;
+  auto store_wave = [&](int part) {
+    if (npages > part_pages) {
+      for (int k = 0; k < part - part_first; ++k)
+        write_rows(s_pend[wave][k], &s_pend_ml[wave][k][0][0], part_first + k);
+      float lt = l + __shfl_xor(l, 16);
+      lt += __shfl_xor(lt, 32);
+      float *st = reinterpret_cast<float *>(vs);
+      if (j16 < G) {
+#pragma unroll
+        for (int n = 0; n < NN; ++n)
+          *reinterpret_cast<float4 *>(&st[j16 * D + 16 * n + 4 * q4]) =
+              make_float4(o[n][0], o[n][1], o[n][2], o[n][3]);
+        if (q4 == 0) {
+          s_pend_ml[wave][kPend][j16][0] = m;
+          s_pend_ml[wave][kPend][j16][1] = lt;
+        }
+      }
+      write_rows(st, &s_pend_ml[wave][kPend][0][0], part);
+      return;
+    }
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (j16 < G) {
+      const size_t row = (size_t)s * num_heads + h0 + j16;
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+#pragma unroll
+      for (int n = 0; n < NN; ++n) {
+        float v[4] = {o[n][0] * inv, o[n][1] * inv, o[n][2] * inv, o[n][3] * inv};
+        BF16::store4(out_b + row * ROW + (16 * n + 4 * q4) * 2, v);
+      }
+    }
+  };
+  // granule index of the next partition's first granule, and the partition
+  // the granules before it belong to.  Past the edge the state restarts
+  // empty.
+  const int pg = part_pages * GPP;
+  int edge = pg;
+  int part = part_first;
+  auto at_edge = [&](int jg) {
+    if constexpr (WPI == 1) {
+      if (jg == edge) {
+        hold_partials(part - part_first);
+        ++part;
+        edge += pg;
+        m = -INFINITY;
+        l = 0.f;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
   // One granule ahead; inside the loop every fetch is unconditional, so the
   // number of loads in flight is the same on every path and the wait before
-  // a granule's use leaves the next one's loads outstanding.
+  // a granule's use leaves the next one's loads outstanding.  A partition
+  // edge before granule j is handled before the loads of granule j + 1 are
+  // issued.
   const int ng = np_w * GPP;
   if (ng > 0) {
     GqaGranule<D, BS, G> ga, gb;
     fetch(ga, 0);
     int j = 0;
     for (; j + 2 < ng; j += 2) {
+      at_edge(j);
       fetch(gb, j + 1);
       process(ga, j);
+      at_edge(j + 1);
       fetch(ga, j + 2);
       process(gb, j + 1);
     }
     if (j + 1 < ng) {
+      at_edge(j);
       fetch(gb, j + 1);
       process(ga, j);
+      at_edge(j + 1);
       process(gb, j + 1);
     } else {
+      at_edge(j);
       process(ga, j);
     }
   }
 
+  if constexpr (WPI == 1) {
+    store_wave(part);
+    return;
+  }
   // this wave's totals: the sum of weights over the 4 lane groups; O is
   // already summed over tokens by the MFMAs
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if constexpr (WPI == 1) {
-    // the wave holds the item's whole state: lane (q4, j16) has
-    // O^T[16n + 4*q4 + r][head j16]; out rows when the sequence is one
-    // partition, else the partition's (max, sum, unnormalised O)
-    if (j16 < G) {
-      const size_t row = (size_t)s * num_heads + h0 + j16;
-      if (npages <= part_pages) {
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
-#pragma unroll
-        for (int n = 0; n < NN; ++n) {
-          float v[4] = {o[n][0] * inv, o[n][1] * inv, o[n][2] * inv, o[n][3] * inv};
-          BF16::store4(out_b + row * ROW + (16 * n + 4 * q4) * 2, v);
-        }
-      } else {
-        float *acc = ws_acc + (row * max_parts + part) * D;
-#pragma unroll
-        for (int n = 0; n < NN; ++n)
-          *reinterpret_cast<float4 *>(acc + 16 * n + 4 * q4) =
-              make_float4(o[n][0], o[n][1], o[n][2], o[n][3]);
-        if (q4 == 0) {
-          ws_ml[(row * max_parts + part) * 2] = m;
-          ws_ml[(row * max_parts + part) * 2 + 1] = l;
-        }
-      }
-    }
-    return;
-  }
   // the V staging area becomes this wave's partial O (its own region)
   float *s_acc = reinterpret_cast<float *>(vs);
   if (j16 < G) {
@@ -305,27 +406,31 @@ __device__ __forceinline__ void decode_unit_gqa(
       },
       [&](int w, int h) { return s_ml[w][h][0]; }, [&](int w, int h) { return s_ml[w][h][1]; },
       npages <= part_pages, out_b + ((size_t)s * num_heads + h0) * ROW,
-      ws_acc + (((size_t)s * num_heads + h0) * max_parts + part) * D,
-      ws_ml + (((size_t)s * num_heads + h0) * max_parts + part) * 2, (size_t)max_parts);
+      ws_acc + (((size_t)s * max_parts + part) * num_heads + h0) * D,
+      ws_ml + (((size_t)s * max_parts + part) * num_heads + h0) * 2);
 }
 
 // Partition kernel over the plan's unit list (largest units first), item
 // i = (list[i / num_kv_heads], kv-head i % num_kv_heads), in the snake order
 // of snake_item.  WPI == NW: one item per workgroup step, on a grid of
-// decode_grid.  WPI == 1: wave w of the workgroup's k-th step takes item
-// NW * snake_item(k) + w, so the NW waves run consecutive items (the kv-heads
-// of one unit) independently.
+// decode_grid; a unit is (sequence, partition).  WPI == 1: wave w of the
+// workgroup's k-th step takes item NW * snake_item(k) + w, so the NW waves
+// run consecutive items (the kv-heads of one unit) independently; a unit is
+// (sequence, run of `chain` partitions).
+// Two waves per SIMD: at most 256 registers (VGPRs and AGPRs) per lane.
 template <int D, int BS, int G, int NW, int WPI, bool AL>
-__global__ __launch_bounds__(64 * NW) void pa_decode_partition_gqa(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void
+pa_decode_partition_gqa(
     void *__restrict__ out, const void *__restrict__ q, const void *__restrict__ k_pool,
     const void *__restrict__ v_pool, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_ml,
     float *__restrict__ ws_acc, const int32_t *__restrict__ plan, int num_seqs, int num_heads,
-    int num_kv_heads, int max_blocks, int num_blocks, int part_pages, int max_parts,
+    int num_kv_heads, int max_blocks, int num_blocks, int part_pages, int max_parts, int chain,
     float scale_log2, const float *__restrict__ alibi) {
-  // the list holds num_seqs * max_parts entries, -1 past the last unit
-  const long long bound = (long long)num_seqs * max_parts * num_kv_heads;
   if constexpr (WPI == 1) {
+    // the list holds num_seqs * max_units entries, -1 past the last unit
+    const int max_units = (max_parts + chain - 1) / chain;
+    const long long bound = (long long)num_seqs * max_units * num_kv_heads;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     for (int k = 0;; ++k) {
       const long long it = (long long)snake_item(k) * NW + wave;
@@ -334,11 +439,13 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_partition_gqa(
       if (unit < 0) break;
       decode_unit_gqa<D, BS, G, NW, 1, AL>(out, q, k_pool, v_pool, block_tables, context_lens,
                                            ws_ml, ws_acc, num_heads, num_kv_heads, max_blocks,
-                                           num_blocks, part_pages, max_parts, scale_log2, alibi,
-                                           unit / max_parts, (int)(it % num_kv_heads),
-                                           unit % max_parts);
+                                           num_blocks, part_pages, max_parts, chain, scale_log2,
+                                           alibi, unit / max_units, (int)(it % num_kv_heads),
+                                           unit % max_units);
     }
   } else {
+    // the list holds num_seqs * max_parts entries, -1 past the last unit
+    const long long bound = (long long)num_seqs * max_parts * num_kv_heads;
     static_assert(WPI == NW, "an item takes one wave or the whole workgroup");
     for (int k = 0;; ++k) {
       const int it = snake_item(k);
@@ -347,8 +454,9 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_partition_gqa(
       if (unit < 0) break;
       decode_unit_gqa<D, BS, G, NW, NW, AL>(out, q, k_pool, v_pool, block_tables, context_lens,
                                             ws_ml, ws_acc, num_heads, num_kv_heads, max_blocks,
-                                            num_blocks, part_pages, max_parts, scale_log2, alibi,
-                                            unit / max_parts, it % num_kv_heads, unit % max_parts);
+                                            num_blocks, part_pages, max_parts, 1, scale_log2,
+                                            alibi, unit / max_parts, it % num_kv_heads,
+                                            unit % max_parts);
       __syncthreads();  // the next unit reuses the LDS the merge just read
     }
   }
@@ -375,7 +483,8 @@ int launch_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
   auto kernel = pa_decode_partition_gqa<D, BS, G, kWavesPerUnit, WPI, AL>;
   static const int per_cu = pa_internal::blocks_per_cu(reinterpret_cast<const void *>(kernel),
                                                        64 * kWavesPerUnit);
-  const long long items = (long long)a.num_seqs * a.max_parts * a.num_kv_heads;
+  const long long items =
+      (long long)a.num_seqs * ((a.max_parts + a.chain - 1) / a.chain) * a.num_kv_heads;
   const unsigned grid =
       WPI == 1 ? pa_internal::persistent_grid_items((items + kWavesPerUnit - 1) / kWavesPerUnit,
                                                     per_cu * pa_internal::kDecodeGridRounds)
@@ -385,7 +494,7 @@ int launch_al(const pa_internal::DecodeLaunch &a, float scale_log2) {
                             a.ev_end, a.out, a.q, a.k_pool, a.v_pool, a.block_tables,
                             a.context_lens, a.ws_ml, a.ws_acc, a.plan,
                      a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks, a.num_blocks,
-                     a.part_pages, a.max_parts, scale_log2, a.alibi);
+                     a.part_pages, a.max_parts, WPI == 1 ? a.chain : 1, scale_log2, a.alibi);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
@@ -423,6 +532,12 @@ namespace pa_internal {
 
 bool gqa_wave_items(const DecodeLaunch &a) {
   return a.part_pages <= kWaveItemPages && a.max_parts >= kWaveItemMinParts;
+}
+
+int decode_chain(const DecodeLaunch &a) {
+  if (a.dtype != 1 || a.num_heads < 2 * a.num_kv_heads || !gqa_wave_items(a)) return 1;
+  const int c = kChainPages / a.part_pages;
+  return c < 1 ? 1 : c > kChainMax ? kChainMax : c;
 }
 
 int launch_partition_gqa(const DecodeLaunch &a, float scale_log2) {

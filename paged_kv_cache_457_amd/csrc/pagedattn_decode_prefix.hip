@@ -356,7 +356,7 @@ __device__ __forceinline__ void prefix_unit(
     // of row j
     if (j16 < rows) {
       const size_t wrow =
-          ((size_t)(seq0 + j16 / G) * num_heads + g * G + j16 % G) * max_slots + slot;
+          ((size_t)(seq0 + j16 / G) * max_slots + slot) * num_heads + g * G + j16 % G;
 #pragma unroll
       for (int n = 0; n < NN; ++n)
         *reinterpret_cast<float4 *>(ws_acc + wrow * D + 16 * n + 4 * q4) =
@@ -408,7 +408,7 @@ __device__ __forceinline__ void prefix_unit(
         }
       }
       const size_t wrow =
-          ((size_t)(seq0 + r / G) * num_heads + g * G + r % G) * max_slots + slot;
+          ((size_t)(seq0 + r / G) * max_slots + slot) * num_heads + g * G + r % G;
       *reinterpret_cast<float4 *>(ws_acc + wrow * D + h * DH + d) =
           make_float4(acc[0], acc[1], acc[2], acc[3]);
       if (h == 0 && d == 0) {

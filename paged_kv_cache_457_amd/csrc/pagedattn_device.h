@@ -164,13 +164,13 @@ __device__ __forceinline__ int snake_item(int k) {
 // w's accumulator for head h at d..d+3, mx / sm its running max (log2 units)
 // and sum.  Each thread handles 4 consecutive outputs of one head.
 //   out_rows     first output row of the unit's G heads ([G][D] of T)
-//   ws_acc_rows  partial accumulator of head 0 of the unit; head h is
-//                parts * D floats further
-//   ws_ml_rows   partial (max, sum) of head 0; head h is parts * 2 further
+//   ws_acc_rows  the partition's partial accumulators of the unit's G heads
+//                ([G][D] floats, consecutive heads adjacent)
+//   ws_ml_rows   their partial (max, sum) pairs ([G][2])
 template <class T, int D, int G, int NW, class AccF, class MaxF, class SumF>
 __device__ __forceinline__ void merge_waves(AccF acc, MaxF mx, SumF sm, bool whole,
                                             char *out_rows, float *ws_acc_rows,
-                                            float *ws_ml_rows, size_t parts) {
+                                            float *ws_ml_rows) {
   for (int idx = threadIdx.x; idx < G * D / 4; idx += 64 * NW) {
     const int h = idx / (D / 4);
     const int d = (idx % (D / 4)) * 4;
@@ -196,11 +196,11 @@ __device__ __forceinline__ void merge_waves(AccF acc, MaxF mx, SumF sm, bool who
       for (int e = 0; e < 4; ++e) o[e] *= inv;
       T::store4(out_rows + ((size_t)h * D + d) * T::kBytes, o);
     } else {
-      *reinterpret_cast<float4 *>(ws_acc_rows + (size_t)h * parts * D + d) =
+      *reinterpret_cast<float4 *>(ws_acc_rows + (size_t)h * D + d) =
           make_float4(o[0], o[1], o[2], o[3]);
       if (d == 0) {
-        ws_ml_rows[(size_t)h * parts * 2] = M;
-        ws_ml_rows[(size_t)h * parts * 2 + 1] = L;
+        ws_ml_rows[h * 2] = M;
+        ws_ml_rows[h * 2 + 1] = L;
       }
     }
   }

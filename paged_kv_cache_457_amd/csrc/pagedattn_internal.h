@@ -27,12 +27,19 @@ struct DecodeLaunch {
   const int32_t *block_tables;
   const int32_t *context_lens;
   int32_t *plan;  // unit list written by the plan kernel
-  float *ws_ml;   // [S, H, max_parts, 2] (running max in log2 units, sum)
-  float *ws_acc;  // [S, H, max_parts, D] unnormalised weighted V
+  // Partials, partition-major within a sequence: the rows one partition
+  // of a sequence writes are adjacent.
+  float *ws_ml;   // [S, max_parts, H, 2] (running max in log2 units, sum)
+  float *ws_acc;  // [S, max_parts, H, D] unnormalised weighted V
   int num_seqs, num_heads, num_kv_heads, head_dim, block_size;
   int max_blocks, num_blocks, dtype;
   int part_pages;  // pages per partition (<= 64)
   int max_parts;   // ceil(max_blocks / part_pages)
+  // partitions one item covers in the one-wave-per-item grouped-query form
+  // (consecutive partitions of one sequence and kv-head, streamed by one
+  // wave); 1 everywhere else.  The plan lists items of chain * part_pages
+  // pages.
+  int chain = 1;
   float scale;
   void *stream;
   void *ev_begin;
@@ -85,6 +92,8 @@ int launch_decode(const DecodeLaunch &a);
 // The partition pass for bf16 with 2, 4 or 8 query heads per kv-head, on
 // the matrix cores; called by launch_decode.
 int launch_partition_gqa(const DecodeLaunch &a, float scale_log2);
+// Partitions per item of a decode call (DecodeLaunch::chain).
+int decode_chain(const DecodeLaunch &a);
 // Workgroups of `kernel` one compute unit holds at once (at least 1).
 int blocks_per_cu(const void *kernel, int block_threads);
 // Grid of a persistent kernel: what the current device holds at once

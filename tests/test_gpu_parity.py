@@ -309,6 +309,33 @@ def test_hundreds_of_partitions(dt, G):
         assert err <= TOL[dt]
 
 
+@pytest.mark.parametrize("D,bs,G", [(128, 16, 4), (128, 32, 8), (64, 16, 2)])
+def test_partition_runs_end_anywhere(D, bs, G):
+    """Two-page partitions over a 48-page table: the grouped-query kernel's
+    one-wave form streams runs of four partitions and writes their partials
+    when a run ends.  Contexts end in each partition of a run, on and next
+    to page edges, and fill the table; every element within the tolerance
+    and within 1 bf16 ulp plus the fp32 bound of tests/_bounds.py."""
+    run = 8 * bs                      # tokens of a run of four two-page partitions
+    ctx = [1, bs, bs + 1, 2 * bs, 2 * bs + 1, 4 * bs - 1, 5 * bs + 3, run - 1, run, run + 1,
+           run + 3 * bs, 2 * run + 6 * bs + 7, 48 * bs - 1, 48 * bs, 0, 3 * run + 2 * bs]
+    w = build_workload("runs", ctx, 4 * G, 4, D, bs, "bf16", seed=77 + D + bs + G,
+                       max_blocks_per_seq=48)
+    ref, kp, vp = oracle_step(w)
+    dw = upload(w)
+    got = gpu_step(dw, partition_size=2 * bs)
+    err = max_err(got, ref, "bf16")
+    delta = _bounds.fp32_delta(
+        m_v=_bounds.max_abs_live(vp, "bf16"),
+        a_dot=_bounds.max_abs_dot(w.q, kp, w.block_tables, w.context_lens, w.num_kv_heads,
+                                  w.block_size, "bf16"),
+        scale=float(w.scale), head_dim=D, part_tokens=2 * bs, parts=24, matrix_cores=True)
+    ratio, at = _bounds.check_ulp_bound(got, ref, delta)
+    say(f"D{D} bs{bs} G{G}: max abs err {err:.3e}; worst |err| / (ulp + delta) {ratio:.3f} "
+        f"at {tuple(int(x) for x in at)}")
+    assert err <= TOL["bf16"] and ratio <= 1.0
+
+
 def _probe_workload(case):
     if isinstance(case, int):
         return make_config(case)
