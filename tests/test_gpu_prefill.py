@@ -2,9 +2,11 @@
 the C ABI, against the CPU oracle's ``prefill``.
 
 Bar: max-abs-error <= 1e-2 with bf16 KV (fp32 accumulation; the softmax
-weights enter P.V rounded to bf16).  Full-size steps are checked on sampled
-rows the oracle computes one by one; small steps that still span several
-key tiles, work items and ragged tails are checked on every row.
+weights enter P.V rounded to bf16).  Full-size steps are checked on rows
+the oracle computes one by one: both edges of every work item's token
+block, both sides of key-tile edges and random rows; small steps that still
+span several key tiles, work items and ragged tails are checked on every
+row.
 """
 import numpy as np
 import pytest
@@ -52,15 +54,27 @@ def max_err(gpu_bits, ref, rows=None):
     return float(np.max(np.abs(g - ref))) if g.size else 0.0
 
 
-def sample_rows(w, per_seq, rng):
-    """First and last row of every sequence plus random ones."""
-    qs = w.query_start
+def structured_rows(w, rng, per_seq=4, tile_rows=8):
+    """Rows that cover the kernel's structure at full size: the first and
+    last row of every work item's token block (256 query rows per item, so
+    256 / G tokens), rows on both sides of 128-key tile edges (spread over
+    the chunk, at most tile_rows per sequence) and per_seq random rows."""
+    qs, G = w.query_start, w.num_heads // w.num_kv_heads
+    tok = 256 // G
     rows = set()
     for s in range(w.num_seqs):
         a, b = int(qs[s]), int(qs[s + 1])
-        if b > a:
-            rows.update([a, b - 1])
-            rows.update(rng.integers(a, b, size=per_seq).tolist())
+        n = b - a
+        if n <= 0:
+            continue
+        p0 = int(w.context_lens[s]) - n
+        for t0 in range(0, n, tok):
+            rows.update([a + t0, a + min(t0 + tok, n) - 1])
+        edges = [i for i in range(n) if (p0 + i) % 128 in (0, 127)]
+        if edges:
+            pick = np.linspace(0, len(edges) - 1, min(tile_rows, len(edges))).round().astype(int)
+            rows.update(a + edges[k] for k in pick)
+        rows.update(rng.integers(a, b, size=per_seq).tolist())
     return np.array(sorted(rows))
 
 
@@ -76,7 +90,7 @@ def test_prefill_tiny_config():
 @pytest.mark.parametrize("idx", [2, 3])
 def test_prefill_full_size_sampled_rows(idx):
     w = make_prefill_config(idx)
-    rows = sample_rows(w, 6, np.random.default_rng(idx))
+    rows = structured_rows(w, np.random.default_rng(idx))
     say(f"prefill p{idx}: T={w.num_tokens} H={w.num_heads}/{w.num_kv_heads}, "
         f"{len(rows)} sampled rows")
     got = gpu_prefill(upload(w))
@@ -133,7 +147,7 @@ def test_prefill_long_context_default_split_sampled_rows():
     dw = upload(w)
     ps = binding.paged_attention_prefill_partition_tokens(dw.q, dw.k_pool, dw.block_tables,
                                                           dw.query_start)
-    rows = sample_rows(w, 6, np.random.default_rng(4))
+    rows = structured_rows(w, np.random.default_rng(4))
     say(f"prefill p4: T={w.num_tokens}, ctx={w.context_lens.tolist()}, default partition {ps}, "
         f"{len(rows)} sampled rows")
     assert ps > 0
