@@ -53,8 +53,16 @@ constexpr int kTiles = kPrefixRows / 16;
 //   plan[kPlanHeader + 5k .. +4]     unit k: seq0, nmem, pb, pe, slot
 //   nslots[s]                        partial slots sequence s fills
 //   seq_pre[s]                       shared prefix pages of s's group
+//                                    (working array of the plan kernel)
+// kLds: every sequence's context length and prefix pages, and every
+// group's bounds, are kept in LDS (at most kPlanLds of each): the kernel
+// reads its inputs in one round of global loads at its start and writes
+// the plan at its end, with no global round trip between its phases.
+// Otherwise (larger batches) seq_pre is the working array in global memory.
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanLds = 2048;
 
+template <bool kLds>
 __global__ __launch_bounds__(kPlanThreads) void pa_prefix_plan(
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ group_starts,
     const int32_t *__restrict__ prefix_lens, int num_groups, int num_seqs, int group_size,
@@ -63,29 +71,62 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefix_plan(
   // size classes (pages per unit) of prefix units [0] and own units [1]
   __shared__ int s_count[2][kMaxPartitionPages + 1];
   __shared__ int s_next[2][kMaxPartitionPages + 1];
+  constexpr int kL = kLds ? kPlanLds : 1;
+  __shared__ int s_ctx[kL], s_pre[kL], s_gb[kL], s_ge[kL], s_gpre[kL];
   const int members_per_chunk = kPrefixRows / group_size;
   const int max_pages = ctx_cap / block_size;
+  // group gi: its sequences [b, e) and its prefix pages
+  auto load_group = [&](int gi, int &b, int &e, int &pre) {
+    b = min(max(group_starts[gi], 0), num_seqs);
+    e = min(max(group_starts[gi + 1], b), num_seqs);
+    pre = min(max(prefix_lens[gi], 0), ctx_cap) / block_size;
+  };
+  auto group = [&](int gi, int &b, int &e, int &pre) {
+    if constexpr (kLds) {
+      b = s_gb[gi];
+      e = s_ge[gi];
+      pre = s_gpre[gi];
+    } else {
+      load_group(gi, b, e, pre);
+    }
+  };
+  auto ctx_of = [&](int s) {
+    if constexpr (kLds) return s_ctx[s];
+    else return min(max(context_lens[s], 0), ctx_cap);
+  };
+  auto pre_of = [&](int s) {
+    if constexpr (kLds) return s_pre[s];
+    else return (int)seq_pre[s];
+  };
+  auto set_pre = [&](int s, int v) {
+    if constexpr (kLds) s_pre[s] = v;
+    else seq_pre[s] = v;
+  };
   for (int i = threadIdx.x; i <= part_pages; i += kPlanThreads) s_count[0][i] = s_count[1][i] = 0;
-  for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) seq_pre[s] = 0;
+  if constexpr (kLds) {
+    for (int gi = threadIdx.x; gi < num_groups; gi += kPlanThreads)
+      load_group(gi, s_gb[gi], s_ge[gi], s_gpre[gi]);
+    for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads)
+      s_ctx[s] = min(max(context_lens[s], 0), ctx_cap);
+  }
+  for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) set_pre(s, 0);
   __syncthreads();
   for (int gi = threadIdx.x; gi < num_groups; gi += kPlanThreads) {
-    const int b = min(max(group_starts[gi], 0), num_seqs);
-    const int e = min(max(group_starts[gi + 1], b), num_seqs);
-    const int pre = min(max(prefix_lens[gi], 0), ctx_cap) / block_size;
-    for (int s = b; s < e; ++s) seq_pre[s] = pre;
+    int b, e, pre;
+    group(gi, b, e, pre);
+    for (int s = b; s < e; ++s) set_pre(s, pre);
   }
   __syncthreads();
   // pages of sequence s past its prefix
   auto own_pages = [&](int s) {
-    const int ctx = min(max(context_lens[s], 0), ctx_cap);
-    return max(0, min((ctx + block_size - 1) / block_size, max_pages) - seq_pre[s]);
+    return max(0, min((ctx_of(s) + block_size - 1) / block_size, max_pages) - pre_of(s));
   };
   // pass 1: count units per size; slots per sequence
   for (int gi = threadIdx.x; gi < num_groups; gi += kPlanThreads) {
-    const int b = min(max(group_starts[gi], 0), num_seqs);
-    const int e = min(max(group_starts[gi + 1], b), num_seqs);
+    int b, e, pre;
+    group(gi, b, e, pre);
     if (e == b) continue;
-    const int pre = seq_pre[b];
+    pre = pre_of(b);
     const int chunks = (e - b + members_per_chunk - 1) / members_per_chunk;
     for (int p0 = 0; p0 < pre; p0 += part_pages)
       atomicAdd(&s_count[0][min(part_pages, pre - p0)], chunks);
@@ -94,7 +135,7 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefix_plan(
     const int own = own_pages(s);
     for (int p0 = 0; p0 < own; p0 += part_pages)
       atomicAdd(&s_count[1][min(part_pages, own - p0)], 1);
-    nslots[s] = (seq_pre[s] + part_pages - 1) / part_pages + (own + part_pages - 1) / part_pages;
+    nslots[s] = (pre_of(s) + part_pages - 1) / part_pages + (own + part_pages - 1) / part_pages;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -119,16 +160,16 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefix_plan(
     r[4] = slot;
   };
   for (int gi = threadIdx.x; gi < num_groups; gi += kPlanThreads) {
-    const int b = min(max(group_starts[gi], 0), num_seqs);
-    const int e = min(max(group_starts[gi + 1], b), num_seqs);
+    int b, e, pre;
+    group(gi, b, e, pre);
     if (e == b) continue;
-    const int pre = seq_pre[b];
+    pre = pre_of(b);
     for (int s0 = b; s0 < e; s0 += members_per_chunk)
       for (int p0 = 0, k = 0; p0 < pre; p0 += part_pages, ++k)
         put(0, s0, min(members_per_chunk, e - s0), p0, min(pre, p0 + part_pages), k);
   }
   for (int s = threadIdx.x; s < num_seqs; s += kPlanThreads) {
-    const int pre = seq_pre[s];
+    const int pre = pre_of(s);
     const int own = own_pages(s);
     const int slot0 = (pre + part_pages - 1) / part_pages;
     for (int p0 = 0, k = 0; p0 < own; p0 += part_pages, ++k)
@@ -494,7 +535,9 @@ namespace pa_internal {
 int launch_prefix_plan(const PrefixLaunch &p) {
   const DecodeLaunch &a = p.base;
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  hipLaunchKernelGGL(pa_prefix_plan, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens,
+  auto kernel = a.num_seqs <= kPlanLds && p.num_groups <= kPlanLds ? pa_prefix_plan<true>
+                                                                  : pa_prefix_plan<false>;
+  hipLaunchKernelGGL(kernel, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens,
                      p.group_starts, p.prefix_lens, p.num_groups, a.num_seqs,
                      a.num_heads / a.num_kv_heads, a.max_blocks * a.block_size, a.block_size,
                      a.part_pages, a.plan, p.nslots, p.seq_pre);

@@ -696,6 +696,24 @@ def test_shared_prefix_long_own_parts_one_wave_and_four_wave_units():
         assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("groups", [520, 2100])
+def test_shared_prefix_plan_in_lds_and_in_global_memory(groups):
+    """Groups of four sharing a short prefix: with at most 2048 sequences
+    and groups the plan kernel keeps its per-sequence state in LDS, beyond
+    that (2080 and 8400 sequences) in the workspace; both against the
+    oracle."""
+    rng = np.random.default_rng(groups)
+    bs, prefix = 16, 32
+    own = [rng.integers(0, 40, size=4) for _ in range(groups)]
+    w = _shared_workload([4] * groups, prefix, own, 8, 2, 64, bs, seed=groups)
+    starts = list(range(0, 4 * groups + 1, 4))
+    ref, _, _ = oracle_step(w)
+    got = shared_step(upload(w), starts, [prefix] * groups)
+    err = max_err(got, ref, "bf16")
+    say(f"{4 * groups} sequences in {groups} groups: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 def test_shared_prefix_matches_plain_decode_on_unshared_batch():
     """Every sequence its own group with no prefix: the own-page units only."""
     w = make_config(3)
