@@ -518,12 +518,13 @@ size_t pa_hbm_read_probe_sink_bytes(void);
  * dealt to the wavefronts in turn (or one
  * wavefront per item where the grouped-query kernel works that way: bf16
  * with 2-8 query heads per kv-head, partitions of at most 64 pages and a
- * table of at least 16 partitions), each (page, kv-head) run as 16-byte
- * non-temporal loads.  Instead of attention it
+ * table of at least 16 partitions; there an item is a run of up to four
+ * consecutive partitions of at most 64 pages in all), each (page, kv-head)
+ * run as 16-byte non-temporal loads.  Instead of attention it
  * stores, for each item, the XOR of every 16-byte word it loaded in the
  * first 16 bytes of the output row of the item's first query head
  * (h = kv-head * num_heads / num_kv_heads); nothing else in `out` is
- * written, and a sequence's partitions overwrite each other's word.
+ * written, and a sequence's items overwrite each other's word.
  * timing_events bracket the read kernel.  Its rate, the decode call's KV
  * bytes over its duration, is the read bandwidth the decode access pattern
  * reaches on the device: the ceiling for the partition kernels.
