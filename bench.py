@@ -2,9 +2,11 @@
 """Decode-step throughput of libpagedattn on one GPU.
 
 A step is one pass of the whole hot path over one batch: the KV-cache write
-of each sequence's new token (reshape_and_cache), then paged decode
-attention over every sequence's context including that token (partition
-kernel + log-sum-exp merge).  The default workload is the Llama-2-7B-shaped
+of each sequence's new token, then paged decode attention over every
+sequence's context including that token (partition kernel + log-sum-exp
+merge), through paged_attention_decode_step (the cache write and the work
+plan in one launch; --two-calls times reshape_and_cache and
+paged_attention_decode instead, which give the same bits).  The default workload is the Llama-2-7B-shaped
 layer: 64 sequences, 32 query / 32 kv heads, head_dim 128, 16-token pages,
 context lengths uniform in [128, 2048], bf16 K/V/q, fp32 softmax and
 accumulation, pool = 1.25x the pages needed, shuffled.
@@ -67,6 +69,10 @@ def parse():
     ap.add_argument("--shared-prefix", action="store_true",
                     help="decode through paged_attention_decode_shared_prefix, using the "
                          "workload's groups of samples that share prompt pages (config 5)")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="decode-step: time reshape_and_cache and paged_attention_decode as two "
+                         "calls instead of paged_attention_decode_step (bit for bit the same "
+                         "result, one launch more)")
     ap.add_argument("--graph", action="store_true",
                     help="decode-step: also capture one step (cache write + attention) in a HIP "
                          "graph and time --steps replays (graph_ms_per_step; value stays the "
@@ -595,7 +601,15 @@ def main():
             dw.q, dw.k_pool, dw.block_tables, args.partition_size), 16),
             dtype=torch.uint8, device="cuda")
 
+    fused = not (args.shared_prefix or args.alibi or args.two_calls)
+
     def step(events=(None, None)):
+        if fused:
+            binding.paged_attention_decode_step(
+                dw.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_pool, dw.v_pool,
+                dw.block_tables, dw.context_lens, scale=scale, partition_size=args.partition_size,
+                workspace=ws, timing_events=events)
+            return
         binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
         if args.shared_prefix:
             binding.paged_attention_decode_shared_prefix(
@@ -767,8 +781,9 @@ def main():
             "sum_context_tokens": int(w.context_lens.sum()),
             "num_blocks": w.num_blocks,
             "partition_size": args.effective_partition,
-            "decode_entry": "paged_attention_decode_shared_prefix" if args.shared_prefix
-            else ("paged_attention_decode_alibi" if args.alibi else "paged_attention_decode"),
+            "decode_entry": "paged_attention_decode_step" if fused else
+            ("reshape_and_cache + " + ("paged_attention_decode_shared_prefix" if args.shared_prefix
+             else "paged_attention_decode_alibi" if args.alibi else "paged_attention_decode")),
             "parallelism": "single GPU",
         },
         "kv_bytes_per_step": kv_bytes,

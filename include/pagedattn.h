@@ -218,6 +218,38 @@ int paged_attention_decode_alibi(void *out, const void *q, const void *k_pool,
                                  const pa_decode_dims *dims);
 
 /*
+ * One decode step: the step's new tokens into the cache, then attention over
+ * the updated cache.  Each iteration yields the next token together with the
+ * updated KV cache (tutorial page, section 4.3, step 3), and the step's own
+ * token is the last context position its attention reads (section 4.2).
+ *
+ * The result -- out and both pools -- is bit for bit that of
+ *   reshape_and_cache(k, v, k_pool, v_pool, slot_mapping, cache dims), then
+ *   paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
+ *                          num_kv_heads, scale, block_size, dims),
+ * with cache dims = {num_tokens = dims->num_seqs, num_kv_heads,
+ * dims->head_dim, block_size, dims->num_blocks, dims->dtype, dims->stream}.
+ * k, v: device [num_seqs, num_kv_heads, head_dim] of dims->dtype, 16-byte
+ * aligned (row s is sequence s's new token); slot_mapping: device int64
+ * [num_seqs], 8-byte aligned, as for reshape_and_cache (a negative or
+ * out-of-pool slot writes nothing; two equal slots are a precondition
+ * violation).  Everything else, workspace included, is as for
+ * paged_attention_decode; with num_seqs = 0 nothing is read or written.
+ *
+ * Launches, all on dims->stream: one kernel whose first workgroup writes the
+ * work plan while the others write the new tokens (the plan reads only
+ * context_lens, so the two are independent), then the partition kernel
+ * (timing_events bracket this one) and the reduce kernel when some sequence
+ * can span more than one partition: one launch fewer than the two calls.
+ * PA_DEBUG_CHECKS=1 checks both calls' device-side preconditions.
+ */
+int paged_attention_decode_step(void *out, const void *q, const void *k, const void *v,
+                                const int64_t *slot_mapping, void *k_pool, void *v_pool,
+                                const int32_t *block_tables, const int32_t *context_lens,
+                                int32_t num_kv_heads, float scale, int32_t block_size,
+                                const pa_decode_dims *dims);
+
+/*
  * Workspace bytes paged_attention_decode needs for these shapes, with
  * P = ceil(max_blocks_per_seq * block_size / partition_size):
  *   the work plan, 4 * (4 + num_seqs * P) rounded up to 256, plus, when

@@ -111,6 +111,11 @@ SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
         ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(DecodeDims)]),
+    "paged_attention_decode_step": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+        ctypes.POINTER(DecodeDims)]),
     "paged_attention_decode_workspace_bytes": (ctypes.c_size_t, [
         ctypes.c_int32, ctypes.POINTER(DecodeDims)]),
     "paged_attention_decode_partition_tokens": (ctypes.c_int32, [

@@ -94,10 +94,11 @@ def paged_attention_decode_partition_tokens(q: torch.Tensor, k_pool: torch.Tenso
 
 
 def _decode_call(entry: str, out, q, k_pool, v_pool, block_tables, context_lens, scale,
-                 partition_size, workspace, stream, timing_events, alibi_slopes):
+                 partition_size, workspace, stream, timing_events, alibi_slopes, new_kv=None):
     """Marshal one call of the decode family: paged_attention_decode,
-    paged_attention_decode_alibi (with slopes) or
-    paged_attention_decode_read_probe, which share arguments and checks."""
+    paged_attention_decode_alibi (with slopes), paged_attention_decode_step
+    (with new_kv = (k, v, slot_mapping)) or paged_attention_decode_read_probe,
+    which share arguments and checks."""
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     for name, t in (("out", out), ("k_pool", k_pool), ("v_pool", v_pool)):
@@ -113,6 +114,14 @@ def _decode_call(entry: str, out, q, k_pool, v_pool, block_tables, context_lens,
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
     hkv, bs = k_pool.shape[1], k_pool.shape[2]
+    if new_kv is not None:
+        k, v, slot_mapping = new_kv
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise ValueError("k and v must have q's dtype")
+        if k.shape != (S, hkv, D) or v.shape != (S, hkv, D):
+            raise ValueError(f"k and v must be [{S}, {hkv}, {D}] (one new token per sequence)")
+        if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (S,):
+            raise ValueError(f"slot_mapping must be int64 [{S}]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     d = decode_dims(q, k_pool, block_tables, partition_size)
@@ -135,6 +144,9 @@ def _decode_call(entry: str, out, q, k_pool, v_pool, block_tables, context_lens,
     ptrs = (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
             _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
             hkv, ctypes.c_float(scale), bs)
+    if new_kv is not None:
+        ptrs = ptrs[:2] + (_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping")) + \
+            ptrs[2:]
     if alibi_slopes is not None:
         _check_slopes(alibi_slopes, H)
         rc = getattr(lib, entry)(*ptrs, _dev(alibi_slopes, "alibi_slopes"), ctypes.byref(d))
@@ -159,6 +171,23 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     entry = "paged_attention_decode" if alibi_slopes is None else "paged_attention_decode_alibi"
     return _decode_call(entry, out, q, k_pool, v_pool, block_tables, context_lens, scale,
                         partition_size, workspace, stream, timing_events, alibi_slopes)
+
+
+def paged_attention_decode_step(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                                v: torch.Tensor, slot_mapping: torch.Tensor,
+                                k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                scale: Optional[float] = None, partition_size: int = 0,
+                                workspace: Optional[torch.Tensor] = None, stream=None,
+                                timing_events: Sequence = (None, None)) -> torch.Tensor:
+    """One decode step (see paged_attention_decode_step in include/pagedattn.h):
+    k[s], v[s] ([S, num_kv_heads, head_dim]) to pool slot slot_mapping[s],
+    then out[S,H,D] <- paged decode attention over the updated pools; bit for
+    bit reshape_and_cache followed by paged_attention_decode, in one launch
+    fewer."""
+    return _decode_call("paged_attention_decode_step", out, q, k_pool, v_pool, block_tables,
+                        context_lens, scale, partition_size, workspace, stream, timing_events,
+                        None, new_kv=(k, v, slot_mapping))
 
 
 def paged_attention_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,

@@ -11,6 +11,7 @@
 
 #include "pagedattn_internal.h"
 #include "pagedattn_probe_launch.h"
+#include "pagedattn_step_launch.h"
 #include "pagedattn_prefill_launch.h"
 #include "pagedattn_runtime.h"
 
@@ -304,10 +305,13 @@ int check_copy_pairs(const int64_t *mapping, int num_pairs, int src_blocks, int 
 // workspace, or the library's static device scratch.
 enum class Workspace { kCaller, kStatic };
 
+// cache: the decode step's new tokens (paged_attention_decode_step), written
+// to the pools before the attention; its pointers are already checked.
 int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                 const int32_t *block_tables, const int32_t *context_lens, int32_t num_kv_heads,
                 float scale, int32_t block_size, const float *alibi, const pa_decode_dims *dims,
-                bool read_probe = false, Workspace where = Workspace::kCaller);
+                bool read_probe = false, Workspace where = Workspace::kCaller,
+                const pa_internal::CacheLaunch *cache = nullptr);
 int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                  const int32_t *block_tables, const int32_t *context_lens,
                  const int32_t *query_start, int32_t num_kv_heads, float scale,
@@ -441,6 +445,35 @@ int paged_attention_decode_alibi(void *out, const void *q, const void *k_pool,
                      block_size, alibi_slopes, dims);
 }
 
+int paged_attention_decode_step(void *out, const void *q, const void *k, const void *v,
+                                const int64_t *slot_mapping, void *k_pool, void *v_pool,
+                                const int32_t *block_tables, const int32_t *context_lens,
+                                int32_t num_kv_heads, float scale, int32_t block_size,
+                                const pa_decode_dims *dims) {
+  if (!dims) return PA_ERR_NULL;
+  const int rc = check_decode_dims(num_kv_heads, block_size, dims);
+  if (rc != PA_OK) return rc;
+  if (dims->num_seqs > 0) {
+    if (!k || !v || !slot_mapping) return PA_ERR_NULL;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8)) return PA_ERR_ALIGN;
+  }
+  pa_internal::CacheLaunch c{};
+  c.k = k;
+  c.v = v;
+  c.k_pool = k_pool;
+  c.v_pool = v_pool;
+  c.slot_mapping = slot_mapping;
+  c.num_tokens = dims->num_seqs;
+  c.num_kv_heads = num_kv_heads;
+  c.head_dim = dims->head_dim;
+  c.block_size = block_size;
+  c.num_blocks = dims->num_blocks;
+  c.elem_bytes = elem_bytes(dims->dtype);
+  c.stream = dims->stream;
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_kv_heads, scale,
+                     block_size, nullptr, dims, false, Workspace::kCaller, &c);
+}
+
 int paged_attention_decode_read_probe(void *out, const void *q, const void *k_pool,
                                       const void *v_pool, const int32_t *block_tables,
                                       const int32_t *context_lens, int32_t num_kv_heads,
@@ -457,7 +490,7 @@ namespace {
 int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                 const int32_t *block_tables, const int32_t *context_lens, int32_t num_kv_heads,
                 float scale, int32_t block_size, const float *alibi, const pa_decode_dims *dims,
-                bool read_probe, Workspace where) {
+                bool read_probe, Workspace where, const pa_internal::CacheLaunch *cache) {
   if (!dims) return PA_ERR_NULL;
   int rc = check_decode_dims(num_kv_heads, block_size, dims);
   if (rc != PA_OK) return rc;
@@ -481,6 +514,9 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
   if (debug_checks()) {
     rc = check_tables(block_tables, context_lens, dims->num_seqs, dims->max_blocks_per_seq,
                       dims->num_blocks, block_size, dims->stream);
+    if (rc == PA_OK && cache)
+      rc = check_slots(cache->slot_mapping, cache->num_tokens, dims->num_blocks, block_size,
+                       dims->stream);
     if (rc != PA_OK) return rc;
   }
   char *ws = nullptr;
@@ -525,7 +561,8 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
   a.ev_begin = dims->timing_events[0];
   a.ev_end = dims->timing_events[1];
   a.alibi = alibi;
-  return read_probe ? pa_internal::launch_decode_read_probe(a) : pa_internal::launch_decode(a);
+  if (read_probe) return pa_internal::launch_decode_read_probe(a);
+  return cache ? pa_internal::launch_decode_step(a, *cache) : pa_internal::launch_decode(a);
 }
 
 }  // namespace

@@ -7,6 +7,7 @@
 // with others before writing into it (tutorial page, section 4.2, shared
 // pages) and when a preempted sequence's pages go to a CPU-side pool and
 // come back (sections 4.4 and 4.5).
+#include "pagedattn_cache_row.h"
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
 #include "pagedattn_probe_launch.h"
@@ -17,53 +18,14 @@ namespace {
 using namespace pa_dev;
 
 // ------------------------------------------------------------ cache write
-// Grid (num_tokens), kCacheThreads threads.  Copies token t's K and V rows,
-// all kv-heads, 16 bytes per lane, to page slot / bs at offset slot % bs.
-// The first kCacheHeld chunks per thread (8 KiB of K and of V per token:
-// 32 kv-heads of 128 bf16) are loaded before the slot is known, so the
-// source reads and the slot read are in flight together.
-constexpr int kCacheThreads = 256;
-constexpr int kCacheHeld = 2;
-
+// Grid (num_tokens), kCacheThreads threads: block t copies token t's K and V
+// rows, all kv-heads, 16 bytes per lane (cache_write_token).
 __global__ __launch_bounds__(kCacheThreads) void pa_reshape_and_cache(
     const u32x4 *__restrict__ k, const u32x4 *__restrict__ v, u32x4 *__restrict__ k_pool,
     u32x4 *__restrict__ v_pool, const int64_t *__restrict__ slot_mapping, int num_kv_heads,
     int row_chunks, int block_size, int64_t num_slots) {
-  const int t = blockIdx.x;
-  const int total = num_kv_heads * row_chunks;
-  const u32x4 *k_row = k + (size_t)t * total;
-  const u32x4 *v_row = v + (size_t)t * total;
-  u32x4 kh[kCacheHeld], vh[kCacheHeld];
-#pragma unroll
-  for (int i = 0; i < kCacheHeld; ++i) {
-    const int c = threadIdx.x + i * kCacheThreads;
-    if (c < total) {
-      kh[i] = k_row[c];
-      vh[i] = v_row[c];
-    }
-  }
-  const int64_t slot = slot_mapping[t];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t page = slot / block_size;
-  const int64_t off = slot - page * block_size;
-  // chunk c of the token (kv-head c / row_chunks) to its slot row in that head's page
-  auto dst = [&](int c) {
-    const int g = c / row_chunks;
-    const int dc = c - g * row_chunks;
-    return (((size_t)page * num_kv_heads + g) * block_size + off) * row_chunks + dc;
-  };
-#pragma unroll
-  for (int i = 0; i < kCacheHeld; ++i) {
-    const int c = threadIdx.x + i * kCacheThreads;
-    if (c < total) {
-      k_pool[dst(c)] = kh[i];
-      v_pool[dst(c)] = vh[i];
-    }
-  }
-  for (int c = threadIdx.x + kCacheHeld * kCacheThreads; c < total; c += kCacheThreads) {
-    k_pool[dst(c)] = k_row[c];
-    v_pool[dst(c)] = v_row[c];
-  }
+  cache_write_token(blockIdx.x, threadIdx.x, k, v, k_pool, v_pool, slot_mapping, num_kv_heads,
+                    row_chunks, block_size, num_slots);
 }
 
 // ------------------------------------------------ cache write with RoPE

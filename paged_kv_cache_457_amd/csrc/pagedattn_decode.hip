@@ -24,9 +24,11 @@
 // folded into the scale.
 #include <atomic>
 
+#include "pagedattn_cache_row.h"
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
 #include "pagedattn_probe_launch.h"
+#include "pagedattn_step_launch.h"
 #include "pagedattn_timed_launch.h"
 
 namespace {
@@ -331,7 +333,8 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_partition(
 // do not depend on the order units run in.
 constexpr int kPlanThreads = 1024;
 
-__global__ __launch_bounds__(kPlanThreads) void pa_decode_plan(
+// The plan, by one workgroup of kPlanThreads threads.
+__device__ __forceinline__ void decode_plan_body(
     const int32_t *__restrict__ context_lens, int32_t *__restrict__ plan, int num_seqs,
     int ctx_cap, int block_size, int part_pages, int max_parts) {
   __shared__ int s_count[kMaxPartitionPages + 1];  // units per size 0..part_pages
@@ -391,6 +394,34 @@ __global__ __launch_bounds__(kPlanThreads) void pa_decode_plan(
   }
   for (int k = s_total + threadIdx.x; k < candidates; k += kPlanThreads)
     plan[kPlanHeader + k] = -1;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void pa_decode_plan(
+    const int32_t *__restrict__ context_lens, int32_t *__restrict__ plan, int num_seqs,
+    int ctx_cap, int block_size, int part_pages, int max_parts) {
+  decode_plan_body(context_lens, plan, num_seqs, ctx_cap, block_size, part_pages, max_parts);
+}
+
+// A decode step's first launch: workgroup 0 writes the plan while the others
+// write the step's new tokens to the cache, kPlanThreads / kCacheThreads
+// tokens each.  The plan reads only context lengths, so the two are
+// independent; the partition kernel, launched after, sees both.
+constexpr int kPrepTokens = kPlanThreads / kCacheThreads;
+
+__global__ __launch_bounds__(kPlanThreads) void pa_decode_step_prep(
+    const int32_t *__restrict__ context_lens, int32_t *__restrict__ plan, int num_seqs,
+    int ctx_cap, int block_size, int part_pages, int max_parts, const u32x4 *__restrict__ k,
+    const u32x4 *__restrict__ v, u32x4 *__restrict__ k_pool, u32x4 *__restrict__ v_pool,
+    const int64_t *__restrict__ slot_mapping, int num_tokens, int num_kv_heads, int row_chunks,
+    int64_t num_slots) {
+  if (blockIdx.x == 0) {
+    decode_plan_body(context_lens, plan, num_seqs, ctx_cap, block_size, part_pages, max_parts);
+    return;
+  }
+  const int t = (blockIdx.x - 1) * kPrepTokens + threadIdx.x / kCacheThreads;
+  if (t < num_tokens)
+    cache_write_token(t, threadIdx.x % kCacheThreads, k, v, k_pool, v_pool, slot_mapping,
+                      num_kv_heads, row_chunks, block_size, num_slots);
 }
 
 // ------------------------------------------------- decode, log-sum-exp merge
@@ -626,11 +657,27 @@ int partition_pass(const pa_internal::DecodeLaunch &a, float scale_log2) {
   }
 }
 
+// The plan launch of a decode call, or with a cache write (c not null), the
+// step's preparation kernel that does both.
+int launch_plan_or_prep(const pa_internal::DecodeLaunch &a, const pa_internal::CacheLaunch *c) {
+  if (!c) return pa_internal::launch_decode_plan(a);
+  const int row_chunks = a.head_dim * c->elem_bytes / 16;
+  const unsigned grid = 1 + (unsigned)((c->num_tokens + kPrepTokens - 1) / kPrepTokens);
+  hipLaunchKernelGGL(pa_decode_step_prep, dim3(grid), dim3(kPlanThreads), 0,
+                     reinterpret_cast<hipStream_t>(a.stream), a.context_lens, a.plan, a.num_seqs,
+                     a.max_blocks * a.block_size, a.block_size, a.part_pages * a.chain,
+                     (a.max_parts + a.chain - 1) / a.chain,
+                     static_cast<const u32x4 *>(c->k), static_cast<const u32x4 *>(c->v),
+                     static_cast<u32x4 *>(c->k_pool), static_cast<u32x4 *>(c->v_pool),
+                     c->slot_mapping, c->num_tokens, c->num_kv_heads, row_chunks,
+                     (int64_t)c->num_blocks * c->block_size);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
 template <class T, int D>
-int run_decode(const pa_internal::DecodeLaunch &a) {
-  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+int run_decode(const pa_internal::DecodeLaunch &a, const pa_internal::CacheLaunch *c) {
   const float scale_log2 = a.scale * kLog2e;
-  if (pa_internal::launch_decode_plan(a) != 0) return 6;
+  if (launch_plan_or_prep(a, c) != 0) return 6;
   // the partition kernel's launch records the timing events, if any
   const int rc = a.block_size == 16 ? partition_pass<T, D, 16>(a, scale_log2)
                                     : partition_pass<T, D, 32>(a, scale_log2);
@@ -640,8 +687,8 @@ int run_decode(const pa_internal::DecodeLaunch &a) {
 }
 
 template <class T>
-int dispatch_dim(const pa_internal::DecodeLaunch &a) {
-  return a.head_dim == 64 ? run_decode<T, 64>(a) : run_decode<T, 128>(a);
+int dispatch_dim(const pa_internal::DecodeLaunch &a, const pa_internal::CacheLaunch *c) {
+  return a.head_dim == 64 ? run_decode<T, 64>(a, c) : run_decode<T, 128>(a, c);
 }
 
 }  // namespace
@@ -678,7 +725,6 @@ unsigned persistent_grid_items(long long items, int per_cu) {
 
 int launch_decode_shared_prefix(const PrefixLaunch &p) {
   const DecodeLaunch &a = p.base;
-  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   int rc = launch_prefix_plan(p);
   if (rc != 0) return rc;
   // the unit kernel's launch records the timing events, if any
@@ -701,7 +747,13 @@ int launch_decode_plan(const DecodeLaunch &a) {
 int launch_decode(const DecodeLaunch &call) {
   DecodeLaunch a = call;
   a.chain = decode_chain(call);
-  return a.dtype == 0 ? dispatch_dim<F32>(a) : dispatch_dim<BF16>(a);
+  return a.dtype == 0 ? dispatch_dim<F32>(a, nullptr) : dispatch_dim<BF16>(a, nullptr);
+}
+
+int launch_decode_step(const DecodeLaunch &call, const CacheLaunch &cache) {
+  DecodeLaunch a = call;
+  a.chain = decode_chain(call);
+  return a.dtype == 0 ? dispatch_dim<F32>(a, &cache) : dispatch_dim<BF16>(a, &cache);
 }
 
 }  // namespace pa_internal

@@ -1,0 +1,15 @@
+// Internal interface of the fused decode step (cache write, then decode)
+// between the host-side C ABI and its HIP launch code, kept apart from the
+// shared internal header so adding it changes no other kernel's sources.
+#pragma once
+
+#include "pagedattn_internal.h"
+
+namespace pa_internal {
+
+// The step's tokens to the cache and the decode call's plan in one launch,
+// then the decode call's partition (and reduce) kernels.  cache.num_tokens
+// is the call's num_seqs; returns 0 or the PA_ERR_HIP code.
+int launch_decode_step(const DecodeLaunch &a, const CacheLaunch &cache);
+
+}  // namespace pa_internal

@@ -462,6 +462,36 @@ fit = dims(num_seqs=3000, num_heads=4, head_dim=64, max_blocks_per_seq=64, parti
            num_blocks=0)
 expect("noalloc shape errors come before the size limit", noalloc(fit, hkv=4), _lib.PA_ERR_SHAPE)
 
+# ---- decode step (cache write, then decode): pointers out, q, k, v,
+# slot_mapping, k_pool, v_pool, block_tables, context_lens
+def step(d, hkv=32, bs=16, scale=0.088, ptrs=None):
+    p = ptrs or [P] * 9
+    return lib.paged_attention_decode_step(*p, hkv, ctypes.c_float(scale), bs, ctypes.byref(d))
+
+
+expect("step dims NULL",
+       lib.paged_attention_decode_step(*([P] * 9), 32, ctypes.c_float(1), 16, None),
+       _lib.PA_ERR_NULL)
+expect("step empty batch is a no-op", step(dims()), _lib.PA_OK)
+expect("step empty batch accepts NULL pointers", step(dims(), ptrs=[None] * 9), _lib.PA_OK)
+for i in range(9):
+    ptrs = [P] * 9
+    ptrs[i] = None
+    expect(f"step pointer {i} NULL", step(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_NULL)
+for i in (0, 1, 2, 3, 5, 6):
+    ptrs = [P] * 9
+    ptrs[i] = MIS
+    expect(f"step pointer {i} misaligned", step(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_ALIGN)
+ptrs = [P] * 9
+ptrs[4] = P + 4
+expect("step slot_mapping misaligned", step(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_ALIGN)
+expect("step head_dim 96 unsupported", step(dims(**ONE, head_dim=96)), _lib.PA_ERR_UNSUPPORTED)
+expect("step block_size 8 unsupported", step(dims(**ONE), bs=8), _lib.PA_ERR_UNSUPPORTED)
+expect("step group 3 unsupported", step(dims(**ONE, num_heads=24), hkv=8),
+       _lib.PA_ERR_UNSUPPORTED)
+expect("step scale NaN", step(dims(**ONE), scale=float("nan")), _lib.PA_ERR_SHAPE)
+expect("step without workspace", step(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
+
 # ---- probe
 expect("probe NULL buffer", lib.pa_hbm_read_probe(None, 1024, P, None), _lib.PA_ERR_NULL)
 expect("probe size not a multiple of 16", lib.pa_hbm_read_probe(P, 1000, P, None), _lib.PA_ERR_SHAPE)

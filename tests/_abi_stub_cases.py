@@ -158,6 +158,27 @@ def run(lib, expect):
     expect("debug: duplicate slot", cache_with([5, 17, 5]), (_lib.PA_ERR_PRECONDITION, 0))
     expect("debug: slot past the pool", cache_with([5, nb * 16]), (_lib.PA_ERR_PRECONDITION, 0))
 
+    # decode step: the table and slot checks of both calls, before one launch
+    def step_with(tab, lens, slots):
+        bt, bt_p = _arr(ctypes.c_int32, tab)
+        cl, cl_p = _arr(ctypes.c_int32, lens)
+        sl, sl_p = _arr(ctypes.c_int64, slots)
+        d = _dims(num_seqs=2, num_heads=4, max_blocks_per_seq=mb, num_blocks=nb, workspace=P,
+                  workspace_bytes=1 << 20)
+        n0 = launches()
+        rc = lib.paged_attention_decode_step(P, P, P, P, sl_p, P, P, bt_p, cl_p, 4,
+                                             ctypes.c_float(0.1), bs, ctypes.byref(d))
+        return rc, launches() - n0
+
+    expect("debug step: valid tables and slots launch once", step_with(tables, ctx, [3, 40]),
+           (_lib.PA_OK, 1))
+    expect("debug step: duplicate slot", step_with(tables, ctx, [3, 3]),
+           (_lib.PA_ERR_PRECONDITION, 0))
+    bad = list(tables)
+    bad[1] = nb
+    expect("debug step: page id past the pool", step_with(bad, ctx, [3, 40]),
+           (_lib.PA_ERR_PRECONDITION, 0))
+
     # sharing groups
     def shared_with(tab, starts, prefixes, lens):
         bt, bt_p = _arr(ctypes.c_int32, tab)

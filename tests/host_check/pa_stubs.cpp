@@ -13,6 +13,7 @@
 #include "pagedattn_internal.h"
 #include "pagedattn_prefill_launch.h"
 #include "pagedattn_probe_launch.h"
+#include "pagedattn_step_launch.h"
 #include "pagedattn_runtime.h"
 
 namespace {
@@ -43,6 +44,7 @@ int launch_decode(const DecodeLaunch &a) {
   return 0;
 }
 int launch_decode_read_probe(const DecodeLaunch &a) { return launch_decode(a); }
+int launch_decode_step(const DecodeLaunch &a, const CacheLaunch &) { return launch_decode(a); }
 int launch_decode_shared_prefix(const PrefixLaunch &p) {
   ++g_launches;
   decode_span(p.base, 0);

@@ -1,0 +1,113 @@
+"""The fused decode step (paged_attention_decode_step) against the two calls
+it stands for -- reshape_and_cache, then paged_attention_decode -- through
+the C ABI.
+
+Bar: bit for bit, the output and both pools, on every decode kernel form
+(the VALU kernel with and without split-K, the grouped-query kernel in its
+four-wave and one-wave forms, fp32 and bf16), with skipped slots; and the
+step itself against the CPU oracle on the small cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_457_amd import binding
+from paged_kv_cache_457_amd.device_inputs import to_host, upload
+from paged_kv_cache_457_amd.workloads import make_config
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def two_calls(dw, ps):
+    binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
+    binding.paged_attention_decode(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
+                                   dw.context_lens, scale=float(dw.w.scale), partition_size=ps)
+
+
+def one_step(dw, ps):
+    binding.paged_attention_decode_step(dw.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping,
+                                        dw.k_pool, dw.v_pool, dw.block_tables, dw.context_lens,
+                                        scale=float(dw.w.scale), partition_size=ps)
+
+
+def compare(a, b):
+    torch.cuda.synchronize()
+    for name in ("out", "k_pool", "v_pool"):
+        x, y = getattr(a, name), getattr(b, name)
+        assert torch.equal(bits(x), bits(y)), f"{name} differs"
+
+
+# (config, partition tokens): c1 fp32 G1 with split-K at one page; c2 the
+# VALU kernel unsplit and at 256 tokens; c3 the four-wave grouped-query
+# kernel unsplit and split; c4 the one-wave grouped-query form (runs of
+# partitions) at 512 tokens and the default; c5 at 256 and the default
+CASES = [(1, 0), (1, 16), (2, 0), (2, 256), (3, 0), (3, 512), (4, 512), (4, 0), (5, 0),
+         (5, 256)]
+
+
+@pytest.mark.parametrize("idx,ps", CASES)
+def test_step_is_the_two_calls_bit_for_bit(idx, ps):
+    w = make_config(idx)
+    assert w.k_new.shape[0] == w.num_seqs
+    say(f"step c{idx} partition {ps}: S={w.num_seqs} H={w.num_heads}/{w.num_kv_heads} "
+        f"D={w.head_dim} bs={w.block_size} {w.dtype}")
+    a, b = upload(w), upload(w)
+    two_calls(a, ps)
+    one_step(b, ps)
+    compare(a, b)
+    # a second step on the updated pools, with the same new tokens: the
+    # rewrite is idempotent and the attention reads the same cache
+    two_calls(a, ps)
+    one_step(b, ps)
+    compare(a, b)
+
+
+def test_step_skips_negative_and_out_of_pool_slots():
+    w = make_config(3)
+    a, b = upload(w), upload(w)
+    for dw in (a, b):
+        dw.slot_mapping[1] = -1
+        dw.slot_mapping[5] = w.k_pool.shape[0] * w.block_size  # first slot past the pool
+    two_calls(a, 0)
+    one_step(b, 0)
+    compare(a, b)
+
+
+@pytest.mark.parametrize("idx", [1, 3])
+def test_step_against_the_oracle(idx):
+    w = make_config(idx)
+    dw = upload(w)
+    one_step(dw, w.partition_size)
+    torch.cuda.synchronize()
+    kp, vp = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping,
+                                      w.block_size)
+    assert to_host(dw.k_pool, w.dtype).tobytes() == kp.tobytes()
+    assert to_host(dw.v_pool, w.dtype).tobytes() == vp.tobytes()
+    ref = oracle.decode(w.q, kp, vp, w.block_tables, w.context_lens, w.num_kv_heads, w.scale,
+                        w.block_size, w.dtype)
+    err = float(np.max(np.abs(oracle.widen(to_host(dw.out, w.dtype), w.dtype) - ref)))
+    say(f"step c{idx}: max abs err {err:.3e} (tolerance {TOL[w.dtype]})")
+    assert err <= TOL[w.dtype]
+
+
+def test_step_empty_batch_is_a_noop():
+    w = make_config(1)
+    dw = upload(w)
+    before = bits(dw.k_pool).clone()
+    e = dw.q[:0]
+    kv = dw.k_new[:0]
+    binding.paged_attention_decode_step(dw.out[:0], e, kv, kv, dw.slot_mapping[:0], dw.k_pool,
+                                        dw.v_pool, dw.block_tables[:0], dw.context_lens[:0])
+    torch.cuda.synchronize()
+    assert torch.equal(bits(dw.k_pool), before)
