@@ -70,9 +70,9 @@ def parse():
                     help="decode through paged_attention_decode_shared_prefix, using the "
                          "workload's groups of samples that share prompt pages (config 5)")
     ap.add_argument("--two-calls", action="store_true",
-                    help="decode-step: time reshape_and_cache and paged_attention_decode as two "
-                         "calls instead of paged_attention_decode_step (bit for bit the same "
-                         "result, one launch more)")
+                    help="decode-step: time reshape_and_cache and paged_attention_decode (or "
+                         "_shared_prefix) as two calls instead of paged_attention_decode_step "
+                         "(_shared_prefix_step): bit for bit the same result, one launch more")
     ap.add_argument("--graph", action="store_true",
                     help="decode-step: also capture one step (cache write + attention) in a HIP "
                          "graph and time --steps replays (graph_ms_per_step; value stays the "
@@ -601,9 +601,15 @@ def main():
             dw.q, dw.k_pool, dw.block_tables, args.partition_size), 16),
             dtype=torch.uint8, device="cuda")
 
-    fused = not (args.shared_prefix or args.alibi or args.two_calls)
+    fused = not (args.alibi or args.two_calls)
 
     def step(events=(None, None)):
+        if fused and args.shared_prefix:
+            binding.paged_attention_decode_shared_prefix_step(
+                dw.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_pool, dw.v_pool,
+                dw.block_tables, dw.context_lens, gs, pl, scale=scale,
+                partition_size=args.partition_size, workspace=ws, timing_events=events)
+            return
         if fused:
             binding.paged_attention_decode_step(
                 dw.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_pool, dw.v_pool,
@@ -781,7 +787,8 @@ def main():
             "sum_context_tokens": int(w.context_lens.sum()),
             "num_blocks": w.num_blocks,
             "partition_size": args.effective_partition,
-            "decode_entry": "paged_attention_decode_step" if fused else
+            "decode_entry": ("paged_attention_decode_shared_prefix_step" if args.shared_prefix
+                             else "paged_attention_decode_step") if fused else
             ("reshape_and_cache + " + ("paged_attention_decode_shared_prefix" if args.shared_prefix
              else "paged_attention_decode_alibi" if args.alibi else "paged_attention_decode")),
             "parallelism": "single GPU",

@@ -308,6 +308,25 @@ int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k
                                          const pa_decode_dims *dims);
 
 /*
+ * One shared-prefix decode step: the step's new tokens into the cache, then
+ * paged_attention_decode_shared_prefix over the updated cache (tutorial
+ * page, section 4.3, step 3; the samples of a group share their prompt's
+ * pages, section 4.2).  Bit for bit reshape_and_cache(k, v, k_pool, v_pool,
+ * slot_mapping, cache dims) followed by paged_attention_decode_shared_prefix
+ * with the other arguments, with k, v, slot_mapping and the cache dims as
+ * for paged_attention_decode_step.  The first launch writes the shared-prefix
+ * work plan in one workgroup and the new tokens in the others; the unit and
+ * reduce kernels follow.  A group's shared pages are read-only for the step:
+ * a member's new token goes to a page of its own (copy_blocks first when a
+ * prefix ends inside a page).
+ */
+int paged_attention_decode_shared_prefix_step(
+    void *out, const void *q, const void *k, const void *v, const int64_t *slot_mapping,
+    void *k_pool, void *v_pool, const int32_t *block_tables, const int32_t *context_lens,
+    int32_t num_kv_heads, float scale, int32_t block_size, const int32_t *group_starts,
+    const int32_t *prefix_lens, int32_t num_groups, const pa_decode_dims *dims);
+
+/*
  * Workspace bytes of paged_attention_decode_shared_prefix, with
  * P = ceil(max_blocks_per_seq * block_size / partition_size) (partition
  * size as that call resolves it):

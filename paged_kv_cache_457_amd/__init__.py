@@ -7,7 +7,7 @@ NumPy only) can be used without torch or a built library.
 """
 __all__ = [
     "paged_attention_decode", "paged_attention_decode_step", "paged_attention_decode_shared_prefix",
-    "reshape_and_cache",
+    "paged_attention_decode_shared_prefix_step", "reshape_and_cache",
     "copy_blocks", "paged_attention_decode_shared_prefix_workspace_bytes",
     "paged_attention_decode_workspace_bytes", "paged_attention_decode_partition_tokens",
     "hbm_read_probe", "PagedAttnError",

@@ -125,6 +125,11 @@ SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
         ctypes.POINTER(DecodeDims)]),
+    "paged_attention_decode_shared_prefix_step": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(DecodeDims)]),
     "paged_attention_decode_shared_prefix_workspace_bytes": (ctypes.c_size_t, [
         ctypes.c_int32, ctypes.POINTER(DecodeDims)]),
     "paged_attention_prefill": (ctypes.c_int, [

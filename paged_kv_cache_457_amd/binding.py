@@ -216,15 +216,11 @@ def paged_attention_decode_read_probe(out: torch.Tensor, q: torch.Tensor, k_pool
                         timing_events, None)
 
 
-def paged_attention_decode_shared_prefix(
-        out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
-        block_tables: torch.Tensor, context_lens: torch.Tensor, group_starts: torch.Tensor,
-        prefix_lens: torch.Tensor, scale: Optional[float] = None, partition_size: int = 0,
-        workspace: Optional[torch.Tensor] = None, stream=None,
-        timing_events: Sequence = (None, None)) -> torch.Tensor:
-    """paged_attention_decode for batches whose groups of consecutive
-    sequences share prefix pages (see paged_attention_decode_shared_prefix
-    in include/pagedattn.h); group_starts int32 [G+1], prefix_lens int32 [G]."""
+def _shared_prefix_call(entry, out, q, k_pool, v_pool, block_tables, context_lens,
+                        group_starts, prefix_lens, scale, partition_size, workspace, stream,
+                        timing_events, new_kv=None):
+    """Marshal paged_attention_decode_shared_prefix, or with new_kv = (k, v,
+    slot_mapping) paged_attention_decode_shared_prefix_step."""
     if q.dtype != torch.bfloat16:
         raise ValueError("shared-prefix decode is built for bf16")
     for name, t in (("out", out), ("k_pool", k_pool), ("v_pool", v_pool)):
@@ -241,13 +237,21 @@ def paged_attention_decode_shared_prefix(
             or k_pool.shape[3] != D or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("shapes as for paged_attention_decode")
     hkv, bs = k_pool.shape[1], k_pool.shape[2]
+    if new_kv is not None:
+        k, v, slot_mapping = new_kv
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise ValueError("k and v must have q's dtype")
+        if k.shape != (S, hkv, D) or v.shape != (S, hkv, D):
+            raise ValueError(f"k and v must be [{S}, {hkv}, {D}] (one new token per sequence)")
+        if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (S,):
+            raise ValueError(f"slot_mapping must be int64 [{S}]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     d = decode_dims(q, k_pool, block_tables, partition_size)
     lib = _lib.load()
     need = lib.paged_attention_decode_shared_prefix_workspace_bytes(bs, ctypes.byref(d))
     if need == _lib.SIZE_MAX:
-        _check(_lib.PA_ERR_SHAPE, "paged_attention_decode_shared_prefix")
+        _check(_lib.PA_ERR_SHAPE, entry)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
@@ -256,13 +260,49 @@ def paged_attention_decode_shared_prefix(
     d.stream = _stream_ptr(stream)
     d.timing_events[0] = _event_ptr(timing_events[0])
     d.timing_events[1] = _event_ptr(timing_events[1])
-    rc = lib.paged_attention_decode_shared_prefix(
-        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), hkv,
-        ctypes.c_float(scale), bs, _dev(group_starts, "group_starts"),
-        _dev(prefix_lens, "prefix_lens"), prefix_lens.shape[0], ctypes.byref(d))
-    _check(rc, "paged_attention_decode_shared_prefix")
+    ptrs = (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), hkv,
+            ctypes.c_float(scale), bs, _dev(group_starts, "group_starts"),
+            _dev(prefix_lens, "prefix_lens"), prefix_lens.shape[0])
+    if new_kv is not None:
+        ptrs = ptrs[:2] + (_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping")) + \
+            ptrs[2:]
+    rc = getattr(lib, entry)(*ptrs, ctypes.byref(d))
+    _check(rc, entry)
     return out
+
+
+def paged_attention_decode_shared_prefix(
+        out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+        block_tables: torch.Tensor, context_lens: torch.Tensor, group_starts: torch.Tensor,
+        prefix_lens: torch.Tensor, scale: Optional[float] = None, partition_size: int = 0,
+        workspace: Optional[torch.Tensor] = None, stream=None,
+        timing_events: Sequence = (None, None)) -> torch.Tensor:
+    """paged_attention_decode for batches whose groups of consecutive
+    sequences share prefix pages (see paged_attention_decode_shared_prefix
+    in include/pagedattn.h); group_starts int32 [G+1], prefix_lens int32 [G]."""
+    return _shared_prefix_call("paged_attention_decode_shared_prefix", out, q, k_pool, v_pool,
+                               block_tables, context_lens, group_starts, prefix_lens, scale,
+                               partition_size, workspace, stream, timing_events)
+
+
+def paged_attention_decode_shared_prefix_step(
+        out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+        slot_mapping: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+        block_tables: torch.Tensor, context_lens: torch.Tensor, group_starts: torch.Tensor,
+        prefix_lens: torch.Tensor, scale: Optional[float] = None, partition_size: int = 0,
+        workspace: Optional[torch.Tensor] = None, stream=None,
+        timing_events: Sequence = (None, None)) -> torch.Tensor:
+    """One shared-prefix decode step (see
+    paged_attention_decode_shared_prefix_step in include/pagedattn.h): the
+    new tokens k[s], v[s] to slot_mapping[s], then shared-prefix decode over
+    the updated pools; bit for bit reshape_and_cache followed by
+    paged_attention_decode_shared_prefix."""
+    return _shared_prefix_call("paged_attention_decode_shared_prefix_step", out, q, k_pool,
+                               v_pool, block_tables, context_lens, group_starts, prefix_lens,
+                               scale, partition_size, workspace, stream, timing_events,
+                               new_kv=(k, v, slot_mapping))
+
 
 
 def paged_attention_decode_shared_prefix_workspace_bytes(q, k_pool, block_tables,

@@ -317,33 +317,40 @@ int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_poo
                  const int32_t *query_start, int32_t num_kv_heads, float scale,
                  int32_t block_size, const float *alibi, const pa_prefill_dims *dims);
 
-}  // namespace
-
-extern "C" {
-
-size_t paged_attention_decode_workspace_bytes(int32_t block_size, const pa_decode_dims *dims) {
-  // The size does not depend on the kv-head count, which the query does
-  // not take; the call itself checks the head group and the item count.
-  if (check_decode_shape(block_size, dims) != PA_OK) return SIZE_MAX;
-  if (dims->num_seqs == 0) return 0;
-  const int mp = max_partitions(block_size, dims);
-  return plan_bytes(dims->num_seqs, mp) + partial_bytes(dims, mp);
+// The cache write of a decode step's entry (one new token per sequence):
+// checks its pointers and fills c; shape checks are the decode call's.
+int step_cache(pa_internal::CacheLaunch *c, const void *k, const void *v,
+               const int64_t *slot_mapping, void *k_pool, void *v_pool, int32_t num_kv_heads,
+               int32_t block_size, const pa_decode_dims *dims) {
+  const int rc = check_decode_dims(num_kv_heads, block_size, dims);
+  if (rc != PA_OK) return rc;
+  if (dims->num_seqs > 0) {
+    if (!k || !v || !slot_mapping) return PA_ERR_NULL;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8)) return PA_ERR_ALIGN;
+  }
+  c->k = k;
+  c->v = v;
+  c->k_pool = k_pool;
+  c->v_pool = v_pool;
+  c->slot_mapping = slot_mapping;
+  c->num_tokens = dims->num_seqs;
+  c->num_kv_heads = num_kv_heads;
+  c->head_dim = dims->head_dim;
+  c->block_size = block_size;
+  c->num_blocks = dims->num_blocks;
+  c->elem_bytes = elem_bytes(dims->dtype);
+  c->stream = dims->stream;
+  return PA_OK;
 }
 
-size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t block_size,
-                                                            const pa_decode_dims *dims) {
-  if (check_decode_shape(block_size, dims) != PA_OK) return SIZE_MAX;
-  if (dims->num_seqs == 0) return 0;
-  return prefix_workspace_bytes(block_size, dims);
-}
-
-int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k_pool,
-                                         const void *v_pool, const int32_t *block_tables,
-                                         const int32_t *context_lens, int32_t num_kv_heads,
-                                         float scale, int32_t block_size,
-                                         const int32_t *group_starts,
-                                         const int32_t *prefix_lens, int32_t num_groups,
-                                         const pa_decode_dims *dims) {
+// cache: the step's new tokens (paged_attention_decode_shared_prefix_step),
+// written to the pools before the attention; its pointers are already checked.
+int shared_prefix_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       int32_t num_kv_heads, float scale, int32_t block_size,
+                       const int32_t *group_starts, const int32_t *prefix_lens,
+                       int32_t num_groups, const pa_decode_dims *dims,
+                       const pa_internal::CacheLaunch *cache) {
   if (!dims) return PA_ERR_NULL;
   int rc = check_decode_dims(num_kv_heads, block_size, dims);
   if (rc != PA_OK) return rc;
@@ -369,6 +376,9 @@ int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k
     if (rc == PA_OK)
       rc = check_groups(group_starts, prefix_lens, num_groups, block_tables, dims->num_seqs,
                         dims->max_blocks_per_seq, dims->num_blocks, block_size, dims->stream);
+    if (rc == PA_OK && cache)
+      rc = check_slots(cache->slot_mapping, cache->num_tokens, dims->num_blocks, block_size,
+                       dims->stream);
     if (rc != PA_OK) return rc;
   }
   int32_t *plan = static_cast<int32_t *>(dims->workspace);
@@ -407,7 +417,54 @@ int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k
   p.nslots = plan + kPlanHeader + (size_t)pa_internal::kPrefixUnitInts * dims->num_seqs * ms;
   p.seq_pre = p.nslots + dims->num_seqs;
   p.max_units = (long long)dims->num_seqs * ms;
-  return pa_internal::launch_decode_shared_prefix(p);
+  return cache ? pa_internal::launch_shared_prefix_step(p, *cache)
+               : pa_internal::launch_decode_shared_prefix(p);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attention_decode_workspace_bytes(int32_t block_size, const pa_decode_dims *dims) {
+  // The size does not depend on the kv-head count, which the query does
+  // not take; the call itself checks the head group and the item count.
+  if (check_decode_shape(block_size, dims) != PA_OK) return SIZE_MAX;
+  if (dims->num_seqs == 0) return 0;
+  const int mp = max_partitions(block_size, dims);
+  return plan_bytes(dims->num_seqs, mp) + partial_bytes(dims, mp);
+}
+
+size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t block_size,
+                                                            const pa_decode_dims *dims) {
+  if (check_decode_shape(block_size, dims) != PA_OK) return SIZE_MAX;
+  if (dims->num_seqs == 0) return 0;
+  return prefix_workspace_bytes(block_size, dims);
+}
+
+int paged_attention_decode_shared_prefix(void *out, const void *q, const void *k_pool,
+                                         const void *v_pool, const int32_t *block_tables,
+                                         const int32_t *context_lens, int32_t num_kv_heads,
+                                         float scale, int32_t block_size,
+                                         const int32_t *group_starts,
+                                         const int32_t *prefix_lens, int32_t num_groups,
+                                         const pa_decode_dims *dims) {
+  return shared_prefix_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_kv_heads,
+                            scale, block_size, group_starts, prefix_lens, num_groups, dims,
+                            nullptr);
+}
+
+int paged_attention_decode_shared_prefix_step(
+    void *out, const void *q, const void *k, const void *v, const int64_t *slot_mapping,
+    void *k_pool, void *v_pool, const int32_t *block_tables, const int32_t *context_lens,
+    int32_t num_kv_heads, float scale, int32_t block_size, const int32_t *group_starts,
+    const int32_t *prefix_lens, int32_t num_groups, const pa_decode_dims *dims) {
+  if (!dims) return PA_ERR_NULL;
+  pa_internal::CacheLaunch c{};
+  const int rc = step_cache(&c, k, v, slot_mapping, k_pool, v_pool, num_kv_heads, block_size,
+                            dims);
+  if (rc != PA_OK) return rc;
+  return shared_prefix_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_kv_heads,
+                            scale, block_size, group_starts, prefix_lens, num_groups, dims, &c);
 }
 
 int32_t paged_attention_decode_partition_tokens(int32_t block_size, const pa_decode_dims *dims) {
@@ -451,25 +508,10 @@ int paged_attention_decode_step(void *out, const void *q, const void *k, const v
                                 int32_t num_kv_heads, float scale, int32_t block_size,
                                 const pa_decode_dims *dims) {
   if (!dims) return PA_ERR_NULL;
-  const int rc = check_decode_dims(num_kv_heads, block_size, dims);
-  if (rc != PA_OK) return rc;
-  if (dims->num_seqs > 0) {
-    if (!k || !v || !slot_mapping) return PA_ERR_NULL;
-    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8)) return PA_ERR_ALIGN;
-  }
   pa_internal::CacheLaunch c{};
-  c.k = k;
-  c.v = v;
-  c.k_pool = k_pool;
-  c.v_pool = v_pool;
-  c.slot_mapping = slot_mapping;
-  c.num_tokens = dims->num_seqs;
-  c.num_kv_heads = num_kv_heads;
-  c.head_dim = dims->head_dim;
-  c.block_size = block_size;
-  c.num_blocks = dims->num_blocks;
-  c.elem_bytes = elem_bytes(dims->dtype);
-  c.stream = dims->stream;
+  const int rc = step_cache(&c, k, v, slot_mapping, k_pool, v_pool, num_kv_heads, block_size,
+                            dims);
+  if (rc != PA_OK) return rc;
   return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_kv_heads, scale,
                      block_size, nullptr, dims, false, Workspace::kCaller, &c);
 }

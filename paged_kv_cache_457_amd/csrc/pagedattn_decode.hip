@@ -723,15 +723,25 @@ unsigned persistent_grid_items(long long items, int per_cu) {
   return (unsigned)(resident < items ? resident : items);
 }
 
-int launch_decode_shared_prefix(const PrefixLaunch &p) {
+namespace {
+
+int shared_prefix(const PrefixLaunch &p, const CacheLaunch *cache) {
   const DecodeLaunch &a = p.base;
-  int rc = launch_prefix_plan(p);
+  int rc = launch_prefix_prep(p, cache);
   if (rc != 0) return rc;
   // the unit kernel's launch records the timing events, if any
   rc = launch_prefix_units(p, a.scale * kLog2e);
   if (rc != 0) return rc;
   return a.head_dim == 64 ? launch_reduce<BF16, 64>(a, p.nslots)
                           : launch_reduce<BF16, 128>(a, p.nslots);
+}
+
+}  // namespace
+
+int launch_decode_shared_prefix(const PrefixLaunch &p) { return shared_prefix(p, nullptr); }
+
+int launch_shared_prefix_step(const PrefixLaunch &p, const CacheLaunch &cache) {
+  return shared_prefix(p, &cache);
 }
 
 int launch_decode_plan(const DecodeLaunch &a) {

@@ -26,8 +26,10 @@
 // sequence's context.  V rows at or past the longest member's context are
 // staged as zeros, so a poisoned slot (NaN) never reaches a multiply; a
 // row's other masked tokens only multiply finite, live values by 0.
+#include "pagedattn_cache_row.h"
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
+#include "pagedattn_step_launch.h"
 #include "pagedattn_timed_launch.h"
 
 namespace {
@@ -63,7 +65,7 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanLds = 2048;
 
 template <bool kLds>
-__global__ __launch_bounds__(kPlanThreads) void pa_prefix_plan(
+__device__ __forceinline__ void prefix_plan_body(
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ group_starts,
     const int32_t *__restrict__ prefix_lens, int num_groups, int num_seqs, int group_size,
     int ctx_cap, int block_size, int part_pages, int32_t *__restrict__ plan,
@@ -175,6 +177,43 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefix_plan(
     for (int p0 = 0, k = 0; p0 < own; p0 += part_pages, ++k)
       put(1, s, 1, pre + p0, pre + min(own, p0 + part_pages), slot0 + k);
   }
+}
+
+template <bool kLds>
+__global__ __launch_bounds__(kPlanThreads) void pa_prefix_plan(
+    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ group_starts,
+    const int32_t *__restrict__ prefix_lens, int num_groups, int num_seqs, int group_size,
+    int ctx_cap, int block_size, int part_pages, int32_t *__restrict__ plan,
+    int32_t *__restrict__ nslots, int32_t *__restrict__ seq_pre) {
+  prefix_plan_body<kLds>(context_lens, group_starts, prefix_lens, num_groups, num_seqs,
+                         group_size, ctx_cap, block_size, part_pages, plan, nslots, seq_pre);
+}
+
+// A shared-prefix decode step's first launch: workgroup 0 writes the plan
+// while the others write the step's new tokens to the cache,
+// kPlanThreads / kCacheThreads tokens each.  The plan reads only context
+// lengths and the groups, so the two are independent; the unit kernel,
+// launched after, sees both.
+constexpr int kPrepTokens = kPlanThreads / kCacheThreads;
+
+template <bool kLds>
+__global__ __launch_bounds__(kPlanThreads) void pa_prefix_step_prep(
+    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ group_starts,
+    const int32_t *__restrict__ prefix_lens, int num_groups, int num_seqs, int group_size,
+    int ctx_cap, int block_size, int part_pages, int32_t *__restrict__ plan,
+    int32_t *__restrict__ nslots, int32_t *__restrict__ seq_pre, const u32x4 *__restrict__ k,
+    const u32x4 *__restrict__ v, u32x4 *__restrict__ k_pool, u32x4 *__restrict__ v_pool,
+    const int64_t *__restrict__ slot_mapping, int num_kv_heads, int row_chunks,
+    int64_t num_slots) {
+  if (blockIdx.x == 0) {
+    prefix_plan_body<kLds>(context_lens, group_starts, prefix_lens, num_groups, num_seqs,
+                           group_size, ctx_cap, block_size, part_pages, plan, nslots, seq_pre);
+    return;
+  }
+  const int t = (blockIdx.x - 1) * kPrepTokens + threadIdx.x / kCacheThreads;
+  if (t < num_seqs)
+    cache_write_token(t, threadIdx.x % kCacheThreads, k, v, k_pool, v_pool, slot_mapping,
+                      num_kv_heads, row_chunks, block_size, num_slots);
 }
 
 // ------------------------------------------------------------ unit kernel
@@ -532,17 +571,33 @@ int by_group(const pa_internal::PrefixLaunch &p, float scale_log2) {
 
 namespace pa_internal {
 
-int launch_prefix_plan(const PrefixLaunch &p) {
+int launch_prefix_prep(const PrefixLaunch &p, const CacheLaunch *cache) {
   const DecodeLaunch &a = p.base;
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  auto kernel = a.num_seqs <= kPlanLds && p.num_groups <= kPlanLds ? pa_prefix_plan<true>
-                                                                  : pa_prefix_plan<false>;
-  hipLaunchKernelGGL(kernel, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens,
-                     p.group_starts, p.prefix_lens, p.num_groups, a.num_seqs,
-                     a.num_heads / a.num_kv_heads, a.max_blocks * a.block_size, a.block_size,
-                     a.part_pages, a.plan, p.nslots, p.seq_pre);
+  const bool lds = a.num_seqs <= kPlanLds && p.num_groups <= kPlanLds;
+  if (cache) {
+    auto kernel = lds ? pa_prefix_step_prep<true> : pa_prefix_step_prep<false>;
+    const unsigned grid = 1 + (unsigned)((a.num_seqs + kPrepTokens - 1) / kPrepTokens);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kPlanThreads), 0, st, a.context_lens,
+                       p.group_starts, p.prefix_lens, p.num_groups, a.num_seqs,
+                       a.num_heads / a.num_kv_heads, a.max_blocks * a.block_size, a.block_size,
+                       a.part_pages, a.plan, p.nslots, p.seq_pre,
+                       static_cast<const u32x4 *>(cache->k), static_cast<const u32x4 *>(cache->v),
+                       static_cast<u32x4 *>(cache->k_pool), static_cast<u32x4 *>(cache->v_pool),
+                       cache->slot_mapping, cache->num_kv_heads,
+                       a.head_dim * cache->elem_bytes / 16,
+                       (int64_t)cache->num_blocks * cache->block_size);
+  } else {
+    auto kernel = lds ? pa_prefix_plan<true> : pa_prefix_plan<false>;
+    hipLaunchKernelGGL(kernel, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens,
+                       p.group_starts, p.prefix_lens, p.num_groups, a.num_seqs,
+                       a.num_heads / a.num_kv_heads, a.max_blocks * a.block_size, a.block_size,
+                       a.part_pages, a.plan, p.nslots, p.seq_pre);
+  }
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
+
+int launch_prefix_plan(const PrefixLaunch &p) { return launch_prefix_prep(p, nullptr); }
 
 int launch_prefix_units(const PrefixLaunch &p, float scale_log2) {
   const DecodeLaunch &a = p.base;

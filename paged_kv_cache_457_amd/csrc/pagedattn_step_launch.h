@@ -11,5 +11,10 @@ namespace pa_internal {
 // then the decode call's partition (and reduce) kernels.  cache.num_tokens
 // is the call's num_seqs; returns 0 or the PA_ERR_HIP code.
 int launch_decode_step(const DecodeLaunch &a, const CacheLaunch &cache);
+// The same for shared-prefix decode: the step's tokens and the shared-prefix
+// plan in one launch, then the unit kernel and the reduce.
+int launch_shared_prefix_step(const PrefixLaunch &p, const CacheLaunch &cache);
+// The shared-prefix plan alone (cache null) or with the step's cache write.
+int launch_prefix_prep(const PrefixLaunch &p, const CacheLaunch *cache);
 
 }  // namespace pa_internal

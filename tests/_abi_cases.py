@@ -492,6 +492,29 @@ expect("step group 3 unsupported", step(dims(**ONE, num_heads=24), hkv=8),
 expect("step scale NaN", step(dims(**ONE), scale=float("nan")), _lib.PA_ERR_SHAPE)
 expect("step without workspace", step(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
 
+# ---- shared-prefix step: pointers out, q, k, v, slot_mapping, k_pool,
+# v_pool, block_tables, context_lens, then group_starts, prefix_lens
+def shared_step(d, ptrs=None, groups=1):
+    p = ptrs or [P] * 11
+    return lib.paged_attention_decode_shared_prefix_step(
+        *p[:9], 32, ctypes.c_float(0.088), 16, p[9], p[10], groups, ctypes.byref(d))
+
+
+expect("shared step dims NULL", lib.paged_attention_decode_shared_prefix_step(
+    *([P] * 9), 32, ctypes.c_float(1), 16, P, P, 1, None), _lib.PA_ERR_NULL)
+expect("shared step empty batch accepts NULL pointers", shared_step(dims(), ptrs=[None] * 11),
+       _lib.PA_OK)
+for i in range(11):
+    ptrs = [P] * 11
+    ptrs[i] = None
+    expect(f"shared step pointer {i} NULL", shared_step(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_NULL)
+ptrs = [P] * 11
+ptrs[4] = P + 4
+expect("shared step slot_mapping misaligned", shared_step(dims(**ONE), ptrs=ptrs), _lib.PA_ERR_ALIGN)
+expect("shared step fp32 unsupported", shared_step(dims(**ONE, dtype=_lib.PA_DTYPE_F32)),
+       _lib.PA_ERR_UNSUPPORTED)
+expect("shared step without workspace", shared_step(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
+
 # ---- probe
 expect("probe NULL buffer", lib.pa_hbm_read_probe(None, 1024, P, None), _lib.PA_ERR_NULL)
 expect("probe size not a multiple of 16", lib.pa_hbm_read_probe(P, 1000, P, None), _lib.PA_ERR_SHAPE)

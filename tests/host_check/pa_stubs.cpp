@@ -45,6 +45,10 @@ int launch_decode(const DecodeLaunch &a) {
 }
 int launch_decode_read_probe(const DecodeLaunch &a) { return launch_decode(a); }
 int launch_decode_step(const DecodeLaunch &a, const CacheLaunch &) { return launch_decode(a); }
+int launch_decode_shared_prefix(const PrefixLaunch &p);
+int launch_shared_prefix_step(const PrefixLaunch &p, const CacheLaunch &) {
+  return launch_decode_shared_prefix(p);
+}
 int launch_decode_shared_prefix(const PrefixLaunch &p) {
   ++g_launches;
   decode_span(p.base, 0);

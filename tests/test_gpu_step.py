@@ -111,3 +111,22 @@ def test_step_empty_batch_is_a_noop():
                                         dw.v_pool, dw.block_tables[:0], dw.context_lens[:0])
     torch.cuda.synchronize()
     assert torch.equal(bits(dw.k_pool), before)
+
+
+# ------------------------------------------------------- shared prefix
+@pytest.mark.parametrize("ps", [0, 256, 1024])
+def test_shared_prefix_step_is_the_two_calls_bit_for_bit(ps):
+    w = make_config(5)
+    gs = torch.from_numpy(w.extra["group_starts"]).cuda()
+    pl = torch.from_numpy(w.extra["prefix_lens"]).cuda()
+    say(f"shared-prefix step c5 partition {ps}: S={w.num_seqs} groups {pl.numel()}")
+    a, b = upload(w), upload(w)
+    for _ in range(2):
+        binding.reshape_and_cache(a.k_new, a.v_new, a.k_pool, a.v_pool, a.slot_mapping)
+        binding.paged_attention_decode_shared_prefix(
+            a.out, a.q, a.k_pool, a.v_pool, a.block_tables, a.context_lens, gs, pl,
+            scale=float(w.scale), partition_size=ps)
+        binding.paged_attention_decode_shared_prefix_step(
+            b.out, b.q, b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool, b.block_tables,
+            b.context_lens, gs, pl, scale=float(w.scale), partition_size=ps)
+        compare(a, b)
