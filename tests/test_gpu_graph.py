@@ -4,7 +4,8 @@ and records no memset, so a captured step must give the eager result bit
 for bit on every replay.  Between replays the test does its own eager work
 (poisoning the output, a cache write, a synchronization), and checks each
 replay.  Covers plain decode with a split-K reduce, the shared-prefix entry,
-prefill with a split-K reduce, and the fused RoPE cache write.
+both step entries (cache write and plan in one launch), prefill with a
+split-K reduce, and the fused RoPE cache write.
 """
 import numpy as np
 import pytest
@@ -90,6 +91,50 @@ def test_shared_prefix_step_replays_bitwise():
     torch.cuda.synchronize()
     ref = dw.out.clone()
     say("c5 shared-prefix decode: eager reference taken; capturing")
+    check_replays(capture(step), dw.out, ref)
+
+
+def test_fused_decode_step_replays_bitwise():
+    """paged_attention_decode_step (cache write and plan in one launch) with a
+    split-K reduce, captured and replayed."""
+    w = make_config(3)
+    dw = upload(w)
+    ps = 512
+    ws = torch.empty(binding.paged_attention_decode_workspace_bytes(
+        dw.q, dw.k_pool, dw.block_tables, ps), dtype=torch.uint8, device="cuda")
+
+    def step():
+        binding.paged_attention_decode_step(dw.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping,
+                                            dw.k_pool, dw.v_pool, dw.block_tables,
+                                            dw.context_lens, scale=float(w.scale),
+                                            partition_size=ps, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = dw.out.clone()
+    say(f"c3 fused decode step, partition {ps}: eager reference taken; capturing")
+    check_replays(capture(step), dw.out, ref, between=lambda: binding.reshape_and_cache(
+        dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping))
+
+
+def test_fused_shared_prefix_step_replays_bitwise():
+    w = make_config(5)
+    dw = upload(w)
+    starts = torch.from_numpy(w.extra["group_starts"]).cuda()
+    prefix = torch.from_numpy(w.extra["prefix_lens"]).cuda()
+    ws = torch.empty(binding.paged_attention_decode_shared_prefix_workspace_bytes(
+        dw.q, dw.k_pool, dw.block_tables), dtype=torch.uint8, device="cuda")
+
+    def step():
+        binding.paged_attention_decode_shared_prefix_step(
+            dw.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_pool, dw.v_pool,
+            dw.block_tables, dw.context_lens, starts, prefix, scale=float(w.scale),
+            workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = dw.out.clone()
+    say("c5 fused shared-prefix step: eager reference taken; capturing")
     check_replays(capture(step), dw.out, ref)
 
 
