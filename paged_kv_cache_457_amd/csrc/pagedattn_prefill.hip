@@ -102,7 +102,8 @@ __device__ __forceinline__ int swz(int r, int c) {
 // that holds keys the block sees.  plan[0] = item count; item k is the
 // kPlanRecord ints at plan[kPlanHeader + kPlanRecord * k] (their order is
 // given beside kPrefillPlanRecord), items ordered by the key tiles they
-// read, most first.  An item's page flag is set when no page it reads lies
+// read, most first (a sequence's blocks by its largest when they are close
+// in size: sort_keys).  An item's page flag is set when no page it reads lies
 // outside the pool: the wave that writes a sequence's items first finds
 // the sequence's first such page (a flag left clear only sends the item
 // down the per-key mask path).  With a split,
@@ -137,6 +138,18 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
   };
   // keys the block starting at t0 sees, and its partitions
   auto keys = [&](int n, int p0, int t0) { return max(0, p0 + min(n, t0 + tok)); };
+  // The keys an item of sequence (n, p0) is sorted by, given its own: the
+  // sequence's total when its first block already sees half of them (a long
+  // cached context under a short chunk), so that the sequence's blocks are
+  // adjacent in the list.  With kv-head fastest, blocks of one (sequence,
+  // kv-head) then run in the same round on the same XCD and read their
+  // common keys through its L2 (Llama-2-7B chunked prefill, 8 x 1024 new
+  // tokens after U[0, 3072] cached: 6-10% faster).  Where a sequence's blocks
+  // differ more (a prompt with nothing cached), each item keeps its own size:
+  // grouping them there cost 3-4% in balance.  Split items keep their own.
+  auto sort_keys = [&](int n, int p0, int ke) {
+    return !kpart && 2 * keys(n, p0, 0) >= max(0, p0 + n) ? max(0, p0 + n) : ke;
+  };
   auto parts = [&](int kv_end) { return kpart && kv_end > 0 ? (kv_end + kpart - 1) / kpart : 1; };
   auto bucket = [&](int kv_end, int kp) {
     const int lo = kpart ? kp * kpart : 0;
@@ -156,7 +169,11 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
     return a;
   };
   for (int s = wave; s < num_seqs; s += kPlanWaves) {
-    const int a = items_of(s, [&](int, int kp, int ke) { atomicAdd(&s_count[bucket(ke, kp)], 1); });
+    int a0, n0, p00;
+    chunk(s, a0, n0, p00);
+    const int a = items_of(s, [&](int, int kp, int ke) {
+      atomicAdd(&s_count[bucket(sort_keys(n0, p00, ke), kp)], 1);
+    });
     if (kpart) {
       int a2, n, p0;
       chunk(s, a2, n, p0);
@@ -196,7 +213,7 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) first_bad = min(first_bad, __shfl_xor(first_bad, o));
     items_of(s, [&](int t0, int kp, int ke) {
-      const int k = atomicAdd(&s_next[bucket(ke, kp)], 1);
+      const int k = atomicAdd(&s_next[bucket(sort_keys(n, p0, ke), kp)], 1);
       if (k >= max_items) return;
       // pages the item's key tiles span
       const int kt_hi = kpart ? min((ke + kKeys - 1) / kKeys, (kp + 1) * (kpart / kKeys))
