@@ -105,3 +105,40 @@ def test_debug_checks_reject_bad_sharing_groups(debug_checks):
     assert _rejected(lambda: shared([0, 2], [prefix]))          # does not end at num_seqs
     dw.block_tables[2, 1] = int(w.block_tables[2, 0])           # member 2 leaves the prefix
     assert _rejected(lambda: shared([0, 3], [prefix]))
+
+
+def test_debug_checks_on_the_step_entry(debug_checks):
+    """paged_attention_decode_step checks both calls' preconditions: a valid
+    step gives the bits of the unchecked step; a duplicate slot or a page id
+    out of the pool is refused with nothing written (pools and out keep
+    their contents)."""
+    w = build_workload("dbg", [40, 300, 17, 1], 16, 4, 128, 16, "bf16", seed=8)
+
+    def step(dw):
+        binding.paged_attention_decode_step(dw.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping,
+                                            dw.k_pool, dw.v_pool, dw.block_tables,
+                                            dw.context_lens, scale=float(w.scale))
+        torch.cuda.synchronize()
+
+    a = upload(w)
+    step(a)
+    os.environ.pop("PA_DEBUG_CHECKS")
+    b = upload(w)
+    step(b)
+    os.environ["PA_DEBUG_CHECKS"] = "1"
+    assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+    assert torch.equal(a.k_pool.view(torch.int16), b.k_pool.view(torch.int16))
+
+    c = upload(w)
+    c.out.fill_(3.0)
+    pool_before = c.k_pool.clone()
+    c.slot_mapping[1] = c.slot_mapping[0]
+    assert _rejected(lambda: step(c))
+    assert torch.equal(c.k_pool.view(torch.int16), pool_before.view(torch.int16))
+    assert bool((c.out == 3.0).all())
+
+    d = upload(w)
+    d.out.fill_(3.0)
+    d.block_tables[1, 4] = w.num_blocks
+    assert _rejected(lambda: step(d))
+    assert bool((d.out == 3.0).all())
