@@ -70,9 +70,11 @@ def parse():
                     help="decode through paged_attention_decode_shared_prefix, using the "
                          "workload's groups of samples that share prompt pages (config 5)")
     ap.add_argument("--two-calls", action="store_true",
-                    help="decode-step: time reshape_and_cache and paged_attention_decode (or "
-                         "_shared_prefix) as two calls instead of paged_attention_decode_step "
-                         "(_shared_prefix_step): bit for bit the same result, one launch more")
+                    help="time reshape_and_cache and paged_attention_decode (or "
+                         "_shared_prefix, or paged_attention_prefill with --op prefill) as two "
+                         "calls instead of the step entry paged_attention_decode_step "
+                         "(_shared_prefix_step, paged_attention_prefill_step): bit for bit the "
+                         "same result, one launch more")
     ap.add_argument("--graph", action="store_true",
                     help="decode-step: also capture one step (cache write + attention) in a HIP "
                          "graph and time --steps replays (graph_ms_per_step; value stays the "
@@ -422,7 +424,8 @@ def bench_cache_rope(args):
 
 def bench_prefill(args):
     """Multi-token step: cache write of every chunk row, then prefill
-    attention.  value = chunk tokens / step time; the roofline prices the
+    attention, through paged_attention_prefill_step (chunk rows and plan in
+    one launch; --two-calls or --alibi: the two calls).  value = chunk tokens / step time; the roofline prices the
     attention pass against the dense bf16 matrix-core peak with its
     algorithmic flops (4 * head_dim per visible (row, key) pair and head)."""
     import numpy as np
@@ -443,7 +446,15 @@ def bench_prefill(args):
     scale = float(w.scale)
     slopes = torch.from_numpy(alibi_slopes(w.num_heads)).cuda() if args.alibi else None
 
+    fused = not (args.alibi or args.two_calls)
+
     def step(events=(None, None)):
+        if fused:
+            binding.paged_attention_prefill_step(
+                dw.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_pool, dw.v_pool,
+                dw.block_tables, dw.context_lens, dw.query_start, scale=scale, workspace=ws,
+                timing_events=events, partition_size=ps)
+            return
         binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
         binding.paged_attention_prefill(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
                                         dw.context_lens, dw.query_start, scale=scale,
@@ -512,7 +523,9 @@ def bench_prefill(args):
             "head_dim": w.head_dim,
             "block_size": w.block_size,
             "sum_context_tokens": int(w.context_lens.sum()),
-            "entry": "paged_attention_prefill_alibi" if args.alibi else "paged_attention_prefill",
+            "entry": ("paged_attention_prefill_step" if fused else
+                      "reshape_and_cache + paged_attention_prefill_alibi" if args.alibi else
+                      "reshape_and_cache + paged_attention_prefill"),
             "partition_size": args.effective_partition,
             "parallelism": "single GPU",
         },

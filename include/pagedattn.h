@@ -424,6 +424,39 @@ int paged_attention_prefill_alibi(void *out, const void *q, const void *k_pool,
                                   const float *alibi_slopes, const pa_prefill_dims *dims);
 
 /*
+ * One chunked-prefill step in one call: the chunk's own K/V rows are written
+ * to their page slots, then the chunk attends over the cache that now holds
+ * them (the new tokens' KV goes to the cache before attention reads it:
+ * tutorial page, section 4.3, step 2 and section 4.2).
+ *
+ * The result -- out and both pools -- is bit for bit that of
+ *   reshape_and_cache(k, v, k_pool, v_pool, slot_mapping, cache dims), then
+ *   paged_attention_prefill(out, q, k_pool, v_pool, block_tables,
+ *                           context_lens, query_start, num_kv_heads, scale,
+ *                           block_size, dims),
+ * with cache dims = {num_tokens = dims->num_tokens, num_kv_heads,
+ * dims->head_dim, block_size, dims->num_blocks, dims->dtype, dims->stream}.
+ * k, v: device [num_tokens, num_kv_heads, head_dim] bf16, 16-byte aligned
+ * (row r is the K/V of q's row r); slot_mapping: device int64 [num_tokens],
+ * 8-byte aligned, as for reshape_and_cache (a negative or out-of-pool slot
+ * writes nothing; two equal slots are a precondition violation).
+ * Everything else, workspace included, is as for paged_attention_prefill;
+ * with num_tokens = 0 nothing is read or written.
+ *
+ * Launches, all on dims->stream: one kernel whose first workgroup writes the
+ * work plan while the others write the chunk's rows (the plan reads only
+ * query_start and context_lens, so the two are independent), then the
+ * attention pass (timing_events bracket this one) and, with a split, the
+ * reduce kernel: one launch fewer than the two calls.  PA_DEBUG_CHECKS=1
+ * checks both calls' device-side preconditions.
+ */
+int paged_attention_prefill_step(void *out, const void *q, const void *k, const void *v,
+                                 const int64_t *slot_mapping, void *k_pool, void *v_pool,
+                                 const int32_t *block_tables, const int32_t *context_lens,
+                                 const int32_t *query_start, int32_t num_kv_heads, float scale,
+                                 int32_t block_size, const pa_prefill_dims *dims);
+
+/*
  * Workspace bytes of paged_attention_prefill, with P the partitions of the
  * capacity (1 without a split):
  *   plan 4 * (4 + 3 * num_tokens * P + num_tokens) rounded up to 256, plus,

@@ -140,6 +140,11 @@ SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
         ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(PrefillDims)]),
+    "paged_attention_prefill_step": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+        ctypes.POINTER(PrefillDims)]),
     "paged_attention_prefill_workspace_bytes": (ctypes.c_size_t, [
         ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(PrefillDims)]),
     "paged_attention_prefill_partition_tokens": (ctypes.c_int32, [

@@ -354,20 +354,12 @@ def paged_attention_prefill_partition_tokens(q: torch.Tensor, k_pool: torch.Tens
     return n
 
 
-def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
-                            v_pool: torch.Tensor, block_tables: torch.Tensor,
-                            context_lens: torch.Tensor, query_start: torch.Tensor,
-                            scale: Optional[float] = None,
-                            workspace: Optional[torch.Tensor] = None, stream=None,
-                            timing_events: Sequence = (None, None),
-                            alibi_slopes: Optional[torch.Tensor] = None,
-                            partition_size: int = 0) -> torch.Tensor:
-    """out[T,H,D] <- multi-token (prefill / chunked prefill) attention over
-    the paged cache (see paged_attention_prefill in include/pagedattn.h);
-    query_start int32 [S + 1] gives each sequence's first row of q.
-    partition_size: keys per split-K partition (0: the library's choice).  A
-    workspace (work plan, split-K partials) is allocated here when none is
-    given."""
+def _prefill_call(entry, out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                  scale, workspace, stream, timing_events, alibi_slopes, partition_size,
+                  new_kv=None):
+    """Marshal paged_attention_prefill, paged_attention_prefill_alibi (with
+    slopes) or, with new_kv = (k, v, slot_mapping),
+    paged_attention_prefill_step."""
     if q.dtype != torch.bfloat16:
         raise ValueError("prefill attention is built for bf16")
     for name, t in (("out", out), ("k_pool", k_pool), ("v_pool", v_pool)):
@@ -387,13 +379,21 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Te
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
     hkv, bs = k_pool.shape[1], k_pool.shape[2]
+    if new_kv is not None:
+        k, v, slot_mapping = new_kv
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise ValueError("k and v must have q's dtype")
+        if k.shape != (T, hkv, D) or v.shape != (T, hkv, D):
+            raise ValueError(f"k and v must be [{T}, {hkv}, {D}] (one row per row of q)")
+        if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+            raise ValueError(f"slot_mapping must be int64 [{T}]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     d = prefill_dims(q, k_pool, block_tables, query_start, partition_size)
     lib = _lib.load()
     need = lib.paged_attention_prefill_workspace_bytes(hkv, bs, ctypes.byref(d))
     if need == _lib.SIZE_MAX:
-        _check(_lib.PA_ERR_SHAPE, "paged_attention_prefill")
+        _check(_lib.PA_ERR_SHAPE, entry)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
@@ -402,21 +402,57 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Te
     d.stream = _stream_ptr(stream)
     d.timing_events[0] = _event_ptr(timing_events[0])
     d.timing_events[1] = _event_ptr(timing_events[1])
+    ptrs = (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+            _dev(query_start, "query_start"), hkv, ctypes.c_float(scale), bs)
+    if new_kv is not None:
+        ptrs = ptrs[:2] + (_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping")) + \
+            ptrs[2:]
     if alibi_slopes is not None:
         _check_slopes(alibi_slopes, H)
-        rc = lib.paged_attention_prefill_alibi(
-            _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
-            _dev(query_start, "query_start"), hkv, ctypes.c_float(scale), bs,
-            _dev(alibi_slopes, "alibi_slopes"), ctypes.byref(d))
-        _check(rc, "paged_attention_prefill_alibi")
-        return out
-    rc = lib.paged_attention_prefill(
-        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
-        _dev(query_start, "query_start"), hkv, ctypes.c_float(scale), bs, ctypes.byref(d))
-    _check(rc, "paged_attention_prefill")
+        rc = getattr(lib, entry)(*ptrs, _dev(alibi_slopes, "alibi_slopes"), ctypes.byref(d))
+    else:
+        rc = getattr(lib, entry)(*ptrs, ctypes.byref(d))
+    _check(rc, entry)
     return out
+
+
+def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                            v_pool: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, query_start: torch.Tensor,
+                            scale: Optional[float] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None,
+                            timing_events: Sequence = (None, None),
+                            alibi_slopes: Optional[torch.Tensor] = None,
+                            partition_size: int = 0) -> torch.Tensor:
+    """out[T,H,D] <- multi-token (prefill / chunked prefill) attention over
+    the paged cache (see paged_attention_prefill in include/pagedattn.h);
+    query_start int32 [S + 1] gives each sequence's first row of q.
+    partition_size: keys per split-K partition (0: the library's choice).  A
+    workspace (work plan, split-K partials) is allocated here when none is
+    given.  With ``alibi_slopes`` (fp32 [H]) the call is
+    paged_attention_prefill_alibi."""
+    entry = "paged_attention_prefill" if alibi_slopes is None else "paged_attention_prefill_alibi"
+    return _prefill_call(entry, out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                         scale, workspace, stream, timing_events, alibi_slopes, partition_size)
+
+
+def paged_attention_prefill_step(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor,
+                                 v: torch.Tensor, slot_mapping: torch.Tensor,
+                                 k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                 block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                 query_start: torch.Tensor, scale: Optional[float] = None,
+                                 workspace: Optional[torch.Tensor] = None, stream=None,
+                                 timing_events: Sequence = (None, None),
+                                 partition_size: int = 0) -> torch.Tensor:
+    """One chunked-prefill step (see paged_attention_prefill_step in
+    include/pagedattn.h): k[r], v[r] ([T, num_kv_heads, head_dim]) to pool
+    slot slot_mapping[r], then out[T,H,D] <- prefill attention over the
+    updated pools; bit for bit reshape_and_cache followed by
+    paged_attention_prefill, in one launch fewer."""
+    return _prefill_call("paged_attention_prefill_step", out, q, k_pool, v_pool, block_tables,
+                         context_lens, query_start, scale, workspace, stream, timing_events,
+                         None, partition_size, new_kv=(k, v, slot_mapping))
 
 
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, k_pool: torch.Tensor,

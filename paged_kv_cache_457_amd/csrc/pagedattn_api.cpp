@@ -312,10 +312,13 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
                 float scale, int32_t block_size, const float *alibi, const pa_decode_dims *dims,
                 bool read_probe = false, Workspace where = Workspace::kCaller,
                 const pa_internal::CacheLaunch *cache = nullptr);
+// cache: the step's chunk rows (paged_attention_prefill_step), written to
+// the pools before the attention; its pointers are already checked.
 int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                  const int32_t *block_tables, const int32_t *context_lens,
                  const int32_t *query_start, int32_t num_kv_heads, float scale,
-                 int32_t block_size, const float *alibi, const pa_prefill_dims *dims);
+                 int32_t block_size, const float *alibi, const pa_prefill_dims *dims,
+                 const pa_internal::CacheLaunch *cache = nullptr);
 
 // The cache write of a decode step's entry (one new token per sequence):
 // checks its pointers and fills c; shape checks are the decode call's.
@@ -646,6 +649,35 @@ int paged_attention_prefill_alibi(void *out, const void *q, const void *k_pool,
                       num_kv_heads, scale, block_size, alibi_slopes, dims);
 }
 
+int paged_attention_prefill_step(void *out, const void *q, const void *k, const void *v,
+                                 const int64_t *slot_mapping, void *k_pool, void *v_pool,
+                                 const int32_t *block_tables, const int32_t *context_lens,
+                                 const int32_t *query_start, int32_t num_kv_heads, float scale,
+                                 int32_t block_size, const pa_prefill_dims *dims) {
+  if (!dims) return PA_ERR_NULL;
+  const int rc = check_prefill_dims(num_kv_heads, block_size, dims);
+  if (rc != PA_OK) return rc;
+  if (dims->num_tokens > 0) {
+    if (!k || !v || !slot_mapping) return PA_ERR_NULL;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8)) return PA_ERR_ALIGN;
+  }
+  pa_internal::CacheLaunch c{};
+  c.k = k;
+  c.v = v;
+  c.k_pool = k_pool;
+  c.v_pool = v_pool;
+  c.slot_mapping = slot_mapping;
+  c.num_tokens = dims->num_tokens;
+  c.num_kv_heads = num_kv_heads;
+  c.head_dim = dims->head_dim;
+  c.block_size = block_size;
+  c.num_blocks = dims->num_blocks;
+  c.elem_bytes = elem_bytes(dims->dtype);
+  c.stream = dims->stream;
+  return prefill_impl(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                      num_kv_heads, scale, block_size, nullptr, dims, &c);
+}
+
 }  // extern "C"
 
 namespace {
@@ -653,7 +685,8 @@ namespace {
 int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                  const int32_t *block_tables, const int32_t *context_lens,
                  const int32_t *query_start, int32_t num_kv_heads, float scale,
-                 int32_t block_size, const float *alibi, const pa_prefill_dims *dims) {
+                 int32_t block_size, const float *alibi, const pa_prefill_dims *dims,
+                 const pa_internal::CacheLaunch *cache) {
   if (!dims) return PA_ERR_NULL;
   int rc = check_prefill_dims(num_kv_heads, block_size, dims);
   if (rc != PA_OK) return rc;
@@ -673,6 +706,9 @@ int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_poo
     if (rc == PA_OK)
       rc = check_tables(block_tables, context_lens, dims->num_seqs, dims->max_blocks_per_seq,
                         dims->num_blocks, block_size, dims->stream);
+    if (rc == PA_OK && cache)
+      rc = check_slots(cache->slot_mapping, cache->num_tokens, dims->num_blocks, block_size,
+                       dims->stream);
     if (rc != PA_OK) return rc;
   }
   const int parts = prefill_max_parts(num_kv_heads, block_size, dims);
@@ -707,7 +743,7 @@ int prefill_impl(void *out, const void *q, const void *k_pool, const void *v_poo
   a.ev_begin = dims->timing_events[0];
   a.ev_end = dims->timing_events[1];
   a.alibi = alibi;
-  return pa_internal::launch_prefill(a);
+  return cache ? pa_internal::launch_prefill_step(a, *cache) : pa_internal::launch_prefill(a);
 }
 
 }  // namespace

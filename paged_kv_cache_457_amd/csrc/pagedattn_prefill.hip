@@ -34,9 +34,11 @@
 // and on valid pages skips the per-key mask.
 #include <type_traits>
 
+#include "pagedattn_cache_row.h"
 #include "pagedattn_device.h"
 #include "pagedattn_internal.h"
 #include "pagedattn_prefill_launch.h"
+#include "pagedattn_step_launch.h"
 #include "pagedattn_timed_launch.h"
 
 namespace {
@@ -115,7 +117,7 @@ __device__ __forceinline__ int swz(int r, int c) {
 // A wave takes one sequence at a time and its lanes the sequence's
 // (block, partition) pairs, so a long chunk over a long context costs a
 // few strided passes rather than one lane's serial loop.
-__global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
+__device__ __forceinline__ void prefill_plan_body(
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
     const int32_t *__restrict__ block_tables, int max_blocks, int num_blocks, int block_size,
     int num_seqs, int num_tokens, int ctx_cap, int tok, int kpart, int max_parts, int max_items,
@@ -230,6 +232,42 @@ __global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
       r[7] = 0;
     });
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void pa_prefill_plan(
+    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
+    const int32_t *__restrict__ block_tables, int max_blocks, int num_blocks, int block_size,
+    int num_seqs, int num_tokens, int ctx_cap, int tok, int kpart, int max_parts, int max_items,
+    int32_t *__restrict__ plan, int32_t *__restrict__ nparts) {
+  prefill_plan_body(context_lens, query_start, block_tables, max_blocks, num_blocks, block_size,
+                    num_seqs, num_tokens, ctx_cap, tok, kpart, max_parts, max_items, plan,
+                    nparts);
+}
+
+// A prefill step's first launch: workgroup 0 writes the plan while the
+// others write the step's chunk rows to the cache, kPlanThreads /
+// kCacheThreads rows each.  The plan reads only context lengths, the chunk
+// bounds and the block table, so the two are independent; the attention
+// kernel, launched after, sees both.
+constexpr int kPrepTokens = kPlanThreads / kCacheThreads;
+
+__global__ __launch_bounds__(kPlanThreads) void pa_prefill_step_prep(
+    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
+    const int32_t *__restrict__ block_tables, int max_blocks, int num_blocks, int block_size,
+    int num_seqs, int num_tokens, int ctx_cap, int tok, int kpart, int max_parts, int max_items,
+    int32_t *__restrict__ plan, int32_t *__restrict__ nparts, const u32x4 *__restrict__ k,
+    const u32x4 *__restrict__ v, u32x4 *__restrict__ k_pool, u32x4 *__restrict__ v_pool,
+    const int64_t *__restrict__ slot_mapping, int num_kv_heads, int row_chunks) {
+  if (blockIdx.x == 0) {
+    prefill_plan_body(context_lens, query_start, block_tables, max_blocks, num_blocks,
+                      block_size, num_seqs, num_tokens, ctx_cap, tok, kpart, max_parts,
+                      max_items, plan, nparts);
+    return;
+  }
+  const int t = (blockIdx.x - 1) * kPrepTokens + threadIdx.x / kCacheThreads;
+  if (t < num_tokens)
+    cache_write_token(t, threadIdx.x % kCacheThreads, k, v, k_pool, v_pool, slot_mapping,
+                      num_kv_heads, row_chunks, block_size, (int64_t)num_blocks * block_size);
 }
 
 // ------------------------------------------------------------- work item
@@ -805,13 +843,30 @@ int by_group(const pa_internal::PrefillLaunch &a) {
 
 namespace pa_internal {
 
-int launch_prefill(const PrefillLaunch &a) {
+namespace {
+
+// The plan launch of a prefill call, or with a cache write (cache not
+// null), the step's preparation kernel that does both.
+int run_prefill(const PrefillLaunch &a, const CacheLaunch *cache) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  hipLaunchKernelGGL(pa_prefill_plan, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens,
-                     a.query_start, a.block_tables, a.max_blocks, a.num_blocks, a.block_size,
-                     a.num_seqs, a.num_tokens, a.max_blocks * a.block_size,
-                     kPrefillRows / (a.num_heads / a.num_kv_heads), a.part_tokens, a.max_parts,
-                     a.num_tokens * a.max_parts, a.plan, a.nparts);
+  const int tok = kPrefillRows / (a.num_heads / a.num_kv_heads);
+  if (cache) {
+    const unsigned grid = 1 + (unsigned)((a.num_tokens + kPrepTokens - 1) / kPrepTokens);
+    hipLaunchKernelGGL(pa_prefill_step_prep, dim3(grid), dim3(kPlanThreads), 0, st,
+                       a.context_lens, a.query_start, a.block_tables, a.max_blocks,
+                       a.num_blocks, a.block_size, a.num_seqs, a.num_tokens,
+                       a.max_blocks * a.block_size, tok, a.part_tokens, a.max_parts,
+                       a.num_tokens * a.max_parts, a.plan, a.nparts,
+                       static_cast<const u32x4 *>(cache->k), static_cast<const u32x4 *>(cache->v),
+                       static_cast<u32x4 *>(cache->k_pool), static_cast<u32x4 *>(cache->v_pool),
+                       cache->slot_mapping, cache->num_kv_heads,
+                       a.head_dim * cache->elem_bytes / 16);
+  } else {
+    hipLaunchKernelGGL(pa_prefill_plan, dim3(1), dim3(kPlanThreads), 0, st, a.context_lens,
+                       a.query_start, a.block_tables, a.max_blocks, a.num_blocks, a.block_size,
+                       a.num_seqs, a.num_tokens, a.max_blocks * a.block_size, tok,
+                       a.part_tokens, a.max_parts, a.num_tokens * a.max_parts, a.plan, a.nparts);
+  }
   if (hipGetLastError() != hipSuccess) return 6;
   // the attention kernel's launch records the timing events, if any
   int rc;
@@ -828,6 +883,14 @@ int launch_prefill(const PrefillLaunch &a) {
     if (hipGetLastError() != hipSuccess) return 6;
   }
   return 0;
+}
+
+}  // namespace
+
+int launch_prefill(const PrefillLaunch &a) { return run_prefill(a, nullptr); }
+
+int launch_prefill_step(const PrefillLaunch &a, const CacheLaunch &cache) {
+  return run_prefill(a, &cache);
 }
 
 }  // namespace pa_internal

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "pagedattn_internal.h"
+#include "pagedattn_prefill_launch.h"
 
 namespace pa_internal {
 
@@ -16,5 +17,9 @@ int launch_decode_step(const DecodeLaunch &a, const CacheLaunch &cache);
 int launch_shared_prefix_step(const PrefixLaunch &p, const CacheLaunch &cache);
 // The shared-prefix plan alone (cache null) or with the step's cache write.
 int launch_prefix_prep(const PrefixLaunch &p, const CacheLaunch *cache);
+// A prefill step: the chunk rows to the cache and the prefill plan in one
+// launch, then the attention (and reduce) kernels; cache.num_tokens is the
+// call's num_tokens.
+int launch_prefill_step(const PrefillLaunch &a, const CacheLaunch &cache);
 
 }  // namespace pa_internal

@@ -515,6 +515,37 @@ expect("shared step fp32 unsupported", shared_step(dims(**ONE, dtype=_lib.PA_DTY
        _lib.PA_ERR_UNSUPPORTED)
 expect("shared step without workspace", shared_step(dims(**ONE)), _lib.PA_ERR_WORKSPACE)
 
+# ---- prefill step: pointers out, q, k, v, slot_mapping, k_pool, v_pool,
+# block_tables, context_lens, query_start
+def prefill_step(d, hkv=8, scale=0.088, ptrs=None):
+    p = ptrs or [P] * 10
+    return lib.paged_attention_prefill_step(*p, hkv, ctypes.c_float(scale), 16, ctypes.byref(d))
+
+
+expect("prefill step dims NULL", lib.paged_attention_prefill_step(
+    *([P] * 10), 8, ctypes.c_float(1), 16, None), _lib.PA_ERR_NULL)
+expect("prefill step empty step accepts NULL pointers",
+       prefill_step(pdims(), ptrs=[None] * 10), _lib.PA_OK)
+for i in range(10):
+    ptrs = [P] * 10
+    ptrs[i] = None
+    expect(f"prefill step pointer {i} NULL", prefill_step(pdims(**ROWS), ptrs=ptrs),
+           _lib.PA_ERR_NULL)
+for i in (2, 3):
+    ptrs = [P] * 10
+    ptrs[i] = MIS
+    expect(f"prefill step pointer {i} misaligned", prefill_step(pdims(**ROWS), ptrs=ptrs),
+           _lib.PA_ERR_ALIGN)
+ptrs = [P] * 10
+ptrs[4] = P + 4
+expect("prefill step slot_mapping misaligned", prefill_step(pdims(**ROWS), ptrs=ptrs),
+       _lib.PA_ERR_ALIGN)
+expect("prefill step fp32 unsupported", prefill_step(pdims(dtype=_lib.PA_DTYPE_F32, **ROWS)),
+       _lib.PA_ERR_UNSUPPORTED)
+expect("prefill step NaN scale", prefill_step(pdims(**ROWS), scale=float("nan")),
+       _lib.PA_ERR_SHAPE)
+expect("prefill step without workspace", prefill_step(pdims(**ROWS)), _lib.PA_ERR_WORKSPACE)
+
 # ---- probe
 expect("probe NULL buffer", lib.pa_hbm_read_probe(None, 1024, P, None), _lib.PA_ERR_NULL)
 expect("probe size not a multiple of 16", lib.pa_hbm_read_probe(P, 1000, P, None), _lib.PA_ERR_SHAPE)

@@ -103,6 +103,11 @@ def run(lib, expect):
         lo, hi = _span(lib)
         expect(f"prefill {sh}: launched", rc, _lib.PA_OK)
         expect(f"prefill {sh}: inside {need} B", P <= lo and hi <= P + need, True)
+        rc = lib.paged_attention_prefill_step(P, P, P, P, P, P, P, P, P, P, 8,
+                                              ctypes.c_float(0.1), 16, ctypes.byref(d))
+        lo, hi = _span(lib)
+        expect(f"prefill step {sh}: launched", rc, _lib.PA_OK)
+        expect(f"prefill step {sh}: inside {need} B", P <= lo and hi <= P + need, True)
 
     # ---- PA_DEBUG_CHECKS=1 on host-resident tables
     bs, mb, nb = 16, 4, 10
@@ -228,6 +233,32 @@ def run(lib, expect):
            (_lib.PA_ERR_PRECONDITION, 0))
     expect("debug: query_start not ending at num_tokens", prefill_with([0, 5, 11]),
            (_lib.PA_ERR_PRECONDITION, 0))
+
+    # prefill step: the query_start, table and slot checks of both calls
+    def prefill_step_with(qs, slots):
+        bt, bt_p = _arr(ctypes.c_int32, tables)
+        cl, cl_p = _arr(ctypes.c_int32, ctx)
+        q, q_p = _arr(ctypes.c_int32, qs)
+        sl, sl_p = _arr(ctypes.c_int64, slots)
+        d = _lib.PrefillDims()
+        d.num_seqs, d.num_tokens, d.num_heads, d.head_dim = 2, len(slots), 8, 128
+        d.max_blocks_per_seq, d.num_blocks, d.dtype = mb, nb, _lib.PA_DTYPE_BF16
+        d.workspace, d.workspace_bytes = P, 1 << 20
+        n0 = launches()
+        rc = lib.paged_attention_prefill_step(P, P, P, P, sl_p, P, P, bt_p, cl_p, q_p, 4,
+                                              ctypes.c_float(0.1), bs, ctypes.byref(d))
+        return rc, launches() - n0
+
+    ok_slots = list(range(20, 23)) + list(range(40, 49))
+    expect("debug prefill step: valid launches once", prefill_step_with([0, 3, 12], ok_slots),
+           (_lib.PA_OK, 1))
+    expect("debug prefill step: duplicate slot",
+           prefill_step_with([0, 3, 12], ok_slots[:-1] + [20]), (_lib.PA_ERR_PRECONDITION, 0))
+    expect("debug prefill step: slot past the pool",
+           prefill_step_with([0, 3, 12], ok_slots[:-1] + [nb * bs]),
+           (_lib.PA_ERR_PRECONDITION, 0))
+    expect("debug prefill step: bad query_start",
+           prefill_step_with([0, 13, 12], ok_slots), (_lib.PA_ERR_PRECONDITION, 0))
 
     # page copies
     def copy_with(pairs, same_pool):

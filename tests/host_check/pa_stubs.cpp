@@ -69,6 +69,9 @@ int launch_prefill(const PrefillLaunch &a) {
   if (a.ws_ml) span(a.ws_ml, rows * 2 * sizeof(float));
   return 0;
 }
+int launch_prefill_step(const PrefillLaunch &a, const CacheLaunch &) {
+  return launch_prefill(a);
+}
 int launch_reshape_and_cache(const CacheLaunch &) { return ++g_launches, 0; }
 int launch_reshape_and_cache_rope(const RopeLaunch &) { return ++g_launches, 0; }
 int launch_copy_pages(const CopyLaunch &) { return ++g_launches, 0; }

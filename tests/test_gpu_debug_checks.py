@@ -142,3 +142,44 @@ def test_debug_checks_on_the_step_entry(debug_checks):
     d.block_tables[1, 4] = w.num_blocks
     assert _rejected(lambda: step(d))
     assert bool((d.out == 3.0).all())
+
+
+def test_debug_checks_on_the_prefill_step_entry(debug_checks):
+    """paged_attention_prefill_step checks both calls' preconditions: a
+    valid step gives the bits of the unchecked step; a duplicate slot or a
+    query_start that does not end at the row count is refused with nothing
+    written."""
+    new = np.array([3, 40, 1, 17])
+    w = build_workload("dbgp", np.array([10, 60, 1, 200]) + new, 8, 2, 128, 16, "bf16", seed=9,
+                       new_tokens=new)
+
+    def step(dw):
+        binding.paged_attention_prefill_step(dw.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping,
+                                             dw.k_pool, dw.v_pool, dw.block_tables,
+                                             dw.context_lens, dw.query_start,
+                                             scale=float(w.scale))
+        torch.cuda.synchronize()
+
+    a = upload(w)
+    step(a)
+    os.environ.pop("PA_DEBUG_CHECKS")
+    b = upload(w)
+    step(b)
+    os.environ["PA_DEBUG_CHECKS"] = "1"
+    assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+    assert torch.equal(a.k_pool.view(torch.int16), b.k_pool.view(torch.int16))
+
+    c = upload(w)
+    c.out.fill_(3.0)
+    pool_before = c.k_pool.clone()
+    c.slot_mapping[5] = c.slot_mapping[0]
+    assert _rejected(lambda: step(c))
+    assert torch.equal(c.k_pool.view(torch.int16), pool_before.view(torch.int16))
+    assert bool((c.out == 3.0).all())
+
+    d = upload(w)
+    d.out.fill_(3.0)
+    d.query_start[2] = d.query_start[3] + 1  # decreasing bounds
+    assert _rejected(lambda: step(d))
+    assert torch.equal(d.k_pool.view(torch.int16), pool_before.view(torch.int16))
+    assert bool((d.out == 3.0).all())

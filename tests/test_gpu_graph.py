@@ -4,8 +4,8 @@ and records no memset, so a captured step must give the eager result bit
 for bit on every replay.  Between replays the test does its own eager work
 (poisoning the output, a cache write, a synchronization), and checks each
 replay.  Covers plain decode with a split-K reduce, the shared-prefix entry,
-both step entries (cache write and plan in one launch), prefill with a
-split-K reduce, and the fused RoPE cache write.
+the three step entries (cache write and plan in one launch), prefill with
+a split-K reduce, and the fused RoPE cache write.
 """
 import numpy as np
 import pytest
@@ -156,6 +156,27 @@ def test_prefill_split_step_replays_bitwise():
     torch.cuda.synchronize()
     ref = dw.out.clone()
     say("p4 split-K prefill: eager reference taken; capturing")
+    check_replays(capture(step), dw.out, ref)
+
+
+def test_fused_prefill_step_replays_bitwise():
+    """paged_attention_prefill_step (chunk rows and plan in one launch) with
+    the default split-K over long contexts, captured and replayed."""
+    w = make_prefill_config(4)
+    dw = upload(w)
+    ws = torch.empty(binding.paged_attention_prefill_workspace_bytes(
+        dw.q, dw.k_pool, dw.block_tables, dw.query_start), dtype=torch.uint8, device="cuda")
+
+    def step():
+        binding.paged_attention_prefill_step(dw.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping,
+                                             dw.k_pool, dw.v_pool, dw.block_tables,
+                                             dw.context_lens, dw.query_start,
+                                             scale=float(w.scale), workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = dw.out.clone()
+    say("p4 fused prefill step: eager reference taken; capturing")
     check_replays(capture(step), dw.out, ref)
 
 

@@ -1,6 +1,8 @@
-"""The fused decode step (paged_attention_decode_step) against the two calls
-it stands for -- reshape_and_cache, then paged_attention_decode -- through
-the C ABI.
+"""The fused step entries against the two calls each stands for, through the
+C ABI: paged_attention_decode_step (reshape_and_cache, then
+paged_attention_decode), the shared-prefix step, and
+paged_attention_prefill_step (reshape_and_cache of the chunk rows, then
+paged_attention_prefill).
 
 Bar: bit for bit, the output and both pools, on every decode kernel form
 (the VALU kernel with and without split-K, the grouped-query kernel in its
@@ -14,7 +16,7 @@ import torch
 import oracle
 from paged_kv_cache_457_amd import binding
 from paged_kv_cache_457_amd.device_inputs import to_host, upload
-from paged_kv_cache_457_amd.workloads import make_config
+from paged_kv_cache_457_amd.workloads import build_workload, make_config, make_prefill_config
 
 pytestmark = pytest.mark.gpu
 
@@ -130,3 +132,98 @@ def test_shared_prefix_step_is_the_two_calls_bit_for_bit(ps):
             b.out, b.q, b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool, b.block_tables,
             b.context_lens, gs, pl, scale=float(w.scale), partition_size=ps)
         compare(a, b)
+
+
+# ------------------------------------------------------------- prefill
+def prefill_two_calls(dw, ps):
+    binding.reshape_and_cache(dw.k_new, dw.v_new, dw.k_pool, dw.v_pool, dw.slot_mapping)
+    binding.paged_attention_prefill(dw.out, dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
+                                    dw.context_lens, dw.query_start, scale=float(dw.w.scale),
+                                    partition_size=ps)
+
+
+def prefill_one_step(dw, ps):
+    binding.paged_attention_prefill_step(dw.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping,
+                                         dw.k_pool, dw.v_pool, dw.block_tables, dw.context_lens,
+                                         dw.query_start, scale=float(dw.w.scale),
+                                         partition_size=ps)
+
+
+def prefill_pair(w, ps, twice=True):
+    a, b = upload(w), upload(w)
+    prefill_two_calls(a, ps)
+    prefill_one_step(b, ps)
+    compare(a, b)
+    if twice:
+        prefill_two_calls(a, ps)
+        prefill_one_step(b, ps)
+        compare(a, b)
+
+
+# (configuration, partition tokens): p1 tiny; p2 and p3 unsplit; p3 split at
+# 128 keys; p4 with the default split over long cached contexts
+PREFILL_CASES = [(1, 0), (1, 128), (2, 0), (3, 0), (3, 128), (4, 0)]
+
+
+@pytest.mark.parametrize("idx,ps", PREFILL_CASES)
+def test_prefill_step_is_the_two_calls_bit_for_bit(idx, ps):
+    w = make_prefill_config(idx)
+    assert w.k_new.shape[0] == w.num_tokens
+    say(f"prefill step p{idx} partition {ps}: T={w.num_tokens} S={w.num_seqs} "
+        f"H={w.num_heads}/{w.num_kv_heads} D={w.head_dim}")
+    prefill_pair(w, ps)
+
+
+SHAPES = [(64, 16, 1), (64, 32, 8), (128, 32, 2), (128, 16, 4)]
+
+
+@pytest.mark.parametrize("D,bs,G", SHAPES, ids=[f"D{a}-bs{b}-G{c}" for a, b, c in SHAPES])
+def test_prefill_step_shapes(D, bs, G):
+    # chunks after nothing, a partial page and several tiles, one single row
+    cached = np.array([0, 70, 5, 131])
+    new = np.array([150, 37, 200, 1])
+    w = build_workload(f"sv{D}-{bs}-{G}", cached + new, 2 * G, 2, D, bs, "bf16",
+                       seed=D + bs + G, new_tokens=new)
+    say(f"prefill step D{D} bs{bs} G{G}: T={w.num_tokens}")
+    prefill_pair(w, 0, twice=False)
+
+
+def test_prefill_step_skips_negative_and_out_of_pool_slots():
+    w = make_prefill_config(1)
+    a, b = upload(w), upload(w)
+    for dw in (a, b):
+        dw.slot_mapping[2] = -1
+        dw.slot_mapping[7] = w.k_pool.shape[0] * w.block_size  # first slot past the pool
+    prefill_two_calls(a, 0)
+    prefill_one_step(b, 0)
+    compare(a, b)
+
+
+def test_prefill_step_against_the_oracle():
+    w = make_prefill_config(1)
+    dw = upload(w)
+    prefill_one_step(dw, 0)
+    torch.cuda.synchronize()
+    kp, vp = oracle.reshape_and_cache(w.k_new, w.v_new, w.k_pool, w.v_pool, w.slot_mapping,
+                                      w.block_size)
+    assert to_host(dw.k_pool, w.dtype).tobytes() == kp.tobytes()
+    assert to_host(dw.v_pool, w.dtype).tobytes() == vp.tobytes()
+    ref = oracle.prefill(w.q, kp, vp, w.block_tables, w.context_lens, w.query_start,
+                         w.num_kv_heads, w.scale, w.block_size, w.dtype)
+    err = float(np.max(np.abs(oracle.widen(to_host(dw.out, w.dtype), w.dtype) - ref)))
+    say(f"prefill step p1: max abs err {err:.3e} (tolerance {TOL[w.dtype]})")
+    assert err <= TOL[w.dtype]
+
+
+def test_prefill_step_empty_is_a_noop():
+    w = make_prefill_config(1)
+    dw = upload(w)
+    before = bits(dw.k_pool).clone()
+    empty = dw.q[:0]
+    kv = dw.k_new[:0]
+    qs = torch.zeros(w.num_seqs + 1, dtype=torch.int32, device="cuda")
+    binding.paged_attention_prefill_step(dw.out[:0], empty, kv, kv, dw.slot_mapping[:0],
+                                         dw.k_pool, dw.v_pool, dw.block_tables,
+                                         dw.context_lens, qs)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(dw.k_pool), before)
