@@ -206,12 +206,22 @@ __device__ __forceinline__ void prefill_plan_body(
   for (int s = wave; s < num_seqs; s += kPlanWaves) {
     int a, n, p0;
     chunk(s, a, n, p0);
-    // first page of the sequence's keys whose id lies outside the pool
+    // first page of the sequence's keys whose id lies outside the pool; a
+    // long table is read kScanBatch loads a lane at a time, all in flight
+    // together
+    constexpr int kScanBatch = 8;
     const int npg = (max(0, p0 + n) + block_size - 1) / block_size;
+    const int32_t *row = block_tables + (size_t)s * max_blocks;
     int first_bad = 0x7fffffff;
-    for (int p = lane; p < npg; p += 64)
-      if ((unsigned)block_tables[(size_t)s * max_blocks + p] >= (unsigned)num_blocks)
-        first_bad = min(first_bad, p);
+    for (int pb = lane; pb < npg; pb += 64 * kScanBatch) {
+      int id[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) id[u] = pb + 64 * u < npg ? row[pb + 64 * u] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u)
+        if (pb + 64 * u < npg && (unsigned)id[u] >= (unsigned)num_blocks)
+          first_bad = min(first_bad, pb + 64 * u);
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) first_bad = min(first_bad, __shfl_xor(first_bad, o));
     items_of(s, [&](int t0, int kp, int ke) {
@@ -725,7 +735,26 @@ __device__ __forceinline__ void prefill_item(
 // Merge of the key partitions of the rows whose block was split: one wave
 // per (row, query head), out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
 // Lanes hold the partitions' (m, l) 64 at a time; each partition's weight
-// is then broadcast while the lanes stream its D accumulator values.
+// is then broadcast while the lanes stream its D accumulator values.  With
+// at most kReduceBatch partitions a lane loads its values of every
+// partition, and the statistics, before using any of them, so the wave
+// waits on memory once; the sums are taken in the same order either way.
+constexpr int kReduceBatch = 16;
+
+// A merged row: acc / L in bf16 (zeros where no key was seen).
+template <int D>
+__device__ __forceinline__ void store_row(void *out, long long rh, int lane,
+                                          const float (&acc)[D / 64], float L) {
+  constexpr int DPL = D / 64;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t *dst = reinterpret_cast<uint16_t *>(out) + rh * D + lane * DPL;
+  if constexpr (DPL == 2)
+    *reinterpret_cast<uint32_t *>(dst) =
+        BF16::round_bits(acc[0] * inv) | (BF16::round_bits(acc[1] * inv) << 16);
+  else
+    dst[0] = (uint16_t)BF16::round_bits(acc[0] * inv);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void pa_prefill_reduce(
     void *__restrict__ out, const float *__restrict__ ws_ml, const float *__restrict__ ws_acc,
@@ -738,10 +767,37 @@ __global__ __launch_bounds__(256) void pa_prefill_reduce(
   const int np = min(nparts[rh / num_heads], max_parts);
   if (np <= 1) return;  // written by its item
   const float2 *ml = reinterpret_cast<const float2 *>(ws_ml) + rh * max_parts;
+  float acc[DPL] = {}, L = 0.f;
+  if (np <= kReduceBatch) {
+    const float *a = ws_acc + rh * max_parts * D + lane * DPL;
+    const float2 st = lane < np ? ml[lane] : make_float2(-INFINITY, 0.f);
+    Vec v[kReduceBatch];
+#pragma unroll
+    for (int p = 0; p < kReduceBatch; ++p)
+      if (p < np) v[p] = *reinterpret_cast<const Vec *>(a + (size_t)p * D);
+    const float M = wave_max(st.x);
+    if (M != -INFINITY) {
+      const float w = lane < np ? fast_exp2(st.x - M) : 0.f;
+      L = wave_sum(lane < np ? fmaf(st.y, w, 0.f) : 0.f);
+#pragma unroll
+      for (int p = 0; p < kReduceBatch; ++p) {
+        if (p < np) {
+          const float wq = __shfl(w, p);
+          if constexpr (DPL == 2) {
+            acc[0] = fmaf(v[p].x, wq, acc[0]);
+            acc[1] = fmaf(v[p].y, wq, acc[1]);
+          } else {
+            acc[0] = fmaf(v[p], wq, acc[0]);
+          }
+        }
+      }
+    }
+    store_row<D>(out, rh, lane, acc, L);
+    return;
+  }
   float M = -INFINITY;
   for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[p].x);
   M = wave_max(M);
-  float acc[DPL] = {}, L = 0.f;
   if (M != -INFINITY) {
     const float *a = ws_acc + rh * max_parts * D + lane * DPL;
     for (int p0 = 0; p0 < np; p0 += 64) {
@@ -766,13 +822,7 @@ __global__ __launch_bounds__(256) void pa_prefill_reduce(
     }
     L = wave_sum(L);
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t *dst = reinterpret_cast<uint16_t *>(out) + rh * D + lane * DPL;
-  if constexpr (DPL == 2)
-    *reinterpret_cast<uint32_t *>(dst) =
-        BF16::round_bits(acc[0] * inv) | (BF16::round_bits(acc[1] * inv) << 16);
-  else
-    dst[0] = (uint16_t)BF16::round_bits(acc[0] * inv);
+  store_row<D>(out, rh, lane, acc, L);
 }
 
 template <int D, int BS, int G, bool AL>
