@@ -6,6 +6,8 @@ edges, and random lengths) and its key partition from one fixed seed, and
 prints them before it runs.  The step goes through the fused step entry.
 The pools must match the oracle's cache write bit for bit, and the output
 must match the oracle's attention within 1e-5 (fp32 KV) or 1e-2 (bf16 KV).
+bf16 decode outputs must also lie within one bf16 ulp of the oracle plus
+the fp32 error bound of tests/_bounds.py, element by element.
 Sizes are small so that the fp64 oracle finishes each case in well under
 a second.
 """
@@ -13,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import _bounds
 import oracle
 from paged_kv_cache_457_amd import binding
 from paged_kv_cache_457_amd.device_inputs import to_host, upload
@@ -85,6 +88,19 @@ def test_decode_step_random(i):
     err = err_of(dw, ref, w.dtype)
     say(f"  max abs err {err:.3e}")
     assert err <= TOL[w.dtype]
+    if w.dtype != "bf16" or not np.any(w.context_lens > 0):
+        return
+    part = binding.paged_attention_decode_partition_tokens(dw.q, dw.k_pool, dw.block_tables,
+                                                           c["ps"])
+    delta = _bounds.fp32_delta(
+        m_v=_bounds.max_abs_live(vp, w.dtype),
+        a_dot=_bounds.max_abs_dot(w.q, kp, w.block_tables, w.context_lens, w.num_kv_heads,
+                                  w.block_size, w.dtype),
+        scale=float(w.scale), head_dim=w.head_dim, part_tokens=part,
+        parts=-(-w.max_blocks_per_seq * w.block_size // part), matrix_cores=w.group >= 2)
+    ratio, at = _bounds.check_ulp_bound(to_host(dw.out, w.dtype), ref, delta)
+    say(f"  delta {delta:.3e}; worst |err| / (ulp(|ref|) + delta) = {ratio:.3f}")
+    assert ratio <= 1.0
 
 
 # ----------------------------------------------------------- shared prefix
